@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark: batched paged-KV MLA decode (absorbed form) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload deepseek]
+
+A step is one pass of the whole decode path (fused decode kernel + split
+merge) over one batch.  The timed region runs K steps back to back; every step
+reads a different copy ("layer") of the KV cache and query, cycling over
+enough copies to exceed the 256 MB last-level cache, so KV bytes come from HBM
+as they would across the layers of a real model.  Inputs are seeded synthetic
+bf16 (N(0,1)*0.5) with the workload's shapes; they are resident in HBM before
+the timed region starts.  Prints one JSON line.
+
+Roofline of the dominant kernel (the fused decode kernel): algorithmic bytes
+per launch = 1152 B per attended KV token + query (1152 B per head) + output
+(1024 B + 4 B lse per head) + page-table bytes, divided by the kernel's mean
+duration from HIP events recorded around that kernel during the timed region.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2516.6    # MI355X dense bf16 MFMA, TFLOP/s (256 CU x 4096 flop/clk x 2.4 GHz)
+MALL_BYTES = 256 << 20
+
+WORKLOAD_DESC = {
+    "deepseek": "DeepSeek-V3-shaped decode: batch 64, 128 heads, kv_lora_rank 512, rope 64, "
+                "page_size 64, kv_len uniform [1024,4096], random page table",
+    "long": "long-context split-KV: batch 8, 128 heads, 512/64, page_size 64, kv_len 32768",
+    "ragged": "ragged decode (16-head share of a 128-head model): batch 256, 16 heads, 512/64, "
+              "page_size 1, kv_len lognormal(median 1024, sigma 1) clipped [1,16384]",
+    "cascade": "cascade shared-prefix decode: batch 128, 128 heads, 512/64, page_size 64, "
+               "8192-token shared prefix + suffix uniform [64,1024]",
+    "tiny": "tiny decode: batch 4, 16 heads, 512/64, page_size 16, kv_len {1,17,64,200}",
+}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "paged_kv_mla_amd", "csrc"))):
+        with open(os.path.join(ROOT, "paged_kv_mla_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def workload_counts(inp):
+    """Attended tokens, unique KV rows and algorithmic bytes/flops of one step."""
+    H = inp.num_heads
+    B = inp.batch
+    if hasattr(inp, "prefix_lens"):
+        attended = inp.attended_tokens()
+        unique = inp.unique_tokens()
+        idx_bytes = 4 * (len(inp.prefix_indices) + len(inp.kv_indices)) + 8 * B
+    else:
+        attended = unique = inp.total_tokens
+        idx_bytes = 4 * len(inp.kv_indices) + 8 * B
+    alg_bytes = unique * 1152 + idx_bytes + B * H * (1152 + 1024 + 4)
+    alg_flops = 2176.0 * H * attended
+    return attended, unique, alg_bytes, alg_flops
+
+
+def cpu_baseline(inp, budget_s: float = 12.0):
+    """Time the fp64 oracle on the host (a reported baseline, not a target)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    is_cas = hasattr(inp, "prefix_lens")
+    done_tokens = 0
+    reqs = 0
+    t0 = time.perf_counter()
+    b = 0
+    while True:
+        sl = slice(b, b + 1)
+        if is_cas:
+            g = inp.group_of(b)
+            oracle.attend_cascade(
+                inp.q_nope[sl], inp.q_pe[sl], inp.ckv, inp.kpe, inp.page_size,
+                np.array([0, 1], np.int32),
+                np.array([0, inp.prefix_indptr[g + 1] - inp.prefix_indptr[g]], np.int32),
+                inp.prefix_indices[inp.prefix_indptr[g]:inp.prefix_indptr[g + 1]],
+                inp.prefix_lens[g:g + 1],
+                np.array([0, inp.kv_indptr[b + 1] - inp.kv_indptr[b]], np.int32),
+                inp.kv_indices[inp.kv_indptr[b]:inp.kv_indptr[b + 1]], inp.kv_lens[sl])
+            done_tokens += int(inp.prefix_lens[g]) + int(inp.kv_lens[b])
+        else:
+            ip = np.array([0, inp.kv_indptr[b + 1] - inp.kv_indptr[b]], np.int32)
+            oracle.attend_flat(inp.q_nope[sl], inp.q_pe[sl], inp.ckv, inp.kpe, ip,
+                               inp.kv_indices[inp.kv_indptr[b]:inp.kv_indptr[b + 1]],
+                               inp.kv_lens[sl], inp.page_size, sm_scale=inp.sm_scale)
+            done_tokens += int(inp.kv_lens[b])
+        reqs += 1
+        b = (b + 1) % inp.batch
+        el = time.perf_counter() - t0
+        if el >= budget_s or reqs >= 64 * inp.batch:
+            break
+    return {"value": done_tokens / el, "unit": "KV-tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{reqs} requests of the same workload in order (cycling), fp64 numpy, "
+                      f"{el:.1f} s wall"}
+
+
+def load_traffic(workload: str, launches_tokens: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_decode_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="deepseek", choices=sorted(WORKLOAD_DESC))
+    ap.add_argument("--layers", type=int, default=0,
+                    help="KV copies cycled over (0: enough to exceed the last-level cache)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (for HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 3}))
+        return
+
+    import paged_kv_mla_amd as pk
+    from mla_workloads import make_config
+
+    t0 = time.perf_counter()
+    inp = make_config(args.workload)
+    gen_s = time.perf_counter() - t0
+    attended, unique, alg_bytes, alg_flops = workload_counts(inp)
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda")
+
+    pool_bytes = inp.ckv.nbytes + inp.kpe.nbytes
+    layers = args.layers or max(2, math.ceil(3 * MALL_BYTES / pool_bytes))
+    ckv0, kpe0 = dev(inp.ckv), dev(inp.kpe)
+    qn0, qp0 = dev(inp.q_nope), dev(inp.q_pe)
+    ckvs = [ckv0] + [ckv0.clone() for _ in range(layers - 1)]
+    kpes = [kpe0] + [kpe0.clone() for _ in range(layers - 1)]
+    qns = [qn0] + [qn0.clone() for _ in range(layers - 1)]
+    qps = [qp0] + [qp0.clone() for _ in range(layers - 1)]
+    B, H = inp.batch, inp.num_heads
+    outs = [torch.empty((B, H, 512), dtype=torch.bfloat16, device="cuda") for _ in range(layers)]
+    lses = [torch.empty((B, H), dtype=torch.float32, device="cuda") for _ in range(layers)]
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    plan = pk.plan_for(inp)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+
+    stream = torch.cuda.current_stream()
+    sh = int(stream.cuda_stream)
+
+    def step(i):
+        k = i % layers
+        plan.run_ptrs(qns[k].data_ptr(), qps[k].data_ptr(), ckvs[k].data_ptr(),
+                      kpes[k].data_ptr(), outs[k].data_ptr(), lses[k].data_ptr(), sh)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    plan.set_timing(True)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    kern_ms, kern_n = plan.kernel_timing()
+    plan.set_timing(False)
+    ms_per_step = total_ms / args.steps
+    kern_avg_ms = kern_ms / max(kern_n, 1)
+
+    value = attended / (ms_per_step * 1e-3)
+    tflops = alg_flops / (ms_per_step * 1e-3) / 1e12
+    # binding roof of the whole step
+    t_hbm = alg_bytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = alg_flops / (MFMA_BF16_PEAK_TFS * 1e12)
+    step_bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    # dominant kernel roofline
+    if step_bound == "hbm":
+        achieved = alg_bytes / (kern_avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = alg_flops / (kern_avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4)}
+    roof["traffic"] = load_traffic(args.workload, attended)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, args.cpu_budget)
+
+    line = {
+        "metric": "MLA paged decode KV-tokens/s (absorbed form), 1 MI355X",
+        "value": round(value, 1),
+        "unit": "KV-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_DESC[args.workload], "batch": B, "num_heads": H,
+                   "page_size": inp.page_size, "attended_kv_tokens": attended,
+                   "unique_kv_tokens": unique, "kv_copies_cycled": layers},
+        "tflops": round(tflops, 2),
+        "step_roofline_frac": round(max(t_hbm, t_mfma) / (ms_per_step * 1e-3), 4),
+        "decode_kernel_ms": round(kern_avg_ms, 5),
+        "alg_bytes_per_step": int(alg_bytes),
+        "alg_flops_per_step": alg_flops,
+        "plan_host_ms": round(plan_ms, 2),
+        "input_gen_s": round(gen_s, 1),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

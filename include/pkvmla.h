@@ -1,0 +1,169 @@
+/*
+ * pkvmla.h -- batched paged-KV Multi-head Latent Attention decode, absorbed
+ * form, for AMD Instinct MI355X (gfx950).  Plain C ABI: no HIP, no torch types.
+ *
+ * What is computed.  Every request b has one query token with H heads.  All
+ * heads share one compressed KV "head" per token: a ckv row of
+ * head_dim_ckv = kv_lora_rank (512) values and a kpe row of
+ * head_dim_kpe = qk_rope_head_dim (64) values (vLLM-metax pull request
+ * "[WIP] support flashinfer_mla", review of the decode_wrapper.plan call).
+ * For each head h and each of the kv_len[b] tokens t of request b:
+ *     s_t    = sm_scale * (q_nope[b,h] . ckv_t + q_pe[b,h] . kpe_t)
+ *     out    = sum_t softmax(s)_t * ckv_t                 (bf16, fp32 accumulation)
+ *     lse    = ln sum_t exp(s_t)                          (fp32, natural log)
+ * Attention is not causal (the same review sets causal=False) and the default
+ * scale is 1/sqrt(ckv_dim + kpe_dim).
+ *
+ * Paged cache.  Token t of request b is stored in page
+ * kv_indices[kv_indptr[b] + t / page_size] at slot t % page_size.  The
+ * descriptors follow the same pull request's metadata review: an indptr of
+ * batch+1 entries and a per-request length array of batch entries, both host
+ * arrays; there is no last_page_len for MLA.  Slots past kv_len and pages no
+ * request lists are never read.
+ *
+ * Cascade.  A two-level plan attends each request to a prefix page list shared
+ * by its group, then to its own suffix pages, and merges the two states by
+ * log-sum-exp; the result equals flat attention over prefix-then-suffix tokens
+ * (vLLM pull request "[V1][Core] FlashInfer attention backend for V1", which
+ * requires cascade and normal attention to agree, with KV dtype = query dtype).
+ *
+ * Device tensor layouts (all contiguous, row-major, bf16 unless noted):
+ *     q_nope    [batch, num_heads, 512]
+ *     q_pe      [batch, num_heads, 64]
+ *     ckv_cache [num_pages, page_size, 512]
+ *     kpe_cache [num_pages, page_size, 64]
+ *     out       [batch, num_heads, 512]
+ *     lse       [batch, num_heads]            float32
+ * Device pointers must be 16-byte aligned.
+ *
+ * Errors.  Every call returns a pkvmla_status; on failure
+ * pkvmla_last_error() returns a message for the calling thread.  An
+ * unsupported request is a hard error, never a silent fallback.
+ */
+#ifndef PKVMLA_H_
+#define PKVMLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKVMLA_OK = 0,
+  PKVMLA_EINVAL = 1,       /* malformed argument (null pointer, bad indptr, ...) */
+  PKVMLA_EUNSUPPORTED = 2, /* well-formed but not supported (dims, heads, page size) */
+  PKVMLA_EHIP = 3,         /* HIP runtime or launch failure */
+  PKVMLA_ENOMEM = 4        /* device allocation failed */
+} pkvmla_status;
+
+typedef struct pkvmla_plan_s* pkvmla_plan;
+
+/* Build a flat decode plan.
+ *   kv_indptr  host int32[batch+1]: kv_indptr[0] == 0, non-decreasing.
+ *   kv_indices host int32[kv_indptr[batch]]: page ids in [0, num_pages).
+ *   kv_lens    host int32[batch]: 1 <= kv_lens[b] <= pages(b) * page_size.
+ *   num_heads in {16, 32, 64, 128}; ckv_dim must be 512 and kpe_dim 64 (a
+ *   ckv_dim equal to the KV head count, 1, is the mistake the plan review
+ *   flags, and is rejected); page_size a power of two in [1, 256].
+ *   sm_scale: 0 selects 1/sqrt(ckv_dim + kpe_dim); otherwise finite and > 0.
+ *   stream: hipStream_t (as void*) used for the table upload; 0 = null stream.
+ * The host arrays are read during the call only.  The plan owns device copies
+ * of the page table and of the work schedule, and its split workspace; it is
+ * bound to the device that was current at creation.  Output: *out. */
+int pkvmla_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
+                       const int32_t* kv_lens, int32_t batch, int32_t num_pages,
+                       int32_t num_heads, int32_t ckv_dim, int32_t kpe_dim,
+                       int32_t page_size, float sm_scale, void* stream,
+                       pkvmla_plan* out);
+
+/* Build a two-level (cascade) plan.  Requests are partitioned into
+ * num_groups contiguous groups by group_req_indptr (host int32[G+1], from 0
+ * to batch).  Group g's shared prefix is prefix_lens[g] tokens in pages
+ * prefix_indices[prefix_indptr[g] ...] (host arrays).  kv_indptr, kv_indices
+ * and kv_lens describe each request's own suffix as in a flat plan, except
+ * that kv_lens[b] may be 0.  prefix_lens[g] + kv_lens[b] >= 1 for every b. */
+int pkvmla_plan_create_cascade(const int32_t* group_req_indptr, int32_t num_groups,
+                               const int32_t* prefix_indptr, const int32_t* prefix_indices,
+                               const int32_t* prefix_lens,
+                               const int32_t* kv_indptr, const int32_t* kv_indices,
+                               const int32_t* kv_lens, int32_t batch, int32_t num_pages,
+                               int32_t num_heads, int32_t ckv_dim, int32_t kpe_dim,
+                               int32_t page_size, float sm_scale, void* stream,
+                               pkvmla_plan* out);
+
+/* Run the decode for one set of tensors (e.g. one layer) on `stream`.
+ * Asynchronous: only kernel launches on `stream`; no allocation, no host
+ * synchronisation, no host<->device copies.  Device pointers are owned by the
+ * caller and must stay valid until the stream reaches the end of the call;
+ * out/lse must not alias the inputs.  One plan must not run on two streams at
+ * once (the split workspace is shared).  Results are bitwise reproducible for
+ * a fixed plan and inputs. */
+int pkvmla_run(pkvmla_plan plan, const void* q_nope, const void* q_pe,
+               const void* ckv_cache, const void* kpe_cache, void* out, float* lse,
+               void* stream);
+
+/* Kernel timing for benchmarks.  With enable != 0, every later pkvmla_run
+ * records a HIP event pair on its stream around the fused decode kernel only
+ * (events are created here, so run still allocates nothing); the counter is
+ * reset.  pkvmla_plan_timing synchronises the device and returns the summed
+ * duration of the last min(n, 256) timed runs' decode kernels and that count. */
+int pkvmla_plan_set_timing(pkvmla_plan plan, int32_t enable);
+int pkvmla_plan_timing(pkvmla_plan plan, double* total_ms, int64_t* n_runs);
+
+/* Free the plan's device buffers (synchronises the device first).  NULL is a no-op. */
+void pkvmla_plan_destroy(pkvmla_plan plan);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* pkvmla_last_error(void);
+
+/* Kernel configuration used for num_heads (values the schedule depends on):
+ * cfg[0] = KV tile tokens, cfg[1] = waves per workgroup, cfg[2] = heads per
+ * wave, cfg[3] = LDS stages, cfg[4] = workgroups per CU, cfg[5] = fixed cost
+ * per segment in tiles.  Host only; needs no GPU. */
+int pkvmla_kernel_config(int32_t num_heads, int32_t* cfg6);
+
+/* The split-KV work schedule, computed on the host exactly as plan_create
+ * does (no GPU needed).  items: host int32[n_items*3] of (request, sequence,
+ * length).  num_wg: workgroup budget.  Outputs (capacities in elements):
+ * wg_indptr int32[grid+1], units int32[n_units*8] records
+ * (request, sequence, kv_begin, kv_end, slot, row, 0, 0) where row is the
+ * number of tokens in all earlier units, merges int32[n*4]
+ * records (request, first_slot, count, 0).  counts[0..2] = grid, n_units,
+ * n_merges.  PKVMLA_EINVAL if a capacity is too small. */
+int pkvmla_schedule_host(const int32_t* items, int32_t n_items, int32_t batch,
+                         int32_t num_wg, int32_t tile, int32_t fixed_cost,
+                         int32_t* wg_indptr, int64_t cap_wg,
+                         int32_t* units, int64_t cap_units,
+                         int32_t* merges, int64_t cap_merges, int32_t* counts);
+
+/* Copy the plan's uploaded device tables back to the host, for bit-exact
+ * checking.  Layout of host int32 buf (cap elements):
+ *   [0..15]  header: version(1), batch, num_heads, page_size, ckv_dim,
+ *            kpe_dim, tile, waves, heads_per_wave, stages, wg_per_cu,
+ *            fixed_cost, grid, n_units, n_merges, n_slots
+ *   [16..31] header 2: num_seqs, n_indices, num_cu, sm_scale (float bits),
+ *            is_cascade, num_groups, 0...
+ *   then wg_indptr[grid+1], units[n_units*8], merges[n_merges*4],
+ *   seq_indptr[num_seqs+1], seq_lens[num_seqs], seq_indices[n_indices].
+ * *used = number of int32 written (or needed, when cap is too small:
+ * PKVMLA_EINVAL).  Synchronises the device. */
+int pkvmla_plan_export(pkvmla_plan plan, int32_t* buf, int64_t cap, int64_t* used);
+
+/* Page-table gather through the same device address path as the decode
+ * kernel: rows (device bf16 [sum of attended tokens, 576]) receives, for every
+ * work unit of the plan in request order and then token order, the ckv row
+ * followed by the kpe row of each token.  For a flat plan this is
+ * [sum(kv_lens), 576] in (request, token) order.  Bit-exact copy. */
+int pkvmla_gather(pkvmla_plan plan, const void* ckv_cache, const void* kpe_cache,
+                  void* rows, void* stream);
+
+/* Number of rows pkvmla_gather writes for this plan. */
+int pkvmla_gather_rows(pkvmla_plan plan, int64_t* n_rows);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKVMLA_H_ */

@@ -24,6 +24,8 @@ Rule (all integers):
   * A request with exactly one unit writes out and lse directly (slot -1);
     otherwise each of its units gets the next partial slot in emission order
     and a merge row (b, first slot, count) is added in request order.
+  * row = number of tokens in all earlier units (emission order): where the
+    unit's tokens start in the gathered-rows view.
 """
 
 from __future__ import annotations
@@ -31,7 +33,7 @@ from __future__ import annotations
 import numpy as np
 
 PLAN_TILE = 32          # KV tokens per tile
-UNIT_INTS = 8           # int32 per unit record: b, seq, kv_begin, kv_end, slot, 0, 0, 0
+UNIT_INTS = 8           # int32 per unit record: b, seq, kv_begin, kv_end, slot, row, 0, 0
 MERGE_INTS = 4          # int32 per merge record: b, first_slot, count, 0
 
 # Per head count: (waves per workgroup, heads per wave, LDS stages,
@@ -107,6 +109,7 @@ def schedule_ref(items, batch: int, num_wg: int, tile: int = PLAN_TILE, fixed: i
     units = np.zeros((len(raw), UNIT_INTS), dtype=np.int32)
     first_slot = {}
     slot = 0
+    row = 0
     for i, (wi, b, s, k0, k1) in enumerate(raw):
         if per_req[b] == 1:
             sl = -1
@@ -114,7 +117,8 @@ def schedule_ref(items, batch: int, num_wg: int, tile: int = PLAN_TILE, fixed: i
             sl = slot
             first_slot.setdefault(b, slot)
             slot += 1
-        units[i, :5] = (b, s, k0, k1, sl)
+        units[i, :6] = (b, s, k0, k1, sl, row)
+        row += k1 - k0
     merges = [(b, first_slot[b], int(per_req[b]), 0) for b in range(batch) if per_req[b] > 1]
     merges = np.asarray(merges, dtype=np.int32).reshape(-1, MERGE_INTS)
     wg_indptr = np.zeros(grid + 1, dtype=np.int32)

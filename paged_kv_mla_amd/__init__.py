@@ -1,0 +1,279 @@
+"""MI355X (gfx950) batched paged-KV MLA decode, absorbed form.
+
+Thin ctypes binding over the C ABI in include/pkvmla.h (libpkvmla.so, built in
+this directory by ``python paged_kv_mla_amd/build.py``).  Argument marshalling
+only: every step of the decode runs in the library's HIP kernels.  PyTorch is
+used for device memory and streams; there is no CPU or PyTorch fallback, and
+importing this package fails if the library has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+
+# PyTorch-ROCm ships its own HIP runtime under the same SONAME as the system
+# one (libamdhip64.so.7).  Importing torch first makes libpkvmla.so bind to the
+# runtime torch already loaded, so one process never mixes two HIP/HSA runtimes.
+import torch  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpkvmla.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python paged_kv_mla_amd/build.py` "
+        "(hipcc, gfx950).  There is no fallback implementation.")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_vp = ctypes.c_void_p
+
+_lib.pkvmla_plan_create.argtypes = [_i32p, _i32p, _i32p, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.c_float, _vp, ctypes.POINTER(_vp)]
+_lib.pkvmla_plan_create_cascade.argtypes = [_i32p, ctypes.c_int32, _i32p, _i32p, _i32p,
+                                            _i32p, _i32p, _i32p, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_float, _vp,
+                                            ctypes.POINTER(_vp)]
+_lib.pkvmla_run.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.pkvmla_plan_destroy.argtypes = [_vp]
+_lib.pkvmla_plan_destroy.restype = None
+_lib.pkvmla_last_error.restype = ctypes.c_char_p
+_lib.pkvmla_kernel_config.argtypes = [ctypes.c_int32, _i32p]
+_lib.pkvmla_schedule_host.argtypes = [_i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_int32, ctypes.c_int32, _i32p, ctypes.c_int64,
+                                      _i32p, ctypes.c_int64, _i32p, ctypes.c_int64, _i32p]
+_lib.pkvmla_plan_export.argtypes = [_vp, _i32p, ctypes.c_int64, _i64p]
+_lib.pkvmla_gather.argtypes = [_vp, _vp, _vp, _vp, _vp]
+_lib.pkvmla_gather_rows.argtypes = [_vp, _i64p]
+_lib.pkvmla_plan_set_timing.argtypes = [_vp, ctypes.c_int32]
+_lib.pkvmla_plan_timing.argtypes = [_vp, ctypes.POINTER(ctypes.c_double), _i64p]
+
+EXPORTED_SYMBOLS = (
+    "pkvmla_plan_create", "pkvmla_plan_create_cascade", "pkvmla_run", "pkvmla_plan_destroy",
+    "pkvmla_last_error", "pkvmla_kernel_config", "pkvmla_schedule_host", "pkvmla_plan_export",
+    "pkvmla_gather", "pkvmla_gather_rows", "pkvmla_plan_set_timing", "pkvmla_plan_timing",
+)
+
+OK, EINVAL, EUNSUPPORTED, EHIP, ENOMEM = 0, 1, 2, 3, 4
+_NAMES = {EINVAL: "EINVAL", EUNSUPPORTED: "EUNSUPPORTED", EHIP: "EHIP", ENOMEM: "ENOMEM"}
+
+
+class PkvmlaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"pkvmla {_NAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+def last_error() -> str:
+    return (_lib.pkvmla_last_error() or b"").decode()
+
+
+def _check(rc: int) -> None:
+    if rc != OK:
+        raise PkvmlaError(rc, last_error())
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(_i32p)
+
+
+def _stream_handle(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def kernel_config(num_heads: int) -> dict:
+    cfg = np.zeros(6, dtype=np.int32)
+    _check(_lib.pkvmla_kernel_config(int(num_heads), _ptr(cfg)))
+    keys = ("tile", "waves", "heads_per_wave", "stages", "wg_per_cu", "fixed_cost")
+    return {k: int(v) for k, v in zip(keys, cfg)}
+
+
+def schedule_host(items, batch: int, num_wg: int, tile: int, fixed_cost: int):
+    """The library's split-KV schedule for (request, sequence, length) items,
+    computed on the host.  Returns (wg_indptr, units [n, 8], merges [m, 4])."""
+    it = _i32(items).reshape(-1, 3)
+    n_tok_tiles = int(sum(-(-int(L) // tile) for L in it[:, 2]))
+    cap_u = 8 * (n_tok_tiles + num_wg + 8)
+    cap_m = 4 * (batch + 1)
+    wg = np.zeros(num_wg + 1, np.int32)
+    units = np.zeros(cap_u, np.int32)
+    merges = np.zeros(cap_m, np.int32)
+    counts = np.zeros(3, np.int32)
+    _check(_lib.pkvmla_schedule_host(_ptr(it), len(it), int(batch), int(num_wg), int(tile),
+                                     int(fixed_cost), _ptr(wg), wg.size, _ptr(units), units.size,
+                                     _ptr(merges), merges.size, _ptr(counts)))
+    grid, nu, nm = (int(c) for c in counts)
+    return wg[:grid + 1].copy(), units[:8 * nu].reshape(nu, 8).copy(), merges[:4 * nm].reshape(nm, 4).copy()
+
+
+@dataclass
+class PlanExport:
+    header: np.ndarray
+    sm_scale: float
+    wg_indptr: np.ndarray
+    units: np.ndarray
+    merges: np.ndarray
+    seq_indptr: np.ndarray
+    seq_lens: np.ndarray
+    seq_indices: np.ndarray
+
+    @property
+    def grid(self) -> int:
+        return int(self.header[12])
+
+    @property
+    def num_cu(self) -> int:
+        return int(self.header[18])
+
+
+class Plan:
+    """A decode plan (page table + work schedule on the device).  Build with
+    :func:`plan` or :func:`plan_cascade`; run it with :meth:`run` for every
+    set of tensors (e.g. once per layer) that shares the page table."""
+
+    def __init__(self, handle: int, batch: int, num_heads: int):
+        self._h = ctypes.c_void_p(handle)
+        self.batch = batch
+        self.num_heads = num_heads
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            _lib.pkvmla_plan_destroy(h)
+            self._h = None
+
+    def destroy(self) -> None:
+        self.__del__()
+
+    def run(self, q_nope, q_pe, ckv_cache, kpe_cache, out=None, lse=None, stream=None):
+        """Decode on the device.  q_nope [B,H,512], q_pe [B,H,64], ckv_cache
+        [P,ps,512], kpe_cache [P,ps,64] are contiguous bf16 CUDA tensors.
+        Returns (out bf16 [B,H,512], lse fp32 [B,H]); out/lse are allocated
+        when not given.  Asynchronous on `stream` (default: current stream)."""
+        import torch
+        B, H = self.batch, self.num_heads
+        for name, t, shape in (("q_nope", q_nope, (B, H, 512)), ("q_pe", q_pe, (B, H, 64))):
+            if tuple(t.shape) != shape or t.dtype != torch.bfloat16 or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous bf16 tensor of shape {shape}")
+        for name, t, d in (("ckv_cache", ckv_cache, 512), ("kpe_cache", kpe_cache, 64)):
+            if t.dim() != 3 or t.shape[2] != d or t.dtype != torch.bfloat16 or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous bf16 [pages, page_size, {d}] tensor")
+        if out is None:
+            out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=q_nope.device)
+        if lse is None:
+            lse = torch.empty((B, H), dtype=torch.float32, device=q_nope.device)
+        _check(_lib.pkvmla_run(self._h, q_nope.data_ptr(), q_pe.data_ptr(), ckv_cache.data_ptr(),
+                               kpe_cache.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                               _stream_handle(stream)))
+        return out, lse
+
+    def run_ptrs(self, q_nope: int, q_pe: int, ckv: int, kpe: int, out: int, lse: int,
+                 stream: int) -> None:
+        """Raw-pointer form of :meth:`run` (no checks beyond the library's)."""
+        _check(_lib.pkvmla_run(self._h, q_nope, q_pe, ckv, kpe, out, lse, stream))
+
+    def set_timing(self, enable: bool = True) -> None:
+        """Record HIP events around the decode kernel of every later run."""
+        _check(_lib.pkvmla_plan_set_timing(self._h, 1 if enable else 0))
+
+    def kernel_timing(self):
+        """(summed decode-kernel ms, number of timed runs), last 256 runs."""
+        ms = ctypes.c_double(0.0)
+        n = ctypes.c_int64(0)
+        _check(_lib.pkvmla_plan_timing(self._h, ctypes.byref(ms), ctypes.byref(n)))
+        return float(ms.value), int(n.value)
+
+    def gather_rows(self) -> int:
+        n = ctypes.c_int64(0)
+        _check(_lib.pkvmla_gather_rows(self._h, ctypes.byref(n)))
+        return int(n.value)
+
+    def gather(self, ckv_cache, kpe_cache, stream=None):
+        """Rows [n, 576] bf16: ckv then kpe of every attended token, gathered
+        through the decode kernel's page-table load path."""
+        import torch
+        rows = torch.empty((self.gather_rows(), 576), dtype=torch.bfloat16, device=ckv_cache.device)
+        _check(_lib.pkvmla_gather(self._h, ckv_cache.data_ptr(), kpe_cache.data_ptr(),
+                                  rows.data_ptr(), _stream_handle(stream)))
+        return rows
+
+    def export(self) -> PlanExport:
+        used = ctypes.c_int64(0)
+        _lib.pkvmla_plan_export(self._h, None, 0, ctypes.byref(used))
+        buf = np.zeros(int(used.value), np.int32)
+        _check(_lib.pkvmla_plan_export(self._h, _ptr(buf), buf.size, ctypes.byref(used)))
+        hdr = buf[:32].copy()
+        grid, nu, nm, ns, ni = int(hdr[12]), int(hdr[13]), int(hdr[14]), int(hdr[16]), int(hdr[17])
+        o = 32
+        parts = []
+        for n in (grid + 1, 8 * nu, 4 * nm, ns + 1, ns, ni):
+            parts.append(buf[o:o + n].copy())
+            o += n
+        return PlanExport(header=hdr, sm_scale=float(hdr[19:20].view(np.float32)[0]),
+                          wg_indptr=parts[0], units=parts[1].reshape(nu, 8),
+                          merges=parts[2].reshape(nm, 4), seq_indptr=parts[3],
+                          seq_lens=parts[4], seq_indices=parts[5])
+
+
+def plan(kv_indptr, kv_indices, kv_lens, num_heads: int, page_size: int, num_pages: int,
+         ckv_dim: int = 512, kpe_dim: int = 64, sm_scale: Optional[float] = None,
+         stream=None) -> Plan:
+    """Flat decode plan from host page-table arrays (int32): kv_indptr [B+1],
+    kv_indices [kv_indptr[B]], kv_lens [B].  sm_scale None selects
+    1/sqrt(ckv_dim + kpe_dim)."""
+    ip, ix, ln = _i32(kv_indptr), _i32(kv_indices), _i32(kv_lens)
+    if ix.size == 0:
+        ix = np.zeros(1, np.int32)
+    h = ctypes.c_void_p()
+    _check(_lib.pkvmla_plan_create(_ptr(ip), _ptr(ix), _ptr(ln), int(len(ln)), int(num_pages),
+                                   int(num_heads), int(ckv_dim), int(kpe_dim), int(page_size),
+                                   float(sm_scale or 0.0), _stream_handle(stream) if stream else None,
+                                   ctypes.byref(h)))
+    return Plan(h.value, int(len(ln)), int(num_heads))
+
+
+def plan_cascade(group_req_indptr, prefix_indptr, prefix_indices, prefix_lens,
+                 kv_indptr, kv_indices, kv_lens, num_heads: int, page_size: int,
+                 num_pages: int, ckv_dim: int = 512, kpe_dim: int = 64,
+                 sm_scale: Optional[float] = None, stream=None) -> Plan:
+    """Two-level plan: per group a shared prefix page list, per request its
+    own suffix list (kv_lens may be 0); states are merged by log-sum-exp."""
+    g, pip, pix, pl = _i32(group_req_indptr), _i32(prefix_indptr), _i32(prefix_indices), _i32(prefix_lens)
+    ip, ix, ln = _i32(kv_indptr), _i32(kv_indices), _i32(kv_lens)
+    if pix.size == 0:
+        pix = np.zeros(1, np.int32)
+    if ix.size == 0:
+        ix = np.zeros(1, np.int32)
+    h = ctypes.c_void_p()
+    _check(_lib.pkvmla_plan_create_cascade(
+        _ptr(g), int(len(pl)), _ptr(pip), _ptr(pix), _ptr(pl), _ptr(ip), _ptr(ix), _ptr(ln),
+        int(len(ln)), int(num_pages), int(num_heads), int(ckv_dim), int(kpe_dim), int(page_size),
+        float(sm_scale or 0.0), _stream_handle(stream) if stream else None, ctypes.byref(h)))
+    return Plan(h.value, int(len(ln)), int(num_heads))
+
+
+def plan_for(inp, stream=None) -> Plan:
+    """Plan for an input bundle from mla_workloads (flat or cascade)."""
+    if hasattr(inp, "prefix_lens"):
+        return plan_cascade(inp.group_req_indptr, inp.prefix_indptr, inp.prefix_indices,
+                            inp.prefix_lens, inp.kv_indptr, inp.kv_indices, inp.kv_lens,
+                            inp.num_heads, inp.page_size, inp.num_pages, sm_scale=inp.sm_scale,
+                            stream=stream)
+    return plan(inp.kv_indptr, inp.kv_indices, inp.kv_lens, inp.num_heads, inp.page_size,
+                inp.num_pages, sm_scale=inp.sm_scale, stream=stream)

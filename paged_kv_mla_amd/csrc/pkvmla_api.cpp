@@ -1,0 +1,510 @@
+// C ABI of the MLA paged-decode library: argument validation, plan lifetime,
+// schedule upload and kernel dispatch.  See include/pkvmla.h for the contract.
+#include "pkvmla.h"
+
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <cmath>
+#include <string>
+#include <vector>
+
+#include "pkvmla_internal.h"
+#include "pkvmla_schedule.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return PKVMLA_OK;
+}
+
+#define PKVMLA_HIP(call)                                                              \
+  do {                                                                                \
+    hipError_t e_ = (call);                                                           \
+    if (e_ != hipSuccess)                                                             \
+      return fail(e_ == hipErrorOutOfMemory ? PKVMLA_ENOMEM : PKVMLA_EHIP, "%s: %s", #call, \
+                  hipGetErrorString(e_));                                             \
+  } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+struct pkvmla_plan_s {
+  int device = 0;
+  int32_t batch = 0, num_heads = 0, page_size = 0, log2_ps = 0;
+  int32_t ckv_dim = 0, kpe_dim = 0, num_pages = 0;
+  float sm_scale = 0.f;
+  int32_t is_cascade = 0, num_groups = 0, num_cu = 0;
+  pkvmla::KernelConfig cfg{};
+  pkvmla::Schedule sched;
+  int32_t num_seqs = 0;
+  int64_t n_indices = 0;
+  // device tables (one allocation) and split workspace
+  int32_t* d_tables = nullptr;
+  int32_t* d_wg_indptr = nullptr;
+  int32_t* d_units = nullptr;
+  int32_t* d_merges = nullptr;
+  int32_t* d_seq_indptr = nullptr;
+  int32_t* d_seq_lens = nullptr;
+  int32_t* d_seq_indices = nullptr;
+  float* d_part = nullptr;  // part_o [slots][H][512] then part_lse [slots][H]
+  size_t table_ints = 0;
+  // optional per-run timing of the decode kernel (events created up front)
+  static constexpr int kTimingSlots = 256;
+  hipEvent_t ev[2 * kTimingSlots] = {};
+  int timing = 0;
+  int64_t timed_runs = 0;
+};
+
+namespace {
+
+// Common checks of the scalar plan parameters.
+int check_shape(int32_t batch, int32_t num_pages, int32_t num_heads, int32_t ckv_dim,
+                int32_t kpe_dim, int32_t page_size, float sm_scale, int32_t* log2_ps,
+                float* scale) {
+  if (batch < 1) return fail(PKVMLA_EINVAL, "batch must be >= 1 (got %d)", batch);
+  if (num_pages < 1) return fail(PKVMLA_EINVAL, "num_pages must be >= 1 (got %d)", num_pages);
+  if (ckv_dim != pkvmla::kCkvDim || kpe_dim != pkvmla::kKpeDim)
+    return fail(PKVMLA_EUNSUPPORTED,
+                "head_dim_ckv must be kv_lora_rank = 512 and head_dim_kpe qk_rope_head_dim = 64 "
+                "(got %d, %d)",
+                ckv_dim, kpe_dim);
+  pkvmla::KernelConfig cfg;
+  if (!pkvmla::kernel_config_for(num_heads, &cfg))
+    return fail(PKVMLA_EUNSUPPORTED, "num_heads must be one of 16, 32, 64, 128 (got %d)",
+                num_heads);
+  if (page_size < 1) return fail(PKVMLA_EINVAL, "page_size must be >= 1 (got %d)", page_size);
+  if (page_size > 256 || (page_size & (page_size - 1)) != 0)
+    return fail(PKVMLA_EUNSUPPORTED, "page_size must be a power of two <= 256 (got %d)",
+                page_size);
+  if ((int64_t)num_pages * page_size > (int64_t)INT32_MAX)
+    return fail(PKVMLA_EUNSUPPORTED, "num_pages * page_size must fit in int32");
+  if (!std::isfinite(sm_scale) || sm_scale < 0.f)
+    return fail(PKVMLA_EINVAL, "sm_scale must be finite and >= 0 (0 = default)");
+  int l = 0;
+  while ((1 << l) < page_size) ++l;
+  *log2_ps = l;
+  *scale = sm_scale == 0.f ? (float)(1.0 / std::sqrt((double)(ckv_dim + kpe_dim))) : sm_scale;
+  return PKVMLA_OK;
+}
+
+// Validate one CSR page list: indptr[n+1], indices, lens[n].
+int check_pages(const char* what, const int32_t* indptr, const int32_t* indices,
+                const int32_t* lens, int32_t n, int32_t num_pages, int32_t page_size,
+                int32_t min_len) {
+  if (!indptr || !lens) return fail(PKVMLA_EINVAL, "%s: null indptr or lens", what);
+  if (indptr[0] != 0) return fail(PKVMLA_EINVAL, "%s: indptr[0] must be 0", what);
+  for (int32_t b = 0; b < n; ++b) {
+    if (indptr[b + 1] < indptr[b])
+      return fail(PKVMLA_EINVAL, "%s: indptr must be non-decreasing (at %d)", what, b);
+    if (lens[b] < min_len)
+      return fail(PKVMLA_EINVAL, "%s: length[%d] = %d is below %d", what, b, lens[b], min_len);
+    const int64_t cap = (int64_t)(indptr[b + 1] - indptr[b]) * page_size;
+    if (lens[b] > cap)
+      return fail(PKVMLA_EINVAL, "%s: length[%d] = %d exceeds its %d pages x page_size %d", what,
+                  b, lens[b], indptr[b + 1] - indptr[b], page_size);
+  }
+  if (indptr[n] > 0 && !indices) return fail(PKVMLA_EINVAL, "%s: null indices", what);
+  for (int64_t i = 0; i < indptr[n]; ++i)
+    if (indices[i] < 0 || indices[i] >= num_pages)
+      return fail(PKVMLA_EINVAL, "%s: page index %d at %lld outside [0, %d)", what, indices[i],
+                  (long long)i, num_pages);
+  return PKVMLA_OK;
+}
+
+// Build the schedule, allocate and upload the device tables.
+int finish_plan(pkvmla_plan_s* P, const std::vector<pkvmla::WorkItem>& items,
+                const std::vector<int32_t>& seq_indptr, const std::vector<int32_t>& seq_lens,
+                const std::vector<int32_t>& seq_indices, hipStream_t stream) {
+  PKVMLA_HIP(hipGetDevice(&P->device));
+  PKVMLA_HIP(hipDeviceGetAttribute(&P->num_cu, hipDeviceAttributeMultiprocessorCount, P->device));
+  const int32_t num_wg = P->num_cu * P->cfg.wg_per_cu;
+  if (!pkvmla::build_schedule(items, P->batch, num_wg, pkvmla::kTile, P->cfg.fixed_cost,
+                              &P->sched))
+    return fail(PKVMLA_EINVAL, "schedule construction failed");
+  if (P->sched.total_rows > INT32_MAX) return fail(PKVMLA_EUNSUPPORTED, "too many tokens");
+  P->num_seqs = (int32_t)seq_lens.size();
+  P->n_indices = (int64_t)seq_indices.size();
+
+  const size_t n_wg = P->sched.wg_indptr.size();
+  const size_t n_units = P->sched.units.size();
+  const size_t n_merges = P->sched.merges.size();
+  // 64-int aligned sub-buffers inside one allocation
+  auto pad = [](size_t n) { return (n + 63) & ~size_t(63); };
+  size_t off_wg = 0, off_units = off_wg + pad(n_wg), off_merges = off_units + pad(n_units);
+  size_t off_sip = off_merges + pad(n_merges), off_sl = off_sip + pad(seq_indptr.size());
+  size_t off_si = off_sl + pad(seq_lens.size());
+  P->table_ints = off_si + pad(seq_indices.size() ? seq_indices.size() : 1);
+  PKVMLA_HIP(hipMalloc(&P->d_tables, P->table_ints * sizeof(int32_t)));
+  P->d_wg_indptr = P->d_tables + off_wg;
+  P->d_units = P->d_tables + off_units;
+  P->d_merges = P->d_tables + off_merges;
+  P->d_seq_indptr = P->d_tables + off_sip;
+  P->d_seq_lens = P->d_tables + off_sl;
+  P->d_seq_indices = P->d_tables + off_si;
+  std::vector<int32_t> host(P->table_ints, 0);
+  std::copy(P->sched.wg_indptr.begin(), P->sched.wg_indptr.end(), host.begin() + off_wg);
+  std::copy(P->sched.units.begin(), P->sched.units.end(), host.begin() + off_units);
+  std::copy(P->sched.merges.begin(), P->sched.merges.end(), host.begin() + off_merges);
+  std::copy(seq_indptr.begin(), seq_indptr.end(), host.begin() + off_sip);
+  std::copy(seq_lens.begin(), seq_lens.end(), host.begin() + off_sl);
+  std::copy(seq_indices.begin(), seq_indices.end(), host.begin() + off_si);
+  PKVMLA_HIP(hipMemcpyAsync(P->d_tables, host.data(), P->table_ints * sizeof(int32_t),
+                            hipMemcpyHostToDevice, stream));
+  if (P->sched.n_slots > 0) {
+    const size_t n = (size_t)P->sched.n_slots * P->num_heads * (pkvmla::kCkvDim + 1);
+    PKVMLA_HIP(hipMalloc(&P->d_part, n * sizeof(float)));
+  }
+  PKVMLA_HIP(hipStreamSynchronize(stream));
+  return PKVMLA_OK;
+}
+
+void free_plan(pkvmla_plan_s* P) {
+  if (!P) return;
+  for (hipEvent_t& e : P->ev)
+    if (e) (void)hipEventDestroy(e);
+  if (P->d_tables) (void)hipFree(P->d_tables);
+  if (P->d_part) (void)hipFree(P->d_part);
+  delete P;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkvmla_last_error(void) { return g_last_error.c_str(); }
+
+int pkvmla_kernel_config(int32_t num_heads, int32_t* cfg6) {
+  if (!cfg6) return fail(PKVMLA_EINVAL, "null output");
+  pkvmla::KernelConfig c;
+  if (!pkvmla::kernel_config_for(num_heads, &c))
+    return fail(PKVMLA_EUNSUPPORTED, "num_heads must be one of 16, 32, 64, 128 (got %d)",
+                num_heads);
+  cfg6[0] = pkvmla::kTile;
+  cfg6[1] = c.waves;
+  cfg6[2] = c.heads_per_wave;
+  cfg6[3] = c.stages;
+  cfg6[4] = c.wg_per_cu;
+  cfg6[5] = c.fixed_cost;
+  return ok();
+}
+
+int pkvmla_schedule_host(const int32_t* items, int32_t n_items, int32_t batch, int32_t num_wg,
+                         int32_t tile, int32_t fixed_cost, int32_t* wg_indptr, int64_t cap_wg,
+                         int32_t* units, int64_t cap_units, int32_t* merges, int64_t cap_merges,
+                         int32_t* counts) {
+  if ((!items && n_items > 0) || !counts || n_items < 0)
+    return fail(PKVMLA_EINVAL, "null or negative argument");
+  if (num_wg < 1 || tile < 1 || fixed_cost < 0 || batch < 1)
+    return fail(PKVMLA_EINVAL, "num_wg, tile, batch must be >= 1 and fixed_cost >= 0");
+  std::vector<pkvmla::WorkItem> v((size_t)n_items);
+  for (int32_t i = 0; i < n_items; ++i) {
+    v[i] = pkvmla::WorkItem{items[3 * i], items[3 * i + 1], items[3 * i + 2]};
+    if (v[i].req < 0 || v[i].req >= batch || v[i].len < 0)
+      return fail(PKVMLA_EINVAL, "item %d: request out of range or negative length", i);
+  }
+  pkvmla::Schedule s;
+  if (!pkvmla::build_schedule(v, batch, num_wg, tile, fixed_cost, &s))
+    return fail(PKVMLA_EINVAL, "schedule construction failed");
+  counts[0] = s.grid;
+  counts[1] = (int32_t)(s.units.size() / pkvmla::kUnitRecordInts);
+  counts[2] = (int32_t)(s.merges.size() / pkvmla::kMergeRecordInts);
+  if ((int64_t)s.wg_indptr.size() > cap_wg || (int64_t)s.units.size() > cap_units ||
+      (int64_t)s.merges.size() > cap_merges)
+    return fail(PKVMLA_EINVAL, "output capacity too small (need %zu, %zu, %zu)",
+                s.wg_indptr.size(), s.units.size(), s.merges.size());
+  if (!s.wg_indptr.empty() && !wg_indptr) return fail(PKVMLA_EINVAL, "null wg_indptr");
+  if (!s.units.empty() && !units) return fail(PKVMLA_EINVAL, "null units");
+  if (!s.merges.empty() && !merges) return fail(PKVMLA_EINVAL, "null merges");
+  std::copy(s.wg_indptr.begin(), s.wg_indptr.end(), wg_indptr);
+  std::copy(s.units.begin(), s.units.end(), units);
+  std::copy(s.merges.begin(), s.merges.end(), merges);
+  return ok();
+}
+
+int pkvmla_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
+                       const int32_t* kv_lens, int32_t batch, int32_t num_pages,
+                       int32_t num_heads, int32_t ckv_dim, int32_t kpe_dim, int32_t page_size,
+                       float sm_scale, void* stream, pkvmla_plan* out) {
+  if (!out) return fail(PKVMLA_EINVAL, "null plan output pointer");
+  *out = nullptr;
+  int32_t log2_ps;
+  float scale;
+  int rc = check_shape(batch, num_pages, num_heads, ckv_dim, kpe_dim, page_size, sm_scale,
+                       &log2_ps, &scale);
+  if (rc) return rc;
+  rc = check_pages("kv", kv_indptr, kv_indices, kv_lens, batch, num_pages, page_size, 1);
+  if (rc) return rc;
+
+  pkvmla_plan_s* P = new pkvmla_plan_s();
+  P->batch = batch;
+  P->num_heads = num_heads;
+  P->page_size = page_size;
+  P->log2_ps = log2_ps;
+  P->ckv_dim = ckv_dim;
+  P->kpe_dim = kpe_dim;
+  P->num_pages = num_pages;
+  P->sm_scale = scale;
+  pkvmla::kernel_config_for(num_heads, &P->cfg);
+  std::vector<pkvmla::WorkItem> items((size_t)batch);
+  for (int32_t b = 0; b < batch; ++b) items[b] = pkvmla::WorkItem{b, b, kv_lens[b]};
+  std::vector<int32_t> sip(kv_indptr, kv_indptr + batch + 1);
+  std::vector<int32_t> sl(kv_lens, kv_lens + batch);
+  std::vector<int32_t> si(kv_indices, kv_indices + kv_indptr[batch]);
+  rc = finish_plan(P, items, sip, sl, si, (hipStream_t)stream);
+  if (rc) {
+    std::string msg = g_last_error;
+    free_plan(P);
+    g_last_error = msg;
+    return rc;
+  }
+  *out = P;
+  return ok();
+}
+
+int pkvmla_plan_create_cascade(const int32_t* group_req_indptr, int32_t num_groups,
+                               const int32_t* prefix_indptr, const int32_t* prefix_indices,
+                               const int32_t* prefix_lens, const int32_t* kv_indptr,
+                               const int32_t* kv_indices, const int32_t* kv_lens, int32_t batch,
+                               int32_t num_pages, int32_t num_heads, int32_t ckv_dim,
+                               int32_t kpe_dim, int32_t page_size, float sm_scale, void* stream,
+                               pkvmla_plan* out) {
+  if (!out) return fail(PKVMLA_EINVAL, "null plan output pointer");
+  *out = nullptr;
+  int32_t log2_ps;
+  float scale;
+  int rc = check_shape(batch, num_pages, num_heads, ckv_dim, kpe_dim, page_size, sm_scale,
+                       &log2_ps, &scale);
+  if (rc) return rc;
+  if (num_groups < 1 || !group_req_indptr)
+    return fail(PKVMLA_EINVAL, "num_groups must be >= 1 with a group_req_indptr");
+  if (group_req_indptr[0] != 0 || group_req_indptr[num_groups] != batch)
+    return fail(PKVMLA_EINVAL, "group_req_indptr must run from 0 to batch");
+  for (int32_t g = 0; g < num_groups; ++g)
+    if (group_req_indptr[g + 1] < group_req_indptr[g])
+      return fail(PKVMLA_EINVAL, "group_req_indptr must be non-decreasing (at %d)", g);
+  rc = check_pages("prefix", prefix_indptr, prefix_indices, prefix_lens, num_groups, num_pages,
+                   page_size, 0);
+  if (rc) return rc;
+  rc = check_pages("suffix", kv_indptr, kv_indices, kv_lens, batch, num_pages, page_size, 0);
+  if (rc) return rc;
+  for (int32_t g = 0; g < num_groups; ++g)
+    for (int32_t b = group_req_indptr[g]; b < group_req_indptr[g + 1]; ++b)
+      if (prefix_lens[g] + kv_lens[b] < 1)
+        return fail(PKVMLA_EINVAL, "request %d attends no token (prefix and suffix empty)", b);
+
+  pkvmla_plan_s* P = new pkvmla_plan_s();
+  P->batch = batch;
+  P->num_heads = num_heads;
+  P->page_size = page_size;
+  P->log2_ps = log2_ps;
+  P->ckv_dim = ckv_dim;
+  P->kpe_dim = kpe_dim;
+  P->num_pages = num_pages;
+  P->sm_scale = scale;
+  P->is_cascade = 1;
+  P->num_groups = num_groups;
+  pkvmla::kernel_config_for(num_heads, &P->cfg);
+  // sequences: G prefix lists, then one suffix list per request
+  std::vector<int32_t> sip, sl, si;
+  sip.reserve(num_groups + batch + 1);
+  for (int32_t g = 0; g <= num_groups; ++g) sip.push_back(prefix_indptr[g]);
+  for (int32_t b = 1; b <= batch; ++b) sip.push_back(prefix_indptr[num_groups] + kv_indptr[b]);
+  for (int32_t g = 0; g < num_groups; ++g) sl.push_back(prefix_lens[g]);
+  for (int32_t b = 0; b < batch; ++b) sl.push_back(kv_lens[b]);
+  si.assign(prefix_indices, prefix_indices + prefix_indptr[num_groups]);
+  si.insert(si.end(), kv_indices, kv_indices + kv_indptr[batch]);
+  std::vector<pkvmla::WorkItem> items;
+  items.reserve(2 * (size_t)batch);
+  for (int32_t g = 0; g < num_groups; ++g)
+    for (int32_t b = group_req_indptr[g]; b < group_req_indptr[g + 1]; ++b) {
+      items.push_back(pkvmla::WorkItem{b, g, prefix_lens[g]});
+      items.push_back(pkvmla::WorkItem{b, num_groups + b, kv_lens[b]});
+    }
+  rc = finish_plan(P, items, sip, sl, si, (hipStream_t)stream);
+  if (rc) {
+    std::string msg = g_last_error;
+    free_plan(P);
+    g_last_error = msg;
+    return rc;
+  }
+  *out = P;
+  return ok();
+}
+
+int pkvmla_run(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* ckv_cache,
+               const void* kpe_cache, void* out, float* lse, void* stream) {
+  if (!P) return fail(PKVMLA_EINVAL, "null plan");
+  if (!q_nope || !q_pe || !ckv_cache || !kpe_cache || !out || !lse)
+    return fail(PKVMLA_EINVAL, "null tensor pointer");
+  if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(ckv_cache) || !aligned16(kpe_cache) ||
+      !aligned16(out) || (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(PKVMLA_EINVAL, "device pointers must be 16-byte aligned (lse 4-byte)");
+  int dev = -1;
+  PKVMLA_HIP(hipGetDevice(&dev));
+  if (dev != P->device)
+    return fail(PKVMLA_EINVAL, "plan was built on device %d, current device is %d", P->device,
+                dev);
+  hipStream_t s = (hipStream_t)stream;
+  const size_t part_o_elems = (size_t)P->sched.n_slots * P->num_heads * pkvmla::kCkvDim;
+  pkvmla::DecodeParams d{};
+  d.q_nope = static_cast<const uint16_t*>(q_nope);
+  d.q_pe = static_cast<const uint16_t*>(q_pe);
+  d.ckv = static_cast<const uint16_t*>(ckv_cache);
+  d.kpe = static_cast<const uint16_t*>(kpe_cache);
+  d.out = static_cast<uint16_t*>(out);
+  d.lse = lse;
+  d.part_o = P->d_part;
+  d.part_lse = P->d_part ? P->d_part + part_o_elems : nullptr;
+  d.wg_indptr = P->d_wg_indptr;
+  d.units = P->d_units;
+  d.seq_indptr = P->d_seq_indptr;
+  d.seq_indices = P->d_seq_indices;
+  d.num_heads = P->num_heads;
+  d.log2_ps = P->log2_ps;
+  d.sm_scale = P->sm_scale;
+  d.score_log2 = (float)((double)P->sm_scale * 1.4426950408889634);
+  const int slot_ev = (int)(P->timed_runs % pkvmla_plan_s::kTimingSlots);
+  if (P->timing) PKVMLA_HIP(hipEventRecord(P->ev[2 * slot_ev], s));
+  PKVMLA_HIP(pkvmla::launch_decode(d, P->sched.grid, s));
+  if (P->timing) {
+    PKVMLA_HIP(hipEventRecord(P->ev[2 * slot_ev + 1], s));
+    ++P->timed_runs;
+  }
+  const int n_merges = (int)(P->sched.merges.size() / pkvmla::kMergeRecordInts);
+  if (n_merges > 0) {
+    pkvmla::MergeParams m{};
+    m.part_o = d.part_o;
+    m.part_lse = d.part_lse;
+    m.merges = P->d_merges;
+    m.out = d.out;
+    m.lse = lse;
+    m.num_heads = P->num_heads;
+    PKVMLA_HIP(pkvmla::launch_merge(m, n_merges, s));
+  }
+  return ok();
+}
+
+void pkvmla_plan_destroy(pkvmla_plan P) { free_plan(P); }
+
+int pkvmla_plan_set_timing(pkvmla_plan P, int32_t enable) {
+  if (!P) return fail(PKVMLA_EINVAL, "null plan");
+  if (enable && !P->ev[0]) {
+    for (hipEvent_t& e : P->ev) PKVMLA_HIP(hipEventCreate(&e));
+  }
+  P->timing = enable ? 1 : 0;
+  P->timed_runs = 0;
+  return ok();
+}
+
+int pkvmla_plan_timing(pkvmla_plan P, double* total_ms, int64_t* n_runs) {
+  if (!P || !total_ms || !n_runs) return fail(PKVMLA_EINVAL, "null argument");
+  PKVMLA_HIP(hipDeviceSynchronize());
+  const int64_t n = std::min<int64_t>(P->timed_runs, pkvmla_plan_s::kTimingSlots);
+  double tot = 0.0;
+  for (int64_t i = 0; i < n; ++i) {
+    float ms = 0.f;
+    PKVMLA_HIP(hipEventElapsedTime(&ms, P->ev[2 * i], P->ev[2 * i + 1]));
+    tot += ms;
+  }
+  *total_ms = tot;
+  *n_runs = n;
+  return ok();
+}
+
+int pkvmla_plan_export(pkvmla_plan P, int32_t* buf, int64_t cap, int64_t* used) {
+  if (!P || !used) return fail(PKVMLA_EINVAL, "null plan or used pointer");
+  const int64_t n_wg = (int64_t)P->sched.wg_indptr.size();
+  const int64_t n_u = (int64_t)P->sched.units.size();
+  const int64_t n_m = (int64_t)P->sched.merges.size();
+  const int64_t need = 32 + n_wg + n_u + n_m + (P->num_seqs + 1) + P->num_seqs + P->n_indices;
+  *used = need;
+  if (!buf || cap < need) return fail(PKVMLA_EINVAL, "buffer too small: need %lld int32", (long long)need);
+  PKVMLA_HIP(hipDeviceSynchronize());
+  memset(buf, 0, 32 * sizeof(int32_t));
+  buf[0] = 1;
+  buf[1] = P->batch;
+  buf[2] = P->num_heads;
+  buf[3] = P->page_size;
+  buf[4] = P->ckv_dim;
+  buf[5] = P->kpe_dim;
+  buf[6] = pkvmla::kTile;
+  buf[7] = P->cfg.waves;
+  buf[8] = P->cfg.heads_per_wave;
+  buf[9] = P->cfg.stages;
+  buf[10] = P->cfg.wg_per_cu;
+  buf[11] = P->cfg.fixed_cost;
+  buf[12] = P->sched.grid;
+  buf[13] = (int32_t)(n_u / pkvmla::kUnitRecordInts);
+  buf[14] = (int32_t)(n_m / pkvmla::kMergeRecordInts);
+  buf[15] = P->sched.n_slots;
+  buf[16] = P->num_seqs;
+  buf[17] = (int32_t)P->n_indices;
+  buf[18] = P->num_cu;
+  memcpy(&buf[19], &P->sm_scale, sizeof(float));
+  buf[20] = P->is_cascade;
+  buf[21] = P->num_groups;
+  int32_t* dst = buf + 32;
+  auto pull = [&](const int32_t* src, int64_t n) -> hipError_t {
+    hipError_t e = n ? hipMemcpy(dst, src, n * sizeof(int32_t), hipMemcpyDeviceToHost) : hipSuccess;
+    dst += n;
+    return e;
+  };
+  PKVMLA_HIP(pull(P->d_wg_indptr, n_wg));
+  PKVMLA_HIP(pull(P->d_units, n_u));
+  PKVMLA_HIP(pull(P->d_merges, n_m));
+  PKVMLA_HIP(pull(P->d_seq_indptr, P->num_seqs + 1));
+  PKVMLA_HIP(pull(P->d_seq_lens, P->num_seqs));
+  PKVMLA_HIP(pull(P->d_seq_indices, P->n_indices));
+  return ok();
+}
+
+int pkvmla_gather_rows(pkvmla_plan P, int64_t* n_rows) {
+  if (!P || !n_rows) return fail(PKVMLA_EINVAL, "null argument");
+  *n_rows = P->sched.total_rows;
+  return ok();
+}
+
+int pkvmla_gather(pkvmla_plan P, const void* ckv_cache, const void* kpe_cache, void* rows,
+                  void* stream) {
+  if (!P) return fail(PKVMLA_EINVAL, "null plan");
+  if (!ckv_cache || !kpe_cache || (!rows && P->sched.total_rows > 0))
+    return fail(PKVMLA_EINVAL, "null tensor pointer");
+  if (!aligned16(ckv_cache) || !aligned16(kpe_cache) || !aligned16(rows))
+    return fail(PKVMLA_EINVAL, "device pointers must be 16-byte aligned");
+  int dev = -1;
+  PKVMLA_HIP(hipGetDevice(&dev));
+  if (dev != P->device)
+    return fail(PKVMLA_EINVAL, "plan was built on device %d, current device is %d", P->device,
+                dev);
+  pkvmla::GatherParams g{};
+  g.ckv = static_cast<const uint16_t*>(ckv_cache);
+  g.kpe = static_cast<const uint16_t*>(kpe_cache);
+  g.rows = static_cast<uint16_t*>(rows);
+  g.units = P->d_units;
+  g.seq_indptr = P->d_seq_indptr;
+  g.seq_indices = P->d_seq_indices;
+  g.log2_ps = P->log2_ps;
+  const int n_units = (int)(P->sched.units.size() / pkvmla::kUnitRecordInts);
+  PKVMLA_HIP(pkvmla::launch_gather(g, n_units, (hipStream_t)stream));
+  return ok();
+}
+
+}  // extern "C"

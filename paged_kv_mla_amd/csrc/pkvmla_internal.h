@@ -1,0 +1,72 @@
+// Internal declarations shared by the host library and the HIP kernels.
+#ifndef PKVMLA_INTERNAL_H_
+#define PKVMLA_INTERNAL_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+namespace pkvmla {
+
+constexpr int kCkvDim = 512;        // head_dim_ckv = kv_lora_rank
+constexpr int kKpeDim = 64;         // head_dim_kpe = qk_rope_head_dim
+constexpr int kTile = 32;           // KV tokens per tile
+constexpr int kUnitInts = 8;        // b, seq, kv_begin, kv_end, slot, row, 0, 0
+constexpr int kMergeInts = 4;       // b, first_slot, count, 0
+constexpr int kStageBytes = kTile * kCkvDim * 2 + kTile * kKpeDim * 2;  // 36864
+
+// Kernel shape for one head count.
+struct KernelConfig {
+  int waves;          // waves per workgroup
+  int heads_per_wave; // 16 * head blocks
+  int stages;         // LDS ring depth (tiles)
+  int wg_per_cu;      // resident workgroups per CU the schedule assumes
+  int fixed_cost;     // schedule cost of one segment, in tiles
+};
+
+bool kernel_config_for(int num_heads, KernelConfig* cfg);
+
+struct DecodeParams {
+  const uint16_t* q_nope;    // [B][H][512] bf16
+  const uint16_t* q_pe;      // [B][H][64]  bf16
+  const uint16_t* ckv;       // [P][ps][512] bf16
+  const uint16_t* kpe;       // [P][ps][64]  bf16
+  uint16_t* out;             // [B][H][512] bf16
+  float* lse;                // [B][H]
+  float* part_o;             // [slots][H][512]
+  float* part_lse;           // [slots][H]
+  const int32_t* wg_indptr;  // [grid + 1]
+  const int32_t* units;      // [n_units][8]
+  const int32_t* seq_indptr; // [num_seqs + 1]
+  const int32_t* seq_indices;
+  int32_t num_heads;
+  int32_t log2_ps;
+  float sm_scale;
+  float score_log2;          // sm_scale * log2(e)
+};
+
+struct MergeParams {
+  const float* part_o;
+  const float* part_lse;
+  const int32_t* merges;     // [n_merges][4]
+  uint16_t* out;
+  float* lse;
+  int32_t num_heads;
+};
+
+struct GatherParams {
+  const uint16_t* ckv;
+  const uint16_t* kpe;
+  uint16_t* rows;            // [n_rows][576]
+  const int32_t* units;
+  const int32_t* seq_indptr;
+  const int32_t* seq_indices;
+  int32_t log2_ps;
+};
+
+hipError_t launch_decode(const DecodeParams& p, int grid, hipStream_t stream);
+hipError_t launch_merge(const MergeParams& p, int n_merges, hipStream_t stream);
+hipError_t launch_gather(const GatherParams& p, int n_units, hipStream_t stream);
+
+}  // namespace pkvmla
+
+#endif  // PKVMLA_INTERNAL_H_

@@ -1,0 +1,144 @@
+"""CPU: the C-ABI library loads, exports every declared symbol, computes the
+same schedule as the independent re-derivation, and rejects bad arguments
+before touching the GPU (no compute calls here)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import paged_kv_mla_amd as pk
+from oracle.schedule_ref import schedule_ref, flat_items, cascade_items, kernel_config
+from mla_workloads import config_lens, CONFIGS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    txt = open(os.path.join(ROOT, "include", "pkvmla.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkvmla_[a-z_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    syms = declared_symbols()
+    assert len(syms) >= 10
+    lib = ctypes.CDLL(pk.LIB_PATH)
+    for s in syms:
+        assert hasattr(lib, s), s
+    assert sorted(pk.EXPORTED_SYMBOLS) == syms
+
+
+@pytest.mark.parametrize("H", [16, 32, 64, 128])
+def test_kernel_config_matches_table(H):
+    lib = pk.kernel_config(H)
+    ref = kernel_config(H)
+    assert lib == {k: ref[k] for k in lib}
+
+
+def test_kernel_config_rejects_other_head_counts():
+    with pytest.raises(pk.PkvmlaError) as e:
+        pk.kernel_config(48)
+    assert e.value.code == pk.EUNSUPPORTED
+
+
+def _compare(items, batch, num_wg, tile, fixed):
+    w1, u1, m1 = pk.schedule_host(items, batch, num_wg, tile, fixed)
+    w2, u2, m2 = schedule_ref(items, batch, num_wg, tile, fixed)
+    np.testing.assert_array_equal(w1, w2)
+    np.testing.assert_array_equal(u1, u2)
+    np.testing.assert_array_equal(m1, m2)
+
+
+@pytest.mark.parametrize("name", ["tiny", "deepseek", "long", "ragged"])
+@pytest.mark.parametrize("num_cu", [256, 304, 80, 7, 1])
+def test_schedule_host_matches_reference(name, num_cu):
+    lens = config_lens(name)
+    kc = kernel_config(CONFIGS[name]["num_heads"])
+    _compare(flat_items(lens), len(lens), num_cu * kc["wg_per_cu"], kc["tile"], kc["fixed_cost"])
+
+
+def test_schedule_host_matches_reference_cascade():
+    prefix, suffix = config_lens("cascade")
+    B = len(suffix)
+    items = cascade_items(np.array([0, B]), np.array([prefix]), suffix)
+    _compare(items, B, 256, 32, 2)
+    items = cascade_items(np.array([0, 2, 5]), np.array([64, 0]), np.array([3, 0, 40, 0, 1]))
+    _compare(items, 5, 512, 32, 1)
+
+
+def test_schedule_host_random_cases():
+    rng = np.random.default_rng(7)
+    for _ in range(200):
+        B = int(rng.integers(1, 40))
+        lens = rng.integers(0, 3000, size=B)
+        lens[rng.integers(0, B)] = max(1, lens.max())
+        items = flat_items(lens)
+        _compare(items, B, int(rng.integers(1, 600)), int(rng.choice([16, 32, 64])),
+                 int(rng.integers(0, 4)))
+
+
+# ---------------------------------------------------------------- validation
+def _flat_args(**kw):
+    a = dict(kv_indptr=[0, 2, 3], kv_indices=[0, 1, 2], kv_lens=[20, 5], num_heads=16,
+             page_size=16, num_pages=4)
+    a.update(kw)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kv_indptr=[1, 2, 3]), pk.EINVAL),                 # indptr[0] != 0
+    (dict(kv_indptr=[0, 3, 2]), pk.EINVAL),                 # non-monotone
+    (dict(kv_lens=[0, 5]), pk.EINVAL),                      # empty request
+    (dict(kv_lens=[33, 5]), pk.EINVAL),                     # more tokens than 2 pages hold
+    (dict(kv_indices=[0, 9, 2]), pk.EINVAL),                # page id outside the pool
+    (dict(kv_indices=[0, -1, 2]), pk.EINVAL),
+    (dict(num_pages=0), pk.EINVAL),
+    (dict(page_size=0), pk.EINVAL),
+    (dict(page_size=24), pk.EUNSUPPORTED),                  # not a power of two
+    (dict(page_size=512), pk.EUNSUPPORTED),
+    (dict(num_heads=8), pk.EUNSUPPORTED),
+    (dict(num_heads=1), pk.EUNSUPPORTED),
+    (dict(ckv_dim=1), pk.EUNSUPPORTED),                     # head_dim_ckv = num_kv_heads mistake
+    (dict(ckv_dim=256), pk.EUNSUPPORTED),
+    (dict(kpe_dim=32), pk.EUNSUPPORTED),
+    (dict(sm_scale=float("nan")), pk.EINVAL),
+    (dict(sm_scale=float("inf")), pk.EINVAL),
+    (dict(sm_scale=-0.5), pk.EINVAL),
+])
+def test_plan_create_rejects(kw, code):
+    with pytest.raises(pk.PkvmlaError) as e:
+        pk.plan(**_flat_args(**kw))
+    assert e.value.code == code
+    assert pk.last_error()
+
+
+def test_cascade_validation():
+    base = dict(group_req_indptr=[0, 2], prefix_indptr=[0, 1], prefix_indices=[0],
+                prefix_lens=[16], kv_indptr=[0, 1, 1], kv_indices=[1], kv_lens=[3, 0],
+                num_heads=16, page_size=16, num_pages=4)
+    for kw, code in [
+        (dict(group_req_indptr=[0, 1]), pk.EINVAL),         # groups must cover the batch
+        (dict(prefix_lens=[17]), pk.EINVAL),                # prefix longer than its page
+        (dict(prefix_lens=[0]), pk.EINVAL),                 # request 1 would attend nothing
+        (dict(kv_lens=[-1, 0]), pk.EINVAL),
+        (dict(prefix_indices=[7]), pk.EINVAL),
+    ]:
+        a = dict(base)
+        a.update(kw)
+        with pytest.raises(pk.PkvmlaError) as e:
+            pk.plan_cascade(**a)
+        assert e.value.code == code, kw
+
+
+def test_null_pointer_arguments_rejected():
+    lib = ctypes.CDLL(pk.LIB_PATH)
+    lib.pkvmla_run.argtypes = [ctypes.c_void_p] * 8
+    assert lib.pkvmla_run(None, None, None, None, None, None, None, None) == pk.EINVAL
+    lib.pkvmla_plan_destroy.argtypes = [ctypes.c_void_p]
+    lib.pkvmla_plan_destroy(None)  # no-op
+    lib.pkvmla_plan_create.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int32] * 6 + \
+        [ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.pkvmla_plan_create(None, None, None, 1, 1, 16, 512, 64, 16, 0.0, None, None) == pk.EINVAL

@@ -1,0 +1,234 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small cases compare every element; full-size workloads compare every request
+the oracle can afford (sampled requests for the largest), in the same launch
+configuration the benchmark times.  Integer work (page-table gather, plan
+tables) is compared bit for bit.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.schedule_ref import schedule_ref, flat_items, cascade_items, kernel_config
+from mla_workloads import (make_flat, make_cascade, make_config, stress_variant,
+                           poison_unreferenced, permute_pages, STRESS_KINDS)
+from gpu_helpers import Dev, run_gpu, oracle_flat, oracle_cascade, compare, bits_of, dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+pk = pytest.importorskip("paged_kv_mla_amd")
+
+
+def note(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _cuda():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+    yield
+
+
+def small(seed, lens, H=16, ps=16, pool=None, extra=0, sm_scale=None):
+    return make_flat(f"s{seed}", seed, len(lens), H, ps, list(lens), pool_pages=pool,
+                     extra_pages=extra, sm_scale=sm_scale)
+
+
+# ------------------------------------------------------------- integer paths
+GATHER_CASES = {
+    "tiny": lambda: make_config("tiny"),
+    "tiny_perm_poison": lambda: poison_unreferenced(permute_pages(make_config("tiny"), 3)),
+    "ps1_scatter": lambda: small(61, [1, 2, 33, 95, 64], H=16, ps=1),
+    "ps64_extra_pages": lambda: small(62, [1, 64, 65, 300], H=128, ps=64, extra=1),
+    "ps256": lambda: small(63, [5, 511, 700], H=32, ps=256),
+}
+
+
+@pytest.mark.parametrize("name", sorted(GATHER_CASES))
+def test_gather_bit_exact(name):
+    inp = GATHER_CASES[name]()
+    note(f"gather {name}")
+    plan = pk.plan_for(inp)
+    d = Dev(inp)
+    rows = plan.gather(d.ckv, d.kpe)
+    torch.cuda.synchronize()
+    ref = oracle.gather_ref(inp.ckv, inp.kpe, inp.kv_indptr, inp.kv_indices, inp.kv_lens,
+                            inp.page_size)
+    assert np.array_equal(bits_of(rows), ref)
+
+
+def test_gather_bit_exact_cascade():
+    cas = make_cascade("cg", 64, 5, 16, 16, [32, 48], [1, 20, 0, 33, 5], groups=2)
+    note("gather cascade")
+    rows = pk.plan_for(cas).gather(dev_bf16(cas.ckv), dev_bf16(cas.kpe))
+    flat = cas.flat_view()
+    ref = oracle.gather_ref(flat.ckv, flat.kpe, flat.kv_indptr, flat.kv_indices, flat.kv_lens,
+                            flat.page_size)
+    assert np.array_equal(bits_of(rows), ref)
+
+
+@pytest.mark.parametrize("name", ["tiny", "deepseek", "ragged"])
+def test_plan_export_bit_exact(name):
+    from mla_workloads import config_lens, CONFIGS
+    cfg = CONFIGS[name]
+    lens = config_lens(name)
+    # page tables only matter for the seq tables: a simple contiguous layout
+    ps = cfg["page_size"]
+    npg = (lens.astype(np.int64) + ps - 1) // ps
+    indptr = np.concatenate([[0], np.cumsum(npg)]).astype(np.int32)
+    indices = np.arange(indptr[-1], dtype=np.int32)[::-1].copy()
+    note(f"export {name}")
+    plan = pk.plan(indptr, indices, lens, cfg["num_heads"], ps, int(indptr[-1]))
+    ex = plan.export()
+    kc = kernel_config(cfg["num_heads"])
+    hdr = ex.header
+    assert list(hdr[:12]) == [1, len(lens), cfg["num_heads"], ps, 512, 64, kc["tile"],
+                              kc["waves"], kc["heads_per_wave"], kc["stages"], kc["wg_per_cu"],
+                              kc["fixed_cost"]]
+    wg, units, merges = schedule_ref(flat_items(lens), len(lens), ex.num_cu * kc["wg_per_cu"],
+                                     kc["tile"], kc["fixed_cost"])
+    np.testing.assert_array_equal(ex.wg_indptr, wg)
+    np.testing.assert_array_equal(ex.units, units)
+    np.testing.assert_array_equal(ex.merges, merges)
+    np.testing.assert_array_equal(ex.seq_indptr, indptr)
+    np.testing.assert_array_equal(ex.seq_lens, lens)
+    np.testing.assert_array_equal(ex.seq_indices, indices)
+    assert ex.sm_scale == np.float32(1.0 / math.sqrt(576))
+
+
+def test_plan_export_cascade():
+    cas = make_cascade("ce", 65, 6, 64, 16, [32, 48], [1, 20, 0, 33, 5, 7], groups=2)
+    note("export cascade")
+    ex = pk.plan_for(cas).export()
+    kc = kernel_config(64)
+    items = cascade_items(cas.group_req_indptr, cas.prefix_lens, cas.kv_lens)
+    wg, units, merges = schedule_ref(items, cas.batch, ex.num_cu * kc["wg_per_cu"], kc["tile"],
+                                     kc["fixed_cost"])
+    np.testing.assert_array_equal(ex.units, units)
+    np.testing.assert_array_equal(ex.merges, merges)
+    np.testing.assert_array_equal(ex.wg_indptr, wg)
+    G = cas.num_groups
+    np.testing.assert_array_equal(ex.seq_lens, np.concatenate([cas.prefix_lens, cas.kv_lens]))
+    np.testing.assert_array_equal(
+        ex.seq_indptr, np.concatenate([cas.prefix_indptr, cas.prefix_indptr[G] + cas.kv_indptr[1:]]))
+
+
+# ------------------------------------------------------------ decode parity
+SMALL_CASES = {
+    "tiny": lambda: make_config("tiny"),
+    "h16_ps1": lambda: small(71, [1, 2, 31, 32, 33, 257], H=16, ps=1),
+    "h32_ps16": lambda: small(72, [1, 17, 64, 200, 513], H=32, ps=16),
+    "h64_ps64": lambda: small(73, [1, 63, 64, 65, 1000], H=64, ps=64),
+    "h128_ps64": lambda: small(74, [1, 33, 100, 700, 2049], H=128, ps=64),
+    "h128_ps16": lambda: small(75, [1, 5, 96, 300], H=128, ps=16),
+    "h128_ps1": lambda: small(76, [1, 31, 160], H=128, ps=1),
+    "h16_ps256": lambda: small(77, [3, 256, 257, 900], H=16, ps=256),
+    "h64_ps2_explicit_scale": lambda: small(78, [1, 9, 77, 130], H=64, ps=2, sm_scale=0.11),
+    "h128_extra_pages": lambda: small(79, [1, 40, 64, 129], H=128, ps=64, extra=2),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL_CASES))
+def test_decode_small(name):
+    inp = SMALL_CASES[name]()
+    note(f"decode {name}")
+    out, lse = run_gpu(pk.plan_for(inp), Dev(inp))
+    ref_o, ref_l = oracle_flat(inp)
+    compare(out, lse, ref_o, ref_l, name=name)
+
+
+@pytest.mark.parametrize("kind", STRESS_KINDS)
+@pytest.mark.parametrize("H,ps", [(16, 16), (128, 64), (64, 1)])
+def test_decode_stress(kind, H, ps):
+    base = small(80 + H + ps, [1, 17, 64, 200, 777], H=H, ps=ps)
+    inp = stress_variant(base, kind)
+    note(f"stress {kind} H{H} ps{ps}")
+    out, lse = run_gpu(pk.plan_for(inp), Dev(inp))
+    ref_o, ref_l = oracle_flat(inp)
+    compare(out, lse, ref_o, ref_l, name=f"{kind}/H{H}/ps{ps}")
+
+
+@pytest.mark.parametrize("H,ps", [(16, 16), (128, 64), (32, 1)])
+def test_poison_permutation_and_determinism(H, ps):
+    inp = small(90 + H, [1, 15, 64, 333], H=H, ps=ps, extra=1)
+    note(f"invariants H{H} ps{ps}")
+    d = Dev(inp)
+    plan = pk.plan_for(inp)
+    o1, l1 = run_gpu(plan, d)
+    o1, l1 = bits_of(o1), l1.cpu().numpy().copy()
+    # run to run: bitwise identical, every output written (NaN-prefilled buffers)
+    out = torch.full((inp.batch, H, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((inp.batch, H), float("nan"), dtype=torch.float32, device="cuda")
+    o2, l2 = run_gpu(plan, d, out=out, lse=lse)
+    assert np.array_equal(bits_of(o2), o1) and np.array_equal(l2.cpu().numpy(), l1)
+    # NaN in every slot no request attends: bitwise identical
+    pz = poison_unreferenced(inp)
+    o3, l3 = run_gpu(pk.plan_for(pz), Dev(pz))
+    assert np.array_equal(bits_of(o3), o1) and np.array_equal(l3.cpu().numpy(), l1)
+    # physical page permutation: bitwise identical
+    pp = permute_pages(inp, seed=11)
+    o4, l4 = run_gpu(pk.plan_for(pp), Dev(pp))
+    assert np.array_equal(bits_of(o4), o1) and np.array_equal(l4.cpu().numpy(), l1)
+
+
+@pytest.mark.parametrize("H", [16, 128])
+def test_single_token_is_exact(H):
+    """kv_len = 1: the softmax weight is exactly 1, so out is the ckv row bit for bit."""
+    inp = small(95, [1, 1, 1, 1], H=H, ps=16, pool=20)
+    note(f"single token H{H}")
+    out, lse = run_gpu(pk.plan_for(inp), Dev(inp))
+    ob = bits_of(out)
+    for b in range(inp.batch):
+        p = inp.kv_indices[inp.kv_indptr[b]]
+        assert np.array_equal(ob[b], np.broadcast_to(inp.ckv[p, 0], ob[b].shape))
+    _, ref_l = oracle_flat(inp)
+    np.testing.assert_allclose(lse.double().cpu().numpy(), ref_l, atol=1e-5, rtol=0)
+
+
+def test_cascade_small():
+    cas = make_cascade("cs", 96, 6, 64, 16, [32, 48], [1, 20, 0, 33, 5, 300], groups=2)
+    note("cascade small")
+    out, lse = run_gpu(pk.plan_for(cas), Dev(cas))
+    ref_o, ref_l = oracle_cascade(cas)
+    compare(out, lse, ref_o, ref_l, name="cascade small")
+    fo, fl = run_gpu(pk.plan_for(cas.flat_view()), Dev(cas))
+    compare(out, lse, *oracle_flat(cas.flat_view()), name="cascade vs flat oracle")
+    # cascade and flat plans on the GPU agree within the same bar
+    compare(out, lse, fo.float().double().cpu().numpy(), fl.double().cpu().numpy(),
+            name="cascade vs flat gpu")
+
+
+# ------------------------------------------------------------- full sizes
+FULL = {"deepseek": None, "long": None, "ragged": None}
+
+
+@pytest.mark.parametrize("name", ["deepseek", "long", "ragged"])
+def test_full_size_flat(name):
+    inp = make_config(name)
+    note(f"full {name}: B={inp.batch} H={inp.num_heads} tokens={inp.total_tokens}")
+    out, lse = run_gpu(pk.plan_for(inp), Dev(inp))
+    if name == "long":
+        reqs = [0, 3, 7]
+    elif name == "deepseek":
+        reqs = list(range(0, inp.batch, 4))
+    else:
+        reqs = list(range(inp.batch))
+    ref_o, ref_l = oracle_flat(inp, reqs)
+    st = compare(out, lse, ref_o, ref_l, requests=reqs, name=name)
+    note(f"full {name} stats {st}")
+
+
+def test_full_size_cascade():
+    cas = make_config("cascade")
+    note(f"full cascade: B={cas.batch} attended={cas.attended_tokens()}")
+    out, lse = run_gpu(pk.plan_for(cas), Dev(cas))
+    reqs = [0, 31, 64, 127]
+    ref_o, ref_l = oracle_cascade(cas, reqs)
+    st = compare(out, lse, ref_o, ref_l, requests=reqs, name="cascade")
+    note(f"full cascade stats {st}")
