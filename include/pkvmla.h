@@ -121,8 +121,10 @@ const char* pkvmla_last_error(void);
 /* Kernel configuration used for num_heads (values the schedule depends on):
  * cfg[0] = KV tile tokens, cfg[1] = waves per workgroup, cfg[2] = heads per
  * wave, cfg[3] = LDS stages, cfg[4] = workgroups per CU, cfg[5] = fixed cost
- * per segment in tiles.  Host only; needs no GPU. */
-int pkvmla_kernel_config(int32_t num_heads, int32_t* cfg6);
+ * per segment in tiles, cfg[6] = head groups (workgroups that share one
+ * token range, each holding num_heads / head_groups heads; the schedule has
+ * num_cu * workgroups_per_cu / head_groups lanes).  Host only; needs no GPU. */
+int pkvmla_kernel_config(int32_t num_heads, int32_t* cfg7);
 
 /* The split-KV work schedule, computed on the host exactly as plan_create
  * does (no GPU needed).  items: host int32[n_items*3] of (request, sequence,
@@ -144,7 +146,7 @@ int pkvmla_schedule_host(const int32_t* items, int32_t n_items, int32_t batch,
  *            kpe_dim, tile, waves, heads_per_wave, stages, wg_per_cu,
  *            fixed_cost, grid, n_units, n_merges, n_slots
  *   [16..31] header 2: num_seqs, n_indices, num_cu, sm_scale (float bits),
- *            is_cascade, num_groups, 0...
+ *            is_cascade, num_groups, head_groups, launched workgroups, 0...
  *   then wg_indptr[grid+1], units[n_units*8], merges[n_merges*4],
  *   seq_indptr[num_seqs+1], seq_lens[num_seqs], seq_indices[n_indices].
  * *used = number of int32 written (or needed, when cap is too small:

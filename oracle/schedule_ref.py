@@ -37,20 +37,26 @@ UNIT_INTS = 8           # int32 per unit record: b, seq, kv_begin, kv_end, slot,
 MERGE_INTS = 4          # int32 per merge record: b, first_slot, count, 0
 
 # Per head count: (waves per workgroup, heads per wave, LDS stages,
-# workgroups per CU, fixed cost per segment in tiles).  The library exports
-# the values it uses; the tests compare them with this table.
+# workgroups per CU, fixed cost per segment in tiles, head groups).  The
+# schedule has (CUs x workgroups per CU) / head groups lanes.  The library
+# exports the values it uses; the tests compare them with this table.
 _KERNEL_CONFIGS = {
-    16: (1, 16, 2, 2, 1),
-    32: (2, 16, 2, 2, 1),
-    64: (4, 16, 4, 1, 2),
-    128: (4, 32, 4, 1, 2),
+    16: (1, 16, 2, 2, 1, 1),
+    32: (2, 16, 2, 2, 1, 1),
+    64: (4, 16, 4, 1, 2, 1),
+    128: (4, 32, 4, 1, 2, 1),
 }
 
 
 def kernel_config(num_heads: int):
-    waves, hpw, stages, wg_per_cu, fixed = _KERNEL_CONFIGS[int(num_heads)]
+    waves, hpw, stages, wg_per_cu, fixed, hg = _KERNEL_CONFIGS[int(num_heads)]
     return dict(waves=waves, heads_per_wave=hpw, stages=stages,
-                wg_per_cu=wg_per_cu, fixed_cost=fixed, tile=PLAN_TILE)
+                wg_per_cu=wg_per_cu, fixed_cost=fixed, head_groups=hg, tile=PLAN_TILE)
+
+
+def schedule_lanes(num_cu: int, num_heads: int) -> int:
+    kc = kernel_config(num_heads)
+    return max(1, num_cu * kc["wg_per_cu"] // kc["head_groups"])
 
 
 def flat_items(kv_lens):

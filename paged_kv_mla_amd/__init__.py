@@ -98,9 +98,9 @@ def _stream_handle(stream) -> int:
 
 
 def kernel_config(num_heads: int) -> dict:
-    cfg = np.zeros(6, dtype=np.int32)
+    cfg = np.zeros(7, dtype=np.int32)
     _check(_lib.pkvmla_kernel_config(int(num_heads), _ptr(cfg)))
-    keys = ("tile", "waves", "heads_per_wave", "stages", "wg_per_cu", "fixed_cost")
+    keys = ("tile", "waves", "heads_per_wave", "stages", "wg_per_cu", "fixed_cost", "head_groups")
     return {k: int(v) for k, v in zip(keys, cfg)}
 
 
@@ -140,6 +140,10 @@ class PlanExport:
     @property
     def num_cu(self) -> int:
         return int(self.header[18])
+
+    @property
+    def head_groups(self) -> int:
+        return int(self.header[22])
 
 
 class Plan:

@@ -135,7 +135,8 @@ int finish_plan(pkvmla_plan_s* P, const std::vector<pkvmla::WorkItem>& items,
                 const std::vector<int32_t>& seq_indices, hipStream_t stream) {
   PKVMLA_HIP(hipGetDevice(&P->device));
   PKVMLA_HIP(hipDeviceGetAttribute(&P->num_cu, hipDeviceAttributeMultiprocessorCount, P->device));
-  const int32_t num_wg = P->num_cu * P->cfg.wg_per_cu;
+  // the schedule's lanes: each lane's token ranges are replicated over the head groups
+  const int32_t num_wg = std::max(1, P->num_cu * P->cfg.wg_per_cu / P->cfg.head_groups);
   if (!pkvmla::build_schedule(items, P->batch, num_wg, pkvmla::kTile, P->cfg.fixed_cost,
                               &P->sched))
     return fail(PKVMLA_EINVAL, "schedule construction failed");
@@ -151,7 +152,9 @@ int finish_plan(pkvmla_plan_s* P, const std::vector<pkvmla::WorkItem>& items,
   size_t off_wg = 0, off_units = off_wg + pad(n_wg), off_merges = off_units + pad(n_units);
   size_t off_sip = off_merges + pad(n_merges), off_sl = off_sip + pad(seq_indptr.size());
   size_t off_si = off_sl + pad(seq_lens.size());
-  P->table_ints = off_si + pad(seq_indices.size() ? seq_indices.size() : 1);
+  // the kernels read page ids of whole tiles unclamped: kIndexPad trailing
+  // entries (page 0, a valid id) keep every such read inside the table
+  P->table_ints = off_si + pad(seq_indices.size() + pkvmla::kIndexPad);
   PKVMLA_HIP(hipMalloc(&P->d_tables, P->table_ints * sizeof(int32_t)));
   P->d_wg_indptr = P->d_tables + off_wg;
   P->d_units = P->d_tables + off_units;
@@ -191,18 +194,19 @@ extern "C" {
 
 const char* pkvmla_last_error(void) { return g_last_error.c_str(); }
 
-int pkvmla_kernel_config(int32_t num_heads, int32_t* cfg6) {
-  if (!cfg6) return fail(PKVMLA_EINVAL, "null output");
+int pkvmla_kernel_config(int32_t num_heads, int32_t* cfg7) {
+  if (!cfg7) return fail(PKVMLA_EINVAL, "null output");
   pkvmla::KernelConfig c;
   if (!pkvmla::kernel_config_for(num_heads, &c))
     return fail(PKVMLA_EUNSUPPORTED, "num_heads must be one of 16, 32, 64, 128 (got %d)",
                 num_heads);
-  cfg6[0] = pkvmla::kTile;
-  cfg6[1] = c.waves;
-  cfg6[2] = c.heads_per_wave;
-  cfg6[3] = c.stages;
-  cfg6[4] = c.wg_per_cu;
-  cfg6[5] = c.fixed_cost;
+  cfg7[0] = pkvmla::kTile;
+  cfg7[1] = c.waves;
+  cfg7[2] = c.heads_per_wave;
+  cfg7[3] = c.stages;
+  cfg7[4] = c.wg_per_cu;
+  cfg7[5] = c.fixed_cost;
+  cfg7[6] = c.head_groups;
   return ok();
 }
 
@@ -378,12 +382,18 @@ int pkvmla_run(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* 
   d.seq_indptr = P->d_seq_indptr;
   d.seq_indices = P->d_seq_indices;
   d.num_heads = P->num_heads;
+  d.head_groups = P->cfg.head_groups;
+  d.n_lanes = P->sched.grid;
+  d.waves = P->cfg.waves;
+  d.heads_per_wave = P->cfg.heads_per_wave;
+  d.stages = P->cfg.stages;
   d.log2_ps = P->log2_ps;
   d.sm_scale = P->sm_scale;
   d.score_log2 = (float)((double)P->sm_scale * 1.4426950408889634);
+  d.rescale_thr = (float)(8.0 / ((double)P->sm_scale * 1.4426950408889634));
   const int slot_ev = (int)(P->timed_runs % pkvmla_plan_s::kTimingSlots);
   if (P->timing) PKVMLA_HIP(hipEventRecord(P->ev[2 * slot_ev], s));
-  PKVMLA_HIP(pkvmla::launch_decode(d, P->sched.grid, s));
+  PKVMLA_HIP(pkvmla::launch_decode(d, s));
   if (P->timing) {
     PKVMLA_HIP(hipEventRecord(P->ev[2 * slot_ev + 1], s));
     ++P->timed_runs;
@@ -461,6 +471,8 @@ int pkvmla_plan_export(pkvmla_plan P, int32_t* buf, int64_t cap, int64_t* used) 
   memcpy(&buf[19], &P->sm_scale, sizeof(float));
   buf[20] = P->is_cascade;
   buf[21] = P->num_groups;
+  buf[22] = P->cfg.head_groups;
+  buf[23] = pkvmla::decode_grid(P->sched.grid, P->cfg.head_groups);
   int32_t* dst = buf + 32;
   auto pull = [&](const int32_t* src, int64_t n) -> hipError_t {
     hipError_t e = n ? hipMemcpy(dst, src, n * sizeof(int32_t), hipMemcpyDeviceToHost) : hipSuccess;

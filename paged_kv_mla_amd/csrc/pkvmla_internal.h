@@ -13,6 +13,7 @@ constexpr int kTile = 32;           // KV tokens per tile
 constexpr int kUnitInts = 8;        // b, seq, kv_begin, kv_end, slot, row, 0, 0
 constexpr int kMergeInts = 4;       // b, first_slot, count, 0
 constexpr int kStageBytes = kTile * kCkvDim * 2 + kTile * kKpeDim * 2;  // 36864
+constexpr int kIndexPad = 64;       // valid trailing page ids after the device index table
 
 // Kernel shape for one head count.
 struct KernelConfig {
@@ -21,6 +22,7 @@ struct KernelConfig {
   int stages;         // LDS ring depth (tiles)
   int wg_per_cu;      // resident workgroups per CU the schedule assumes
   int fixed_cost;     // schedule cost of one segment, in tiles
+  int head_groups;    // workgroups sharing one token range, each with H / head_groups heads
 };
 
 bool kernel_config_for(int num_heads, KernelConfig* cfg);
@@ -39,9 +41,13 @@ struct DecodeParams {
   const int32_t* seq_indptr; // [num_seqs + 1]
   const int32_t* seq_indices;
   int32_t num_heads;
+  int32_t head_groups;
+  int32_t n_lanes;           // schedule lanes (workgroups per head group)
+  int32_t waves, heads_per_wave, stages;
   int32_t log2_ps;
   float sm_scale;
   float score_log2;          // sm_scale * log2(e)
+  float rescale_thr;         // raw-score margin before the running max moves (8 / score_log2)
 };
 
 struct MergeParams {
@@ -63,7 +69,8 @@ struct GatherParams {
   int32_t log2_ps;
 };
 
-hipError_t launch_decode(const DecodeParams& p, int grid, hipStream_t stream);
+int decode_grid(int n_lanes, int head_groups);
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int n_merges, hipStream_t stream);
 hipError_t launch_gather(const GatherParams& p, int n_units, hipStream_t stream);
 

@@ -17,6 +17,8 @@
 
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
 
 #include "pkvmla_internal.h"
 
@@ -34,19 +36,24 @@ typedef uint32_t u32x4_t __attribute__((__vector_size__(16)));
 // LDS tile layout (one stage, 36864 bytes):
 //   [0, 32768)      ckv rows: token t at t*1024, its 16-byte chunk c (dims
 //                   8c..8c+7) at chunk position c ^ swz16(t)
-//   [32768, 36864)  kpe rows: token t at 32768 + t*128, chunk c at c ^ (t & 7)
-// The XOR swizzles keep the MFMA operand reads free of bank conflicts: 16
-// consecutive tokens reading one chunk hit 16 different 16-byte bank groups,
-// and the transposed V reads (4 tokens x 2 chunks per 16 lanes) hit 8.
+//   [32768, 36864)  kpe rows: token t at 32768 + t*128, chunk c at c ^ swz8(t)
+// The XOR swizzles keep every MFMA operand read free of bank conflicts for
+// both a 64-bank (16 lanes x 16 B or 32 lanes x 8 B per cycle) and a 32-bank
+// LDS: 16 consecutive tokens reading one chunk cover all 16 16-byte slots of
+// 256 bytes, and the transposed V reads (8 tokens x 2 chunks per 32 lanes)
+// do too.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int swz16(int t) {
-  return ((t & 3) << 1) | ((t >> 2) & 1) | (t & 8);
+  return (((t >> 2) ^ (t >> 3)) & 1) | ((t & 7) << 1);
+}
+__device__ __forceinline__ int swz8(int t) {
+  return (t ^ (t >> 3)) & 7;
 }
 __device__ __forceinline__ int lds_ckv_off(int t, int c) {
   return t * 1024 + ((c ^ swz16(t)) << 4);
 }
 __device__ __forceinline__ int lds_kpe_off(int t, int c) {
-  return kTile * 1024 + t * 128 + ((c ^ (t & 7)) << 4);
+  return kTile * 1024 + t * 128 + ((c ^ swz8(t)) << 4);
 }
 
 // gfx9 s_waitcnt immediate: wait until at most N vector-memory ops are
@@ -83,49 +90,135 @@ __device__ __forceinline__ constexpr int loads_per_tile(int wave) {
   return kTile / NW + ((NW >= 4) ? (wave < 4 ? 1 : 0) : 4 / NW);
 }
 
-// Issue this wave's share of the direct-to-LDS loads of one KV tile.
-// Tokens past kv_end are clamped to the last valid token (finite data; their
-// scores are masked and their probabilities are exactly zero), so slots past
-// kv_len and unlisted pages are never read.  Every page id is read with a
-// wave-uniform address, i.e. through the scalar cache, so the vector-memory
-// counter only ever tracks the tile loads themselves.
-template <int NW>
-__device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ ckv,
-                                           const uint16_t* __restrict__ kpe,
-                                           const int32_t* __restrict__ pages, int log2_ps,
-                                           int tok0, int kv_end, uint32_t stage_base,
-                                           int wave, int lane) {
-  const int ps_mask = (1 << log2_ps) - 1;
+// Page ids of one KV tile, as far as this wave needs them to issue its loads.
+// Read with wave-uniform addresses, i.e. through the scalar cache, one tile
+// ahead of the copies that use them, so the scalar-load latency never sits
+// between a tile becoming free and its next copy starting.  When a page holds
+// whole tiles (page_size >= 32; tiles start at multiples of 32 tokens) one id
+// serves the entire tile.  Otherwise each token's id is read unclamped (the
+// device index table carries kIndexPad valid trailing entries, so the read
+// stays inside it) and tokens past kv_end use the row of the last valid token
+// instead: slots past kv_len and unlisted pages are never copied, and every
+// copied row is finite data whose probability is masked to exactly zero.
+template <int NW, bool BIG>
+struct TilePages {
+  static constexpr int kRows = kTile / NW;                  // ckv rows copied by this wave
+  static constexpr int kKpe = (4 + NW - 1) / NW;            // kpe blocks of 8 tokens (bound)
+  static constexpr int kIds = BIG ? 1 : kRows;
+  static constexpr int kKpeIds = (BIG || NW == 1) ? 1 : kKpe * 8;  // one wave reuses its ckv ids
+  int pc[kIds];
+  int pk[kKpeIds];
+  int plast;  // page id of the last valid token of the tile
+};
+
+template <int NW, bool BIG>
+__device__ __forceinline__ void load_tile_pages(TilePages<NW, BIG>& tp,
+                                                const int32_t* __restrict__ pages, int log2_ps,
+                                                int tok0, int kv_end, int wave) {
+  if constexpr (BIG) {
+    tp.pc[0] = pages[tok0 >> log2_ps];
+  } else {
+    const int last = min(kv_end - 1 - tok0, kTile - 1);
+    tp.plast = pages[(tok0 + last) >> log2_ps];
 #pragma unroll
-  for (int k = 0; k < kTile / NW; ++k) {
-    const int t = k * NW + wave;
-    const int tok = min(tok0 + t, kv_end - 1);
-    const int page = pages[tok >> log2_ps];
-    const size_t row = ((size_t)(uint32_t)page << log2_ps) + (size_t)(tok & ps_mask);
-    const char* src = reinterpret_cast<const char*>(ckv) + row * (kCkvDim * 2) +
-                      ((lane ^ swz16(t)) << 4);
-    dma16(src, stage_base + t * 1024);
-  }
-  // kpe: 4 loads of 8 tokens (64 lanes x 16 bytes); lane -> token 8j + lane/8
+    for (int k = 0; k < TilePages<NW, BIG>::kRows; ++k)
+      tp.pc[k] = pages[(tok0 + k * NW + wave) >> log2_ps];
+    if constexpr (NW > 1) {
 #pragma unroll
-  for (int jj = 0; jj < (4 + NW - 1) / NW; ++jj) {
-    const int j = jj * NW + wave;
-    if (j < 4) {
-      int pg = 0;
+      for (int jj = 0; jj < TilePages<NW, BIG>::kKpe; ++jj) {
+        const int j = jj * NW + wave;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int tk = min(tok0 + 8 * j + k, kv_end - 1);
-        const int pk = pages[tk >> log2_ps];
-        pg = ((lane >> 3) == k) ? pk : pg;
+        for (int k = 0; k < 8; ++k)
+          tp.pk[jj * 8 + k] = (j < 4) ? pages[(tok0 + 8 * j + k) >> log2_ps] : 0;
       }
-      const int t = 8 * j + (lane >> 3);
-      const int tok = min(tok0 + t, kv_end - 1);
-      const size_t row = ((size_t)(uint32_t)pg << log2_ps) + (size_t)(tok & ps_mask);
-      const char* src = reinterpret_cast<const char*>(kpe) + row * (kKpeDim * 2) +
-                        (((lane & 7) ^ (t & 7)) << 4);
-      dma16(src, stage_base + kTile * 1024 + j * 1024);
     }
   }
+}
+
+// Issue the direct-to-LDS loads [K0, K1) of this wave's share of one KV tile:
+// index k < kRows is ckv row k*NW + wave, then kpe block (k - kRows)*NW + wave
+// (8 tokens, 64 lanes x 16 bytes).  Splitting the issue lets the loads of the
+// next tile go out between the MFMAs of the current one.
+// K0/K1 are compile-time constants at every call site once the caller's loop
+// is unrolled, so the page-id arrays are always indexed statically.
+template <int NW, bool BIG>
+__device__ __forceinline__ void issue_dma(const TilePages<NW, BIG>& tp,
+                                          const uint16_t* __restrict__ ckv,
+                                          const uint16_t* __restrict__ kpe, int log2_ps, int tok0,
+                                          int kv_end, uint32_t stage_base, int wave, int lane,
+                                          const int K0, const int K1) {
+  constexpr int kRows = TilePages<NW, BIG>::kRows;
+  constexpr int kKpe = TilePages<NW, BIG>::kKpe;
+  const int ps_mask = (1 << log2_ps) - 1;
+  const int last = kv_end - 1 - tok0;
+  const char* ckv_b = reinterpret_cast<const char*>(ckv);
+  const char* kpe_b = reinterpret_cast<const char*>(kpe);
+  size_t base = 0, row_last = 0;
+  if constexpr (BIG) {
+    base = ((size_t)(uint32_t)tp.pc[0] << log2_ps) + (size_t)(tok0 & ps_mask);
+  } else {
+    const int tlast = min(last, kTile - 1);
+    row_last = ((size_t)(uint32_t)tp.plast << log2_ps) + (size_t)((tok0 + tlast) & ps_mask);
+  }
+#pragma unroll
+  for (int k = K0; k < K1 && k < kRows; ++k) {
+    const int t = k * NW + wave;
+    size_t row;
+    if constexpr (BIG) {
+      row = base + (size_t)min(t, last);
+    } else {
+      const size_t row_t = ((size_t)(uint32_t)tp.pc[k] << log2_ps) + (size_t)((tok0 + t) & ps_mask);
+      row = t <= last ? row_t : row_last;
+    }
+    dma16(ckv_b + row * (kCkvDim * 2) + ((lane ^ swz16(t)) << 4), stage_base + t * 1024);
+  }
+#pragma unroll
+  for (int jj = (K0 > kRows ? K0 - kRows : 0); jj < kKpe && kRows + jj < K1; ++jj) {
+    const int j = jj * NW + wave;
+    if (j < 4) {
+      const int t = 8 * j + (lane >> 3);
+      size_t row;
+      if constexpr (BIG) {
+        row = base + (size_t)min(t, last);
+      } else {
+        int pg;
+        if constexpr (NW == 1) {
+          pg = tp.pc[8 * j];
+#pragma unroll
+          for (int k = 1; k < 8; ++k) pg = ((lane >> 3) == k) ? tp.pc[8 * j + k] : pg;
+        } else {
+          pg = tp.pk[jj * 8];
+#pragma unroll
+          for (int k = 1; k < 8; ++k) pg = ((lane >> 3) == k) ? tp.pk[jj * 8 + k] : pg;
+        }
+        const size_t row_t = ((size_t)(uint32_t)pg << log2_ps) + (size_t)((tok0 + t) & ps_mask);
+        row = t <= last ? row_t : row_last;
+      }
+      dma16(kpe_b + row * (kKpeDim * 2) + (((lane & 7) ^ swz8(t)) << 4),
+            stage_base + kTile * 1024 + j * 1024);
+    }
+  }
+}
+
+// All of this wave's loads of one KV tile.
+template <int NW, bool BIG>
+__device__ __forceinline__ void issue_tile(const TilePages<NW, BIG>& tp,
+                                           const uint16_t* __restrict__ ckv,
+                                           const uint16_t* __restrict__ kpe, int log2_ps,
+                                           int tok0, int kv_end, uint32_t stage_base,
+                                           int wave, int lane) {
+  issue_dma<NW, BIG>(tp, ckv, kpe, log2_ps, tok0, kv_end, stage_base, wave, lane, 0, 64);
+}
+
+// Maximum over the four 16-lane rows (lanes l, l^16, l^32, l^48 hold one head)
+// with the gfx950 row-swap permutes, which stay in the VALU.
+__device__ __forceinline__ float max_over_rows(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = fmaxf(__builtin_bit_cast(float, (uint32_t)a[0]), __builtin_bit_cast(float, (uint32_t)a[1]));
+  const uint32_t v = __builtin_bit_cast(uint32_t, y);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)b[0]), __builtin_bit_cast(float, (uint32_t)b[1]));
 }
 
 // Wait until this wave's loads of all but the last `pending` issued tiles landed.
@@ -148,7 +241,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // ---------------------------------------------------------------------------
 // Fused decode kernel.  NW waves x NB head blocks of 16 = heads per request.
 // ---------------------------------------------------------------------------
-template <int NW, int NB, int NSTAGE>
+template <int NW, int NB, int NSTAGE, bool BIG>
 __global__ void __launch_bounds__(NW * 64)
 mla_decode_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
                   const uint16_t* __restrict__ ckv, const uint16_t* __restrict__ kpe,
@@ -156,11 +249,19 @@ mla_decode_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restric
                   float* __restrict__ part_o, float* __restrict__ part_lse,
                   const int32_t* __restrict__ wg_indptr, const int32_t* __restrict__ units,
                   const int32_t* __restrict__ seq_indptr,
-                  const int32_t* __restrict__ seq_indices, int H, int log2_ps,
-                  float sm_scale, float C) {
+                  const int32_t* __restrict__ seq_indices, int H, int n_hg, int n_lanes,
+                  int log2_ps, float sm_scale, float C, float rescale_thr) {
   static_assert(NSTAGE >= 2, "need at least double buffering");
   static_assert(kTile / NW * NW == kTile, "waves must divide the tile");
-  __shared__ __attribute__((aligned(1024))) char smem_raw[NSTAGE * kStageBytes];
+  constexpr int HBN = NW * NB;       // head blocks of 16 in the workgroup
+  constexpr int DBW = 32 / NW;       // output-dim blocks of 16 owned by each wave in PV
+  constexpr int NDMA = kTile / NW + (4 + NW - 1) / NW;
+  constexpr int DMA_PER_STEP = (NDMA + 17) / 18;
+  // LDS: NSTAGE tile stages, then the P^T exchange (1 KB per head block) and
+  // one float per head (rescale factors, later row sums).
+  constexpr int xp_off = NSTAGE * kStageBytes;
+  constexpr int xa_off = xp_off + HBN * 1024;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[xa_off + HBN * 16 * 4];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
   const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
 
@@ -168,8 +269,16 @@ mla_decode_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restric
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;    // 16-lane group
   const int li = lane & 15;
-  const int u_begin = wg_indptr[blockIdx.x];
-  const int u_end = wg_indptr[blockIdx.x + 1];
+  // Workgroups are dispatched round-robin over the 8 XCDs (block b on XCD
+  // b % 8).  The head-group replicas of one schedule lane take blocks
+  // b, b+8, ..., so they share an XCD's L2 and start together: the KV tile
+  // they all read comes from HBM once.
+  const int hg = (blockIdx.x >> 3) % n_hg;
+  const int sl = (blockIdx.x / (8 * n_hg)) * 8 + (blockIdx.x & 7);
+  if (sl >= n_lanes) return;
+  const int head0 = hg * (NW * NB * 16);
+  const int u_begin = wg_indptr[sl];
+  const int u_end = wg_indptr[sl + 1];
 
   // Per-lane LDS offsets that do not depend on the unit (stage-relative).
   // QK A operand: token t = tb*16 + li, chunk ks*4 + g  -> base ^ (ks << 6)
@@ -202,14 +311,16 @@ mla_decode_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restric
     // Tile 0 first, then the query; one full vector-memory wait covers both, so
     // the compiler's own wait tracking sees the query registers as complete
     // before the loop (it does not see the tile loads, which are inline asm).
-    issue_tile<NW>(ckv, kpe, pages, log2_ps, kv0, kv1, smem_base, wave, lane);
+    TilePages<NW, BIG> tp;
+    load_tile_pages<NW, BIG>(tp, pages, log2_ps, kv0, kv1, wave);
+    issue_tile<NW, BIG>(tp, ckv, kpe, log2_ps, kv0, kv1, smem_base, wave, lane);
 
     // Q^T operand, registers for the whole unit: lane (g, li) holds
     // Q[head nb*16 + li][ks*32 + g*8 .. +7].
     bf16x8_t q[NB][18];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int h = wave * (16 * NB) + nb * 16 + li;
+      const int h = head0 + wave * (16 * NB) + nb * 16 + li;
       const bf16x8_t* qn = reinterpret_cast<const bf16x8_t*>(
           q_nope + ((size_t)b * H + h) * kCkvDim + g * 8);
       const bf16x8_t* qp = reinterpret_cast<const bf16x8_t*>(
@@ -223,20 +334,29 @@ mla_decode_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restric
 
 #pragma unroll
     for (int s = 1; s < NSTAGE - 1; ++s) {
-      if (s < ntiles)
-        issue_tile<NW>(ckv, kpe, pages, log2_ps, kv0 + s * kTile, kv1,
-                       smem_base + s * kStageBytes, wave, lane);
+      if (s < ntiles) {
+        load_tile_pages<NW, BIG>(tp, pages, log2_ps, kv0 + s * kTile, kv1, wave);
+        issue_tile<NW, BIG>(tp, ckv, kpe, log2_ps, kv0 + s * kTile, kv1,
+                            smem_base + s * kStageBytes, wave, lane);
+      }
     }
+    // page ids of the next tile to issue are always fetched one iteration early
+    if (NSTAGE - 1 < ntiles)
+      load_tile_pages<NW, BIG>(tp, pages, log2_ps, kv0 + (NSTAGE - 1) * kTile, kv1, wave);
 
+    // Softmax state of this wave's own heads (rows of S it computes).
     float m_run[NB], l_run[NB];
-    f32x4_t o[NB][32];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       m_run[nb] = -INFINITY;
       l_run[nb] = 0.f;
-#pragma unroll
-      for (int db = 0; db < 32; ++db) o[nb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
+    // PV accumulators: this wave's DBW output-dim blocks for all HBN head blocks.
+    f32x4_t o[DBW][HBN];
+#pragma unroll
+    for (int db = 0; db < DBW; ++db)
+#pragma unroll
+      for (int hb = 0; hb < HBN; ++hb) o[db][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     for (int it = 0; it < ntiles; ++it) {
       // this wave's loads of tile `it` have landed (later tiles may still fly)
@@ -244,30 +364,35 @@ mla_decode_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restric
       if (NSTAGE >= 4 && later >= 2) wait_tiles<NW, (NSTAGE >= 4 ? 2 : 0)>(wave);
       else if (NSTAGE >= 3 && later >= 1) wait_tiles<NW, (NSTAGE >= 3 ? 1 : 0)>(wave);
       else wait_tiles<NW, 0>(wave);
-      __syncthreads();  // every wave's loads of tile `it` landed; tile it-1 is consumed
-      {
-        const int nt = it + NSTAGE - 1;
-        if (nt < ntiles)
-          issue_tile<NW>(ckv, kpe, pages, log2_ps, kv0 + nt * kTile, kv1,
-                         smem_base + (nt % NSTAGE) * kStageBytes, wave, lane);
-      }
+      __syncthreads();  // tile `it` landed for every wave; tile it-1 and its P exchange are consumed
+      // Per-lane LDS offsets and the lane id go through an empty asm each tile:
+      // otherwise the compiler hoists every derived operand address out of
+      // the loop and spills them, and a spill reload inside the loop would
+      // wait for all outstanding tile loads.
+      int oA0 = offA[0], oA1 = offA[1], oK0 = offK[0], oK1 = offK[1], oV0 = offV[0], oV1 = offV[1];
+      int lane_o = lane;
+      asm volatile("" : "+v"(oA0), "+v"(oA1), "+v"(oK0), "+v"(oK1), "+v"(oV0), "+v"(oV1), "+v"(lane_o));
+      const int nt = it + NSTAGE - 1;          // tile whose loads go out during this QK
+      const bool issue = nt < ntiles;
+      const uint32_t nt_base = smem_base + (nt % NSTAGE) * kStageBytes;
+      const int nt_tok0 = kv0 + nt * kTile;
       const int stage_off = (it % NSTAGE) * kStageBytes;
       const int tok0 = kv0 + it * kTile;
       const int valid = kv1 - tok0;
 
-      // ---- QK: 18 k-steps of 32 dims, A fragments prefetched two steps ahead ----
+      // ---- QK: 18 k-steps of 32 dims, A fragments prefetched, next tile's
+      // loads interleaved (DMA_PER_STEP per k-step) ----
       f32x4_t sacc[2][NB];
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) sacc[tb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const int a0 = stage_off + offA[0], a1 = stage_off + offA[1];
-      const int k0 = stage_off + offK[0], k1 = stage_off + offK[1];
+      const int a0 = stage_off + oA0, a1 = stage_off + oA1;
+      const int k0 = stage_off + oK0, k1 = stage_off + oK1;
       auto ldA = [&](int ks, int tb) -> bf16x8_t {
         const int off = ks < 16 ? ((tb ? a1 : a0) ^ (ks << 6)) : ((tb ? k1 : k0) ^ ((ks - 16) << 6));
         return *(const LDS_AS bf16x8_t*)(smem + off);
       };
-      // prefetch distance: two k-steps, one when 32 heads per wave leave no room
       constexpr int AP = NB >= 2 ? 1 : 2;
       bf16x8_t A[AP + 1][2];
 #pragma unroll
@@ -277,6 +402,10 @@ mla_decode_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restric
       }
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) {
+        if (issue) {
+          issue_dma<NW, BIG>(tp, ckv, kpe, log2_ps, nt_tok0, kv1, nt_base, wave, lane_o,
+                             ks * DMA_PER_STEP, (ks + 1) * DMA_PER_STEP);
+        }
         if (ks + AP < 18) {
           A[(ks + AP) % (AP + 1)][0] = ldA(ks + AP, 0);
           A[(ks + AP) % (AP + 1)][1] = ldA(ks + AP, 1);
@@ -289,9 +418,12 @@ mla_decode_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restric
                                                                    sacc[tb][nb], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
+      if (issue && nt + 1 < ntiles)
+        load_tile_pages<NW, BIG>(tp, pages, log2_ps, kv0 + (nt + 1) * kTile, kv1, wave);
 
-      // ---- online softmax (per lane: one head, 8 tokens of the tile) ----
+      // ---- online softmax of this wave's heads (per lane: one head, 8 tokens) ----
       bf16x8_t pT[NB];
+      float alpha_own[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         float sv[8];
@@ -305,10 +437,13 @@ mla_decode_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restric
             sv[tb * 4 + i] = v;
             mx = fmaxf(mx, v);
           }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run[nb], mx);
-        const float alpha = __builtin_amdgcn_exp2f((m_run[nb] - m_new) * C);
+        mx = max_over_rows(mx);
+        // Lazy running max: the reference m moves only when the tile max exceeds
+        // it by more than rescale_thr (probabilities stay <= 2^8, exact in
+        // fp32/bf16 range), so O is rarely rescaled.  The first tile always sets m.
+        const bool grow = mx > m_run[nb] + rescale_thr;
+        const float m_new = grow ? mx : m_run[nb];
+        alpha_own[nb] = __builtin_amdgcn_exp2f((m_run[nb] - m_new) * C);
         m_run[nb] = m_new;
         const float mc = m_new * C;
         float psum = 0.f;
@@ -318,72 +453,130 @@ mla_decode_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restric
           psum += e;
           pT[nb][k] = (__bf16)e;
         }
-        l_run[nb] = l_run[nb] * alpha + psum;
-        // Rescale O only when some head's running max moved (never on the
-        // unit's first tile, where O is still zero).  The empty asm statements
-        // pin the accumulators to AGPRs so the MFMAs keep their AGPR form; the
-        // multiply itself goes through VGPRs (compiler-generated moves).
-        if (it > 0 && __builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+        l_run[nb] = l_run[nb] * alpha_own[nb] + psum;
+      }
+
+      // ---- exchange: every wave's P^T fragments and rescale factors ----
+      bf16x8_t pB[HBN];
+      float alpha[HBN];
+      if constexpr (NW == 1) {
 #pragma unroll
-          for (int db = 0; db < 32; ++db) {
-            asm volatile("" : "+a"(o[nb][db]));
-            o[nb][db] *= alpha;
-            asm volatile("" : "+a"(o[nb][db]));
-          }
+        for (int hb = 0; hb < HBN; ++hb) {
+          pB[hb] = pT[hb];
+          alpha[hb] = alpha_own[hb];
+        }
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int hb = wave * NB + nb;
+          *(LDS_AS bf16x8_t*)(smem + xp_off + hb * 1024 + lane * 16) = pT[nb];
+          if (g == 0) *(LDS_AS float*)(smem + xa_off + (hb * 16 + li) * 4) = alpha_own[nb];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int hb = 0; hb < HBN; ++hb) {
+          pB[hb] = *(const LDS_AS bf16x8_t*)(smem + xp_off + hb * 1024 + lane * 16);
+          alpha[hb] = *(const LDS_AS float*)(smem + xa_off + (hb * 16 + li) * 4);
+        }
+      }
+      // Rescale O only when some head's reference max moved (never on the
+      // unit's first tile, where O is still zero).  The empty asm statements
+      // pin the accumulators to AGPRs so the MFMAs keep their AGPR form; the
+      // multiply itself goes through VGPRs (compiler-generated moves).
+      if (it > 0) {
+        bool need = false;
+#pragma unroll
+        for (int hb = 0; hb < HBN; ++hb) need |= alpha[hb] != 1.0f;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+#pragma unroll
+          for (int db = 0; db < DBW; ++db)
+#pragma unroll
+            for (int hb = 0; hb < HBN; ++hb) {
+              asm volatile("" : "+a"(o[db][hb]));
+              o[db][hb] *= alpha[hb];
+              asm volatile("" : "+a"(o[db][hb]));
+            }
         }
       }
       __builtin_amdgcn_sched_barrier(0);
 
-      // ---- PV: 32 blocks of 16 output dims, V^T fragments prefetched two ahead ----
-      const int v0 = stage_off + offV[0], v1 = stage_off + offV[1];
+      // ---- PV over this wave's dims: V^T fragments (transposed reads of the
+      // same LDS tile) feed HBN MFMAs each ----
+      const int v0 = stage_off + oV0, v1 = stage_off + oV1;
       auto ldV = [&](int db, int tb) -> bf16x4_t {
+        const int dbg = wave * DBW + db;
         return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (LDS_AS bf16x4_t*)(smem + ((tb ? v1 : v0) ^ (db << 5))));
+            (LDS_AS bf16x4_t*)(smem + ((tb ? v1 : v0) ^ (dbg << 5))));
       };
-      bf16x4_t V[3][2];
-      V[0][0] = ldV(0, 0);
-      V[0][1] = ldV(0, 1);
-      V[1][0] = ldV(1, 0);
-      V[1][1] = ldV(1, 1);
+      constexpr int VP = 2;
+      bf16x4_t V[VP + 1][2];
 #pragma unroll
-      for (int db = 0; db < 32; ++db) {
-        if (db + 2 < 32) {
-          V[(db + 2) % 3][0] = ldV(db + 2, 0);
-          V[(db + 2) % 3][1] = ldV(db + 2, 1);
+      for (int pp = 0; pp < VP && pp < DBW; ++pp) {
+        V[pp][0] = ldV(pp, 0);
+        V[pp][1] = ldV(pp, 1);
+      }
+#pragma unroll
+      for (int db = 0; db < DBW; ++db) {
+        if (db + VP < DBW) {
+          V[(db + VP) % (VP + 1)][0] = ldV(db + VP, 0);
+          V[(db + VP) % (VP + 1)][1] = ldV(db + VP, 1);
         }
-        const bf16x8_t a = __builtin_shufflevector(V[db % 3][0], V[db % 3][1], 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8_t a = __builtin_shufflevector(V[db % (VP + 1)][0], V[db % (VP + 1)][1], 0, 1, 2,
+                                                   3, 4, 5, 6, 7);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          o[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pT[nb], o[nb][db], 0, 0, 0);
+        for (int hb = 0; hb < HBN; ++hb)
+          o[db][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pB[hb], o[db][hb], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
 
-    // ---- epilogue ----
+    // ---- epilogue: row sums and maxima of every head, then this wave's dims ----
+    float linv[HBN], lse_v[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       float l = l_run[nb];
       l += __shfl_xor(l, 16);
       l += __shfl_xor(l, 32);
-      const float inv = 1.0f / l;
-      const float lse_v = m_run[nb] * sm_scale + __builtin_amdgcn_logf(l) * 0.69314718055994531f;
-      const int h = wave * (16 * NB) + nb * 16 + li;
-      if (slot < 0) {
-        uint16_t* orow = out + ((size_t)b * H + h) * kCkvDim + g * 4;
+      l_run[nb] = l;
+      lse_v[nb] = m_run[nb] * sm_scale + __builtin_amdgcn_logf(l) * 0.69314718055994531f;
+    }
+    if constexpr (NW == 1) {
 #pragma unroll
-        for (int db = 0; db < 32; ++db) {
-          const f32x4_t v = o[nb][db] * inv;
+      for (int hb = 0; hb < HBN; ++hb) linv[hb] = 1.0f / l_run[hb];
+    } else {
+      __syncthreads();  // every wave is done reading the exchange area
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        if (g == 0) *(LDS_AS float*)(smem + xa_off + ((wave * NB + nb) * 16 + li) * 4) = l_run[nb];
+      __syncthreads();
+#pragma unroll
+      for (int hb = 0; hb < HBN; ++hb) linv[hb] = 1.0f / *(const LDS_AS float*)(smem + xa_off + (hb * 16 + li) * 4);
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int h = head0 + (wave * NB + nb) * 16 + li;
+      if (g == 0) {
+        if (slot < 0) lse_out[(size_t)b * H + h] = lse_v[nb];
+        else part_lse[(size_t)slot * H + h] = lse_v[nb];
+      }
+    }
+#pragma unroll
+    for (int hb = 0; hb < HBN; ++hb) {
+      const int h = head0 + hb * 16 + li;
+      if (slot < 0) {
+        uint16_t* orow = out + ((size_t)b * H + h) * kCkvDim + wave * (DBW * 16) + g * 4;
+#pragma unroll
+        for (int db = 0; db < DBW; ++db) {
+          const f32x4_t v = o[db][hb] * linv[hb];
           const uint32_t lo = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
           const uint32_t hi = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
           *reinterpret_cast<uint2*>(orow + db * 16) = make_uint2(lo, hi);
         }
-        if (g == 0) lse_out[(size_t)b * H + h] = lse_v;
       } else {
-        float* prow = part_o + ((size_t)slot * H + h) * kCkvDim + g * 4;
+        float* prow = part_o + ((size_t)slot * H + h) * kCkvDim + wave * (DBW * 16) + g * 4;
 #pragma unroll
-        for (int db = 0; db < 32; ++db)
-          *reinterpret_cast<f32x4_t*>(prow + db * 16) = o[nb][db] * inv;
-        if (g == 0) part_lse[(size_t)slot * H + h] = lse_v;
+        for (int db = 0; db < DBW; ++db)
+          *reinterpret_cast<f32x4_t*>(prow + db * 16) = o[db][hb] * linv[hb];
       }
     }
   }
@@ -432,6 +625,7 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(MergeParams p) {
 // Gather through the decode kernel's load path: issue_tile into LDS, then copy
 // each valid token's ckv and kpe chunks back out of the swizzled tile.
 // ---------------------------------------------------------------------------
+template <bool BIG>
 __global__ void __launch_bounds__(256)
 mla_gather_kernel(const uint16_t* __restrict__ ckv, const uint16_t* __restrict__ kpe,
                   uint16_t* __restrict__ rows, const int32_t* __restrict__ units,
@@ -447,7 +641,9 @@ mla_gather_kernel(const uint16_t* __restrict__ ckv, const uint16_t* __restrict__
   const int32_t* pages = seq_indices + seq_indptr[seq];
   for (int tok0 = kv0; tok0 < kv1; tok0 += kTile) {
     __syncthreads();
-    issue_tile<4>(ckv, kpe, pages, log2_ps, tok0, kv1, smem_base, wave, lane);
+    TilePages<4, BIG> tp;
+    load_tile_pages<4, BIG>(tp, pages, log2_ps, tok0, kv1, wave);
+    issue_tile<4, BIG>(tp, ckv, kpe, log2_ps, tok0, kv1, smem_base, wave, lane);
     wait_vmcnt<0>();
     __syncthreads();
     const int n = min(kTile, kv1 - tok0);
@@ -466,25 +662,54 @@ mla_gather_kernel(const uint16_t* __restrict__ ckv, const uint16_t* __restrict__
 // ---------------------------------------------------------------------------
 bool kernel_config_for(int num_heads, KernelConfig* cfg) {
   switch (num_heads) {
-    case 16: *cfg = KernelConfig{1, 16, 2, 2, 1}; return true;
-    case 32: *cfg = KernelConfig{2, 16, 2, 2, 1}; return true;
-    case 64: *cfg = KernelConfig{4, 16, 4, 1, 2}; return true;
-    case 128: *cfg = KernelConfig{4, 32, 4, 1, 2}; return true;
+    case 16: *cfg = KernelConfig{1, 16, 2, 2, 1, 1}; break;
+    case 32: *cfg = KernelConfig{2, 16, 2, 2, 1, 1}; break;
+    case 64: *cfg = KernelConfig{4, 16, 4, 1, 2, 1}; break;
+    case 128: *cfg = KernelConfig{4, 32, 4, 1, 2, 1}; break;
     default: return false;
   }
+  // Experiments only: PKVMLA_CONFIG="waves,heads_per_wave,stages,wg_per_cu,fixed,head_groups"
+  // overrides the table when that kernel shape exists for num_heads.
+  if (const char* e = getenv("PKVMLA_CONFIG")) {
+    KernelConfig c{};
+    if (sscanf(e, "%d,%d,%d,%d,%d,%d", &c.waves, &c.heads_per_wave, &c.stages, &c.wg_per_cu,
+               &c.fixed_cost, &c.head_groups) == 6 &&
+        c.head_groups >= 1 && c.waves * c.heads_per_wave * c.head_groups == num_heads &&
+        c.wg_per_cu >= 1 && c.fixed_cost >= 0) {
+      const bool exists = (c.waves == 1 && c.heads_per_wave == 16 && c.stages == 2) ||
+                          (c.waves == 2 && c.heads_per_wave == 16 && c.stages == 2) ||
+                          (c.waves == 4 && c.heads_per_wave == 16 && c.stages == 4) ||
+                          (c.waves == 4 && c.heads_per_wave == 32 && c.stages == 4);
+      if (exists) *cfg = c;
+    }
+  }
+  return true;
+}
+
+int decode_grid(int n_lanes, int head_groups) {
+  return ((n_lanes + 7) / 8) * 8 * head_groups;
 }
 
 #define PKVMLA_DECODE_ARGS                                                               \
   p.q_nope, p.q_pe, p.ckv, p.kpe, p.out, p.lse, p.part_o, p.part_lse, p.wg_indptr, p.units, \
-      p.seq_indptr, p.seq_indices, p.num_heads, p.log2_ps, p.sm_scale, p.score_log2
+      p.seq_indptr, p.seq_indices, p.num_heads, p.head_groups, p.n_lanes, p.log2_ps,      \
+      p.sm_scale, p.score_log2, p.rescale_thr
 
-hipError_t launch_decode(const DecodeParams& p, int grid, hipStream_t stream) {
-  if (grid <= 0) return hipSuccess;
-  switch (p.num_heads) {
-    case 16: mla_decode_kernel<1, 1, 2><<<grid, 64, 0, stream>>>(PKVMLA_DECODE_ARGS); break;
-    case 32: mla_decode_kernel<2, 1, 2><<<grid, 128, 0, stream>>>(PKVMLA_DECODE_ARGS); break;
-    case 64: mla_decode_kernel<4, 1, 4><<<grid, 256, 0, stream>>>(PKVMLA_DECODE_ARGS); break;
-    case 128: mla_decode_kernel<4, 2, 4><<<grid, 256, 0, stream>>>(PKVMLA_DECODE_ARGS); break;
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
+  if (p.n_lanes <= 0) return hipSuccess;
+  const int grid = decode_grid(p.n_lanes, p.head_groups);
+  // big: every page holds whole 32-token tiles (page_size >= 32)
+  const int key = p.waves * 10000 + p.heads_per_wave * 100 + p.stages * 10 + (p.log2_ps >= 5);
+  switch (key) {
+#define PKVMLA_CASE(W, NB, S, BIG)                                                         \
+  case W * 10000 + NB * 1600 + S * 10 + BIG:                                               \
+    mla_decode_kernel<W, NB, S, BIG><<<grid, W * 64, 0, stream>>>(PKVMLA_DECODE_ARGS);     \
+    break;
+    PKVMLA_CASE(1, 1, 2, 0) PKVMLA_CASE(1, 1, 2, 1)
+    PKVMLA_CASE(2, 1, 2, 0) PKVMLA_CASE(2, 1, 2, 1)
+    PKVMLA_CASE(4, 1, 4, 0) PKVMLA_CASE(4, 1, 4, 1)
+    PKVMLA_CASE(4, 2, 4, 0) PKVMLA_CASE(4, 2, 4, 1)
+#undef PKVMLA_CASE
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -499,8 +724,12 @@ hipError_t launch_merge(const MergeParams& p, int n_merges, hipStream_t stream) 
 
 hipError_t launch_gather(const GatherParams& p, int n_units, hipStream_t stream) {
   if (n_units <= 0) return hipSuccess;
-  mla_gather_kernel<<<n_units, 256, 0, stream>>>(p.ckv, p.kpe, p.rows, p.units, p.seq_indptr,
-                                                 p.seq_indices, p.log2_ps);
+  if (p.log2_ps >= 5)
+    mla_gather_kernel<true><<<n_units, 256, 0, stream>>>(p.ckv, p.kpe, p.rows, p.units,
+                                                         p.seq_indptr, p.seq_indices, p.log2_ps);
+  else
+    mla_gather_kernel<false><<<n_units, 256, 0, stream>>>(p.ckv, p.kpe, p.rows, p.units,
+                                                          p.seq_indptr, p.seq_indices, p.log2_ps);
   return hipGetLastError();
 }
 

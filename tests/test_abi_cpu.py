@@ -57,7 +57,8 @@ def _compare(items, batch, num_wg, tile, fixed):
 def test_schedule_host_matches_reference(name, num_cu):
     lens = config_lens(name)
     kc = kernel_config(CONFIGS[name]["num_heads"])
-    _compare(flat_items(lens), len(lens), num_cu * kc["wg_per_cu"], kc["tile"], kc["fixed_cost"])
+    _compare(flat_items(lens), len(lens), max(1, num_cu * kc["wg_per_cu"] // kc["head_groups"]),
+             kc["tile"], kc["fixed_cost"])
 
 
 def test_schedule_host_matches_reference_cascade():

@@ -7,6 +7,7 @@ tables) is compared bit for bit.
 """
 
 import math
+import os
 
 import numpy as np
 import pytest
@@ -88,11 +89,13 @@ def test_plan_export_bit_exact(name):
     ex = plan.export()
     kc = kernel_config(cfg["num_heads"])
     hdr = ex.header
-    assert list(hdr[:12]) == [1, len(lens), cfg["num_heads"], ps, 512, 64, kc["tile"],
-                              kc["waves"], kc["heads_per_wave"], kc["stages"], kc["wg_per_cu"],
-                              kc["fixed_cost"]]
-    wg, units, merges = schedule_ref(flat_items(lens), len(lens), ex.num_cu * kc["wg_per_cu"],
-                                     kc["tile"], kc["fixed_cost"])
+    assert list(hdr[:7]) == [1, len(lens), cfg["num_heads"], ps, 512, 64, kc["tile"]]
+    if not os.environ.get("PKVMLA_CONFIG"):
+        assert list(hdr[7:12]) == [kc["waves"], kc["heads_per_wave"], kc["stages"],
+                                   kc["wg_per_cu"], kc["fixed_cost"]]
+        assert ex.head_groups == kc["head_groups"]
+    lanes = max(1, ex.num_cu * int(hdr[10]) // ex.head_groups)
+    wg, units, merges = schedule_ref(flat_items(lens), len(lens), lanes, kc["tile"], int(hdr[11]))
     np.testing.assert_array_equal(ex.wg_indptr, wg)
     np.testing.assert_array_equal(ex.units, units)
     np.testing.assert_array_equal(ex.merges, merges)
@@ -107,9 +110,10 @@ def test_plan_export_cascade():
     note("export cascade")
     ex = pk.plan_for(cas).export()
     kc = kernel_config(64)
+    hdr = ex.header
     items = cascade_items(cas.group_req_indptr, cas.prefix_lens, cas.kv_lens)
-    wg, units, merges = schedule_ref(items, cas.batch, ex.num_cu * kc["wg_per_cu"], kc["tile"],
-                                     kc["fixed_cost"])
+    lanes = max(1, ex.num_cu * int(hdr[10]) // ex.head_groups)
+    wg, units, merges = schedule_ref(items, cas.batch, lanes, kc["tile"], int(hdr[11]))
     np.testing.assert_array_equal(ex.units, units)
     np.testing.assert_array_equal(ex.merges, merges)
     np.testing.assert_array_equal(ex.wg_indptr, wg)
