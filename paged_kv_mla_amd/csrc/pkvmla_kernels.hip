@@ -20,68 +20,9 @@
 #include <stdio.h>
 #include <stdlib.h>
 
-#include "pkvmla_internal.h"
-
-#define LDS_AS __attribute__((address_space(3)))
-#define GLB_AS __attribute__((address_space(1)))
+#include "pkvmla_device.h"
 
 namespace pkvmla {
-
-typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
-typedef __bf16 bf16x4_t __attribute__((__vector_size__(8)));
-typedef float f32x4_t __attribute__((__vector_size__(16)));
-typedef uint32_t u32x4_t __attribute__((__vector_size__(16)));
-
-// ---------------------------------------------------------------------------
-// LDS tile layout (one stage, 36864 bytes):
-//   [0, 32768)      ckv rows: token t at t*1024, its 16-byte chunk c (dims
-//                   8c..8c+7) at chunk position c ^ swz16(t)
-//   [32768, 36864)  kpe rows: token t at 32768 + t*128, chunk c at c ^ swz8(t)
-// The XOR swizzles keep every MFMA operand read free of bank conflicts for
-// both a 64-bank (16 lanes x 16 B or 32 lanes x 8 B per cycle) and a 32-bank
-// LDS: 16 consecutive tokens reading one chunk cover all 16 16-byte slots of
-// 256 bytes, and the transposed V reads (8 tokens x 2 chunks per 32 lanes)
-// do too.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ int swz16(int t) {
-  return (((t >> 2) ^ (t >> 3)) & 1) | ((t & 7) << 1);
-}
-__device__ __forceinline__ int swz8(int t) {
-  return (t ^ (t >> 3)) & 7;
-}
-__device__ __forceinline__ int lds_ckv_off(int t, int c) {
-  return t * 1024 + ((c ^ swz16(t)) << 4);
-}
-__device__ __forceinline__ int lds_kpe_off(int t, int c) {
-  return kTile * 1024 + t * 128 + ((c ^ swz8(t)) << 4);
-}
-
-// gfx9 s_waitcnt immediate: wait until at most N vector-memory ops are
-// outstanding (expcnt and lgkmcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Direct HBM -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane i
-// of the wave lands at LDS byte lds_base + 16*i.  Issued through inline asm so
-// that the compiler neither reorders it nor inserts its own conservative
-// vector-memory waits before every LDS read; completion is tracked explicitly
-// with s_waitcnt vmcnt before the workgroup barrier that publishes a tile.
-// M0 (the LDS base register of the instruction) is saved and restored.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(gptr), "s"(lds_base)
-      : "memory");
-}
 
 // Loads per tile issued by `wave`: the 32 ckv rows go round-robin over the
 // waves, the 4 kpe blocks (8 tokens each) to waves 0..3.
@@ -210,17 +151,6 @@ __device__ __forceinline__ void issue_tile(const TilePages<NW, BIG>& tp,
   issue_dma<NW, BIG>(tp, ckv, kpe, log2_ps, tok0, kv_end, stage_base, wave, lane, 0, 64);
 }
 
-// Maximum over the four 16-lane rows (lanes l, l^16, l^32, l^48 hold one head)
-// with the gfx950 row-swap permutes, which stay in the VALU.
-__device__ __forceinline__ float max_over_rows(float x) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, x);
-  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  const float y = fmaxf(__builtin_bit_cast(float, (uint32_t)a[0]), __builtin_bit_cast(float, (uint32_t)a[1]));
-  const uint32_t v = __builtin_bit_cast(uint32_t, y);
-  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return fmaxf(__builtin_bit_cast(float, (uint32_t)b[0]), __builtin_bit_cast(float, (uint32_t)b[1]));
-}
-
 // Wait until this wave's loads of all but the last `pending` issued tiles landed.
 template <int NW, int PENDING>
 __device__ __forceinline__ void wait_tiles(int wave) {
@@ -230,12 +160,6 @@ __device__ __forceinline__ void wait_tiles(int wave) {
   } else {
     wait_vmcnt<PENDING * loads_per_tile<NW>(0)>();
   }
-}
-
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
 }
 
 // ---------------------------------------------------------------------------
@@ -697,6 +621,8 @@ int decode_grid(int n_lanes, int head_groups) {
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   if (p.n_lanes <= 0) return hipSuccess;
+  hipError_t err = hipSuccess;
+  if (launch_decode_w4(p, stream, &err)) return err;
   const int grid = decode_grid(p.n_lanes, p.head_groups);
   // big: every page holds whole 32-token tiles (page_size >= 32)
   const int key = p.waves * 10000 + p.heads_per_wave * 100 + p.stages * 10 + (p.log2_ps >= 5);
