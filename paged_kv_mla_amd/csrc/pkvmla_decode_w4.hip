@@ -34,135 +34,19 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
-#include "pkvmla_device.h"
+#include "pkvmla_tiles.h"
 
 namespace pkvmla {
 
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kRowsW = kTile / kWaves;  // ckv rows each wave copies per tile (8)
-constexpr int kDmaW = kRowsW + 1;       // plus one kpe block of 8 tokens
+static_assert(kWaves == kCopyWaves, "the tile copies assume four waves");
+constexpr int kDmaW = kCopiesPerWave;   // copy instructions per wave and tile: 8 ckv rows + 1 kpe block
 constexpr int kRing = 3;                // LDS stages: PV tile, QK tile, one tile in flight
 #ifndef QK_AHEAD
 #define QK_AHEAD 1
 #endif
-
-// Index tables (schedule, page lists) are read through the constant address
-// space: they never change while a kernel runs, and wave-uniform reads from it
-// always become scalar loads (a vector load would have to be waited for with a
-// vmcnt that also waits for the tile copies in flight).
-#define CONST_AS __attribute__((address_space(4)))
-typedef const CONST_AS int32_t* idx_ptr;
-
-// Wait until at most n (wave-uniform, >= 0) of this wave's vector-memory
-// operations are outstanding: the largest encodable count <= n, so the wait
-// is never weaker than asked.  The counter holds at most 63 operations (issue
-// stalls beyond), so 63 or more later operations imply completion.
-__device__ __forceinline__ void wait_vm_le(int n) {
-  if (n >= 63) return;
-  if (n >= 54) wait_vmcnt<54>();
-  else if (n >= 45) wait_vmcnt<45>();
-  else if (n >= 36) wait_vmcnt<36>();
-  else if (n >= 27) wait_vmcnt<27>();
-  else if (n >= 18) wait_vmcnt<18>();
-  else if (n >= 9) wait_vmcnt<9>();
-  else wait_vmcnt<0>();
-}
-
-// Producer side of the tile stream: the unit and tile whose copies go out
-// next.  All fields are wave-uniform (scalar registers).
-struct TileStream {
-  int u, u_end;           // unit of the next tile; end of the workgroup's list
-  int tile, ntiles;       // tile index inside that unit, tiles in the unit
-  int kv0, kv1;           // token range of the unit
-  idx_ptr pages;          // page list of the unit's sequence
-  int g;                  // stream position of the next tile (its ring stage is g % kRing)
-  int pid;                // page id of the next tile's first token (prefetched)
-};
-
-__device__ __forceinline__ void stream_load_unit(TileStream& s, idx_ptr units, idx_ptr seq_indptr,
-                                                 idx_ptr seq_indices, int log2_ps) {
-  idx_ptr rec = units + (size_t)s.u * kUnitInts;
-  const int seq = rec[1];
-  s.kv0 = rec[2];
-  s.kv1 = rec[3];
-  s.ntiles = (s.kv1 - s.kv0 + kTile - 1) / kTile;
-  s.tile = 0;
-  s.pages = seq_indices + seq_indptr[seq];
-  s.pid = s.pages[s.kv0 >> log2_ps];
-}
-
-__device__ __forceinline__ void stream_advance(TileStream& s, idx_ptr units, idx_ptr seq_indptr,
-                                               idx_ptr seq_indices, int log2_ps) {
-  ++s.g;
-  if (++s.tile < s.ntiles) {
-    s.pid = s.pages[(s.kv0 + s.tile * kTile) >> log2_ps];
-  } else if (++s.u < s.u_end) {
-    stream_load_unit(s, units, seq_indptr, seq_indices, log2_ps);
-  }
-}
-
-// Scalar description of one tile's copies for this wave, computed once per
-// tile so that each copy instruction costs a few scalar operations.
-struct TileCopy {
-  const char* crow;       // BIG: ckv row of the tile's first token
-  const char* krow;       // BIG: kpe row of the tile's first token
-  idx_ptr pages;          // !BIG: page list, with tok0 and log2_ps below
-  int tok0, last, log2_ps;
-  uint32_t st;            // LDS stage base
-};
-
-__device__ __forceinline__ TileCopy tile_copy(const TileStream& s, const char* __restrict__ ckv,
-                                              const char* __restrict__ kpe, int log2_ps,
-                                              uint32_t smem_base) {
-  TileCopy c;
-  c.tok0 = s.kv0 + s.tile * kTile;
-  c.last = min(s.kv1 - 1 - c.tok0, kTile - 1);
-  c.log2_ps = log2_ps;
-  c.pages = s.pages;
-  c.st = smem_base + (uint32_t)(s.g % kRing) * kStageBytes;
-  const int64_t rowbase = ((int64_t)(uint32_t)s.pid << log2_ps) + (c.tok0 & ((1 << log2_ps) - 1));
-  c.crow = ckv + rowbase * (kCkvDim * 2);
-  c.krow = kpe + rowbase * (kKpeDim * 2);
-  return c;
-}
-
-// Part k of this wave's copies of a tile: k < 8 is ckv row 8w + k (one 1 KB
-// row per instruction), k == 8 the kpe rows of tokens 8w..8w+7 (one
-// instruction).  Tokens past kv_end copy the last valid row.
-// BIG: a page holds whole tiles (page_size >= 32), so one page id serves the
-// tile and every address is a scalar base plus a lane offset.
-template <bool BIG>
-__device__ __forceinline__ void tile_copy_part(const TileCopy& c, const char* __restrict__ ckv,
-                                               const char* __restrict__ kpe, int wave, const int k) {
-  const int lane = lane_id_fresh();
-  const int ps_mask = (1 << c.log2_ps) - 1;
-  auto row_of = [&](int kk) -> int64_t {  // !BIG: global row of this wave's token 8w + kk
-    const int tok = c.tok0 + min(kRowsW * wave + kk, c.last);
-    return ((int64_t)(uint32_t)c.pages[tok >> c.log2_ps] << c.log2_ps) + (tok & ps_mask);
-  };
-  if (k < kRowsW) {
-    const int t = kRowsW * wave + k;
-    const uint32_t voff = ((uint32_t)lane << 4) ^ (uint32_t)(swz16(t) << 4);
-    const char* src = BIG ? c.crow + (int64_t)min(t, c.last) * (kCkvDim * 2)
-                          : ckv + row_of(k) * (kCkvDim * 2);
-    dma16_s(src, voff, c.st + (uint32_t)t * 1024u);
-  } else {
-    const int tl = kRowsW * wave + (lane >> 3);  // this lane's kpe token
-    const uint32_t kchunk = (uint32_t)(((lane & 7) ^ swz8(tl)) << 4);
-    if constexpr (BIG) {
-      dma16_s(c.krow, (uint32_t)min(tl, c.last) * (kKpeDim * 2) + kchunk,
-              c.st + kTile * 1024 + (uint32_t)wave * 1024u);
-    } else {
-      // lane group j = lane / 8 copies token 8w + j (clamped)
-      int64_t row = row_of(0);
-#pragma unroll
-      for (int kk = 1; kk < kRowsW; ++kk) row = ((lane >> 3) == kk) ? row_of(kk) : row;
-      dma16(kpe + row * (kKpeDim * 2) + kchunk, c.st + kTile * 1024 + (uint32_t)wave * 1024u);
-    }
-  }
-}
 
 }  // namespace
 
@@ -240,9 +124,9 @@ mla_decode_w4_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
     stream_advance(ts, units, seq_indptr, seq_indices, log2_ps);
   };
   auto issue_one = [&]() {
-    const TileCopy c = tile_copy(ts, ckv, kpe, log2_ps, smem_base);
-#pragma unroll
-    for (int k = 0; k < kDmaW; ++k) tile_copy_part<BIG>(c, ckv, kpe, wave, k);
+    const TileCopy c = tile_copy(ts, ckv, kpe, log2_ps,
+                                 smem_base + (uint32_t)(ts.g % kRing) * kStageBytes);
+    tile_copy_wave<BIG>(c, ckv, kpe, wave);
     book_tile();
   };
   // the stream may issue tile j once tiles < j - kRing + 1 are consumed

@@ -21,17 +21,19 @@ typedef uint32_t u32x4_t __attribute__((__vector_size__(16)));
 //   [0, 32768)      ckv rows: token t at t*1024, its 16-byte chunk c (dims
 //                   8c..8c+7) at chunk position c ^ swz16(t)
 //   [32768, 36864)  kpe rows: token t at 32768 + t*128, chunk c at c ^ swz8(t)
-// The XOR swizzles keep every MFMA operand read free of bank conflicts for
-// both a 64-bank (16 lanes x 16 B or 32 lanes x 8 B per cycle) and a 32-bank
-// LDS: 16 consecutive tokens reading one chunk cover all 16 16-byte slots of
-// 256 bytes, and the transposed V reads (8 tokens x 2 chunks per 32 lanes)
-// do too.
+// Swizzles chosen by measuring LDS bank-conflict cycles on gfx950: with the
+// chunk position c ^ (t mod 16) the QK operand reads (ds_read_b128: 16
+// tokens, one chunk each) take 4 LDS cycles per instruction, the conflict-free
+// minimum; the transposed V reads (ds_read_b64_tr_b16) then take 4 cycles
+// instead of 2.  No XOR of this form serves both (the b128 reads want lanes
+// 2k, 2k+1 on adjacent chunks, the transposed reads want 8 consecutive tokens
+// on distinct chunk pairs), and QK moves 4.5x more bytes per tile than PV.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int swz16(int t) {
-  return (((t >> 2) ^ (t >> 3)) & 1) | ((t & 7) << 1);
+  return t & 15;
 }
 __device__ __forceinline__ int swz8(int t) {
-  return (t ^ (t >> 3)) & 7;
+  return t & 7;
 }
 __device__ __forceinline__ int lds_ckv_off(int t, int c) {
   return t * 1024 + ((c ^ swz16(t)) << 4);
@@ -94,6 +96,24 @@ __device__ __forceinline__ void dma16_s(const void* sbase_any, uint32_t voff, ui
       : "=&s"(saved)
       : "v"(voff), "s"(sbase), "s"(lds_base)
       : "memory");
+}
+
+// Copies with M0 already holding the LDS base: global address = sbase + voff +
+// OFF and LDS address = M0 + OFF + 16 * lane (the instruction offset moves both
+// sides).  set_m0 loads M0; the compiler itself never uses M0 in these
+// kernels, so it stays valid between the copies of one tile.
+__device__ __forceinline__ void set_m0(uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0" : : "s"(lds_base) : "memory");
+}
+template <int OFF>
+__device__ __forceinline__ void dma16_m0(const void* sbase_any, uint32_t voff) {
+  static_assert(OFF >= 0 && OFF < 4096, "instruction offset range");
+  const void* sbase = to_sgpr(sbase_any);
+  asm volatile("global_load_lds_dwordx4 %0, %1 offset:%2" : : "v"(voff), "s"(sbase), "i"(OFF) : "memory");
+}
+// Per-lane 64-bit address form with M0 already set (offset 0).
+__device__ __forceinline__ void dma16_m0v(const void* gptr) {
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(gptr) : "memory");
 }
 
 // Maximum over the four 16-lane rows (lanes l, l^16, l^32, l^48 hold one head)

@@ -588,8 +588,8 @@ bool kernel_config_for(int num_heads, KernelConfig* cfg) {
   switch (num_heads) {
     case 16: *cfg = KernelConfig{1, 16, 2, 2, 1, 1}; break;
     case 32: *cfg = KernelConfig{2, 16, 2, 2, 1, 1}; break;
-    case 64: *cfg = KernelConfig{4, 16, 4, 1, 2, 1}; break;
-    case 128: *cfg = KernelConfig{4, 32, 4, 1, 2, 1}; break;
+    case 64: *cfg = KernelConfig{4, 16, 3, 1, 2, 1}; break;
+    case 128: *cfg = KernelConfig{4, 32, 3, 1, 2, 1}; break;
     default: return false;
   }
   // Experiments only: PKVMLA_CONFIG="waves,heads_per_wave,stages,wg_per_cu,fixed,head_groups"
@@ -602,8 +602,8 @@ bool kernel_config_for(int num_heads, KernelConfig* cfg) {
         c.wg_per_cu >= 1 && c.fixed_cost >= 0) {
       const bool exists = (c.waves == 1 && c.heads_per_wave == 16 && c.stages == 2) ||
                           (c.waves == 2 && c.heads_per_wave == 16 && c.stages == 2) ||
-                          (c.waves == 4 && c.heads_per_wave == 16 && c.stages == 4) ||
-                          (c.waves == 4 && c.heads_per_wave == 32 && c.stages == 4);
+                          (c.waves == 4 && c.heads_per_wave == 16 && c.stages == 3 && c.head_groups == 1) ||
+                          (c.waves == 4 && c.heads_per_wave == 32 && c.stages == 3 && c.head_groups == 1);
       if (exists) *cfg = c;
     }
   }
