@@ -17,19 +17,23 @@
 // of the workgroup (a tile of the next unit can be in flight while the current
 // unit finishes); each wave copies its share of a tile straight from HBM into
 // a 3-stage LDS ring with global_load_lds_dwordx4.  While PV reads tile t and
-// QK reads tile t+1, exactly one tile (t+2) is in flight: a CU that has more
-// than about 44 vector-memory instructions outstanding stalls every further
-// issue until one completes, and one 36 KB tile (36 instructions per CU)
-// already keeps HBM streaming at full rate.  Inside a unit, the softmax of tile t
-// is computed between the MFMAs of QK(t+1), so the VALU work overlaps the
-// matrix cores.  Every wave counts the vector-memory operations it has
-// issued; waiting for a tile is an s_waitcnt vmcnt with the exact number of
-// later operations, so copies of later tiles, the next query and the
-// epilogue stores of the previous unit stay in flight.
+// QK reads tile t+1, one tile (t+2) is in flight: 36 KB per CU keeps HBM
+// streaming at full rate on a full chip.  Its copies go out one per k-step
+// over the first nine k-steps of QK(t+1): the CU's memory pipeline accepts
+// about one 1 KB copy every 23 clocks, and the four waves meet at a barrier
+// every tile, so a burst of 36 copies would hold all of them for about 800
+// clocks.  The copies take their lane offsets from registers that are never
+// rewritten (a copy reads its address registers only when it is accepted).
+// Inside a unit, the softmax of tile t is computed between the MFMAs of
+// QK(t+1), so the VALU work overlaps the matrix cores.  Every wave counts the
+// vector-memory operations it has issued; waiting for a tile is an s_waitcnt
+// vmcnt with the exact number of later operations, so copies of later tiles,
+// the next query and the epilogue stores of the previous unit stay in flight.
 //
-// Masking.  Only the last tile of a unit can be partial.  Its slots past
-// kv_end are filled with the last valid token's row (finite data) and their
-// scores are set to -inf before the softmax, so they add exactly zero to PV.
+// Masking.  Only the last tile of a unit can be partial.  Its ckv slots past
+// kv_end are filled with the last valid token's row (finite data), its kpe
+// slots with the page's own rows past kv_end, and those slots' scores are
+// set to -inf (a select) before the softmax, so they add exactly zero to PV.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -44,9 +48,7 @@ constexpr int kWaves = 4;
 static_assert(kWaves == kCopyWaves, "the tile copies assume four waves");
 constexpr int kDmaW = kCopiesPerWave;   // copy instructions per wave and tile: 8 ckv rows + 1 kpe block
 constexpr int kRing = 3;                // LDS stages: PV tile, QK tile, one tile in flight
-#ifndef QK_AHEAD
-#define QK_AHEAD 1
-#endif
+constexpr int kQkAhead = 2;             // k-steps between a K fragment's LDS read and its MFMA
 
 }  // namespace
 
@@ -72,7 +74,12 @@ mla_decode_w4_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
   constexpr int xp_off = kRing * kStageBytes;
   constexpr int xa_off = xp_off + HBN * 1024;
   constexpr int xl_off = xa_off + HBN * 64;
-  __shared__ __attribute__((aligned(1024))) char smem_raw[xl_off + HBN * 64];
+  // q_pe of the unit's request: head block hb, rope k-step k2 at
+  // qp_off + (hb * 2 + k2) * 1 KB, lane (g, li) at 16 * lane (the MFMA B layout)
+  constexpr int qp_off = (xl_off + HBN * 64 + 1023) / 1024 * 1024;
+  constexpr int lds_bytes = qp_off + HBN * 2048;
+  static_assert(lds_bytes <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) char smem_raw[lds_bytes];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
   const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
 
@@ -125,8 +132,8 @@ mla_decode_w4_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
   };
   auto issue_one = [&]() {
     const TileCopy c = tile_copy(ts, ckv, kpe, log2_ps,
-                                 smem_base + (uint32_t)(ts.g % kRing) * kStageBytes);
-    tile_copy_wave<BIG>(c, ckv, kpe, wave);
+                                 smem_base + (uint32_t)(ts.g % kRing) * kStageBytes, wave);
+    tile_copy_wave<BIG>(c, ckv, kpe, wave, copy_lanes(wave));
     book_tile();
   };
   // the stream may issue tile j once tiles < j - kRing + 1 are consumed
@@ -142,9 +149,12 @@ mla_decode_w4_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
   for (int i = 0; i < kRing - 1; ++i)
     if (ts.u < ts.u_end) issue_one();
 
-  // Q^T operand, registers for a whole unit: lane (g, li) holds
-  // Q[head nb*16 + li][ks*32 + g*8 .. +7].
-  bf16x8_t q[NB][18];
+  // Q^T operand for a whole unit: lane (g, li) holds
+  // Q[head nb*16 + li][ks*32 + g*8 .. +7]; the q_nope k-steps (0..15) stay in
+  // registers, the two q_pe k-steps are copied into LDS (16 fewer registers,
+  // which buys a deeper K prefetch).  Each wave reads only its own q_pe
+  // blocks, after its own copies have landed.
+  bf16x8_t q[NB][16];
   int q_vmc = 0;
   // (a request's rows as a scalar base, lanes as 32-bit offsets: few address registers)
   auto load_q = [&](int b) {
@@ -158,8 +168,11 @@ mla_decode_w4_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
       const uint32_t op = (h * kKpeDim + (lq >> 4) * 8) * 2;
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) q[nb][ks] = *reinterpret_cast<const bf16x8_t*>(qn + on + ks * 64);
-      q[nb][16] = *reinterpret_cast<const bf16x8_t*>(qp + op);
-      q[nb][17] = *reinterpret_cast<const bf16x8_t*>(qp + op + 64);
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        set_m0(smem_base + (uint32_t)(qp_off + ((wave * NB + nb) * 2 + k2) * 1024));
+        dma16_m0<0>(qp, op + (uint32_t)k2 * 64);
+      }
     }
     vmc += 18 * NB;
     q_vmc = vmc;
@@ -188,6 +201,11 @@ mla_decode_w4_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
       oV[0] = offV[0]; oV[1] = offV[1];
       asm volatile("" : "+v"(oA[0]), "+v"(oA[1]), "+v"(oK[0]), "+v"(oK[1]), "+v"(oV[0]), "+v"(oV[1]));
     };
+    // this lane's q_pe fragment of head block nb, rope k-step k2
+    auto ldQpe = [&](int nb, int k2) -> bf16x8_t {
+      const int off = qp_off + ((wave * NB + nb) * 2 + k2) * 1024 + lane_id_fresh() * 16;
+      return *(const LDS_AS bf16x8_t*)(smem + off);
+    };
 
     // ---- QK of one stage into acc (fresh), with `mid(ks)` after each k-step ----
     auto qk = [&](int stage, const int (&oA)[2], const int (&oK)[2], f32x4_t (&acc)[2][NB],
@@ -205,29 +223,40 @@ mla_decode_w4_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
           acc[tb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
           acc2[tb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
-      // K fragments are read QK_AHEAD k-steps ahead of their MFMAs (LDS latency
+      // K fragments are read kQkAhead k-steps ahead of their MFMAs (LDS latency
       // under load exceeds one k-step of matrix work)
-      constexpr int AH = QK_AHEAD;
+      constexpr int AH = kQkAhead;
       bf16x8_t A[AH + 1][2];
 #pragma unroll
       for (int pp = 0; pp < AH; ++pp) {
         A[pp][0] = ldA(pp, 0);
         A[pp][1] = ldA(pp, 1);
       }
+      // q_pe fragments: read from LDS a few k-steps before the rope k-steps
+      constexpr int QPE_AT = 12;
+      bf16x8_t qpe[NB][2];
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) {
         if (ks + AH < 18) {
           A[(ks + AH) % (AH + 1)][0] = ldA(ks + AH, 0);
           A[(ks + AH) % (AH + 1)][1] = ldA(ks + AH, 1);
         }
+        if (ks == QPE_AT) {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            qpe[nb][0] = ldQpe(nb, 0);
+            qpe[nb][1] = ldQpe(nb, 1);
+          }
+        }
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
+            const bf16x8_t bq = ks < 16 ? q[nb][ks & 15] : qpe[nb][(ks - 16) & 1];
             if (NB == 1 && (ks & 1))
-              acc2[tb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ks % (AH + 1)][tb], q[nb][ks], acc2[tb][nb], 0, 0, 0);
+              acc2[tb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ks % (AH + 1)][tb], bq, acc2[tb][nb], 0, 0, 0);
             else
-              acc[tb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ks % (AH + 1)][tb], q[nb][ks], acc[tb][nb], 0, 0, 0);
+              acc[tb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ks % (AH + 1)][tb], bq, acc[tb][nb], 0, 0, 0);
           }
         mid(ks);
         __builtin_amdgcn_sched_barrier(0);
@@ -392,6 +421,8 @@ mla_decode_w4_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
     }
 
     // ---- all tiles but the last: QK(t+1) with the softmax of tile t in between ----
+    // (the copies' lane offsets stay in registers through the unit's tiles)
+    const CopyLanes CL = copy_lanes(wave);
     for (int t = 0; t + 1 < n; ++t) {
       const int gi = gc + t;
       wait_vm_le(vmc - vmc_of(gi + 1));
@@ -400,12 +431,30 @@ mla_decode_w4_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
       fresh(oA, oK, oV);
       SoftmaxTmp T;
       f32x4_t snext[2][NB];
-      // the copies of tile gi+2 (the stage PV(gi-1) just released) go out
-      // after the first k-step (spreading them between later k-steps measured
-      // slower: every copy instruction orders the LDS reads around it)
+      // the copies of tile gi+2 go into the stage PV(gi-1) just released
       const bool iss = may_issue(gi);
+      // BIG whole tiles: one copy part per k-step (k-steps 0..8), from ready
+      // bases.  The CU's memory pipeline takes a copy about every 23 clocks,
+      // so a burst of 36 copies would hold the waves (which meet at a barrier
+      // every tile) for about 800.  A unit's last (partial) tile, and the
+      // small-page path with its per-row page lookups, issue their share at
+      // once before the k-loop.
+      TileCopy cp{};
+      bool spread = false;
+      if (iss) {
+        cp = tile_copy(ts, ckv, kpe, log2_ps, smem_base + (uint32_t)(ts.g % kRing) * kStageBytes, wave);
+        if (BIG && cp.full) {
+          spread = true;
+        } else {
+          tile_copy_wave<BIG>(cp, ckv, kpe, wave, CL);
+          book_tile();
+        }
+      }
       qk((gi + 1) % kRing, oA, oK, snext, [&](int ks) {
-        if (ks == 0 && iss) issue_one();
+        if (spread && ks < kDmaW) {
+          tile_copy_part_full(cp, wave, ks, CL);
+          if (ks == kDmaW - 1) book_tile();
+        }
         switch (ks) {
           case 0: sm_load(T, sacc, kTile); sm_max(T); break;
           case 1: sm_rows(T); break;
