@@ -588,8 +588,8 @@ bool kernel_config_for(int num_heads, KernelConfig* cfg) {
   switch (num_heads) {
     case 16: *cfg = KernelConfig{1, 16, 2, 2, 1, 1}; break;
     case 32: *cfg = KernelConfig{2, 16, 2, 2, 1, 1}; break;
-    case 64: *cfg = KernelConfig{4, 16, 3, 1, 2, 1}; break;
-    case 128: *cfg = KernelConfig{4, 32, 3, 1, 2, 1}; break;
+    case 64: *cfg = KernelConfig{4, 16, 3, 1, 4, 1}; break;
+    case 128: *cfg = KernelConfig{4, 32, 3, 1, 4, 1}; break;
     default: return false;
   }
   // Experiments only: PKVMLA_CONFIG="waves,heads_per_wave,stages,wg_per_cu,fixed,head_groups"
