@@ -43,8 +43,8 @@ MERGE_INTS = 4          # int32 per merge record: b, first_slot, count, 0
 _KERNEL_CONFIGS = {
     16: (1, 16, 2, 2, 1, 1),
     32: (2, 16, 2, 2, 1, 1),
-    64: (4, 16, 3, 1, 4, 1),
-    128: (4, 32, 3, 1, 4, 1),
+    64: (8, 16, 4, 1, 4, 1),
+    128: (8, 16, 4, 1, 4, 2),
 }
 
 

@@ -1,0 +1,430 @@
+// Fused absorbed-MLA decode kernel with split wave roles, for 64 and 128 query
+// heads on gfx950.
+//
+// A workgroup of eight waves keeps 64 query heads of its work units (split-KV
+// segments: a token range [kv_begin, kv_end) of one request's page list); at
+// 128 heads two workgroups, one per head group, walk the same token ranges on
+// the same XCD, so each KV tile comes from HBM once and from L2 the second
+// time.  The waves split by role, one of each role per SIMD:
+//   QK waves (0..3)  wave r holds Q for heads 16r..16r+15 and computes
+//                    S^T[token, head] = K[token, 576] . Q^T[576, head] with
+//                    MFMA 16x16x32 bf16 (K from LDS), then the softmax of those
+//                    heads (running max m, running sum l), and publishes
+//                    P^T[token, head] in bf16 and the rescale factors in LDS;
+//   PV waves (4..7)  wave 4+r accumulates O^T[dim, head] += V^T[dim, token] .
+//                    P^T[token, head] for dims 128r..128r+127 and all 64 heads
+//                    (128 accumulator registers), one tile behind the QK waves;
+//                    it also issues the KV tile copies and writes the unit's
+//                    output rows.
+// With O at 64 heads (128 KB per workgroup) a wave needs at most 256 registers,
+// so two waves share each SIMD: while one waits for LDS data, a copy to be
+// accepted or a VALU chain, the matrix core runs the other.
+//
+// Pipeline.  After a first barrier (tile 0 landed), iteration i runs QK and
+// softmax of tile i on the QK waves and PV of tile i-1 (with the epilogue when
+// tile i-1 ends a unit) on the PV waves, which also issue the copies of tile
+// i+2; then one barrier.  KV tiles of 32 tokens live in
+// a 4-stage LDS ring (two tiles in flight), P^T and the per-head factors in
+// two-deep exchange buffers.  Every PV wave counts the vector-memory
+// operations it has issued; before the barrier it waits, with an exact
+// s_waitcnt vmcnt, until its share of tile i+1 has landed.
+//
+// Masking.  Only the last tile of a unit can be partial.  Its ckv slots past
+// kv_end copy the last valid row (finite data), its kpe slots the page's own
+// rows; the QK waves set those slots' scores to -inf (a select) before the
+// softmax, so they add exactly zero to PV.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "pkvmla_tiles.h"
+
+namespace pkvmla {
+
+namespace {
+
+constexpr int kRsWaves = 8;
+constexpr int kRsHeads = 64;   // heads per workgroup
+constexpr int kRsHB = 4;       // head blocks of 16
+constexpr int kRsRing = 4;     // LDS stages: PV tile, QK tile, two tiles in flight
+constexpr int kRsAhead = 6;    // k-steps between a K fragment's LDS read and its MFMA
+constexpr int kRsVAhead = 3;   // dim blocks between a V fragment's LDS read and its MFMAs
+constexpr int kRsDBW = 8;      // output-dim blocks of 16 per PV wave (128 dims)
+static_assert(kRsWaves / 2 == kCopyWaves, "the PV waves issue the tile copies");
+
+// LDS layout
+constexpr int kXpOff = kRsRing * kStageBytes;      // P^T exchange: [parity][hb] 1 KB blocks
+constexpr int kXaOff = kXpOff + 2 * kRsHB * 1024;  // rescale factors: [parity][li][hb] floats
+constexpr int kXlOff = kXaOff + 2 * 64 * 4;        // unit row sums:   [parity][li][hb] floats
+constexpr int kRsLds = kXlOff + 2 * 64 * 4;
+static_assert(kRsLds <= 160 * 1024, "LDS budget");
+
+// Unit cursor: the unit and tile a role is at, with the unit's fields.
+struct UnitCursor {
+  int u;        // unit index
+  int tile;     // tile index within the unit
+  int ntiles;   // tiles in the unit
+  int b, kv0, kv1, slot;
+};
+
+__device__ __forceinline__ void cursor_load(UnitCursor& c, idx_ptr units) {
+  idx_ptr rec = units + (size_t)c.u * kUnitInts;
+  c.b = rec[0];
+  c.kv0 = rec[2];
+  c.kv1 = rec[3];
+  c.slot = rec[4];
+  c.ntiles = (c.kv1 - c.kv0 + kTile - 1) / kTile;
+  c.tile = 0;
+}
+
+__device__ __forceinline__ void cursor_next(UnitCursor& c, idx_ptr units, int u_end) {
+  if (++c.tile >= c.ntiles) {
+    if (++c.u < u_end) cursor_load(c, units);
+  }
+}
+
+}  // namespace
+
+template <bool BIG>
+__global__ void __launch_bounds__(kRsWaves * 64, 1)
+mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
+                     const uint16_t* __restrict__ ckv_cache, const uint16_t* __restrict__ kpe_cache,
+                     uint16_t* __restrict__ out, float* __restrict__ lse_out,
+                     float* __restrict__ part_o, float* __restrict__ part_lse,
+                     const int32_t* __restrict__ wg_indptr_g, const int32_t* __restrict__ units_g,
+                     const int32_t* __restrict__ seq_indptr_g,
+                     const int32_t* __restrict__ seq_indices_g, int H, int n_hg, int n_lanes,
+                     int log2_ps, float sm_scale, float C, float thr) {
+  const idx_ptr wg_indptr = (idx_ptr)wg_indptr_g;
+  const idx_ptr units = (idx_ptr)units_g;
+  const idx_ptr seq_indptr = (idx_ptr)seq_indptr_g;
+  const idx_ptr seq_indices = (idx_ptr)seq_indices_g;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kRsLds];
+  LDS_AS char* smem = (LDS_AS char*)smem_raw;
+  const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = wave & 3;  // QK: head block; PV: dim quarter
+  // Block -> (head group, lane): the head groups of one lane are 8 blocks
+  // apart, which the dispatcher places on the same XCD.
+  const int hg = (int)(blockIdx.x >> 3) % n_hg;
+  const int sl = (int)(blockIdx.x / (8 * n_hg)) * 8 + (int)(blockIdx.x & 7);
+  if (sl >= n_lanes) return;
+  const int u_begin = wg_indptr[sl];
+  const int u_end = wg_indptr[sl + 1];
+  if (u_begin >= u_end) return;
+  const char* ckv = reinterpret_cast<const char*>(ckv_cache);
+  const char* kpe = reinterpret_cast<const char*>(kpe_cache);
+
+  // Tiles of the workgroup (both roles run the same number of barriers).
+  int G = 0;
+  for (int u = u_begin; u < u_end; ++u) {
+    idx_ptr rec = units + (size_t)u * kUnitInts;
+    G += (rec[3] - rec[2] + kTile - 1) / kTile;
+  }
+
+  if (wave < 4) {
+    // ======================= QK and softmax role =======================
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4;
+    const int li = lane & 15;
+    const int head = hg * kRsHeads + r * 16 + li;
+    int offA[2], offK[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      offA[tb] = lds_ckv_off(tb * 16 + li, g);
+      offK[tb] = lds_kpe_off(tb * 16 + li, g);
+    }
+    UnitCursor cq;
+    cq.u = u_begin;
+    cursor_load(cq, units);
+    bf16x8_t q[18];
+    float m_run = -INFINITY, l_run = 0.f;
+
+    lds_barrier();  // tile 0 has landed
+    for (int i = 0; i <= G; ++i) {
+      if (i < G) {
+        const int stage = i % kRsRing;
+        const int par = i & 1;
+        if (cq.tile == 0) {
+          // the unit's query: lane (g, li) holds Q[head][ks*32 + g*8 .. +7]
+          const char* qn = reinterpret_cast<const char*>(q_nope + ((size_t)cq.b * H + head) * kCkvDim);
+          const char* qp = reinterpret_cast<const char*>(q_pe + ((size_t)cq.b * H + head) * kKpeDim);
+#pragma unroll
+          for (int ks = 0; ks < 16; ++ks)
+            q[ks] = *reinterpret_cast<const bf16x8_t*>(qn + (ks * 32 + g * 8) * 2);
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2)
+            q[16 + k2] = *reinterpret_cast<const bf16x8_t*>(qp + (k2 * 32 + g * 8) * 2);
+          m_run = -INFINITY;
+          l_run = 0.f;
+        }
+        // ---- QK: S^T = K . Q^T, 18 k-steps x 2 token blocks ----
+        const int so = stage * kStageBytes;
+        int oA0 = offA[0], oA1 = offA[1], oK0 = offK[0], oK1 = offK[1];
+        asm volatile("" : "+v"(oA0), "+v"(oA1), "+v"(oK0), "+v"(oK1));
+        auto ldA = [&](int ks, int tb) -> bf16x8_t {
+          const int base = tb ? (ks < 16 ? oA1 : oK1) : (ks < 16 ? oA0 : oK0);
+          const int off = ks < 16 ? ((so + base) ^ (ks << 6)) : ((so + base) ^ ((ks - 16) << 6));
+          return *(const LDS_AS bf16x8_t*)(smem + off);
+        };
+        constexpr int AH = kRsAhead;
+        bf16x8_t A[AH + 1][2];
+#pragma unroll
+        for (int pp = 0; pp < AH; ++pp) {
+          A[pp][0] = ldA(pp, 0);
+          A[pp][1] = ldA(pp, 1);
+        }
+        f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int ks = 0; ks < 18; ++ks) {
+          if (ks + AH < 18) {
+            A[(ks + AH) % (AH + 1)][0] = ldA(ks + AH, 0);
+            A[(ks + AH) % (AH + 1)][1] = ldA(ks + AH, 1);
+          }
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb)
+            acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ks % (AH + 1)][tb], q[ks], acc[tb], 0, 0, 0);
+        }
+        // ---- softmax of this tile: lane (g, li) holds tokens tb*16 + g*4 + k ----
+        const int valid = min(cq.kv1 - (cq.kv0 + cq.tile * kTile), kTile);
+        float sv[8];
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int t = tb * 16 + g * 4 + k;
+            sv[tb * 4 + k] = (valid >= kTile || t < valid) ? acc[tb][k] : -INFINITY;
+          }
+        float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+        mx = fmaxf(mx, fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+        mx = max_over_rows(mx);
+        // lazy running max: m moves only when the tile max exceeds it by more
+        // than thr (probabilities stay <= 2^thr*C); the first tile always sets it
+        const bool grow = mx > m_run + thr;
+        const float m_new = grow ? mx : m_run;
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * C);
+        m_run = m_new;
+        const float mc = m_run * C;
+        float ps = 0.f;
+        bf16x8_t pT;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sv[k], C, -mc));
+          ps += p;
+          pT[k] = (__bf16)p;
+        }
+        l_run = l_run * alpha + ps;
+        *(LDS_AS bf16x8_t*)(smem + kXpOff + (par * kRsHB + r) * 1024 + lane * 16) = pT;
+        if (g == 0) *(LDS_AS float*)(smem + kXaOff + (par * 64 + li * 4 + r) * 4) = alpha;
+        if (cq.tile == cq.ntiles - 1) {
+          // unit done: row sums for the PV waves, lse for the output
+          float l = l_run;
+          l += __shfl_xor(l, 16);
+          l += __shfl_xor(l, 32);
+          const float lse = m_run * sm_scale + __builtin_amdgcn_logf(l) * 0.69314718055994531f;
+          if (g == 0) {
+            *(LDS_AS float*)(smem + kXlOff + (par * 64 + li * 4 + r) * 4) = l;
+            if (cq.slot < 0) lse_out[(size_t)cq.b * H + head] = lse;
+            else part_lse[(size_t)cq.slot * H + head] = lse;
+          }
+        }
+        cursor_next(cq, units, u_end);
+      }
+      lds_barrier();
+    }
+  } else {
+    // ======================= PV, copies and epilogue role =======================
+    const int lane0 = threadIdx.x & 63;
+    const int g0 = lane0 >> 4;
+    const int li0 = lane0 & 15;
+    int offV[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int tV = tb * 16 + g0 * 4 + (li0 >> 2);
+      const int qq = li0 & 3;
+      offV[tb] = lds_ckv_off(tV, qq >> 1) + (qq & 1) * 8;
+    }
+    const CopyLanes CL = copy_lanes(r);
+
+    // ---- tile stream (copies) ----
+    TileStream ts;
+    ts.u = u_begin;
+    ts.u_end = u_end;
+    ts.g = 0;
+    stream_load_unit(ts, units, seq_indptr, seq_indices, log2_ps);
+    int vmc = 0;
+    int rv0 = 0, rv1 = 0, rv2 = 0, rv3 = 0;
+    auto book_tile = [&]() {
+      vmc += kCopiesPerWave;
+      const int st = ts.g % kRsRing;
+      rv0 = st == 0 ? vmc : rv0;
+      rv1 = st == 1 ? vmc : rv1;
+      rv2 = st == 2 ? vmc : rv2;
+      rv3 = st == 3 ? vmc : rv3;
+      stream_advance(ts, units, seq_indptr, seq_indices, log2_ps);
+    };
+    auto vmc_of = [&](int gidx) {
+      const int st = gidx % kRsRing;
+      return st == 0 ? rv0 : st == 1 ? rv1 : st == 2 ? rv2 : rv3;
+    };
+    auto issue_whole = [&]() {
+      const TileCopy c = tile_copy(ts, ckv, kpe, log2_ps,
+                                   smem_base + (uint32_t)(ts.g % kRsRing) * kStageBytes, r);
+      tile_copy_wave<BIG>(c, ckv, kpe, r, CL);
+      book_tile();
+    };
+    // prologue: tiles 0 and 1 in flight; tile 0 lands before the first barrier
+    if (ts.u < ts.u_end) issue_whole();
+    if (ts.u < ts.u_end) issue_whole();
+    wait_vm_le(vmc - vmc_of(0));
+    lds_barrier();
+
+    UnitCursor cp;
+    cp.u = u_begin;
+    cursor_load(cp, units);
+    // O (128 VGPRs, MFMAs in VGPR form) starts at zero once.  A tile whose
+    // rescale factors are not all 1 multiplies O by them, one dim block at a
+    // time just before its MFMAs; the factors are exactly 0 on a unit's first
+    // tile (the running max starts at -inf), which clears the previous unit.
+    f32x4_t o[kRsDBW][kRsHB];
+#pragma unroll
+    for (int db = 0; db < kRsDBW; ++db)
+#pragma unroll
+      for (int hb = 0; hb < kRsHB; ++hb) o[db][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // copies of tile j go into the stage PV(j-4) released before the barrier
+    // of the iteration that issues them; whole tiles spread one part per dim
+    // block of PV, other tiles go out at once
+    auto start_copies = [&](TileCopy& cpy) -> bool {
+      if (ts.u >= ts.u_end) return false;
+      cpy = tile_copy(ts, ckv, kpe, log2_ps, smem_base + (uint32_t)(ts.g % kRsRing) * kStageBytes, r);
+      if (BIG && cpy.full) return true;
+      tile_copy_wave<BIG>(cpy, ckv, kpe, r, CL);
+      book_tile();
+      return false;
+    };
+
+    // ---- iteration 0: the QK waves take tile 0; tile 2 goes out ----
+    {
+      TileCopy cpy{};
+      if (start_copies(cpy)) {
+#pragma unroll
+        for (int k = 0; k < kCopiesPerWave; ++k) tile_copy_part_full(cpy, r, k, CL);
+        book_tile();
+      }
+      if (G > 1) wait_vm_le(vmc - vmc_of(1));
+      lds_barrier();
+    }
+
+    // ---- iteration t+1: PV of tile t, copies of tile t+3 ----
+    for (int t = 0; t < G; ++t) {
+      TileCopy cpy{};
+      const bool spread = start_copies(cpy);
+      const int stage = t % kRsRing;
+      const int par = t & 1;
+      const int lane = lane_id_fresh();
+      bf16x8_t pB[kRsHB];
+#pragma unroll
+      for (int hb = 0; hb < kRsHB; ++hb)
+        pB[hb] = *(const LDS_AS bf16x8_t*)(smem + kXpOff + (par * kRsHB + hb) * 1024 + lane * 16);
+      const f32x4_t a4 = *(const LDS_AS f32x4_t*)(smem + kXaOff + (par * 64 + (lane & 15) * 4) * 4);
+      const bool need = a4[0] != 1.0f || a4[1] != 1.0f || a4[2] != 1.0f || a4[3] != 1.0f;
+      const bool rescale = __builtin_amdgcn_ballot_w64(need) != 0;
+      __builtin_amdgcn_sched_barrier(0);
+      int oV0 = offV[0], oV1 = offV[1];
+      asm volatile("" : "+v"(oV0), "+v"(oV1));
+      const int so = stage * kStageBytes;
+      auto ldV = [&](int db, int tb) -> bf16x4_t {
+        const int dbg = r * kRsDBW + db;
+        return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (LDS_AS bf16x4_t*)(smem + ((so + (tb ? oV1 : oV0)) ^ (dbg << 5))));
+      };
+      constexpr int VP = kRsVAhead;
+      {
+        bf16x4_t V[VP + 1][2];
+#pragma unroll
+        for (int pp = 0; pp < VP; ++pp) {
+          V[pp][0] = ldV(pp, 0);
+          V[pp][1] = ldV(pp, 1);
+        }
+#pragma unroll
+        for (int db = 0; db < kRsDBW; ++db) {
+          if (db + VP < kRsDBW) {
+            V[(db + VP) % (VP + 1)][0] = ldV(db + VP, 0);
+            V[(db + VP) % (VP + 1)][1] = ldV(db + VP, 1);
+          }
+          const bf16x8_t a = __builtin_shufflevector(V[db % (VP + 1)][0], V[db % (VP + 1)][1], 0, 1,
+                                                     2, 3, 4, 5, 6, 7);
+          if (rescale) {
+#pragma unroll
+            for (int hb = 0; hb < kRsHB; ++hb) o[db][hb] *= a4[hb];
+          }
+#pragma unroll
+          for (int hb = 0; hb < kRsHB; ++hb) {
+            o[db][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pB[hb], o[db][hb], 0, 0, 0);
+          }
+          if (spread) tile_copy_part_full(cpy, r, db, CL);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (cp.tile == cp.ntiles - 1) {
+        // ---- epilogue: this wave's 128 dims of the unit's 64 heads ----
+        const int le = lane_id_fresh();
+        const int ge = le >> 4, lie = le & 15;
+        const f32x4_t l4 = *(const LDS_AS f32x4_t*)(smem + kXlOff + (par * 64 + lie * 4) * 4);
+        float linv[kRsHB];
+#pragma unroll
+        for (int hb = 0; hb < kRsHB; ++hb) linv[hb] = __builtin_amdgcn_rcpf(l4[hb]);
+        // lane (g, li) holds dims r*128 + db*16 + g*4 .. +3 of head hb*16 + li
+        const uint32_t col = (uint32_t)(lie * kCkvDim + r * (kRsDBW * 16) + ge * 4);
+        char* obase = reinterpret_cast<char*>(out + ((size_t)cp.b * H + hg * kRsHeads) * kCkvDim);
+        char* pbase = reinterpret_cast<char*>(part_o + ((size_t)max(cp.slot, 0) * H + hg * kRsHeads) * kCkvDim);
+        const bool to_out = cp.slot < 0;
+#pragma unroll
+        for (int hb = 0; hb < kRsHB; ++hb) {
+          const uint32_t row = col + (uint32_t)hb * 16 * kCkvDim;
+#pragma unroll
+          for (int db = 0; db < kRsDBW; ++db) {
+            const f32x4_t v = o[db][hb] * linv[hb];
+            if (to_out)
+              *reinterpret_cast<bf16x4_t*>(obase + row * 2 + db * 32) =
+                  __builtin_convertvector(v, bf16x4_t);  // RNE
+            else
+              *reinterpret_cast<f32x4_t*>(pbase + row * 4 + db * 64) = v;
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        vmc += kRsDBW * kRsHB;
+      }
+      cursor_next(cp, units, u_end);
+      if (spread) {
+        tile_copy_part_full(cpy, r, kCopiesPerWave - 1, CL);
+        book_tile();
+      }
+      // tile t+2 must have landed before the barrier that starts QK(t+2)
+      if (t + 2 < G) wait_vm_le(vmc - vmc_of(t + 2));
+      lds_barrier();
+    }
+    // no copy may still be writing LDS when the workgroup retires
+    wait_vmcnt<0>();
+  }
+}
+
+bool launch_decode_rs(const DecodeParams& p, hipStream_t stream, hipError_t* err) {
+  if (p.waves != kRsWaves || p.heads_per_wave != 16 || p.num_heads != kRsHeads * p.head_groups)
+    return false;
+  const bool big = p.log2_ps >= 5;
+  const dim3 grid(decode_grid(p.n_lanes, p.head_groups)), block(kRsWaves * 64);
+#define PKVMLA_RS_ARGS                                                                   \
+  p.q_nope, p.q_pe, p.ckv, p.kpe, p.out, p.lse, p.part_o, p.part_lse, p.wg_indptr, p.units, \
+      p.seq_indptr, p.seq_indices, p.num_heads, p.head_groups, p.n_lanes, p.log2_ps,      \
+      p.sm_scale, p.score_log2, p.rescale_thr
+  if (big) mla_decode_rs_kernel<true><<<grid, block, 0, stream>>>(PKVMLA_RS_ARGS);
+  else mla_decode_rs_kernel<false><<<grid, block, 0, stream>>>(PKVMLA_RS_ARGS);
+#undef PKVMLA_RS_ARGS
+  *err = hipGetLastError();
+  return true;
+}
+
+}  // namespace pkvmla

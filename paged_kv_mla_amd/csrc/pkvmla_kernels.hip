@@ -588,8 +588,8 @@ bool kernel_config_for(int num_heads, KernelConfig* cfg) {
   switch (num_heads) {
     case 16: *cfg = KernelConfig{1, 16, 2, 2, 1, 1}; break;
     case 32: *cfg = KernelConfig{2, 16, 2, 2, 1, 1}; break;
-    case 64: *cfg = KernelConfig{4, 16, 3, 1, 4, 1}; break;
-    case 128: *cfg = KernelConfig{4, 32, 3, 1, 4, 1}; break;
+    case 64: *cfg = KernelConfig{8, 16, 4, 1, 4, 1}; break;
+    case 128: *cfg = KernelConfig{8, 16, 4, 1, 4, 2}; break;
     default: return false;
   }
   // Experiments only: PKVMLA_CONFIG="waves,heads_per_wave,stages,wg_per_cu,fixed,head_groups"
@@ -598,12 +598,14 @@ bool kernel_config_for(int num_heads, KernelConfig* cfg) {
     KernelConfig c{};
     if (sscanf(e, "%d,%d,%d,%d,%d,%d", &c.waves, &c.heads_per_wave, &c.stages, &c.wg_per_cu,
                &c.fixed_cost, &c.head_groups) == 6 &&
-        c.head_groups >= 1 && c.waves * c.heads_per_wave * c.head_groups == num_heads &&
+        c.head_groups >= 1 &&
+        (c.waves == 8 ? 4 : c.waves) * c.heads_per_wave * c.head_groups == num_heads &&
         c.wg_per_cu >= 1 && c.fixed_cost >= 0) {
       const bool exists = (c.waves == 1 && c.heads_per_wave == 16 && c.stages == 2) ||
                           (c.waves == 2 && c.heads_per_wave == 16 && c.stages == 2) ||
                           (c.waves == 4 && c.heads_per_wave == 16 && c.stages == 3 && c.head_groups == 1) ||
-                          (c.waves == 4 && c.heads_per_wave == 32 && c.stages == 3 && c.head_groups == 1);
+                          (c.waves == 4 && c.heads_per_wave == 32 && c.stages == 3 && c.head_groups == 1) ||
+                          (c.waves == 8 && c.heads_per_wave == 16 && c.stages == 4);
       if (exists) *cfg = c;
     }
   }
@@ -622,6 +624,7 @@ int decode_grid(int n_lanes, int head_groups) {
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   if (p.n_lanes <= 0) return hipSuccess;
   hipError_t err = hipSuccess;
+  if (launch_decode_rs(p, stream, &err)) return err;
   if (launch_decode_w4(p, stream, &err)) return err;
   const int grid = decode_grid(p.n_lanes, p.head_groups);
   // big: every page holds whole 32-token tiles (page_size >= 32)
