@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpkvmla.so")
 ARCH = "gfx950"
 
-SOURCES = ["pkvmla_api.cpp", "pkvmla_schedule.cpp", "pkvmla_kernels.hip", "pkvmla_decode_w4.hip", "pkvmla_decode_rs.hip"]
+SOURCES = ["pkvmla_api.cpp", "pkvmla_schedule.cpp", "pkvmla_kernels.hip", "pkvmla_decode_rs.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

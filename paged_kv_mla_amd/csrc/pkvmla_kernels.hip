@@ -603,8 +603,6 @@ bool kernel_config_for(int num_heads, KernelConfig* cfg) {
         c.wg_per_cu >= 1 && c.fixed_cost >= 0) {
       const bool exists = (c.waves == 1 && c.heads_per_wave == 16 && c.stages == 2) ||
                           (c.waves == 2 && c.heads_per_wave == 16 && c.stages == 2) ||
-                          (c.waves == 4 && c.heads_per_wave == 16 && c.stages == 3 && c.head_groups == 1) ||
-                          (c.waves == 4 && c.heads_per_wave == 32 && c.stages == 3 && c.head_groups == 1) ||
                           (c.waves == 8 && c.heads_per_wave == 16 && c.stages == 4);
       if (exists) *cfg = c;
     }
@@ -625,7 +623,6 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   if (p.n_lanes <= 0) return hipSuccess;
   hipError_t err = hipSuccess;
   if (launch_decode_rs(p, stream, &err)) return err;
-  if (launch_decode_w4(p, stream, &err)) return err;
   const int grid = decode_grid(p.n_lanes, p.head_groups);
   // big: every page holds whole 32-token tiles (page_size >= 32)
   const int key = p.waves * 10000 + p.heads_per_wave * 100 + p.stages * 10 + (p.log2_ps >= 5);
