@@ -71,10 +71,9 @@ struct GatherParams {
 
 int decode_grid(int n_lanes, int head_groups);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
-// Four-wave kernel (64 and 128 heads, one head group); false when the
-// configuration is not its own, else *err holds the launch status.
+// Role-split kernel (64 heads per workgroup, one or two head groups); false
+// when the configuration is not its own, else *err holds the launch status.
 bool launch_decode_rs(const DecodeParams& p, hipStream_t stream, hipError_t* err);
-// Eight-wave kernel (64 heads per workgroup, one or two head groups).
 hipError_t launch_merge(const MergeParams& p, int n_merges, hipStream_t stream);
 hipError_t launch_gather(const GatherParams& p, int n_units, hipStream_t stream);
 
