@@ -1,11 +1,11 @@
 // Fused absorbed-MLA decode kernel with split wave roles, for 64 and 128 query
 // heads on gfx950.
 //
-// A workgroup of eight waves keeps 64 query heads of its work units (split-KV
+// A workgroup of ten waves keeps 64 query heads of its work units (split-KV
 // segments: a token range [kv_begin, kv_end) of one request's page list); at
 // 128 heads two workgroups, one per head group, walk the same token ranges on
 // the same XCD, so each KV tile comes from HBM once and from L2 the second
-// time.  The waves split by role, one of each role per SIMD:
+// time.  The waves split by role:
 //   QK waves (0..3)  wave r holds Q for heads 16r..16r+15 and computes
 //                    S^T[token, head] = K[token, 576] . Q^T[576, head] with
 //                    MFMA 16x16x32 bf16 (K from LDS), then the softmax of those
@@ -13,21 +13,26 @@
 //                    P^T[token, head] in bf16 and the rescale factors in LDS;
 //   PV waves (4..7)  wave 4+r accumulates O^T[dim, head] += V^T[dim, token] .
 //                    P^T[token, head] for dims 128r..128r+127 and all 64 heads
-//                    (128 accumulator registers), one tile behind the QK waves;
-//                    it also issues the KV tile copies and writes the unit's
-//                    output rows.
-// With O at 64 heads (128 KB per workgroup) a wave needs at most 256 registers,
-// so two waves share each SIMD: while one waits for LDS data, a copy to be
-// accepted or a VALU chain, the matrix core runs the other.
+//                    (128 accumulator registers), one tile behind the QK waves,
+//                    and writes the unit's output rows;
+//   copy waves (8, 9) issue the HBM -> LDS copies of the KV tiles (direct
+//                    LDS loads), each half of every tile.
+// A copy instruction holds its wave until the CU's memory pipeline accepts it
+// (about one 1 KB copy every 23 clocks per CU, 36 per tile), so copies issued
+// from a computing wave stall its MFMAs; the copy waves take that wait
+// instead.  Ten waves put three on two of the SIMDs, so every wave gets at
+// most 168 registers (the PV waves' 128 accumulators fit with a V prefetch
+// depth of two).
 //
 // Pipeline.  After a first barrier (tile 0 landed), iteration i runs QK and
 // softmax of tile i on the QK waves and PV of tile i-1 (with the epilogue when
-// tile i-1 ends a unit) on the PV waves, which also issue the copies of tile
-// i+2; then one barrier.  KV tiles of 32 tokens live in
-// a 4-stage LDS ring (two tiles in flight), P^T and the per-head factors in
-// two-deep exchange buffers.  Every PV wave counts the vector-memory
-// operations it has issued; before the barrier it waits, with an exact
-// s_waitcnt vmcnt, until its share of tile i+1 has landed.
+// tile i-1 ends a unit) on the PV waves, while the copy waves issue tile i+2
+// right after the barrier and then wait, with an exact s_waitcnt vmcnt, until
+// their share of tile i+1 has landed; then one barrier.  KV tiles of 32
+// tokens live in a 4-stage LDS ring (two tiles in flight), P^T and the
+// per-head factors in two-deep exchange buffers.  A copy wave keeps at most
+// two tiles' shares (36 operations) in flight: the vmcnt counter holds at
+// most 63, and a wave with more outstanding cannot wait for them exactly.
 //
 // Masking.  Only the last tile of a unit can be partial.  Its ckv slots past
 // kv_end copy the last valid row (finite data), its kpe slots the page's own
@@ -43,14 +48,17 @@ namespace pkvmla {
 
 namespace {
 
-constexpr int kRsWaves = 8;
+constexpr int kRsWaves = 8;    // compute waves (QK and PV)
+constexpr int kRsCopyWaves = 2;
+constexpr int kRsThreads = (kRsWaves + kRsCopyWaves) * 64;
 constexpr int kRsHeads = 64;   // heads per workgroup
 constexpr int kRsHB = 4;       // head blocks of 16
 constexpr int kRsRing = 4;     // LDS stages: PV tile, QK tile, two tiles in flight
 constexpr int kRsAhead = 6;    // k-steps between a K fragment's LDS read and its MFMA
-constexpr int kRsVAhead = 3;   // dim blocks between a V fragment's LDS read and its MFMAs
+constexpr int kRsVAhead = 2;   // dim blocks between a V fragment's LDS read and its MFMAs
+                               // (two: the register budget at ten waves)
 constexpr int kRsDBW = 8;      // output-dim blocks of 16 per PV wave (128 dims)
-static_assert(kRsWaves / 2 == kCopyWaves, "the PV waves issue the tile copies");
+static_assert(kCopyWaves == 2 * kRsCopyWaves, "each copy wave issues two copy slots' shares");
 
 // LDS layout
 constexpr int kXpOff = kRsRing * kStageBytes;      // P^T exchange: [parity][hb] 1 KB blocks
@@ -86,7 +94,7 @@ __device__ __forceinline__ void cursor_next(UnitCursor& c, idx_ptr units, int u_
 }  // namespace
 
 template <bool BIG>
-__global__ void __launch_bounds__(kRsWaves * 64, 1)
+__global__ void __launch_bounds__(kRsThreads, 1)
 mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
                      const uint16_t* __restrict__ ckv_cache, const uint16_t* __restrict__ kpe_cache,
                      uint16_t* __restrict__ out, float* __restrict__ lse_out,
@@ -233,8 +241,8 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
       }
       lds_barrier();
     }
-  } else {
-    // ======================= PV, copies and epilogue role =======================
+  } else if (wave < 8) {
+    // ======================= PV and epilogue role =======================
     const int lane0 = threadIdx.x & 63;
     const int g0 = lane0 >> 4;
     const int li0 = lane0 & 15;
@@ -245,39 +253,6 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
       const int qq = li0 & 3;
       offV[tb] = lds_ckv_off(tV, qq >> 1) + (qq & 1) * 8;
     }
-    const CopyLanes CL = copy_lanes(r);
-
-    // ---- tile stream (copies) ----
-    TileStream ts;
-    ts.u = u_begin;
-    ts.u_end = u_end;
-    ts.g = 0;
-    stream_load_unit(ts, units, seq_indptr, seq_indices, log2_ps);
-    int vmc = 0;
-    int rv0 = 0, rv1 = 0, rv2 = 0, rv3 = 0;
-    auto book_tile = [&]() {
-      vmc += kCopiesPerWave;
-      const int st = ts.g % kRsRing;
-      rv0 = st == 0 ? vmc : rv0;
-      rv1 = st == 1 ? vmc : rv1;
-      rv2 = st == 2 ? vmc : rv2;
-      rv3 = st == 3 ? vmc : rv3;
-      stream_advance(ts, units, seq_indptr, seq_indices, log2_ps);
-    };
-    auto vmc_of = [&](int gidx) {
-      const int st = gidx % kRsRing;
-      return st == 0 ? rv0 : st == 1 ? rv1 : st == 2 ? rv2 : rv3;
-    };
-    auto issue_whole = [&]() {
-      const TileCopy c = tile_copy(ts, ckv, kpe, log2_ps,
-                                   smem_base + (uint32_t)(ts.g % kRsRing) * kStageBytes, r);
-      tile_copy_wave<BIG>(c, ckv, kpe, r, CL);
-      book_tile();
-    };
-    // prologue: tiles 0 and 1 in flight; tile 0 lands before the first barrier
-    if (ts.u < ts.u_end) issue_whole();
-    if (ts.u < ts.u_end) issue_whole();
-    wait_vm_le(vmc - vmc_of(0));
     lds_barrier();
 
     UnitCursor cp;
@@ -293,34 +268,11 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
 #pragma unroll
       for (int hb = 0; hb < kRsHB; ++hb) o[db][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // copies of tile j go into the stage PV(j-4) released before the barrier
-    // of the iteration that issues them; whole tiles spread one part per dim
-    // block of PV, other tiles go out at once
-    auto start_copies = [&](TileCopy& cpy) -> bool {
-      if (ts.u >= ts.u_end) return false;
-      cpy = tile_copy(ts, ckv, kpe, log2_ps, smem_base + (uint32_t)(ts.g % kRsRing) * kStageBytes, r);
-      if (BIG && cpy.full) return true;
-      tile_copy_wave<BIG>(cpy, ckv, kpe, r, CL);
-      book_tile();
-      return false;
-    };
-
-    // ---- iteration 0: the QK waves take tile 0; tile 2 goes out ----
-    {
-      TileCopy cpy{};
-      if (start_copies(cpy)) {
-#pragma unroll
-        for (int k = 0; k < kCopiesPerWave; ++k) tile_copy_part_full(cpy, r, k, CL);
-        book_tile();
-      }
-      if (G > 1) wait_vm_le(vmc - vmc_of(1));
-      lds_barrier();
-    }
+    // ---- iteration 0: the QK waves take tile 0 ----
+    lds_barrier();
 
     // ---- iteration t+1: PV of tile t, copies of tile t+3 ----
     for (int t = 0; t < G; ++t) {
-      TileCopy cpy{};
-      const bool spread = start_copies(cpy);
       const int stage = t % kRsRing;
       const int par = t & 1;
       const int lane = lane_id_fresh();
@@ -364,7 +316,6 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
           for (int hb = 0; hb < kRsHB; ++hb) {
             o[db][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pB[hb], o[db][hb], 0, 0, 0);
           }
-          if (spread) tile_copy_part_full(cpy, r, db, CL);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -395,18 +346,63 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
             __builtin_amdgcn_sched_barrier(0);
           }
         }
-        vmc += kRsDBW * kRsHB;
       }
       cursor_next(cp, units, u_end);
-      if (spread) {
-        tile_copy_part_full(cpy, r, kCopiesPerWave - 1, CL);
-        book_tile();
-      }
-      // tile t+2 must have landed before the barrier that starts QK(t+2)
-      if (t + 2 < G) wait_vm_le(vmc - vmc_of(t + 2));
       lds_barrier();
     }
-    // no copy may still be writing LDS when the workgroup retires
+  } else {
+    // ======================= copy role =======================
+    // copy wave cw issues copy slots 2cw and 2cw+1 of every tile (18 copies;
+    // at most two tiles, 36 operations, in flight)
+    const int cw = wave - kRsWaves;
+    CopyLanes CLw[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) CLw[h] = copy_lanes(2 * cw + h);
+    TileStream ts;
+    ts.u = u_begin;
+    ts.u_end = u_end;
+    ts.g = 0;
+    stream_load_unit(ts, units, seq_indptr, seq_indices, log2_ps);
+    int vmc = 0;
+    int rv0 = 0, rv1 = 0, rv2 = 0, rv3 = 0;
+    auto book_tile = [&]() {
+      vmc += 2 * kCopiesPerWave;
+      const int st = ts.g % kRsRing;
+      rv0 = st == 0 ? vmc : rv0;
+      rv1 = st == 1 ? vmc : rv1;
+      rv2 = st == 2 ? vmc : rv2;
+      rv3 = st == 3 ? vmc : rv3;
+      stream_advance(ts, units, seq_indptr, seq_indices, log2_ps);
+    };
+    auto vmc_of = [&](int gidx) {
+      const int st = gidx % kRsRing;
+      return st == 0 ? rv0 : st == 1 ? rv1 : st == 2 ? rv2 : rv3;
+    };
+    auto issue_tile = [&]() {
+      const uint32_t sb = smem_base + (uint32_t)(ts.g % kRsRing) * kStageBytes;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int w = 2 * cw + h;
+        const TileCopy c = tile_copy(ts, ckv, kpe, log2_ps, sb, w);
+        if (BIG && c.full) {
+#pragma unroll
+          for (int k = 0; k < kCopiesPerWave; ++k) tile_copy_part_full(c, w, k, CLw[h]);
+        } else {
+          tile_copy_wave<BIG>(c, ckv, kpe, w, CLw[h]);
+        }
+      }
+      book_tile();
+    };
+    if (ts.u < ts.u_end) issue_tile();
+    if (ts.u < ts.u_end) issue_tile();
+    wait_vm_le(vmc - vmc_of(0));
+    lds_barrier();
+    for (int i = 0; i <= G; ++i) {
+      // tile i+2 into the stage PV(i-2) released at the last barrier
+      if (ts.u < ts.u_end) issue_tile();
+      if (i + 1 < G) wait_vm_le(vmc - vmc_of(i + 1));
+      lds_barrier();
+    }
     wait_vmcnt<0>();
   }
 }
@@ -415,7 +411,7 @@ bool launch_decode_rs(const DecodeParams& p, hipStream_t stream, hipError_t* err
   if (p.waves != kRsWaves || p.heads_per_wave != 16 || p.num_heads != kRsHeads * p.head_groups)
     return false;
   const bool big = p.log2_ps >= 5;
-  const dim3 grid(decode_grid(p.n_lanes, p.head_groups)), block(kRsWaves * 64);
+  const dim3 grid(decode_grid(p.n_lanes, p.head_groups)), block(kRsThreads);
 #define PKVMLA_RS_ARGS                                                                   \
   p.q_nope, p.q_pe, p.ckv, p.kpe, p.out, p.lse, p.part_o, p.part_lse, p.wg_indptr, p.units, \
       p.seq_indptr, p.seq_indices, p.num_heads, p.head_groups, p.n_lanes, p.log2_ps,      \

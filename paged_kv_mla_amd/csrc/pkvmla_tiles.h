@@ -99,7 +99,9 @@ __device__ __forceinline__ TileCopy tile_copy(const TileStream& s, const char* _
   return c;
 }
 
-// One wave's share of a tile's copies in a four-wave workgroup: the ckv rows
+// The copies of a tile are four shares ("copy slots", one per wave of a
+// four-wave workgroup, or two per copy wave of the role-split kernel).  The
+// share of slot `wave`: the ckv rows
 // t = 4*wave + j and t = 4*wave + j + 16 (j = 0..3; one 1 KB row per
 // instruction) and the kpe block of tokens 8*wave .. 8*wave+7 (one instruction,
 // 128 bytes per token).  The 16-byte chunks of a row are XOR-swizzled on the
