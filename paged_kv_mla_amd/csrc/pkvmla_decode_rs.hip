@@ -200,10 +200,14 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int t = tb * 16 + g * 4 + k;
-            sv[tb * 4 + k] = (valid >= kTile || t < valid) ? acc[tb][k] : -INFINITY;
-          }
+          for (int k = 0; k < 4; ++k) sv[tb * 4 + k] = acc[tb][k];
+        if (valid < kTile) {  // a unit's partial last tile (uniform branch)
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              sv[tb * 4 + k] = tb * 16 + g * 4 + k < valid ? sv[tb * 4 + k] : -INFINITY;
+        }
         float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
         mx = fmaxf(mx, fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
         mx = max_over_rows(mx);
@@ -214,14 +218,15 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
         const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * C);
         m_run = m_new;
         const float mc = m_run * C;
-        float ps = 0.f;
+        float pv[8];
         bf16x8_t pT;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sv[k], C, -mc));
-          ps += p;
-          pT[k] = (__bf16)p;
+          pv[k] = __builtin_amdgcn_exp2f(fmaf(sv[k], C, -mc));
+          pT[k] = (__bf16)pv[k];
         }
+        // the lane's share of the row sum as a tree (depth 3, not 8)
+        const float ps = ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
         l_run = l_run * alpha + ps;
         *(LDS_AS bf16x8_t*)(smem + kXpOff + (par * kRsHB + r) * 1024 + lane * 16) = pT;
         if (g == 0) *(LDS_AS float*)(smem + kXaOff + (par * 64 + li * 4 + r) * 4) = alpha;
