@@ -64,7 +64,7 @@ struct pkvmla_plan_s {
   int32_t* d_seq_indptr = nullptr;
   int32_t* d_seq_lens = nullptr;
   int32_t* d_seq_indices = nullptr;
-  float* d_part = nullptr;  // part_o [slots][H][512] then part_lse [slots][H]
+  void* d_part = nullptr;  // part_o bf16 [slots][H][512] then part_lse fp32 [slots][H]
   size_t table_ints = 0;
   // optional per-run timing of the decode kernel (events created up front)
   static constexpr int kTimingSlots = 256;
@@ -172,8 +172,8 @@ int finish_plan(pkvmla_plan_s* P, const std::vector<pkvmla::WorkItem>& items,
   PKVMLA_HIP(hipMemcpyAsync(P->d_tables, host.data(), P->table_ints * sizeof(int32_t),
                             hipMemcpyHostToDevice, stream));
   if (P->sched.n_slots > 0) {
-    const size_t n = (size_t)P->sched.n_slots * P->num_heads * (pkvmla::kCkvDim + 1);
-    PKVMLA_HIP(hipMalloc(&P->d_part, n * sizeof(float)));
+    const size_t rows = (size_t)P->sched.n_slots * P->num_heads;
+    PKVMLA_HIP(hipMalloc(&P->d_part, rows * (pkvmla::kCkvDim * sizeof(uint16_t) + sizeof(float))));
   }
   PKVMLA_HIP(hipStreamSynchronize(stream));
   return PKVMLA_OK;
@@ -368,6 +368,7 @@ int pkvmla_run(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* 
                 dev);
   hipStream_t s = (hipStream_t)stream;
   const size_t part_o_elems = (size_t)P->sched.n_slots * P->num_heads * pkvmla::kCkvDim;
+  uint16_t* part_o = static_cast<uint16_t*>(P->d_part);
   pkvmla::DecodeParams d{};
   d.q_nope = static_cast<const uint16_t*>(q_nope);
   d.q_pe = static_cast<const uint16_t*>(q_pe);
@@ -375,8 +376,8 @@ int pkvmla_run(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* 
   d.kpe = static_cast<const uint16_t*>(kpe_cache);
   d.out = static_cast<uint16_t*>(out);
   d.lse = lse;
-  d.part_o = P->d_part;
-  d.part_lse = P->d_part ? P->d_part + part_o_elems : nullptr;
+  d.part_o = part_o;
+  d.part_lse = part_o ? reinterpret_cast<float*>(part_o + part_o_elems) : nullptr;
   d.wg_indptr = P->d_wg_indptr;
   d.units = P->d_units;
   d.seq_indptr = P->d_seq_indptr;

@@ -98,7 +98,7 @@ __global__ void __launch_bounds__(kRsThreads, 1)
 mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
                      const uint16_t* __restrict__ ckv_cache, const uint16_t* __restrict__ kpe_cache,
                      uint16_t* __restrict__ out, float* __restrict__ lse_out,
-                     float* __restrict__ part_o, float* __restrict__ part_lse,
+                     uint16_t* __restrict__ part_o, float* __restrict__ part_lse,
                      const int32_t* __restrict__ wg_indptr_g, const int32_t* __restrict__ units_g,
                      const int32_t* __restrict__ seq_indptr_g,
                      const int32_t* __restrict__ seq_indices_g, int H, int n_hg, int n_lanes,
@@ -334,20 +334,19 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
         for (int hb = 0; hb < kRsHB; ++hb) linv[hb] = __builtin_amdgcn_rcpf(l4[hb]);
         // lane (g, li) holds dims r*128 + db*16 + g*4 .. +3 of head hb*16 + li
         const uint32_t col = (uint32_t)(lie * kCkvDim + r * (kRsDBW * 16) + ge * 4);
-        char* obase = reinterpret_cast<char*>(out + ((size_t)cp.b * H + hg * kRsHeads) * kCkvDim);
-        char* pbase = reinterpret_cast<char*>(part_o + ((size_t)max(cp.slot, 0) * H + hg * kRsHeads) * kCkvDim);
-        const bool to_out = cp.slot < 0;
+        // a whole request's rows go to out, a split unit's to its partial slot
+        // (both bf16)
+        char* obase = reinterpret_cast<char*>(
+            cp.slot < 0 ? out + ((size_t)cp.b * H + hg * kRsHeads) * kCkvDim
+                        : part_o + ((size_t)cp.slot * H + hg * kRsHeads) * kCkvDim);
 #pragma unroll
         for (int hb = 0; hb < kRsHB; ++hb) {
           const uint32_t row = col + (uint32_t)hb * 16 * kCkvDim;
 #pragma unroll
           for (int db = 0; db < kRsDBW; ++db) {
             const f32x4_t v = o[db][hb] * linv[hb];
-            if (to_out)
-              *reinterpret_cast<bf16x4_t*>(obase + row * 2 + db * 32) =
-                  __builtin_convertvector(v, bf16x4_t);  // RNE
-            else
-              *reinterpret_cast<f32x4_t*>(pbase + row * 4 + db * 64) = v;
+            *reinterpret_cast<bf16x4_t*>(obase + row * 2 + db * 32) =
+                __builtin_convertvector(v, bf16x4_t);  // RNE
             __builtin_amdgcn_sched_barrier(0);
           }
         }

@@ -34,7 +34,7 @@ struct DecodeParams {
   const uint16_t* kpe;       // [P][ps][64]  bf16
   uint16_t* out;             // [B][H][512] bf16
   float* lse;                // [B][H]
-  float* part_o;             // [slots][H][512]
+  uint16_t* part_o;          // [slots][H][512] bf16 (normalized partial outputs)
   float* part_lse;           // [slots][H]
   const int32_t* wg_indptr;  // [grid + 1]
   const int32_t* units;      // [n_units][8]
@@ -51,7 +51,7 @@ struct DecodeParams {
 };
 
 struct MergeParams {
-  const float* part_o;
+  const uint16_t* part_o;    // [slots][H][512] bf16
   const float* part_lse;
   const int32_t* merges;     // [n_merges][4]
   uint16_t* out;

@@ -170,7 +170,7 @@ __global__ void __launch_bounds__(NW * 64)
 mla_decode_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
                   const uint16_t* __restrict__ ckv, const uint16_t* __restrict__ kpe,
                   uint16_t* __restrict__ out, float* __restrict__ lse_out,
-                  float* __restrict__ part_o, float* __restrict__ part_lse,
+                  uint16_t* __restrict__ part_o, float* __restrict__ part_lse,
                   const int32_t* __restrict__ wg_indptr, const int32_t* __restrict__ units,
                   const int32_t* __restrict__ seq_indptr,
                   const int32_t* __restrict__ seq_indices, int H, int n_hg, int n_lanes,
@@ -487,20 +487,16 @@ mla_decode_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restric
 #pragma unroll
     for (int hb = 0; hb < HBN; ++hb) {
       const int h = head0 + hb * 16 + li;
-      if (slot < 0) {
-        uint16_t* orow = out + ((size_t)b * H + h) * kCkvDim + wave * (DBW * 16) + g * 4;
+      // a whole request's row goes to out, a split unit's to its partial slot (both bf16)
+      uint16_t* orow = (slot < 0 ? out + ((size_t)b * H + h) * kCkvDim
+                                 : part_o + ((size_t)slot * H + h) * kCkvDim) +
+                       wave * (DBW * 16) + g * 4;
 #pragma unroll
-        for (int db = 0; db < DBW; ++db) {
-          const f32x4_t v = o[db][hb] * linv[hb];
-          const uint32_t lo = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
-          const uint32_t hi = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
-          *reinterpret_cast<uint2*>(orow + db * 16) = make_uint2(lo, hi);
-        }
-      } else {
-        float* prow = part_o + ((size_t)slot * H + h) * kCkvDim + wave * (DBW * 16) + g * 4;
-#pragma unroll
-        for (int db = 0; db < DBW; ++db)
-          *reinterpret_cast<f32x4_t*>(prow + db * 16) = o[db][hb] * linv[hb];
+      for (int db = 0; db < DBW; ++db) {
+        const f32x4_t v = o[db][hb] * linv[hb];
+        const uint32_t lo = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+        *reinterpret_cast<uint2*>(orow + db * 16) = make_uint2(lo, hi);
       }
     }
   }
@@ -509,7 +505,9 @@ mla_decode_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restric
 // ---------------------------------------------------------------------------
 // Split-KV merge: per (request, head) combine the partial states by
 // log-sum-exp: lse = M + ln sum_i e^(lse_i - M), out = sum_i e^(lse_i - lse) o_i.
-// Block: 4 heads x 64 lanes, 8 dims per lane.
+// The partial outputs o_i are bf16 (each already normalized by its own row
+// sum), the combination runs in fp32.  Block: 4 heads x 64 lanes, 8 dims per
+// lane (one 16-byte load per partial row).
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) mla_merge_kernel(MergeParams p) {
   const int32_t* mr = p.merges + (size_t)blockIdx.x * kMergeInts;
@@ -524,12 +522,12 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(MergeParams p) {
   for (int i = 0; i < n; ++i) {
     const size_t base = (size_t)(s0 + i) * H + h;
     const float w = __builtin_amdgcn_exp2f((p.part_lse[base] - M) * 1.4426950408889634f);
-    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(p.part_o + base * kCkvDim + d0);
-    const f32x4_t x0 = src[0], x1 = src[1];
+    const uint4 x = *reinterpret_cast<const uint4*>(p.part_o + base * kCkvDim + d0);
+    const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      acc[k] = fmaf(w, x0[k], acc[k]);
-      acc[4 + k] = fmaf(w, x1[k], acc[4 + k]);
+      acc[2 * k] = fmaf(w, __builtin_bit_cast(float, xw[k] << 16), acc[2 * k]);
+      acc[2 * k + 1] = fmaf(w, __builtin_bit_cast(float, xw[k] & 0xFFFF0000u), acc[2 * k + 1]);
     }
     wsum += w;
   }
