@@ -54,7 +54,7 @@ constexpr int kRsThreads = (kRsWaves + kRsCopyWaves) * 64;
 constexpr int kRsHeads = 64;   // heads per workgroup
 constexpr int kRsHB = 4;       // head blocks of 16
 constexpr int kRsRing = 4;     // LDS stages: PV tile, QK tile, two tiles in flight
-constexpr int kRsAhead = 6;    // k-steps between a K fragment's LDS read and its MFMA
+constexpr int kRsAhead = 2;    // k-steps between a K fragment's LDS read and its MFMA
 constexpr int kRsVAhead = 2;   // dim blocks between a V fragment's LDS read and its MFMAs
                                // (two: the register budget at ten waves)
 constexpr int kRsDBW = 8;      // output-dim blocks of 16 per PV wave (128 dims)
@@ -176,6 +176,12 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
           const int off = ks < 16 ? ((so + base) ^ (ks << 6)) : ((so + base) ^ ((ks - 16) << 6));
           return *(const LDS_AS bf16x8_t*)(smem + off);
         };
+        // The k-loop runs at raised issue priority: when both waves of a SIMD
+        // have an MFMA ready the QK wave's goes first, so its softmax (VALU)
+        // overlaps the PV wave's MFMAs instead of following them.  Each K
+        // fragment is read AH k-steps ahead (the scheduling barriers keep the
+        // compiler from sinking the reads next to their MFMAs).
+        __builtin_amdgcn_s_setprio(3);
         constexpr int AH = kRsAhead;
         bf16x8_t A[AH + 1][2];
 #pragma unroll
@@ -193,7 +199,9 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb)
             acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ks % (AH + 1)][tb], q[ks], acc[tb], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_s_setprio(0);
         // ---- softmax of this tile: lane (g, li) holds tokens tb*16 + g*4 + k ----
         const int valid = min(cq.kv1 - (cq.kv0 + cq.tile * kTile), kTile);
         float sv[8];
