@@ -146,7 +146,19 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
     UnitCursor cq;
     cq.u = u_begin;
     cursor_load(cq, units);
+    // the unit's query: lane (g, li) holds Q[head][ks*32 + g*8 .. +7]
     bf16x8_t q[18];
+    auto load_q = [&](int b) {
+      const char* qn = reinterpret_cast<const char*>(q_nope + ((size_t)b * H + head) * kCkvDim);
+      const char* qp = reinterpret_cast<const char*>(q_pe + ((size_t)b * H + head) * kKpeDim);
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks)
+        q[ks] = *reinterpret_cast<const bf16x8_t*>(qn + (ks * 32 + g * 8) * 2);
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+        q[16 + k2] = *reinterpret_cast<const bf16x8_t*>(qp + (k2 * 32 + g * 8) * 2);
+    };
+    load_q(cq.b);
     float m_run = -INFINITY, l_run = 0.f;
 
     lds_barrier();  // tile 0 has landed
@@ -155,15 +167,6 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
         const int stage = i % kRsRing;
         const int par = i & 1;
         if (cq.tile == 0) {
-          // the unit's query: lane (g, li) holds Q[head][ks*32 + g*8 .. +7]
-          const char* qn = reinterpret_cast<const char*>(q_nope + ((size_t)cq.b * H + head) * kCkvDim);
-          const char* qp = reinterpret_cast<const char*>(q_pe + ((size_t)cq.b * H + head) * kKpeDim);
-#pragma unroll
-          for (int ks = 0; ks < 16; ++ks)
-            q[ks] = *reinterpret_cast<const bf16x8_t*>(qn + (ks * 32 + g * 8) * 2);
-#pragma unroll
-          for (int k2 = 0; k2 < 2; ++k2)
-            q[16 + k2] = *reinterpret_cast<const bf16x8_t*>(qp + (k2 * 32 + g * 8) * 2);
           m_run = -INFINITY;
           l_run = 0.f;
         }
@@ -202,6 +205,9 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
           __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_setprio(0);
+        // Q of the next unit goes out once the last k-step has read this
+        // unit's, so its latency hides behind the softmax and the barrier
+        if (cq.tile == cq.ntiles - 1 && cq.u + 1 < u_end) load_q(units[(size_t)(cq.u + 1) * kUnitInts]);
         // ---- softmax of this tile: lane (g, li) holds tokens tb*16 + g*4 + k ----
         const int valid = min(cq.kv1 - (cq.kv0 + cq.tile * kTile), kTile);
         float sv[8];
