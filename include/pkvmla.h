@@ -119,8 +119,9 @@ void pkvmla_plan_destroy(pkvmla_plan plan);
 const char* pkvmla_last_error(void);
 
 /* Kernel configuration used for num_heads (values the schedule depends on):
- * cfg[0] = KV tile tokens, cfg[1] = waves per workgroup, cfg[2] = heads per
- * wave, cfg[3] = LDS stages, cfg[4] = workgroups per CU, cfg[5] = fixed cost
+ * cfg[0] = KV tile tokens, cfg[1] = compute waves per workgroup (the QK
+ * waves, one per 16 heads, and four PV waves; two copy waves come on top),
+ * cfg[2] = heads per QK wave, cfg[3] = LDS stages, cfg[4] = workgroups per CU, cfg[5] = fixed cost
  * per segment in tiles, cfg[6] = head groups (workgroups that share one
  * token range, each holding num_heads / head_groups heads; the schedule has
  * num_cu * workgroups_per_cu / head_groups lanes).  Host only; needs no GPU. */

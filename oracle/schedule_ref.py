@@ -36,13 +36,15 @@ PLAN_TILE = 32          # KV tokens per tile
 UNIT_INTS = 8           # int32 per unit record: b, seq, kv_begin, kv_end, slot, row, 0, 0
 MERGE_INTS = 4          # int32 per merge record: b, first_slot, count, 0
 
-# Per head count: (waves per workgroup, heads per wave, LDS stages,
-# workgroups per CU, fixed cost per segment in tiles, head groups).  The
+# Per head count: (compute waves per workgroup: QK and PV, heads per QK wave,
+# LDS stages, workgroups per CU, fixed cost per segment in tiles, head
+# groups).  These mirror the library's plan parameters; nothing below
+# computes with them except the lane count.  The
 # schedule has (CUs x workgroups per CU) / head groups lanes.  The library
 # exports the values it uses; the tests compare them with this table.
 _KERNEL_CONFIGS = {
-    16: (1, 16, 2, 2, 1, 1),
-    32: (2, 16, 2, 2, 1, 1),
+    16: (5, 16, 4, 1, 2, 1),
+    32: (6, 16, 4, 1, 2, 1),
     64: (8, 16, 4, 1, 4, 1),
     128: (8, 16, 4, 1, 4, 2),
 }

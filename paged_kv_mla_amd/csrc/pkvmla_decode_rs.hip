@@ -48,21 +48,22 @@ namespace pkvmla {
 
 namespace {
 
-constexpr int kRsWaves = 8;    // compute waves (QK and PV)
+// A workgroup holds HB head blocks of 16 heads (HB = 1, 2 or 4): HB QK waves,
+// kRsPvWaves PV waves, kRsCopyWaves copy waves.
+constexpr int kRsPvWaves = 4;
 constexpr int kRsCopyWaves = 2;
-constexpr int kRsThreads = (kRsWaves + kRsCopyWaves) * 64;
-constexpr int kRsHeads = 64;   // heads per workgroup
-constexpr int kRsHB = 4;       // head blocks of 16
+constexpr int kRsMaxHB = 4;
+__host__ __device__ constexpr int rs_threads(int hb) { return (hb + kRsPvWaves + kRsCopyWaves) * 64; }
 constexpr int kRsRing = 4;     // LDS stages: PV tile, QK tile, two tiles in flight
 constexpr int kRsAhead = 2;    // k-steps between a K fragment's LDS read and its MFMA
 constexpr int kRsVAhead = 2;   // dim blocks between a V fragment's LDS read and its MFMAs
-                               // (two: the register budget at ten waves)
+                               // (two: the register budget at ten waves, HB = 4)
 constexpr int kRsDBW = 8;      // output-dim blocks of 16 per PV wave (128 dims)
 static_assert(kCopyWaves == 2 * kRsCopyWaves, "each copy wave issues two copy slots' shares");
 
 // LDS layout
-constexpr int kXpOff = kRsRing * kStageBytes;      // P^T exchange: [parity][hb] 1 KB blocks
-constexpr int kXaOff = kXpOff + 2 * kRsHB * 1024;  // rescale factors: [parity][li][hb] floats
+constexpr int kXpOff = kRsRing * kStageBytes;         // P^T exchange: [parity][hb] 1 KB blocks
+constexpr int kXaOff = kXpOff + 2 * kRsMaxHB * 1024;  // rescale factors: [parity][li][hb] floats
 constexpr int kXlOff = kXaOff + 2 * 64 * 4;        // unit row sums:   [parity][li][hb] floats
 constexpr int kRsLds = kXlOff + 2 * 64 * 4;
 static_assert(kRsLds <= 160 * 1024, "LDS budget");
@@ -93,8 +94,8 @@ __device__ __forceinline__ void cursor_next(UnitCursor& c, idx_ptr units, int u_
 
 }  // namespace
 
-template <bool BIG>
-__global__ void __launch_bounds__(kRsThreads, 1)
+template <bool BIG, int HB>
+__global__ void __launch_bounds__(rs_threads(HB), 1)
 mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
                      const uint16_t* __restrict__ ckv_cache, const uint16_t* __restrict__ kpe_cache,
                      uint16_t* __restrict__ out, float* __restrict__ lse_out,
@@ -111,8 +112,11 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
   const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
 
+  constexpr int HEADS = 16 * HB;  // heads per workgroup
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = wave & 3;  // QK: head block; PV: dim quarter
+  // QK waves 0..HB-1 (r: head block), PV waves HB..HB+3 (r: dim quarter),
+  // then the copy waves
+  const int r = wave < HB ? wave : wave - HB;
   // Block -> (head group, lane): the head groups of one lane are 8 blocks
   // apart, which the dispatcher places on the same XCD.
   const int hg = (int)(blockIdx.x >> 3) % n_hg;
@@ -131,12 +135,12 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
     G += (rec[3] - rec[2] + kTile - 1) / kTile;
   }
 
-  if (wave < 4) {
+  if (wave < HB) {
     // ======================= QK and softmax role =======================
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4;
     const int li = lane & 15;
-    const int head = hg * kRsHeads + r * 16 + li;
+    const int head = hg * HEADS + r * 16 + li;
     int offA[2], offK[2];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
@@ -242,7 +246,7 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
         // the lane's share of the row sum as a tree (depth 3, not 8)
         const float ps = ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
         l_run = l_run * alpha + ps;
-        *(LDS_AS bf16x8_t*)(smem + kXpOff + (par * kRsHB + r) * 1024 + lane * 16) = pT;
+        *(LDS_AS bf16x8_t*)(smem + kXpOff + (par * kRsMaxHB + r) * 1024 + lane * 16) = pT;
         if (g == 0) *(LDS_AS float*)(smem + kXaOff + (par * 64 + li * 4 + r) * 4) = alpha;
         if (cq.tile == cq.ntiles - 1) {
           // unit done: row sums for the PV waves, lse for the output
@@ -260,7 +264,7 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
       }
       lds_barrier();
     }
-  } else if (wave < 8) {
+  } else if (wave < HB + kRsPvWaves) {
     // ======================= PV and epilogue role =======================
     const int lane0 = threadIdx.x & 63;
     const int g0 = lane0 >> 4;
@@ -281,11 +285,11 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
     // rescale factors are not all 1 multiplies O by them, one dim block at a
     // time just before its MFMAs; the factors are exactly 0 on a unit's first
     // tile (the running max starts at -inf), which clears the previous unit.
-    f32x4_t o[kRsDBW][kRsHB];
+    f32x4_t o[kRsDBW][HB];
 #pragma unroll
     for (int db = 0; db < kRsDBW; ++db)
 #pragma unroll
-      for (int hb = 0; hb < kRsHB; ++hb) o[db][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int hb = 0; hb < HB; ++hb) o[db][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     // ---- iteration 0: the QK waves take tile 0 ----
     lds_barrier();
@@ -295,12 +299,14 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
       const int stage = t % kRsRing;
       const int par = t & 1;
       const int lane = lane_id_fresh();
-      bf16x8_t pB[kRsHB];
+      bf16x8_t pB[HB];
 #pragma unroll
-      for (int hb = 0; hb < kRsHB; ++hb)
-        pB[hb] = *(const LDS_AS bf16x8_t*)(smem + kXpOff + (par * kRsHB + hb) * 1024 + lane * 16);
+      for (int hb = 0; hb < HB; ++hb)
+        pB[hb] = *(const LDS_AS bf16x8_t*)(smem + kXpOff + (par * kRsMaxHB + hb) * 1024 + lane * 16);
       const f32x4_t a4 = *(const LDS_AS f32x4_t*)(smem + kXaOff + (par * 64 + (lane & 15) * 4) * 4);
-      const bool need = a4[0] != 1.0f || a4[1] != 1.0f || a4[2] != 1.0f || a4[3] != 1.0f;
+      bool need = false;
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) need |= a4[hb] != 1.0f;
       const bool rescale = __builtin_amdgcn_ballot_w64(need) != 0;
       __builtin_amdgcn_sched_barrier(0);
       int oV0 = offV[0], oV1 = offV[1];
@@ -329,10 +335,10 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
                                                      2, 3, 4, 5, 6, 7);
           if (rescale) {
 #pragma unroll
-            for (int hb = 0; hb < kRsHB; ++hb) o[db][hb] *= a4[hb];
+            for (int hb = 0; hb < HB; ++hb) o[db][hb] *= a4[hb];
           }
 #pragma unroll
-          for (int hb = 0; hb < kRsHB; ++hb) {
+          for (int hb = 0; hb < HB; ++hb) {
             o[db][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pB[hb], o[db][hb], 0, 0, 0);
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -343,18 +349,18 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
         const int le = lane_id_fresh();
         const int ge = le >> 4, lie = le & 15;
         const f32x4_t l4 = *(const LDS_AS f32x4_t*)(smem + kXlOff + (par * 64 + lie * 4) * 4);
-        float linv[kRsHB];
+        float linv[HB];
 #pragma unroll
-        for (int hb = 0; hb < kRsHB; ++hb) linv[hb] = __builtin_amdgcn_rcpf(l4[hb]);
+        for (int hb = 0; hb < HB; ++hb) linv[hb] = __builtin_amdgcn_rcpf(l4[hb]);
         // lane (g, li) holds dims r*128 + db*16 + g*4 .. +3 of head hb*16 + li
         const uint32_t col = (uint32_t)(lie * kCkvDim + r * (kRsDBW * 16) + ge * 4);
         // a whole request's rows go to out, a split unit's to its partial slot
         // (both bf16)
         char* obase = reinterpret_cast<char*>(
-            cp.slot < 0 ? out + ((size_t)cp.b * H + hg * kRsHeads) * kCkvDim
-                        : part_o + ((size_t)cp.slot * H + hg * kRsHeads) * kCkvDim);
+            cp.slot < 0 ? out + ((size_t)cp.b * H + hg * HEADS) * kCkvDim
+                        : part_o + ((size_t)cp.slot * H + hg * HEADS) * kCkvDim);
 #pragma unroll
-        for (int hb = 0; hb < kRsHB; ++hb) {
+        for (int hb = 0; hb < HB; ++hb) {
           const uint32_t row = col + (uint32_t)hb * 16 * kCkvDim;
 #pragma unroll
           for (int db = 0; db < kRsDBW; ++db) {
@@ -372,7 +378,7 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
     // ======================= copy role =======================
     // copy wave cw issues copy slots 2cw and 2cw+1 of every tile (18 copies;
     // at most two tiles, 36 operations, in flight)
-    const int cw = wave - kRsWaves;
+    const int cw = wave - (HB + kRsPvWaves);
     CopyLanes CLw[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) CLw[h] = copy_lanes(2 * cw + h);
@@ -406,7 +412,7 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
 #pragma unroll
           for (int k = 0; k < kCopiesPerWave; ++k) tile_copy_part_full(c, w, k, CLw[h]);
         } else {
-          tile_copy_wave<BIG>(c, ckv, kpe, w, CLw[h]);
+          tile_copy_slot<BIG>(c, ckv, kpe, w, CLw[h]);
         }
       }
       book_tile();
@@ -425,17 +431,31 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
   }
 }
 
+int decode_rs_head_blocks(int waves, int heads_per_wave, int num_heads, int head_groups) {
+  if (heads_per_wave != 16 || head_groups < 1) return 0;
+  const int hb = waves - kRsPvWaves;
+  if ((hb != 1 && hb != 2 && hb != 4) || num_heads != 16 * hb * head_groups) return 0;
+  return hb;
+}
+
 bool launch_decode_rs(const DecodeParams& p, hipStream_t stream, hipError_t* err) {
-  if (p.waves != kRsWaves || p.heads_per_wave != 16 || p.num_heads != kRsHeads * p.head_groups)
-    return false;
+  const int hb = decode_rs_head_blocks(p.waves, p.heads_per_wave, p.num_heads, p.head_groups);
+  if (!hb) return false;
   const bool big = p.log2_ps >= 5;
-  const dim3 grid(decode_grid(p.n_lanes, p.head_groups)), block(kRsThreads);
+  const dim3 grid(decode_grid(p.n_lanes, p.head_groups)), block(rs_threads(hb));
 #define PKVMLA_RS_ARGS                                                                   \
   p.q_nope, p.q_pe, p.ckv, p.kpe, p.out, p.lse, p.part_o, p.part_lse, p.wg_indptr, p.units, \
       p.seq_indptr, p.seq_indices, p.num_heads, p.head_groups, p.n_lanes, p.log2_ps,      \
       p.sm_scale, p.score_log2, p.rescale_thr
-  if (big) mla_decode_rs_kernel<true><<<grid, block, 0, stream>>>(PKVMLA_RS_ARGS);
-  else mla_decode_rs_kernel<false><<<grid, block, 0, stream>>>(PKVMLA_RS_ARGS);
+#define PKVMLA_RS_LAUNCH(HBV)                                                                  \
+  if (big) mla_decode_rs_kernel<true, HBV><<<grid, block, 0, stream>>>(PKVMLA_RS_ARGS);        \
+  else mla_decode_rs_kernel<false, HBV><<<grid, block, 0, stream>>>(PKVMLA_RS_ARGS);
+  switch (hb) {
+    case 1: PKVMLA_RS_LAUNCH(1) break;
+    case 2: PKVMLA_RS_LAUNCH(2) break;
+    default: PKVMLA_RS_LAUNCH(4) break;
+  }
+#undef PKVMLA_RS_LAUNCH
 #undef PKVMLA_RS_ARGS
   *err = hipGetLastError();
   return true;

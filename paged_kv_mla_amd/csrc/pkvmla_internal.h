@@ -71,9 +71,13 @@ struct GatherParams {
 
 int decode_grid(int n_lanes, int head_groups);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
-// Role-split kernel (64 heads per workgroup, one or two head groups); false
-// when the configuration is not its own, else *err holds the launch status.
+// Role-split kernel (16, 32 or 64 heads per workgroup, one or more head
+// groups); false when the configuration is not its own, else *err holds the
+// launch status.
 bool launch_decode_rs(const DecodeParams& p, hipStream_t stream, hipError_t* err);
+// Head blocks of 16 per workgroup of the role-split kernel for a configuration
+// (waves = head blocks + 4 PV waves), or 0 when it is not that kernel's.
+int decode_rs_head_blocks(int waves, int heads_per_wave, int num_heads, int head_groups);
 hipError_t launch_merge(const MergeParams& p, int n_merges, hipStream_t stream);
 hipError_t launch_gather(const GatherParams& p, int n_units, hipStream_t stream);
 

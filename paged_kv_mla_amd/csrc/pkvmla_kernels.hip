@@ -584,8 +584,8 @@ mla_gather_kernel(const uint16_t* __restrict__ ckv, const uint16_t* __restrict__
 // ---------------------------------------------------------------------------
 bool kernel_config_for(int num_heads, KernelConfig* cfg) {
   switch (num_heads) {
-    case 16: *cfg = KernelConfig{1, 16, 2, 2, 1, 1}; break;
-    case 32: *cfg = KernelConfig{2, 16, 2, 2, 1, 1}; break;
+    case 16: *cfg = KernelConfig{5, 16, 4, 1, 2, 1}; break;
+    case 32: *cfg = KernelConfig{6, 16, 4, 1, 2, 1}; break;
     case 64: *cfg = KernelConfig{8, 16, 4, 1, 4, 1}; break;
     case 128: *cfg = KernelConfig{8, 16, 4, 1, 4, 2}; break;
     default: return false;
@@ -596,13 +596,13 @@ bool kernel_config_for(int num_heads, KernelConfig* cfg) {
     KernelConfig c{};
     if (sscanf(e, "%d,%d,%d,%d,%d,%d", &c.waves, &c.heads_per_wave, &c.stages, &c.wg_per_cu,
                &c.fixed_cost, &c.head_groups) == 6 &&
-        c.head_groups >= 1 &&
-        (c.waves == 8 ? 4 : c.waves) * c.heads_per_wave * c.head_groups == num_heads &&
-        c.wg_per_cu >= 1 && c.fixed_cost >= 0) {
-      const bool exists = (c.waves == 1 && c.heads_per_wave == 16 && c.stages == 2) ||
-                          (c.waves == 2 && c.heads_per_wave == 16 && c.stages == 2) ||
-                          (c.waves == 8 && c.heads_per_wave == 16 && c.stages == 4);
-      if (exists) *cfg = c;
+        c.head_groups >= 1 && c.wg_per_cu >= 1 && c.fixed_cost >= 0) {
+      const bool rs = c.stages == 4 &&
+                      decode_rs_head_blocks(c.waves, c.heads_per_wave, num_heads, c.head_groups);
+      const bool generic = c.heads_per_wave == 16 && c.stages == 2 &&
+                           (c.waves == 1 || c.waves == 2) &&
+                           c.waves * c.heads_per_wave * c.head_groups == num_heads;
+      if (rs || generic) *cfg = c;
     }
   }
   return true;

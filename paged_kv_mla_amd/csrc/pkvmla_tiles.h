@@ -77,6 +77,7 @@ struct TileCopy {
   const char* g0;
   const char* g1;
   const char* kb;
+  uint32_t row0;          // BIG: cache row of the tile's first token
   bool full;
 };
 
@@ -90,6 +91,7 @@ __device__ __forceinline__ TileCopy tile_copy(const TileStream& s, const char* _
   c.pages = s.pages;
   c.st = stage_base;
   const int64_t rowbase = ((int64_t)(uint32_t)s.pid << log2_ps) + (c.tok0 & ((1 << log2_ps) - 1));
+  c.row0 = (uint32_t)rowbase;
   c.crow = ckv + rowbase * (kCkvDim * 2);
   c.krow = kpe + rowbase * (kKpeDim * 2);
   c.full = c.last == kTile - 1;
@@ -139,56 +141,56 @@ __device__ __forceinline__ CopyLanes copy_lanes(int wave) {
   return L;
 }
 
-// Copy part k (0..kCopiesPerWave-1) of this wave's share: parts 0..7 are the
-// ckv rows (4*wave + k%4 + 16*(k/4)), part 8 the kpe block.  Parts must be
-// issued in order with no other M0 user in between: M0 is loaded at parts 0,
-// 4 and 8 only.
+// One copy slot's share of a tile that is not one ready block of rows (page
+// size below 32, or a unit's partial last tile): the cache rows of the slot's
+// 8 ckv tokens (4*wave + j and 4*wave + 16 + j) and 8 kpe tokens (8*wave + k)
+// are resolved first, clamped to the last valid token, in one batch of scalar
+// page-id loads with one wait; then its 9 copies go out (M0 loaded three
+// times, as in the whole-tile path).
 template <bool BIG>
-__device__ __forceinline__ void tile_copy_part(const TileCopy& c, const char* __restrict__ ckv,
-                                               const char* __restrict__ kpe, int wave, const int k,
+__device__ __forceinline__ void tile_copy_slot(const TileCopy& c, const char* __restrict__ ckv,
+                                               const char* __restrict__ kpe, int wave,
                                                const CopyLanes& L) {
-  const int ps_mask = (1 << c.log2_ps) - 1;
-  auto row_of = [&](int t) -> int64_t {  // global row of tile token t (clamped), !BIG
-    const int tok = c.tok0 + min(t, c.last);
-    return ((int64_t)(uint32_t)c.pages[tok >> c.log2_ps] << c.log2_ps) + (tok & ps_mask);
-  };
-  if (k < 8) {
-    const int j = k & 3;
-    const int t0 = 4 * wave + 16 * (k >> 2);  // first row of the group of four
-    const int t = t0 + j;
-    if (j == 0) set_m0(c.st + (uint32_t)t0 * 1024u);
-    // global source = base + voff + j KB: the base of row t is its own row
-    // address minus j KB
-    const char* rowp = BIG ? c.crow + (int64_t)min(t, c.last) * (kCkvDim * 2)
-                           : ckv + row_of(t) * (kCkvDim * 2);
-    const char* base = rowp - j * 1024;
-    // (!BIG: the persistent offsets do not pay for their registers there)
-    const CopyLanes& LL = BIG ? L : copy_lanes(wave);
-    switch (j) {
-      case 0: dma16_m0<0>(base, LL.v0); break;
-      case 1: dma16_m0<1024>(base, LL.v1); break;
-      case 2: dma16_m0<2048>(base, LL.v2); break;
-      default: dma16_m0<3072>(base, LL.v3); break;
-    }
-  } else {
-    set_m0(c.st + kTile * 1024 + (uint32_t)wave * 1024u);
-    if constexpr (BIG) {
-      // Units start on tile boundaries and a page holds whole tiles, so all
-      // 32 kpe rows of the tile lie inside the tile's page; rows past kv_end
-      // are copied unclamped (their scores are replaced by -inf with a select
-      // before the softmax, so whatever they hold never reaches the output).
-      dma16_m0<0>(c.krow + wave * 8 * (kKpeDim * 2), L.vk);
-    } else {
-      // lane group j = lane / 8 copies token 8*wave + j (clamped)
-      const int lane = lane_id_fresh();
-      const int tl = 8 * wave + (lane >> 3);
-      const uint32_t kchunk = (uint32_t)(((lane & 7) ^ swz8(tl)) << 4);
-      int64_t row = row_of(8 * wave);
+  // slot tokens: ckv rows 4*wave + j, 4*wave + 16 + j; kpe tokens 8*wave + k
+  auto tok_of = [&](int i) { return i < 4 ? 4 * wave + i : i < 8 ? 4 * wave + 12 + i : 8 * wave + i - 8; };
+  uint32_t rows[16];
+  if constexpr (BIG) {
 #pragma unroll
-      for (int kk = 1; kk < 8; ++kk) row = ((lane >> 3) == kk) ? row_of(8 * wave + kk) : row;
-      dma16_m0v(kpe + row * (kKpeDim * 2) + kchunk);
-    }
+    for (int i = 0; i < 16; ++i) rows[i] = c.row0 + (uint32_t)min(tok_of(i), c.last);  // one page
+  } else {
+    // all 16 page-id loads go out before the first use (one wait, not 16)
+    const int ps_mask = (1 << c.log2_ps) - 1;
+    uint32_t pid[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pid[i] = (uint32_t)c.pages[(c.tok0 + min(tok_of(i), c.last)) >> c.log2_ps];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      rows[i] = (pid[i] << c.log2_ps) + (uint32_t)((c.tok0 + min(tok_of(i), c.last)) & ps_mask);
   }
+  const uint32_t* rc = rows;
+  const uint32_t* rk = rows + 8;
+  // ckv: the source of row t is its row address; the copy's instruction
+  // offset (j KB) moves source and LDS destination alike, so the base is
+  // the row address minus j KB
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    set_m0(c.st + (uint32_t)(4 * wave + 16 * g) * 1024u);
+    dma16_m0<0>(ckv + (size_t)rc[4 * g + 0] * (kCkvDim * 2), L.v0);
+    dma16_m0<1024>(ckv + (size_t)rc[4 * g + 1] * (kCkvDim * 2) - 1024, L.v1);
+    dma16_m0<2048>(ckv + (size_t)rc[4 * g + 2] * (kCkvDim * 2) - 2048, L.v2);
+    dma16_m0<3072>(ckv + (size_t)rc[4 * g + 3] * (kCkvDim * 2) - 3072, L.v3);
+  }
+  // kpe: lane group g8 = lane / 8 copies token 8*wave + g8 (chunk swizzle
+  // g8, since 8*wave is a multiple of 8)
+  set_m0(c.st + kTile * 1024 + (uint32_t)wave * 1024u);
+  const int lane = lane_id_fresh();
+  const int g8 = lane >> 3;
+  uint32_t row = rk[0];
+#pragma unroll
+  for (int k = 1; k < 8; ++k) row = g8 == k ? rk[k] : row;
+  const uint32_t kchunk = (uint32_t)(((lane & 7) ^ g8) << 4);
+  dma16_m0v(kpe + (size_t)row * (kKpeDim * 2) + kchunk);
 }
 
 // Part k of a whole tile's copies (BIG and full): ready bases, no clamping.
@@ -208,14 +210,6 @@ __device__ __forceinline__ void tile_copy_part_full(const TileCopy& c, int wave,
     set_m0(c.st + kTile * 1024 + (uint32_t)wave * 1024u);
     dma16_m0<0>(c.kb, L.vk);
   }
-}
-
-template <bool BIG>
-__device__ __forceinline__ void tile_copy_wave(const TileCopy& c, const char* __restrict__ ckv,
-                                               const char* __restrict__ kpe, int wave,
-                                               const CopyLanes& L) {
-#pragma unroll
-  for (int k = 0; k < kCopiesPerWave; ++k) tile_copy_part<BIG>(c, ckv, kpe, wave, k, L);
 }
 
 }  // namespace pkvmla
