@@ -352,8 +352,13 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
         float linv[HB];
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) linv[hb] = __builtin_amdgcn_rcpf(l4[hb]);
-        // lane (g, li) holds dims r*128 + db*16 + g*4 .. +3 of head hb*16 + li
-        const uint32_t col = (uint32_t)(lie * kCkvDim + r * (kRsDBW * 16) + ge * 4);
+        // Lane (g, li) holds dims r*128 + db*16 + g*4 .. +3 of head hb*16 + li.
+        // For a pair of dim blocks (2dp, 2dp+1) one row swap (rows 0<->1 and
+        // 2<->3, v_permlane16_swap) gives every lane 8 consecutive dims: even
+        // rows dims (g/2)*8 .. +7 of block 2dp, odd rows those of block 2dp+1.
+        // So each lane stores 16 bytes, half the store instructions of
+        // 8-byte stores.
+        const uint32_t col = (uint32_t)(lie * kCkvDim + r * (kRsDBW * 16) + (ge >> 1) * 8);
         // a whole request's rows go to out, a split unit's to its partial slot
         // (both bf16)
         char* obase = reinterpret_cast<char*>(
@@ -363,10 +368,16 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
         for (int hb = 0; hb < HB; ++hb) {
           const uint32_t row = col + (uint32_t)hb * 16 * kCkvDim;
 #pragma unroll
-          for (int db = 0; db < kRsDBW; ++db) {
-            const f32x4_t v = o[db][hb] * linv[hb];
-            *reinterpret_cast<bf16x4_t*>(obase + row * 2 + db * 32) =
-                __builtin_convertvector(v, bf16x4_t);  // RNE
+          for (int dp = 0; dp < kRsDBW / 2; ++dp) {
+            const uint2 x = __builtin_bit_cast(
+                uint2, __builtin_convertvector(o[2 * dp][hb] * linv[hb], bf16x4_t));  // RNE
+            const uint2 y = __builtin_bit_cast(
+                uint2, __builtin_convertvector(o[2 * dp + 1][hb] * linv[hb], bf16x4_t));
+            const auto s0 = __builtin_amdgcn_permlane16_swap(x.x, y.x, false, false);
+            const auto s1 = __builtin_amdgcn_permlane16_swap(x.y, y.y, false, false);
+            const uint32_t blk = (uint32_t)(2 * dp + (ge & 1));
+            *reinterpret_cast<uint4*>(obase + (row + blk * 16) * 2) =
+                make_uint4((uint32_t)s0[0], (uint32_t)s1[0], (uint32_t)s0[1], (uint32_t)s1[1]);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
