@@ -48,6 +48,9 @@ GATHER_CASES = {
     "ps1_scatter": lambda: small(61, [1, 2, 33, 95, 64], H=16, ps=1),
     "ps64_extra_pages": lambda: small(62, [1, 64, 65, 300], H=128, ps=64, extra=1),
     "ps256": lambda: small(63, [5, 511, 700], H=32, ps=256),
+    # one page per tile: the smallest page size of the whole-tile copy path
+    "ps32_tile_pages": lambda: small(64, [1, 31, 32, 33, 95, 97], H=128, ps=32),
+    "ps8": lambda: small(65, [3, 8, 9, 40, 161], H=64, ps=8),
 }
 
 
@@ -135,6 +138,9 @@ SMALL_CASES = {
     "h16_ps256": lambda: small(77, [3, 256, 257, 900], H=16, ps=256),
     "h64_ps2_explicit_scale": lambda: small(78, [1, 9, 77, 130], H=64, ps=2, sm_scale=0.11),
     "h128_extra_pages": lambda: small(79, [1, 40, 64, 129], H=128, ps=64, extra=2),
+    "h128_ps32": lambda: small(66, [1, 31, 32, 33, 500, 1025], H=128, ps=32),
+    "h32_ps8": lambda: small(67, [2, 8, 33, 250], H=32, ps=8),
+    "h16_ps32": lambda: small(68, [32, 64, 65, 700], H=16, ps=32),
 }
 
 
