@@ -20,26 +20,44 @@ namespace pkvmla {
 // lane (one 16-byte load per partial row).
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) mla_merge_kernel(MergeParams p) {
+  constexpr int kChunk = 4;  // partial states whose loads are in flight together
   const int32_t* mr = p.merges + (size_t)blockIdx.x * kMergeInts;
   const int b = mr[0], s0 = mr[1], n = mr[2];
   const int H = p.num_heads;
   const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
   const int d0 = (threadIdx.x & 63) * 8;
+  // Chunks past the last state re-read the last one (valid memory) and carry
+  // weight 0 (a select, so they add exactly nothing).
   float M = -INFINITY;
-  for (int i = 0; i < n; ++i) M = fmaxf(M, p.part_lse[(size_t)(s0 + i) * H + h]);
+  for (int i0 = 0; i0 < n; i0 += kChunk) {
+    float lv[kChunk];
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) lv[j] = p.part_lse[(size_t)(s0 + min(i0 + j, n - 1)) * H + h];
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) M = fmaxf(M, lv[j]);
+  }
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
-  for (int i = 0; i < n; ++i) {
-    const size_t base = (size_t)(s0 + i) * H + h;
-    const float w = __builtin_amdgcn_exp2f((p.part_lse[base] - M) * 1.4426950408889634f);
-    const uint4 x = *reinterpret_cast<const uint4*>(p.part_o + base * kCkvDim + d0);
-    const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+  for (int i0 = 0; i0 < n; i0 += kChunk) {
+    uint4 x[kChunk];
+    float lv[kChunk];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      acc[2 * k] = fmaf(w, __builtin_bit_cast(float, xw[k] << 16), acc[2 * k]);
-      acc[2 * k + 1] = fmaf(w, __builtin_bit_cast(float, xw[k] & 0xFFFF0000u), acc[2 * k + 1]);
+    for (int j = 0; j < kChunk; ++j) {
+      const size_t base = (size_t)(s0 + min(i0 + j, n - 1)) * H + h;
+      lv[j] = p.part_lse[base];
+      x[j] = *reinterpret_cast<const uint4*>(p.part_o + base * kCkvDim + d0);
     }
-    wsum += w;
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      const float w = i0 + j < n ? __builtin_amdgcn_exp2f((lv[j] - M) * 1.4426950408889634f) : 0.f;
+      const uint32_t xw[4] = {x[j].x, x[j].y, x[j].z, x[j].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc[2 * k] = fmaf(w, __builtin_bit_cast(float, xw[k] << 16), acc[2 * k]);
+        acc[2 * k + 1] = fmaf(w, __builtin_bit_cast(float, xw[k] & 0xFFFF0000u), acc[2 * k + 1]);
+      }
+      wsum += w;
+    }
   }
   const float inv = 1.0f / wsum;
   uint32_t packed[4];
