@@ -152,8 +152,9 @@ int finish_plan(pkvmla_plan_s* P, const std::vector<pkvmla::WorkItem>& items,
   size_t off_wg = 0, off_units = off_wg + pad(n_wg), off_merges = off_units + pad(n_units);
   size_t off_sip = off_merges + pad(n_merges), off_sl = off_sip + pad(seq_indptr.size());
   size_t off_si = off_sl + pad(seq_lens.size());
-  // the kernels read page ids of whole tiles unclamped: kIndexPad trailing
-  // entries (page 0, a valid id) keep every such read inside the table
+  // every page-id read of the kernels lies inside its sequence's list (tile
+  // starts below kv_end, tokens clamped to the last valid one); the kIndexPad
+  // trailing entries (page 0, a valid id) are a margin beyond that
   P->table_ints = off_si + pad(seq_indices.size() + pkvmla::kIndexPad);
   PKVMLA_HIP(hipMalloc(&P->d_tables, P->table_ints * sizeof(int32_t)));
   P->d_wg_indptr = P->d_tables + off_wg;

@@ -13,7 +13,7 @@ constexpr int kTile = 32;           // KV tokens per tile
 constexpr int kUnitInts = 8;        // b, seq, kv_begin, kv_end, slot, row, 0, 0
 constexpr int kMergeInts = 4;       // b, first_slot, count, 0
 constexpr int kStageBytes = kTile * kCkvDim * 2 + kTile * kKpeDim * 2;  // 36864
-constexpr int kIndexPad = 64;       // valid trailing page ids after the device index table
+constexpr int kIndexPad = 64;       // margin of valid page ids after the device index table
 
 // Kernel shape for one head count.
 struct KernelConfig {
