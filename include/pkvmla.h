@@ -150,6 +150,9 @@ int pkvmla_schedule_host(const int32_t* items, int32_t n_items, int32_t batch,
  *            is_cascade, num_groups, head_groups, launched workgroups, 0...
  *   then wg_indptr[grid+1], units[n_units*8], merges[n_merges*4],
  *   seq_indptr[num_seqs+1], seq_lens[num_seqs], seq_indices[n_indices].
+ *   The unit records are those of pkvmla_schedule_host with their last two
+ *   fields filled: page_base = seq_indptr[sequence] and first_page =
+ *   seq_indices[page_base + kv_begin / page_size].
  * *used = number of int32 written (or needed, when cap is too small:
  * PKVMLA_EINVAL).  Synchronises the device. */
 int pkvmla_plan_export(pkvmla_plan plan, int32_t* buf, int64_t cap, int64_t* used);

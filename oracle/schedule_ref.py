@@ -33,7 +33,8 @@ from __future__ import annotations
 import numpy as np
 
 PLAN_TILE = 32          # KV tokens per tile
-UNIT_INTS = 8           # int32 per unit record: b, seq, kv_begin, kv_end, slot, row, 0, 0
+UNIT_INTS = 8           # int32 per unit record: b, seq, kv_begin, kv_end, slot, row,
+                        # page_base, first_page (the last two: unit_page_fields)
 MERGE_INTS = 4          # int32 per merge record: b, first_slot, count, 0
 
 # Per head count: (compute waves per workgroup: QK and PV, heads per QK wave,
@@ -134,3 +135,19 @@ def schedule_ref(items, batch: int, num_wg: int, tile: int = PLAN_TILE, fixed: i
         wg_indptr[r[0] + 1] += 1
     wg_indptr = np.cumsum(wg_indptr).astype(np.int32)
     return wg_indptr, units, merges
+
+
+def unit_page_fields(units, seq_indptr, seq_indices, page_size: int):
+    """The two page fields of each unit record, from the sequences' page tables:
+    page_base = seq_indptr[seq] (where the sequence's page list starts in
+    seq_indices) and first_page = the page holding token kv_begin, i.e.
+    seq_indices[page_base + kv_begin // page_size].  Returns a filled copy."""
+    out = np.array(units, dtype=np.int32, copy=True)
+    seq_indptr = np.asarray(seq_indptr, dtype=np.int64)
+    seq_indices = np.asarray(seq_indices, dtype=np.int64)
+    for i in range(out.shape[0]):
+        seq, k0 = int(out[i, 1]), int(out[i, 2])
+        base = int(seq_indptr[seq])
+        out[i, 6] = base
+        out[i, 7] = seq_indices[base + k0 // page_size]
+    return out

@@ -143,6 +143,15 @@ int finish_plan(pkvmla_plan_s* P, const std::vector<pkvmla::WorkItem>& items,
   if (P->sched.total_rows > INT32_MAX) return fail(PKVMLA_EUNSUPPORTED, "too many tokens");
   P->num_seqs = (int32_t)seq_lens.size();
   P->n_indices = (int64_t)seq_indices.size();
+  // page fields of the unit records: where the sequence's page list starts and
+  // the page of the unit's first token, so a workgroup's first copies need one
+  // dependent load (the record) instead of three
+  for (size_t i = 0; i < P->sched.units.size(); i += pkvmla::kUnitRecordInts) {
+    int32_t* u = &P->sched.units[i];
+    const int32_t base = seq_indptr[u[1]];
+    u[6] = base;
+    u[7] = seq_indices[(size_t)base + (size_t)(u[2] / P->page_size)];
+  }
 
   const size_t n_wg = P->sched.wg_indptr.size();
   const size_t n_units = P->sched.units.size();
@@ -381,7 +390,6 @@ int pkvmla_run(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* 
   d.part_lse = part_o ? reinterpret_cast<float*>(part_o + part_o_elems) : nullptr;
   d.wg_indptr = P->d_wg_indptr;
   d.units = P->d_units;
-  d.seq_indptr = P->d_seq_indptr;
   d.seq_indices = P->d_seq_indices;
   d.num_heads = P->num_heads;
   d.head_groups = P->cfg.head_groups;
@@ -513,7 +521,6 @@ int pkvmla_gather(pkvmla_plan P, const void* ckv_cache, const void* kpe_cache, v
   g.kpe = static_cast<const uint16_t*>(kpe_cache);
   g.rows = static_cast<uint16_t*>(rows);
   g.units = P->d_units;
-  g.seq_indptr = P->d_seq_indptr;
   g.seq_indices = P->d_seq_indices;
   g.log2_ps = P->log2_ps;
   const int n_units = (int)(P->sched.units.size() / pkvmla::kUnitRecordInts);

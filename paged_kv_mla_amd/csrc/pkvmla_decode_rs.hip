@@ -28,7 +28,10 @@
 // softmax of tile i on the QK waves and PV of tile i-1 (with the epilogue when
 // tile i-1 ends a unit) on the PV waves, while the copy waves issue tile i+2
 // right after the barrier and then wait, with an exact s_waitcnt vmcnt, until
-// their share of tile i+1 has landed; then one barrier.  KV tiles of 32
+// their share of tile i+1 has landed; then one barrier.  The PV waves write no
+// LDS, so they enter that barrier without waiting for their own reads: the
+// first V fragments of their next tile (landed, and resident two more
+// iterations) are read before it and arrive while the waves wait there.  KV tiles of 32
 // tokens live in a 4-stage LDS ring (two tiles in flight), P^T and the
 // per-head factors in two-deep exchange buffers.  A copy wave keeps at most
 // two tiles' shares (36 operations) in flight: the vmcnt counter holds at
@@ -101,12 +104,10 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
                      uint16_t* __restrict__ out, float* __restrict__ lse_out,
                      uint16_t* __restrict__ part_o, float* __restrict__ part_lse,
                      const int32_t* __restrict__ wg_indptr_g, const int32_t* __restrict__ units_g,
-                     const int32_t* __restrict__ seq_indptr_g,
                      const int32_t* __restrict__ seq_indices_g, int H, int n_hg, int n_lanes,
                      int log2_ps, float sm_scale, float C, float thr) {
   const idx_ptr wg_indptr = (idx_ptr)wg_indptr_g;
   const idx_ptr units = (idx_ptr)units_g;
-  const idx_ptr seq_indptr = (idx_ptr)seq_indptr_g;
   const idx_ptr seq_indices = (idx_ptr)seq_indices_g;
   __shared__ __attribute__((aligned(1024))) char smem_raw[kRsLds];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
@@ -282,9 +283,10 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
     cp.u = u_begin;
     cursor_load(cp, units);
     // O (128 VGPRs, MFMAs in VGPR form) starts at zero once.  A tile whose
-    // rescale factors are not all 1 multiplies O by them, one dim block at a
-    // time just before its MFMAs; the factors are exactly 0 on a unit's first
-    // tile (the running max starts at -inf), which clears the previous unit.
+    // rescale factors are not all 1 multiplies O by them before its MFMAs
+    // (rare: the running max moves only in steps of more than the threshold);
+    // the factors are exactly 0 on a unit's first tile (the running max
+    // starts at -inf), which clears the previous unit.
     f32x4_t o[kRsDBW][HB];
 #pragma unroll
     for (int db = 0; db < kRsDBW; ++db)
@@ -293,6 +295,17 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
 
     // ---- iteration 0: the QK waves take tile 0 ----
     lds_barrier();
+    constexpr int VP = kRsVAhead;
+    int oV0 = offV[0], oV1 = offV[1];
+    asm volatile("" : "+v"(oV0), "+v"(oV1));
+    auto ldV = [&](int so, int db, int tb) -> bf16x4_t {
+      const int dbg = r * kRsDBW + db;
+      return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (LDS_AS bf16x4_t*)(smem + ((so + (tb ? oV1 : oV0)) ^ (dbg << 5))));
+    };
+    // the first dim block's V fragments of the next tile, read before the
+    // barrier that starts its iteration (one block: the register budget)
+    bf16x4_t vn0 = ldV(0, 0, 0), vn1 = ldV(0, 0, 1);
 
     // ---- iteration t+1: PV of tile t, copies of tile t+3 ----
     for (int t = 0; t < G; ++t) {
@@ -309,40 +322,43 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
       for (int hb = 0; hb < HB; ++hb) need |= a4[hb] != 1.0f;
       const bool rescale = __builtin_amdgcn_ballot_w64(need) != 0;
       __builtin_amdgcn_sched_barrier(0);
-      int oV0 = offV[0], oV1 = offV[1];
-      asm volatile("" : "+v"(oV0), "+v"(oV1));
       const int so = stage * kStageBytes;
-      auto ldV = [&](int db, int tb) -> bf16x4_t {
-        const int dbg = r * kRsDBW + db;
-        return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (LDS_AS bf16x4_t*)(smem + ((so + (tb ? oV1 : oV0)) ^ (dbg << 5))));
-      };
-      constexpr int VP = kRsVAhead;
+      if (rescale) {
+#pragma unroll
+        for (int db = 0; db < kRsDBW; ++db)
+#pragma unroll
+          for (int hb = 0; hb < HB; ++hb) o[db][hb] *= a4[hb];
+      }
       {
         bf16x4_t V[VP + 1][2];
+        V[0][0] = vn0;
+        V[0][1] = vn1;
 #pragma unroll
-        for (int pp = 0; pp < VP; ++pp) {
-          V[pp][0] = ldV(pp, 0);
-          V[pp][1] = ldV(pp, 1);
+        for (int pp = 1; pp < VP; ++pp) {
+          V[pp][0] = ldV(so, pp, 0);
+          V[pp][1] = ldV(so, pp, 1);
         }
 #pragma unroll
         for (int db = 0; db < kRsDBW; ++db) {
           if (db + VP < kRsDBW) {
-            V[(db + VP) % (VP + 1)][0] = ldV(db + VP, 0);
-            V[(db + VP) % (VP + 1)][1] = ldV(db + VP, 1);
+            V[(db + VP) % (VP + 1)][0] = ldV(so, db + VP, 0);
+            V[(db + VP) % (VP + 1)][1] = ldV(so, db + VP, 1);
           }
           const bf16x8_t a = __builtin_shufflevector(V[db % (VP + 1)][0], V[db % (VP + 1)][1], 0, 1,
                                                      2, 3, 4, 5, 6, 7);
-          if (rescale) {
-#pragma unroll
-            for (int hb = 0; hb < HB; ++hb) o[db][hb] *= a4[hb];
-          }
 #pragma unroll
           for (int hb = 0; hb < HB; ++hb) {
             o[db][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pB[hb], o[db][hb], 0, 0, 0);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
+      }
+      // the next tile's first V fragments (that tile landed before this
+      // iteration began; the QK waves read it now)
+      if (t + 1 < G) {
+        const int so1 = ((t + 1) % kRsRing) * kStageBytes;
+        vn0 = ldV(so1, 0, 0);
+        vn1 = ldV(so1, 0, 1);
       }
       if (cp.tile == cp.ntiles - 1) {
         // ---- epilogue: this wave's 128 dims of the unit's 64 heads ----
@@ -383,7 +399,11 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
         }
       }
       cursor_next(cp, units, u_end);
-      lds_barrier();
+      // this role writes no LDS, and its reads still in flight are of a tile
+      // that stays resident for two more iterations: no wait before the barrier
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
     }
   } else {
     // ======================= copy role =======================
@@ -397,7 +417,7 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
     ts.u = u_begin;
     ts.u_end = u_end;
     ts.g = 0;
-    stream_load_unit(ts, units, seq_indptr, seq_indices, log2_ps);
+    stream_load_unit(ts, units, seq_indices);
     int vmc = 0;
     int rv0 = 0, rv1 = 0, rv2 = 0, rv3 = 0;
     auto book_tile = [&]() {
@@ -407,7 +427,7 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
       rv1 = st == 1 ? vmc : rv1;
       rv2 = st == 2 ? vmc : rv2;
       rv3 = st == 3 ? vmc : rv3;
-      stream_advance(ts, units, seq_indptr, seq_indices, log2_ps);
+      stream_advance(ts, units, seq_indices, log2_ps);
     };
     auto vmc_of = [&](int gidx) {
       const int st = gidx % kRsRing;
@@ -456,7 +476,7 @@ bool launch_decode_rs(const DecodeParams& p, hipStream_t stream, hipError_t* err
   const dim3 grid(decode_grid(p.n_lanes, p.head_groups)), block(rs_threads(hb));
 #define PKVMLA_RS_ARGS                                                                   \
   p.q_nope, p.q_pe, p.ckv, p.kpe, p.out, p.lse, p.part_o, p.part_lse, p.wg_indptr, p.units, \
-      p.seq_indptr, p.seq_indices, p.num_heads, p.head_groups, p.n_lanes, p.log2_ps,      \
+      p.seq_indices, p.num_heads, p.head_groups, p.n_lanes, p.log2_ps,      \
       p.sm_scale, p.score_log2, p.rescale_thr
 #define PKVMLA_RS_LAUNCH(HBV)                                                                  \
   if (big) mla_decode_rs_kernel<true, HBV><<<grid, block, 0, stream>>>(PKVMLA_RS_ARGS);        \

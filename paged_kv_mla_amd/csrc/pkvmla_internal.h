@@ -10,7 +10,9 @@ namespace pkvmla {
 constexpr int kCkvDim = 512;        // head_dim_ckv = kv_lora_rank
 constexpr int kKpeDim = 64;         // head_dim_kpe = qk_rope_head_dim
 constexpr int kTile = 32;           // KV tokens per tile
-constexpr int kUnitInts = 8;        // b, seq, kv_begin, kv_end, slot, row, 0, 0
+constexpr int kUnitInts = 8;        // b, seq, kv_begin, kv_end, slot, row, page_base, first_page
+                                    // (page_base: start of seq's page list in seq_indices;
+                                    //  first_page: the page of token kv_begin)
 constexpr int kMergeInts = 4;       // b, first_slot, count, 0
 constexpr int kStageBytes = kTile * kCkvDim * 2 + kTile * kKpeDim * 2;  // 36864
 constexpr int kIndexPad = 64;       // margin of valid page ids after the device index table
@@ -38,7 +40,6 @@ struct DecodeParams {
   float* part_lse;           // [slots][H]
   const int32_t* wg_indptr;  // [grid + 1]
   const int32_t* units;      // [n_units][8]
-  const int32_t* seq_indptr; // [num_seqs + 1]
   const int32_t* seq_indices;
   int32_t num_heads;
   int32_t head_groups;
@@ -64,7 +65,6 @@ struct GatherParams {
   const uint16_t* kpe;
   uint16_t* rows;            // [n_rows][576]
   const int32_t* units;
-  const int32_t* seq_indptr;
   const int32_t* seq_indices;
   int32_t log2_ps;
 };

@@ -82,13 +82,11 @@ template <bool BIG>
 __global__ void __launch_bounds__(kCopyWaves * 64)
 mla_gather_kernel(const uint16_t* __restrict__ ckv_cache, const uint16_t* __restrict__ kpe_cache,
                   uint16_t* __restrict__ rows, const int32_t* __restrict__ units_g,
-                  const int32_t* __restrict__ seq_indptr_g,
                   const int32_t* __restrict__ seq_indices_g, int log2_ps) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[kStageBytes];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
   const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
   const idx_ptr units = (idx_ptr)units_g;
-  const idx_ptr seq_indptr = (idx_ptr)seq_indptr_g;
   const idx_ptr seq_indices = (idx_ptr)seq_indices_g;
   const char* ckv = reinterpret_cast<const char*>(ckv_cache);
   const char* kpe = reinterpret_cast<const char*>(kpe_cache);
@@ -100,7 +98,7 @@ mla_gather_kernel(const uint16_t* __restrict__ ckv_cache, const uint16_t* __rest
   ts.u = blockIdx.x;
   ts.u_end = blockIdx.x + 1;
   ts.g = 0;
-  stream_load_unit(ts, units, seq_indptr, seq_indices, log2_ps);
+  stream_load_unit(ts, units, seq_indices);
   for (int tok0 = kv0; tok0 < kv1; tok0 += kTile) {
     __syncthreads();  // the previous tile has been read out
     const TileCopy c = tile_copy(ts, ckv, kpe, log2_ps, smem_base, wave);
@@ -110,7 +108,7 @@ mla_gather_kernel(const uint16_t* __restrict__ ckv_cache, const uint16_t* __rest
     } else {
       tile_copy_slot<BIG>(c, ckv, kpe, wave, CL);
     }
-    stream_advance(ts, units, seq_indptr, seq_indices, log2_ps);
+    stream_advance(ts, units, seq_indices, log2_ps);
     wait_vmcnt<0>();
     __syncthreads();
     const int n = min(kTile, kv1 - tok0);
@@ -176,10 +174,10 @@ hipError_t launch_gather(const GatherParams& p, int n_units, hipStream_t stream)
   if (n_units <= 0) return hipSuccess;
   if (p.log2_ps >= 5)
     mla_gather_kernel<true><<<n_units, kCopyWaves * 64, 0, stream>>>(
-        p.ckv, p.kpe, p.rows, p.units, p.seq_indptr, p.seq_indices, p.log2_ps);
+        p.ckv, p.kpe, p.rows, p.units, p.seq_indices, p.log2_ps);
   else
     mla_gather_kernel<false><<<n_units, kCopyWaves * 64, 0, stream>>>(
-        p.ckv, p.kpe, p.rows, p.units, p.seq_indptr, p.seq_indices, p.log2_ps);
+        p.ckv, p.kpe, p.rows, p.units, p.seq_indices, p.log2_ps);
   return hipGetLastError();
 }
 

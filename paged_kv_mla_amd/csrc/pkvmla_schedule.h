@@ -8,7 +8,9 @@
 
 namespace pkvmla {
 
-constexpr int kUnitRecordInts = 8;   // req, seq, kv_begin, kv_end, slot, row, 0, 0
+// req, seq, kv_begin, kv_end, slot, row, page_base, first_page; the scheduler
+// leaves the last two 0, the plan fills them from the page tables
+constexpr int kUnitRecordInts = 8;
 constexpr int kMergeRecordInts = 4;  // req, first_slot, count, 0
 
 struct WorkItem {

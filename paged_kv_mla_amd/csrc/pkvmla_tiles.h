@@ -40,25 +40,25 @@ struct TileStream {
   int pid;                // page id of the next tile's first token (prefetched)
 };
 
-__device__ __forceinline__ void stream_load_unit(TileStream& s, idx_ptr units, idx_ptr seq_indptr,
-                                                 idx_ptr seq_indices, int log2_ps) {
+// The unit record carries its page list's start and its first page id, so a
+// unit's first copies wait for one load (the record), not three.
+__device__ __forceinline__ void stream_load_unit(TileStream& s, idx_ptr units, idx_ptr seq_indices) {
   idx_ptr rec = units + (size_t)s.u * kUnitInts;
-  const int seq = rec[1];
   s.kv0 = rec[2];
   s.kv1 = rec[3];
   s.ntiles = (s.kv1 - s.kv0 + kTile - 1) / kTile;
   s.tile = 0;
-  s.pages = seq_indices + seq_indptr[seq];
-  s.pid = s.pages[s.kv0 >> log2_ps];
+  s.pages = seq_indices + rec[6];
+  s.pid = rec[7];
 }
 
-__device__ __forceinline__ void stream_advance(TileStream& s, idx_ptr units, idx_ptr seq_indptr,
-                                               idx_ptr seq_indices, int log2_ps) {
+__device__ __forceinline__ void stream_advance(TileStream& s, idx_ptr units, idx_ptr seq_indices,
+                                               int log2_ps) {
   ++s.g;
   if (++s.tile < s.ntiles) {
     s.pid = s.pages[(s.kv0 + s.tile * kTile) >> log2_ps];
   } else if (++s.u < s.u_end) {
-    stream_load_unit(s, units, seq_indptr, seq_indices, log2_ps);
+    stream_load_unit(s, units, seq_indices);
   }
 }
 

@@ -14,7 +14,8 @@ import pytest
 import torch
 
 import oracle
-from oracle.schedule_ref import schedule_ref, flat_items, cascade_items, kernel_config
+from oracle.schedule_ref import (schedule_ref, flat_items, cascade_items, kernel_config,
+                                 unit_page_fields)
 from mla_workloads import (make_flat, make_cascade, make_config, stress_variant,
                            poison_unreferenced, permute_pages, STRESS_KINDS)
 from gpu_helpers import Dev, run_gpu, oracle_flat, oracle_cascade, compare, bits_of, dev_bf16
@@ -99,6 +100,7 @@ def test_plan_export_bit_exact(name):
         assert ex.head_groups == kc["head_groups"]
     lanes = max(1, ex.num_cu * int(hdr[10]) // ex.head_groups)
     wg, units, merges = schedule_ref(flat_items(lens), len(lens), lanes, kc["tile"], int(hdr[11]))
+    units = unit_page_fields(units, indptr, indices, ps)
     np.testing.assert_array_equal(ex.wg_indptr, wg)
     np.testing.assert_array_equal(ex.units, units)
     np.testing.assert_array_equal(ex.merges, merges)
@@ -117,13 +119,16 @@ def test_plan_export_cascade():
     items = cascade_items(cas.group_req_indptr, cas.prefix_lens, cas.kv_lens)
     lanes = max(1, ex.num_cu * int(hdr[10]) // ex.head_groups)
     wg, units, merges = schedule_ref(items, cas.batch, lanes, kc["tile"], int(hdr[11]))
+    G = cas.num_groups
+    seq_indptr = np.concatenate([cas.prefix_indptr, cas.prefix_indptr[G] + cas.kv_indptr[1:]])
+    seq_indices = np.concatenate([cas.prefix_indices[:cas.prefix_indptr[G]], cas.kv_indices])
+    units = unit_page_fields(units, seq_indptr, seq_indices, cas.page_size)
     np.testing.assert_array_equal(ex.units, units)
     np.testing.assert_array_equal(ex.merges, merges)
     np.testing.assert_array_equal(ex.wg_indptr, wg)
-    G = cas.num_groups
     np.testing.assert_array_equal(ex.seq_lens, np.concatenate([cas.prefix_lens, cas.kv_lens]))
-    np.testing.assert_array_equal(
-        ex.seq_indptr, np.concatenate([cas.prefix_indptr, cas.prefix_indptr[G] + cas.kv_indptr[1:]]))
+    np.testing.assert_array_equal(ex.seq_indptr, seq_indptr)
+    np.testing.assert_array_equal(ex.seq_indices, seq_indices)
 
 
 # ------------------------------------------------------------ decode parity
