@@ -24,18 +24,20 @@
 // most 168 registers (the PV waves' 128 accumulators fit with a V prefetch
 // depth of two).
 //
-// Pipeline.  After a first barrier (tile 0 landed), iteration i runs QK and
-// softmax of tile i on the QK waves and PV of tile i-1 (with the epilogue when
-// tile i-1 ends a unit) on the PV waves, while the copy waves issue tile i+2
-// right after the barrier and then wait, with an exact s_waitcnt vmcnt, until
-// their share of tile i+1 has landed; then one barrier.  The PV waves write no
-// LDS, so they enter that barrier without waiting for their own reads: the
-// first V fragments of their next tile (landed, and resident two more
-// iterations) are read before it and arrive while the waves wait there.  KV tiles of 32
-// tokens live in a 4-stage LDS ring (two tiles in flight), P^T and the
-// per-head factors in two-deep exchange buffers.  A copy wave keeps at most
-// two tiles' shares (36 operations) in flight: the vmcnt counter holds at
-// most 63, and a wave with more outstanding cannot wait for them exactly.
+// Pipeline.  A first barrier follows the copy waves' issue of tile 0 (the QK
+// waves load their queries only then, so those loads do not delay the tile),
+// a second one tile 0's landing.  Then iteration i runs QK and softmax of
+// tile i on the QK waves and PV of tile i-1 (with the epilogue when tile i-1
+// ends a unit) on the PV waves, while the copy waves issue tile i+2 right
+// after the barrier and then wait, with an exact s_waitcnt vmcnt, until their
+// share of tile i+1 has landed; then one barrier.  The PV waves write no LDS,
+// so they enter that barrier without waiting for their own reads: the first V
+// fragments of their next tile (landed, and resident two more iterations) are
+// read before it and arrive while the waves wait there.  KV tiles of 32 tokens
+// live in a 4-stage LDS ring (two tiles in flight), P^T and the per-head
+// factors in two-deep exchange buffers.  A copy wave keeps at most two tiles'
+// shares (36 operations) in flight: the vmcnt counter holds at most 63, and a
+// wave with more outstanding cannot wait for them exactly.
 //
 // Masking.  Only the last tile of a unit can be partial.  Its ckv slots past
 // kv_end copy the last valid row (finite data), its kpe slots the page's own
@@ -163,6 +165,9 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
       for (int k2 = 0; k2 < 2; ++k2)
         q[16 + k2] = *reinterpret_cast<const bf16x8_t*>(qp + (k2 * 32 + g * 8) * 2);
     };
+    // the query loads go out after the copy waves have issued tile 0, so that
+    // tile's copies do not queue behind them in the memory pipeline
+    lds_barrier();
     load_q(cq.b);
     float m_run = -INFINITY, l_run = 0.f;
 
@@ -277,7 +282,8 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
       const int qq = li0 & 3;
       offV[tb] = lds_ckv_off(tV, qq >> 1) + (qq & 1) * 8;
     }
-    lds_barrier();
+    lds_barrier();  // tile 0's copies are out
+    lds_barrier();  // tile 0 has landed
 
     UnitCursor cp;
     cp.u = u_begin;
@@ -449,6 +455,7 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
       book_tile();
     };
     if (ts.u < ts.u_end) issue_tile();
+    lds_barrier();  // the QK waves load their queries from here on
     if (ts.u < ts.u_end) issue_tile();
     wait_vm_le(vmc - vmc_of(0));
     lds_barrier();
