@@ -78,6 +78,40 @@ int pkvmla_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
                        int32_t page_size, float sm_scale, void* stream,
                        pkvmla_plan* out);
 
+/* Build a flat decode plan whose device tables, split workspace and launch
+ * shapes are sized once for later page-table updates (pkvmla_plan_update),
+ * so that a HIP graph captured around pkvmla_run stays valid while the
+ * batch's pages and lengths change between replays.  The vLLM pull-request
+ * page "[WIP][Kernel] Flashinfer MLA support" reports graph capture of the
+ * MLA decode path as the recurring failure; this is the capture-safe form.
+ *   Arguments as pkvmla_plan_create, plus
+ *   index_capacity: the most page ids (kv_indptr[batch]) any later update may
+ *   bring, >= the first table's count; 0 builds an ordinary plan (exact launch
+ *   shapes, as pkvmla_plan_create).
+ * With index_capacity > 0 every pkvmla_run launches the decode kernel over
+ * all schedule lanes (lanes without work return at once) and the merge
+ * kernel over one record slot per request (unused slots are skipped), so the
+ * sequence of kernels and their arguments never changes.  Units, partial
+ * slots and lanes need no capacity: a lane boundary splits at most one
+ * request, so units <= batch + lanes always.  Output: *out. */
+int pkvmla_plan_create_with_capacity(const int32_t* kv_indptr, const int32_t* kv_indices,
+                                     const int32_t* kv_lens, int32_t batch, int32_t num_pages,
+                                     int32_t num_heads, int32_t ckv_dim, int32_t kpe_dim,
+                                     int32_t page_size, float sm_scale, int64_t index_capacity,
+                                     void* stream, pkvmla_plan* out);
+
+/* Replace a flat plan's page table and lengths (same batch; host arrays as in
+ * pkvmla_plan_create, read during the call only) and recompute its schedule,
+ * in place: no allocation, no pointer or launch-shape change.  The new tables
+ * are copied on `stream` and the call waits for that copy, so every run queued
+ * earlier on `stream` has finished with the old tables and every later run
+ * (eager, or a graph replayed on `stream`) sees the new ones; work on other
+ * streams must be ordered by the caller.  PKVMLA_EINVAL when the arrays are
+ * malformed or kv_indptr[batch] exceeds the plan's page-id capacity (the
+ * plan is then unchanged); PKVMLA_EUNSUPPORTED for a cascade plan. */
+int pkvmla_plan_update(pkvmla_plan plan, const int32_t* kv_indptr, const int32_t* kv_indices,
+                       const int32_t* kv_lens, void* stream);
+
 /* Build a two-level (cascade) plan.  Requests are partitioned into
  * num_groups contiguous groups by group_req_indptr (host int32[G+1], from 0
  * to batch).  Group g's shared prefix is prefix_lens[g] tokens in pages
@@ -108,7 +142,8 @@ int pkvmla_run(pkvmla_plan plan, const void* q_nope, const void* q_pe,
  * records a HIP event pair on its stream around the fused decode kernel only
  * (events are created here, so run still allocates nothing); the counter is
  * reset.  pkvmla_plan_timing synchronises the device and returns the summed
- * duration of the last min(n, 256) timed runs' decode kernels and that count. */
+ * duration of the last min(n, 256) timed runs' decode kernels and that count.
+ * Timing must be off while a run is being captured into a HIP graph. */
 int pkvmla_plan_set_timing(pkvmla_plan plan, int32_t enable);
 int pkvmla_plan_timing(pkvmla_plan plan, double* total_ms, int64_t* n_runs);
 
@@ -147,7 +182,8 @@ int pkvmla_schedule_host(const int32_t* items, int32_t n_items, int32_t batch,
  *            kpe_dim, tile, waves, heads_per_wave, stages, wg_per_cu,
  *            fixed_cost, grid, n_units, n_merges, n_slots
  *   [16..31] header 2: num_seqs, n_indices, num_cu, sm_scale (float bits),
- *            is_cascade, num_groups, head_groups, launched workgroups, 0...
+ *            is_cascade, num_groups, head_groups, launched workgroups,
+ *            fixed launch shapes (0/1), page-id capacity, 0...
  *   then wg_indptr[grid+1], units[n_units*8], merges[n_merges*4],
  *   seq_indptr[num_seqs+1], seq_lens[num_seqs], seq_indices[n_indices].
  *   The unit records are those of pkvmla_schedule_host with their last two

@@ -43,6 +43,11 @@ _lib.pkvmla_plan_create_cascade.argtypes = [_i32p, ctypes.c_int32, _i32p, _i32p,
                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, ctypes.c_float, _vp,
                                             ctypes.POINTER(_vp)]
+_lib.pkvmla_plan_create_with_capacity.argtypes = [_i32p, _i32p, _i32p, ctypes.c_int32,
+                                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                                                  ctypes.c_int64, _vp, ctypes.POINTER(_vp)]
+_lib.pkvmla_plan_update.argtypes = [_vp, _i32p, _i32p, _i32p, _vp]
 _lib.pkvmla_run.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.pkvmla_plan_destroy.argtypes = [_vp]
 _lib.pkvmla_plan_destroy.restype = None
@@ -58,7 +63,8 @@ _lib.pkvmla_plan_set_timing.argtypes = [_vp, ctypes.c_int32]
 _lib.pkvmla_plan_timing.argtypes = [_vp, ctypes.POINTER(ctypes.c_double), _i64p]
 
 EXPORTED_SYMBOLS = (
-    "pkvmla_plan_create", "pkvmla_plan_create_cascade", "pkvmla_run", "pkvmla_plan_destroy",
+    "pkvmla_plan_create", "pkvmla_plan_create_with_capacity", "pkvmla_plan_update",
+    "pkvmla_plan_create_cascade", "pkvmla_run", "pkvmla_plan_destroy",
     "pkvmla_last_error", "pkvmla_kernel_config", "pkvmla_schedule_host", "pkvmla_plan_export",
     "pkvmla_gather", "pkvmla_gather_rows", "pkvmla_plan_set_timing", "pkvmla_plan_timing",
 )
@@ -187,6 +193,19 @@ class Plan:
                                _stream_handle(stream)))
         return out, lse
 
+    def update(self, kv_indptr, kv_indices, kv_lens, stream=None) -> None:
+        """Replace the page table and lengths of a flat plan in place (same
+        batch): no pointer or launch shape changes, so a HIP graph captured
+        around :meth:`run` replays the new tables.  Waits for earlier work on
+        `stream` (default: current stream)."""
+        ip, ix, ln = _i32(kv_indptr), _i32(kv_indices), _i32(kv_lens)
+        if len(ln) != self.batch or len(ip) != self.batch + 1:
+            raise ValueError(f"update needs batch {self.batch} (kv_lens) and batch + 1 (kv_indptr)")
+        if ix.size == 0:
+            ix = np.zeros(1, np.int32)
+        _check(_lib.pkvmla_plan_update(self._h, _ptr(ip), _ptr(ix), _ptr(ln),
+                                       _stream_handle(stream)))
+
     def run_ptrs(self, q_nope: int, q_pe: int, ckv: int, kpe: int, out: int, lse: int,
                  stream: int) -> None:
         """Raw-pointer form of :meth:`run` (no checks beyond the library's)."""
@@ -237,18 +256,20 @@ class Plan:
 
 def plan(kv_indptr, kv_indices, kv_lens, num_heads: int, page_size: int, num_pages: int,
          ckv_dim: int = 512, kpe_dim: int = 64, sm_scale: Optional[float] = None,
-         stream=None) -> Plan:
+         stream=None, index_capacity: int = 0) -> Plan:
     """Flat decode plan from host page-table arrays (int32): kv_indptr [B+1],
     kv_indices [kv_indptr[B]], kv_lens [B].  sm_scale None selects
-    1/sqrt(ckv_dim + kpe_dim)."""
+    1/sqrt(ckv_dim + kpe_dim).  index_capacity > 0 sizes the plan for later
+    :meth:`Plan.update` calls with up to that many page ids and fixes its
+    launch shapes (for HIP-graph capture of :meth:`Plan.run`)."""
     ip, ix, ln = _i32(kv_indptr), _i32(kv_indices), _i32(kv_lens)
     if ix.size == 0:
         ix = np.zeros(1, np.int32)
     h = ctypes.c_void_p()
-    _check(_lib.pkvmla_plan_create(_ptr(ip), _ptr(ix), _ptr(ln), int(len(ln)), int(num_pages),
-                                   int(num_heads), int(ckv_dim), int(kpe_dim), int(page_size),
-                                   float(sm_scale or 0.0), _stream_handle(stream) if stream else None,
-                                   ctypes.byref(h)))
+    _check(_lib.pkvmla_plan_create_with_capacity(
+        _ptr(ip), _ptr(ix), _ptr(ln), int(len(ln)), int(num_pages), int(num_heads), int(ckv_dim),
+        int(kpe_dim), int(page_size), float(sm_scale or 0.0), int(index_capacity),
+        _stream_handle(stream) if stream else None, ctypes.byref(h)))
     return Plan(h.value, int(len(ln)), int(num_heads))
 
 

@@ -56,6 +56,19 @@ struct pkvmla_plan_s {
   pkvmla::Schedule sched;
   int32_t num_seqs = 0;
   int64_t n_indices = 0;
+  // Capacities fixed at creation: the device tables, the split workspace and
+  // every launch configuration are sized by them, so a later page-table update
+  // changes no pointer and no grid (a captured HIP graph stays valid).
+  int32_t cap_lanes = 0;     // schedule lanes (workgroups per head group)
+  int32_t cap_units = 0;     // unit records: work items + lanes bound the splits
+  int32_t cap_merges = 0;    // merge records: one per request at most
+  int64_t cap_indices = 0;   // page ids
+  int64_t index_capacity_request = 0;  // caller's page-id capacity (0: the first table's)
+  // Launch shapes: exact (lanes in use; the merge kernel only when a request
+  // is split) or, for a plan built with a capacity, fixed at the capacities so
+  // that the kernels a captured graph replays stay right after updates.
+  int fixed_launch = 0;
+  size_t off_wg = 0, off_units = 0, off_merges = 0, off_sip = 0, off_sl = 0, off_si = 0;
   // device tables (one allocation) and split workspace
   int32_t* d_tables = nullptr;
   int32_t* d_wg_indptr = nullptr;
@@ -129,64 +142,89 @@ int check_pages(const char* what, const int32_t* indptr, const int32_t* indices,
   return PKVMLA_OK;
 }
 
-// Build the schedule, allocate and upload the device tables.
+// Build the schedule for `items` into *sched, with the page fields of its unit
+// records (the sequence's page-list start and the page of the unit's first
+// token, so a workgroup's first copies need one dependent load, the record,
+// instead of three).
+int build_plan_schedule(const pkvmla_plan_s* P, const std::vector<pkvmla::WorkItem>& items,
+                        const std::vector<int32_t>& seq_indptr,
+                        const std::vector<int32_t>& seq_indices, pkvmla::Schedule* sched) {
+  if (!pkvmla::build_schedule(items, P->batch, P->cap_lanes, pkvmla::kTile, P->cfg.fixed_cost,
+                              sched))
+    return fail(PKVMLA_EINVAL, "schedule construction failed");
+  if (sched->total_rows > INT32_MAX) return fail(PKVMLA_EUNSUPPORTED, "too many tokens");
+  for (size_t i = 0; i < sched->units.size(); i += pkvmla::kUnitRecordInts) {
+    int32_t* u = &sched->units[i];
+    const int32_t base = seq_indptr[u[1]];
+    u[6] = base;
+    u[7] = seq_indices[(size_t)base + (size_t)(u[2] / P->page_size)];
+  }
+  return PKVMLA_OK;
+}
+
+// Write the schedule and the sequences' page tables into the capacity-sized
+// device tables (one copy on `stream`, then a wait for it: the host staging
+// buffer is local).  Entries past the live ones: wg_indptr repeats its last
+// value (empty lanes), merge records have count 0 (skipped).
+int upload_tables(pkvmla_plan_s* P, const std::vector<int32_t>& seq_indptr,
+                  const std::vector<int32_t>& seq_lens, const std::vector<int32_t>& seq_indices,
+                  hipStream_t stream) {
+  std::vector<int32_t> host(P->table_ints, 0);
+  const std::vector<int32_t>& wg = P->sched.wg_indptr;
+  for (int32_t l = 0; l <= P->cap_lanes; ++l)
+    host[P->off_wg + l] = l < (int32_t)wg.size() ? wg[l] : wg.back();
+  std::copy(P->sched.units.begin(), P->sched.units.end(), host.begin() + P->off_units);
+  std::copy(P->sched.merges.begin(), P->sched.merges.end(), host.begin() + P->off_merges);
+  std::copy(seq_indptr.begin(), seq_indptr.end(), host.begin() + P->off_sip);
+  std::copy(seq_lens.begin(), seq_lens.end(), host.begin() + P->off_sl);
+  std::copy(seq_indices.begin(), seq_indices.end(), host.begin() + P->off_si);
+  PKVMLA_HIP(hipMemcpyAsync(P->d_tables, host.data(), P->table_ints * sizeof(int32_t),
+                            hipMemcpyHostToDevice, stream));
+  PKVMLA_HIP(hipStreamSynchronize(stream));
+  P->num_seqs = (int32_t)seq_lens.size();
+  P->n_indices = (int64_t)seq_indices.size();
+  return PKVMLA_OK;
+}
+
+// Fix the capacities, build the schedule, allocate and upload the device tables.
 int finish_plan(pkvmla_plan_s* P, const std::vector<pkvmla::WorkItem>& items,
                 const std::vector<int32_t>& seq_indptr, const std::vector<int32_t>& seq_lens,
                 const std::vector<int32_t>& seq_indices, hipStream_t stream) {
   PKVMLA_HIP(hipGetDevice(&P->device));
   PKVMLA_HIP(hipDeviceGetAttribute(&P->num_cu, hipDeviceAttributeMultiprocessorCount, P->device));
   // the schedule's lanes: each lane's token ranges are replicated over the head groups
-  const int32_t num_wg = std::max(1, P->num_cu * P->cfg.wg_per_cu / P->cfg.head_groups);
-  if (!pkvmla::build_schedule(items, P->batch, num_wg, pkvmla::kTile, P->cfg.fixed_cost,
-                              &P->sched))
-    return fail(PKVMLA_EINVAL, "schedule construction failed");
-  if (P->sched.total_rows > INT32_MAX) return fail(PKVMLA_EUNSUPPORTED, "too many tokens");
-  P->num_seqs = (int32_t)seq_lens.size();
-  P->n_indices = (int64_t)seq_indices.size();
-  // page fields of the unit records: where the sequence's page list starts and
-  // the page of the unit's first token, so a workgroup's first copies need one
-  // dependent load (the record) instead of three
-  for (size_t i = 0; i < P->sched.units.size(); i += pkvmla::kUnitRecordInts) {
-    int32_t* u = &P->sched.units[i];
-    const int32_t base = seq_indptr[u[1]];
-    u[6] = base;
-    u[7] = seq_indices[(size_t)base + (size_t)(u[2] / P->page_size)];
-  }
+  P->cap_lanes = std::max(1, P->num_cu * P->cfg.wg_per_cu / P->cfg.head_groups);
+  // a lane boundary splits at most one work item, so units <= items + lanes - 1
+  P->cap_units = (int32_t)items.size() + P->cap_lanes;
+  P->cap_merges = P->batch;
+  P->cap_indices = std::max<int64_t>((int64_t)seq_indices.size(), P->index_capacity_request);
+  int rc = build_plan_schedule(P, items, seq_indptr, seq_indices, &P->sched);
+  if (rc) return rc;
 
-  const size_t n_wg = P->sched.wg_indptr.size();
-  const size_t n_units = P->sched.units.size();
-  const size_t n_merges = P->sched.merges.size();
   // 64-int aligned sub-buffers inside one allocation
   auto pad = [](size_t n) { return (n + 63) & ~size_t(63); };
-  size_t off_wg = 0, off_units = off_wg + pad(n_wg), off_merges = off_units + pad(n_units);
-  size_t off_sip = off_merges + pad(n_merges), off_sl = off_sip + pad(seq_indptr.size());
-  size_t off_si = off_sl + pad(seq_lens.size());
+  P->off_wg = 0;
+  P->off_units = P->off_wg + pad((size_t)P->cap_lanes + 1);
+  P->off_merges = P->off_units + pad((size_t)P->cap_units * pkvmla::kUnitRecordInts);
+  P->off_sip = P->off_merges + pad((size_t)P->cap_merges * pkvmla::kMergeRecordInts);
+  P->off_sl = P->off_sip + pad(seq_indptr.size());
+  P->off_si = P->off_sl + pad(seq_lens.size());
   // every page-id read of the kernels lies inside its sequence's list (tile
   // starts below kv_end, tokens clamped to the last valid one); the kIndexPad
   // trailing entries (page 0, a valid id) are a margin beyond that
-  P->table_ints = off_si + pad(seq_indices.size() + pkvmla::kIndexPad);
+  P->table_ints = P->off_si + pad((size_t)P->cap_indices + pkvmla::kIndexPad);
   PKVMLA_HIP(hipMalloc(&P->d_tables, P->table_ints * sizeof(int32_t)));
-  P->d_wg_indptr = P->d_tables + off_wg;
-  P->d_units = P->d_tables + off_units;
-  P->d_merges = P->d_tables + off_merges;
-  P->d_seq_indptr = P->d_tables + off_sip;
-  P->d_seq_lens = P->d_tables + off_sl;
-  P->d_seq_indices = P->d_tables + off_si;
-  std::vector<int32_t> host(P->table_ints, 0);
-  std::copy(P->sched.wg_indptr.begin(), P->sched.wg_indptr.end(), host.begin() + off_wg);
-  std::copy(P->sched.units.begin(), P->sched.units.end(), host.begin() + off_units);
-  std::copy(P->sched.merges.begin(), P->sched.merges.end(), host.begin() + off_merges);
-  std::copy(seq_indptr.begin(), seq_indptr.end(), host.begin() + off_sip);
-  std::copy(seq_lens.begin(), seq_lens.end(), host.begin() + off_sl);
-  std::copy(seq_indices.begin(), seq_indices.end(), host.begin() + off_si);
-  PKVMLA_HIP(hipMemcpyAsync(P->d_tables, host.data(), P->table_ints * sizeof(int32_t),
-                            hipMemcpyHostToDevice, stream));
-  if (P->sched.n_slots > 0) {
-    const size_t rows = (size_t)P->sched.n_slots * P->num_heads;
-    PKVMLA_HIP(hipMalloc(&P->d_part, rows * (pkvmla::kCkvDim * sizeof(uint16_t) + sizeof(float))));
-  }
-  PKVMLA_HIP(hipStreamSynchronize(stream));
-  return PKVMLA_OK;
+  P->d_wg_indptr = P->d_tables + P->off_wg;
+  P->d_units = P->d_tables + P->off_units;
+  P->d_merges = P->d_tables + P->off_merges;
+  P->d_seq_indptr = P->d_tables + P->off_sip;
+  P->d_seq_lens = P->d_tables + P->off_sl;
+  P->d_seq_indices = P->d_tables + P->off_si;
+  // split workspace for the largest slot count any schedule can need
+  // (slots <= units)
+  const size_t rows = (size_t)P->cap_units * P->num_heads;
+  PKVMLA_HIP(hipMalloc(&P->d_part, rows * (pkvmla::kCkvDim * sizeof(uint16_t) + sizeof(float))));
+  return upload_tables(P, seq_indptr, seq_lens, seq_indices, stream);
 }
 
 void free_plan(pkvmla_plan_s* P) {
@@ -253,10 +291,11 @@ int pkvmla_schedule_host(const int32_t* items, int32_t n_items, int32_t batch, i
   return ok();
 }
 
-int pkvmla_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
-                       const int32_t* kv_lens, int32_t batch, int32_t num_pages,
-                       int32_t num_heads, int32_t ckv_dim, int32_t kpe_dim, int32_t page_size,
-                       float sm_scale, void* stream, pkvmla_plan* out) {
+int pkvmla_plan_create_with_capacity(const int32_t* kv_indptr, const int32_t* kv_indices,
+                                     const int32_t* kv_lens, int32_t batch, int32_t num_pages,
+                                     int32_t num_heads, int32_t ckv_dim, int32_t kpe_dim,
+                                     int32_t page_size, float sm_scale, int64_t index_capacity,
+                                     void* stream, pkvmla_plan* out) {
   if (!out) return fail(PKVMLA_EINVAL, "null plan output pointer");
   *out = nullptr;
   int32_t log2_ps;
@@ -266,6 +305,10 @@ int pkvmla_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
   if (rc) return rc;
   rc = check_pages("kv", kv_indptr, kv_indices, kv_lens, batch, num_pages, page_size, 1);
   if (rc) return rc;
+  if (index_capacity < 0) return fail(PKVMLA_EINVAL, "index_capacity must be >= 0");
+  if (index_capacity > 0 && index_capacity < kv_indptr[batch])
+    return fail(PKVMLA_EINVAL, "index_capacity %lld is below the table's %d page ids",
+                (long long)index_capacity, kv_indptr[batch]);
 
   pkvmla_plan_s* P = new pkvmla_plan_s();
   P->batch = batch;
@@ -276,6 +319,8 @@ int pkvmla_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
   P->kpe_dim = kpe_dim;
   P->num_pages = num_pages;
   P->sm_scale = scale;
+  P->index_capacity_request = index_capacity;
+  P->fixed_launch = index_capacity > 0 ? 1 : 0;
   pkvmla::kernel_config_for(num_heads, &P->cfg);
   std::vector<pkvmla::WorkItem> items((size_t)batch);
   for (int32_t b = 0; b < batch; ++b) items[b] = pkvmla::WorkItem{b, b, kv_lens[b]};
@@ -290,6 +335,47 @@ int pkvmla_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
     return rc;
   }
   *out = P;
+  return ok();
+}
+
+int pkvmla_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
+                       const int32_t* kv_lens, int32_t batch, int32_t num_pages,
+                       int32_t num_heads, int32_t ckv_dim, int32_t kpe_dim, int32_t page_size,
+                       float sm_scale, void* stream, pkvmla_plan* out) {
+  return pkvmla_plan_create_with_capacity(kv_indptr, kv_indices, kv_lens, batch, num_pages,
+                                          num_heads, ckv_dim, kpe_dim, page_size, sm_scale, 0,
+                                          stream, out);
+}
+
+int pkvmla_plan_update(pkvmla_plan P, const int32_t* kv_indptr, const int32_t* kv_indices,
+                       const int32_t* kv_lens, void* stream) {
+  if (!P) return fail(PKVMLA_EINVAL, "null plan");
+  if (P->is_cascade) return fail(PKVMLA_EUNSUPPORTED, "update of a cascade plan");
+  int rc = check_pages("kv", kv_indptr, kv_indices, kv_lens, P->batch, P->num_pages,
+                       P->page_size, 1);
+  if (rc) return rc;
+  if ((int64_t)kv_indptr[P->batch] > P->cap_indices)
+    return fail(PKVMLA_EINVAL, "%d page ids exceed the plan's capacity of %lld",
+                kv_indptr[P->batch], (long long)P->cap_indices);
+  int dev = -1;
+  PKVMLA_HIP(hipGetDevice(&dev));
+  if (dev != P->device)
+    return fail(PKVMLA_EINVAL, "plan was built on device %d, current device is %d", P->device,
+                dev);
+  std::vector<pkvmla::WorkItem> items((size_t)P->batch);
+  for (int32_t b = 0; b < P->batch; ++b) items[b] = pkvmla::WorkItem{b, b, kv_lens[b]};
+  std::vector<int32_t> sip(kv_indptr, kv_indptr + P->batch + 1);
+  std::vector<int32_t> sl(kv_lens, kv_lens + P->batch);
+  std::vector<int32_t> si(kv_indices, kv_indices + kv_indptr[P->batch]);
+  pkvmla::Schedule sched;
+  rc = build_plan_schedule(P, items, sip, si, &sched);
+  if (rc) return rc;
+  if ((int64_t)sched.units.size() > (int64_t)P->cap_units * pkvmla::kUnitRecordInts ||
+      sched.grid > P->cap_lanes || sched.n_slots > P->cap_units)
+    return fail(PKVMLA_EINVAL, "schedule exceeds the plan's capacities");
+  P->sched = std::move(sched);
+  rc = upload_tables(P, sip, sl, si, (hipStream_t)stream);
+  if (rc) return rc;
   return ok();
 }
 
@@ -377,7 +463,7 @@ int pkvmla_run(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* 
     return fail(PKVMLA_EINVAL, "plan was built on device %d, current device is %d", P->device,
                 dev);
   hipStream_t s = (hipStream_t)stream;
-  const size_t part_o_elems = (size_t)P->sched.n_slots * P->num_heads * pkvmla::kCkvDim;
+  const size_t part_o_elems = (size_t)P->cap_units * P->num_heads * pkvmla::kCkvDim;
   uint16_t* part_o = static_cast<uint16_t*>(P->d_part);
   pkvmla::DecodeParams d{};
   d.q_nope = static_cast<const uint16_t*>(q_nope);
@@ -393,7 +479,8 @@ int pkvmla_run(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* 
   d.seq_indices = P->d_seq_indices;
   d.num_heads = P->num_heads;
   d.head_groups = P->cfg.head_groups;
-  d.n_lanes = P->sched.grid;
+  // lanes past the schedule's have no units (their workgroups return at once)
+  d.n_lanes = P->fixed_launch ? P->cap_lanes : P->sched.grid;
   d.waves = P->cfg.waves;
   d.heads_per_wave = P->cfg.heads_per_wave;
   d.stages = P->cfg.stages;
@@ -408,7 +495,11 @@ int pkvmla_run(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* 
     PKVMLA_HIP(hipEventRecord(P->ev[2 * slot_ev + 1], s));
     ++P->timed_runs;
   }
-  const int n_merges = (int)(P->sched.merges.size() / pkvmla::kMergeRecordInts);
+  // fixed launches cover every merge record slot (records past the live ones
+  // have count 0 and are skipped by the kernel)
+  const int n_merges = P->fixed_launch
+                           ? P->cap_merges
+                           : (int)(P->sched.merges.size() / pkvmla::kMergeRecordInts);
   if (n_merges > 0) {
     pkvmla::MergeParams m{};
     m.part_o = d.part_o;
@@ -482,7 +573,10 @@ int pkvmla_plan_export(pkvmla_plan P, int32_t* buf, int64_t cap, int64_t* used) 
   buf[20] = P->is_cascade;
   buf[21] = P->num_groups;
   buf[22] = P->cfg.head_groups;
-  buf[23] = pkvmla::decode_grid(P->sched.grid, P->cfg.head_groups);
+  buf[23] = pkvmla::decode_grid(P->fixed_launch ? P->cap_lanes : P->sched.grid,
+                                P->cfg.head_groups);
+  buf[24] = P->fixed_launch;
+  buf[25] = (int32_t)std::min<int64_t>(P->cap_indices, INT32_MAX);
   int32_t* dst = buf + 32;
   auto pull = [&](const int32_t* src, int64_t n) -> hipError_t {
     hipError_t e = n ? hipMemcpy(dst, src, n * sizeof(int32_t), hipMemcpyDeviceToHost) : hipSuccess;

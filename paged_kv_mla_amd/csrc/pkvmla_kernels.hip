@@ -23,6 +23,7 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(MergeParams p) {
   constexpr int kChunk = 4;  // partial states whose loads are in flight together
   const int32_t* mr = p.merges + (size_t)blockIdx.x * kMergeInts;
   const int b = mr[0], s0 = mr[1], n = mr[2];
+  if (n <= 0) return;  // an unused record slot of a plan with fixed launches
   const int H = p.num_heads;
   const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
   const int d0 = (threadIdx.x & 63) * 8;

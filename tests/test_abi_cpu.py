@@ -108,6 +108,8 @@ def _flat_args(**kw):
     (dict(sm_scale=float("nan")), pk.EINVAL),
     (dict(sm_scale=float("inf")), pk.EINVAL),
     (dict(sm_scale=-0.5), pk.EINVAL),
+    (dict(index_capacity=-1), pk.EINVAL),                   # negative page-id capacity
+    (dict(index_capacity=2), pk.EINVAL),                    # below the table's 3 page ids
 ])
 def test_plan_create_rejects(kw, code):
     with pytest.raises(pk.PkvmlaError) as e:
@@ -143,3 +145,5 @@ def test_null_pointer_arguments_rejected():
     lib.pkvmla_plan_create.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int32] * 6 + \
         [ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
     assert lib.pkvmla_plan_create(None, None, None, 1, 1, 16, 512, 64, 16, 0.0, None, None) == pk.EINVAL
+    lib.pkvmla_plan_update.argtypes = [ctypes.c_void_p] * 5
+    assert lib.pkvmla_plan_update(None, None, None, None, None) == pk.EINVAL

@@ -1,0 +1,133 @@
+"""HIP-graph capture of the decode and in-place page-table updates.
+
+A plan built with a page-id capacity keeps its device tables, split workspace
+and launch shapes across `Plan.update`, so one HIP graph captured around
+`Plan.run` serves successive page tables.  The graph-capture failure of the
+MLA decode path is the recurring problem on the vLLM pull-request page
+"[WIP][Kernel] Flashinfer MLA support".
+
+Every replay is checked bit for bit against an eager run of the same plan
+state (and of a fresh ordinary plan for the same tables), with the program's
+own eager work and synchronisations between replays, and the updated tables'
+results against the fp64 oracle.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from mla_workloads import make_flat
+from gpu_helpers import Dev, oracle_flat, compare, dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+pk = pytest.importorskip("paged_kv_mla_amd")
+
+
+def note(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _cuda():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+    yield
+
+
+POOL = 160
+
+
+def tables(seed, lens, H, ps):
+    return make_flat(f"g{seed}", seed, len(lens), H, ps, list(lens), pool_pages=POOL)
+
+
+def load_into(dev: Dev, inp) -> None:
+    """Copy another bundle's tensors into the captured tensors (same shapes)."""
+    dev.q_nope.copy_(dev_bf16(inp.q_nope))
+    dev.q_pe.copy_(dev_bf16(inp.q_pe))
+    dev.ckv.copy_(dev_bf16(inp.ckv))
+    dev.kpe.copy_(dev_bf16(inp.kpe))
+
+
+def eager(plan, dev, out, lse, stream):
+    with torch.cuda.stream(stream):
+        plan.run(dev.q_nope, dev.q_pe, dev.ckv, dev.kpe, out=out, lse=lse, stream=stream)
+    torch.cuda.synchronize()
+    return out.clone(), lse.clone()
+
+
+@pytest.mark.parametrize("H,ps", [(128, 64), (16, 1), (64, 16)])
+def test_graph_replay_and_update(H, ps):
+    # three page tables of one batch: different lengths, page counts and
+    # split patterns (the long request splits across lanes, the others not)
+    specs = [[1, 40, 333, 1000, 64], [700, 3, 129, 64, 1200], [5, 5, 5, 5, 5]]
+    if ps == 1:
+        specs = [[1, 20, 33, 50, 4], [30, 3, 9, 64, 40], [5, 5, 5, 5, 5]]
+    bundles = [tables(200 + i, s, H, ps) for i, s in enumerate(specs)]
+    cap = max(len(b.kv_indices) for b in bundles) + 7
+    A = bundles[0]
+    note(f"graph H={H} ps={ps} cap={cap}")
+    plan = pk.plan(A.kv_indptr, A.kv_indices, A.kv_lens, H, ps, POOL, index_capacity=cap)
+    assert plan.export().header[24] == 1
+    dev = Dev(A)
+    out = torch.empty((A.batch, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((A.batch, H), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    ref_o, ref_l = eager(plan, dev, out, lse, side)
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        plan.run(dev.q_nope, dev.q_pe, dev.ckv, dev.kpe, out=out, lse=lse, stream=side)
+    torch.cuda.synchronize()
+
+    for step, inp in enumerate(bundles + [A]):
+        if step > 0:
+            plan.update(inp.kv_indptr, inp.kv_indices, inp.kv_lens, stream=side)
+            load_into(dev, inp)
+            torch.cuda.synchronize()
+            ref_o, ref_l = eager(plan, dev, out, lse, side)
+            # a fresh ordinary plan (exact launch shapes) gives the same bits
+            fresh = pk.plan(inp.kv_indptr, inp.kv_indices, inp.kv_lens, H, ps, POOL)
+            fo, fl = eager(fresh, dev, torch.empty_like(out), torch.empty_like(lse), side)
+            assert torch.equal(fo, ref_o) and torch.equal(fl, ref_l)
+            o64, l64 = oracle_flat(inp)
+            compare(ref_o, ref_l, o64, l64, name=f"update {step}")
+        for rep in range(3):
+            out.fill_(7.0)          # eager work between replays
+            lse.fill_(-1.0)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref_o), (step, rep)
+            assert torch.equal(lse, ref_l), (step, rep)
+        note(f"graph step {step}: 3 replays bit-identical")
+
+
+def test_update_rejects_and_keeps_tables():
+    A = tables(210, [10, 200, 31], 32, 16)
+    B = tables(211, [300, 300, 300], 32, 16)
+    plan = pk.plan(A.kv_indptr, A.kv_indices, A.kv_lens, 32, 16, POOL,
+                   index_capacity=len(A.kv_indices))
+    before = plan.export()
+    with pytest.raises(pk.PkvmlaError) as e:
+        plan.update(B.kv_indptr, B.kv_indices, B.kv_lens)
+    assert e.value.code == pk.EINVAL and "capacity" in str(e.value)
+    bad = A.kv_indices.copy()
+    bad[0] = POOL                          # page id outside the pool
+    with pytest.raises(pk.PkvmlaError) as e:
+        plan.update(A.kv_indptr, bad, A.kv_lens)
+    assert e.value.code == pk.EINVAL
+    after = plan.export()
+    for f in ("wg_indptr", "units", "merges", "seq_indptr", "seq_lens", "seq_indices"):
+        assert np.array_equal(getattr(before, f), getattr(after, f)), f
+    # an ordinary plan accepts updates within its first table's page count
+    plain = pk.plan(B.kv_indptr, B.kv_indices, B.kv_lens, 32, 16, POOL)
+    assert plain.export().header[24] == 0
+    plain.update(A.kv_indptr, A.kv_indices, A.kv_lens)
+    dev = Dev(A)
+    o, l = plain.run(dev.q_nope, dev.q_pe, dev.ckv, dev.kpe)
+    torch.cuda.synchronize()
+    o64, l64 = oracle_flat(A)
+    compare(o, l, o64, l64, name="plain update")
