@@ -4,7 +4,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload deepseek]
 
 A step is one pass of the whole decode path (fused decode kernel + split
-merge) over one batch.  The timed region runs K steps back to back; every step
+merge) over one batch.  The timed region runs K steps back to back, with no
+instrumentation inside it; every step
 reads a different copy ("layer") of the KV cache and query, cycling over
 enough copies to exceed the 256 MB last-level cache, so KV bytes come from HBM
 as they would across the layers of a real model.  Inputs are seeded synthetic
@@ -14,7 +15,9 @@ the timed region starts.  Prints one JSON line.
 Roofline of the dominant kernel (the fused decode kernel): algorithmic bytes
 per launch = 1152 B per attended KV token + query (1152 B per head) + output
 (1024 B + 4 B lse per head) + page-table bytes, divided by the kernel's mean
-duration from HIP events recorded around that kernel during the timed region.
+duration from HIP events recorded around that kernel (on its own stream) in a
+second run of K steps right after the timed region (the event records would
+otherwise add their own cost to the measured steps).
 """
 
 from __future__ import annotations
@@ -202,7 +205,6 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    plan.set_timing(True)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -212,6 +214,12 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     total_ms = ev0.elapsed_time(ev1)
+    # the decode kernel's own duration: the same K steps again, with a HIP
+    # event pair around every decode launch
+    plan.set_timing(True)
+    for i in range(args.steps):
+        step(args.warmup + args.steps + i)
+    torch.cuda.synchronize()
     kern_ms, kern_n = plan.kernel_timing()
     plan.set_timing(False)
     ms_per_step = total_ms / args.steps
