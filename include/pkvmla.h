@@ -138,6 +138,22 @@ int pkvmla_run(pkvmla_plan plan, const void* q_nope, const void* q_pe,
                const void* ckv_cache, const void* kpe_cache, void* out, float* lse,
                void* stream);
 
+/* pkvmla_run for caches whose rows are not packed: ckv row r starts at
+ * ckv_cache + r * ckv_row_stride elements and kpe row r at kpe_cache + r *
+ * kpe_row_stride (r = page * page_size + slot).  A cache kept as one
+ * [pages, page_size, 576] tensor (each row the 512 compressed-KV values, then
+ * the 64 rope values; dims as in the plan-argument review of the vLLM-metax
+ * page "[WIP] support flashinfer_mla") is passed as its two views:
+ * ckv_cache = base, kpe_cache = base + 512, both strides 576.
+ * Strides are in bf16 elements, multiples of 8 (whole 16-byte chunks), at
+ * least 512 (ckv) and 64 (kpe), at most 2^20; both base pointers 16-byte
+ * aligned; every row of the pool must lie inside the caller's allocation.
+ * pkvmla_run is this call with strides 512 and 64.  Same semantics and
+ * errors as pkvmla_run, plus PKVMLA_EINVAL for a stride out of range. */
+int pkvmla_run_strided(pkvmla_plan plan, const void* q_nope, const void* q_pe,
+                       const void* ckv_cache, const void* kpe_cache, int64_t ckv_row_stride,
+                       int64_t kpe_row_stride, void* out, float* lse, void* stream);
+
 /* Kernel timing for benchmarks.  With enable != 0, every later pkvmla_run
  * records a HIP event pair on its stream around the fused decode kernel only
  * (events are created here, so run still allocates nothing); the counter is

@@ -49,6 +49,8 @@ _lib.pkvmla_plan_create_with_capacity.argtypes = [_i32p, _i32p, _i32p, ctypes.c_
                                                   ctypes.c_int64, _vp, ctypes.POINTER(_vp)]
 _lib.pkvmla_plan_update.argtypes = [_vp, _i32p, _i32p, _i32p, _vp]
 _lib.pkvmla_run.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.pkvmla_run_strided.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int64, ctypes.c_int64,
+                                    _vp, _vp, _vp]
 _lib.pkvmla_plan_destroy.argtypes = [_vp]
 _lib.pkvmla_plan_destroy.restype = None
 _lib.pkvmla_last_error.restype = ctypes.c_char_p
@@ -64,7 +66,7 @@ _lib.pkvmla_plan_timing.argtypes = [_vp, ctypes.POINTER(ctypes.c_double), _i64p]
 
 EXPORTED_SYMBOLS = (
     "pkvmla_plan_create", "pkvmla_plan_create_with_capacity", "pkvmla_plan_update",
-    "pkvmla_plan_create_cascade", "pkvmla_run", "pkvmla_plan_destroy",
+    "pkvmla_plan_create_cascade", "pkvmla_run", "pkvmla_run_strided", "pkvmla_plan_destroy",
     "pkvmla_last_error", "pkvmla_kernel_config", "pkvmla_schedule_host", "pkvmla_plan_export",
     "pkvmla_gather", "pkvmla_gather_rows", "pkvmla_plan_set_timing", "pkvmla_plan_timing",
 )
@@ -172,25 +174,34 @@ class Plan:
         self.__del__()
 
     def run(self, q_nope, q_pe, ckv_cache, kpe_cache, out=None, lse=None, stream=None):
-        """Decode on the device.  q_nope [B,H,512], q_pe [B,H,64], ckv_cache
-        [P,ps,512], kpe_cache [P,ps,64] are contiguous bf16 CUDA tensors.
-        Returns (out bf16 [B,H,512], lse fp32 [B,H]); out/lse are allocated
-        when not given.  Asynchronous on `stream` (default: current stream)."""
+        """Decode on the device.  q_nope [B,H,512], q_pe [B,H,64] are
+        contiguous bf16 CUDA tensors; ckv_cache [P,ps,512] and kpe_cache
+        [P,ps,64] are bf16 with unit stride inside a row and packed rows within
+        a page (row stride S, page stride ps*S): contiguous tensors, or the two
+        views [..., :512] and [..., 512:] of one [P,ps,576] cache.  Returns
+        (out bf16 [B,H,512], lse fp32 [B,H]); out/lse are allocated when not
+        given.  Asynchronous on `stream` (default: current stream)."""
         import torch
         B, H = self.batch, self.num_heads
         for name, t, shape in (("q_nope", q_nope, (B, H, 512)), ("q_pe", q_pe, (B, H, 64))):
             if tuple(t.shape) != shape or t.dtype != torch.bfloat16 or not t.is_contiguous():
                 raise ValueError(f"{name} must be a contiguous bf16 tensor of shape {shape}")
+        strides = []
         for name, t, d in (("ckv_cache", ckv_cache, 512), ("kpe_cache", kpe_cache, 64)):
-            if t.dim() != 3 or t.shape[2] != d or t.dtype != torch.bfloat16 or not t.is_contiguous():
-                raise ValueError(f"{name} must be a contiguous bf16 [pages, page_size, {d}] tensor")
+            ok = t.dim() == 3 and t.shape[2] == d and t.dtype == torch.bfloat16
+            S = t.stride(1) if ok else 0
+            if not ok or t.stride(2) != 1 or t.stride(0) != t.shape[1] * S:
+                raise ValueError(f"{name} must be a bf16 [pages, page_size, {d}] tensor with "
+                                 "unit stride in a row and packed rows")
+            strides.append(S)
         if out is None:
             out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=q_nope.device)
         if lse is None:
             lse = torch.empty((B, H), dtype=torch.float32, device=q_nope.device)
-        _check(_lib.pkvmla_run(self._h, q_nope.data_ptr(), q_pe.data_ptr(), ckv_cache.data_ptr(),
-                               kpe_cache.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                               _stream_handle(stream)))
+        _check(_lib.pkvmla_run_strided(self._h, q_nope.data_ptr(), q_pe.data_ptr(),
+                                       ckv_cache.data_ptr(), kpe_cache.data_ptr(), strides[0],
+                                       strides[1], out.data_ptr(), lse.data_ptr(),
+                                       _stream_handle(stream)))
         return out, lse
 
     def update(self, kv_indptr, kv_indices, kv_lens, stream=None) -> None:

@@ -449,11 +449,21 @@ int pkvmla_plan_create_cascade(const int32_t* group_req_indptr, int32_t num_grou
   return ok();
 }
 
-int pkvmla_run(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* ckv_cache,
-               const void* kpe_cache, void* out, float* lse, void* stream) {
+int pkvmla_run_strided(pkvmla_plan P, const void* q_nope, const void* q_pe,
+                       const void* ckv_cache, const void* kpe_cache, int64_t ckv_row_stride,
+                       int64_t kpe_row_stride, void* out, float* lse, void* stream) {
   if (!P) return fail(PKVMLA_EINVAL, "null plan");
   if (!q_nope || !q_pe || !ckv_cache || !kpe_cache || !out || !lse)
     return fail(PKVMLA_EINVAL, "null tensor pointer");
+  // strides in bf16 elements: whole 16-byte chunks, at least one row, and
+  // every row offset (pages x page_size rows) inside 32-bit row arithmetic
+  if (ckv_row_stride < pkvmla::kCkvDim || kpe_row_stride < pkvmla::kKpeDim ||
+      (ckv_row_stride & 7) || (kpe_row_stride & 7) || ckv_row_stride > (1 << 20) ||
+      kpe_row_stride > (1 << 20))
+    return fail(PKVMLA_EINVAL,
+                "row strides must be multiples of 8 elements, >= 512 (ckv) and >= 64 (kpe), "
+                "<= 2^20 (got %lld, %lld)",
+                (long long)ckv_row_stride, (long long)kpe_row_stride);
   if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(ckv_cache) || !aligned16(kpe_cache) ||
       !aligned16(out) || (reinterpret_cast<uintptr_t>(lse) & 3u))
     return fail(PKVMLA_EINVAL, "device pointers must be 16-byte aligned (lse 4-byte)");
@@ -470,6 +480,8 @@ int pkvmla_run(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* 
   d.q_pe = static_cast<const uint16_t*>(q_pe);
   d.ckv = static_cast<const uint16_t*>(ckv_cache);
   d.kpe = static_cast<const uint16_t*>(kpe_cache);
+  d.ckv_stride = (int32_t)(ckv_row_stride * 2);
+  d.kpe_stride = (int32_t)(kpe_row_stride * 2);
   d.out = static_cast<uint16_t*>(out);
   d.lse = lse;
   d.part_o = part_o;
@@ -513,12 +525,21 @@ int pkvmla_run(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* 
   return ok();
 }
 
+int pkvmla_run(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* ckv_cache,
+               const void* kpe_cache, void* out, float* lse, void* stream) {
+  return pkvmla_run_strided(P, q_nope, q_pe, ckv_cache, kpe_cache, pkvmla::kCkvDim,
+                            pkvmla::kKpeDim, out, lse, stream);
+}
+
 void pkvmla_plan_destroy(pkvmla_plan P) { free_plan(P); }
 
 int pkvmla_plan_set_timing(pkvmla_plan P, int32_t enable) {
   if (!P) return fail(PKVMLA_EINVAL, "null plan");
   if (enable && !P->ev[0]) {
-    for (hipEvent_t& e : P->ev) PKVMLA_HIP(hipEventCreate(&e));
+    // timing-only events: no system-scope fence (cache write-back and
+    // invalidation) at each record, which would add its own cost to the
+    // interval and to the kernels that follow
+    for (hipEvent_t& e : P->ev) PKVMLA_HIP(hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
   }
   P->timing = enable ? 1 : 0;
   P->timed_runs = 0;
@@ -617,6 +638,8 @@ int pkvmla_gather(pkvmla_plan P, const void* ckv_cache, const void* kpe_cache, v
   g.units = P->d_units;
   g.seq_indices = P->d_seq_indices;
   g.log2_ps = P->log2_ps;
+  g.ckv_stride = pkvmla::kCkvDim * 2;
+  g.kpe_stride = pkvmla::kKpeDim * 2;
   const int n_units = (int)(P->sched.units.size() / pkvmla::kUnitRecordInts);
   PKVMLA_HIP(pkvmla::launch_gather(g, n_units, (hipStream_t)stream));
   return ok();

@@ -99,7 +99,11 @@ __device__ __forceinline__ void cursor_next(UnitCursor& c, idx_ptr units, int u_
 
 }  // namespace
 
-template <bool BIG, int HB>
+// PACKED: the caches are packed [pages, page_size, 512] and [.., 64] tensors
+// (row strides 1 KB and 128 B, compile-time constants); otherwise the row
+// strides cs_arg and ks_arg (bytes) apply, e.g. the two views of one
+// [pages, page_size, 576] cache.
+template <bool BIG, int HB, bool PACKED>
 __global__ void __launch_bounds__(rs_threads(HB), 1)
 mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
                      const uint16_t* __restrict__ ckv_cache, const uint16_t* __restrict__ kpe_cache,
@@ -107,7 +111,10 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
                      uint16_t* __restrict__ part_o, float* __restrict__ part_lse,
                      const int32_t* __restrict__ wg_indptr_g, const int32_t* __restrict__ units_g,
                      const int32_t* __restrict__ seq_indices_g, int H, int n_hg, int n_lanes,
-                     int log2_ps, float sm_scale, float C, float thr) {
+                     int log2_ps, float sm_scale, float C, float thr, int cs_arg,
+                     int ks_arg) {
+  const int cs = PACKED ? kCkvDim * 2 : cs_arg;
+  const int ks = PACKED ? kKpeDim * 2 : ks_arg;
   const idx_ptr wg_indptr = (idx_ptr)wg_indptr_g;
   const idx_ptr units = (idx_ptr)units_g;
   const idx_ptr seq_indices = (idx_ptr)seq_indices_g;
@@ -418,7 +425,7 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
     const int cw = wave - (HB + kRsPvWaves);
     CopyLanes CLw[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) CLw[h] = copy_lanes(2 * cw + h);
+    for (int h = 0; h < 2; ++h) CLw[h] = copy_lanes(2 * cw + h, ks);
     TileStream ts;
     ts.u = u_begin;
     ts.u_end = u_end;
@@ -444,12 +451,12 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int w = 2 * cw + h;
-        const TileCopy c = tile_copy(ts, ckv, kpe, log2_ps, sb, w);
+        const TileCopy c = tile_copy(ts, ckv, kpe, log2_ps, sb, w, cs, ks);
         if (BIG && c.full) {
 #pragma unroll
           for (int k = 0; k < kCopiesPerWave; ++k) tile_copy_part_full(c, w, k, CLw[h]);
         } else {
-          tile_copy_slot<BIG>(c, ckv, kpe, w, CLw[h]);
+          tile_copy_slot<BIG, PACKED>(c, ckv, kpe, w, CLw[h]);
         }
       }
       book_tile();
@@ -480,20 +487,25 @@ bool launch_decode_rs(const DecodeParams& p, hipStream_t stream, hipError_t* err
   const int hb = decode_rs_head_blocks(p.waves, p.heads_per_wave, p.num_heads, p.head_groups);
   if (!hb) return false;
   const bool big = p.log2_ps >= 5;
+  const bool packed = p.ckv_stride == kCkvDim * 2 && p.kpe_stride == kKpeDim * 2;
   const dim3 grid(decode_grid(p.n_lanes, p.head_groups)), block(rs_threads(hb));
 #define PKVMLA_RS_ARGS                                                                   \
   p.q_nope, p.q_pe, p.ckv, p.kpe, p.out, p.lse, p.part_o, p.part_lse, p.wg_indptr, p.units, \
-      p.seq_indices, p.num_heads, p.head_groups, p.n_lanes, p.log2_ps,      \
-      p.sm_scale, p.score_log2, p.rescale_thr
-#define PKVMLA_RS_LAUNCH(HBV)                                                                  \
-  if (big) mla_decode_rs_kernel<true, HBV><<<grid, block, 0, stream>>>(PKVMLA_RS_ARGS);        \
-  else mla_decode_rs_kernel<false, HBV><<<grid, block, 0, stream>>>(PKVMLA_RS_ARGS);
+      p.seq_indices, p.num_heads, p.head_groups, p.n_lanes, p.log2_ps, p.sm_scale,     \
+      p.score_log2, p.rescale_thr, p.ckv_stride, p.kpe_stride
+#define PKVMLA_RS_LAUNCH2(HBV, PK)                                                             \
+  if (big) mla_decode_rs_kernel<true, HBV, PK><<<grid, block, 0, stream>>>(PKVMLA_RS_ARGS);    \
+  else mla_decode_rs_kernel<false, HBV, PK><<<grid, block, 0, stream>>>(PKVMLA_RS_ARGS);
+#define PKVMLA_RS_LAUNCH(HBV)                 \
+  if (packed) { PKVMLA_RS_LAUNCH2(HBV, true) } \
+  else { PKVMLA_RS_LAUNCH2(HBV, false) }
   switch (hb) {
     case 1: PKVMLA_RS_LAUNCH(1) break;
     case 2: PKVMLA_RS_LAUNCH(2) break;
     default: PKVMLA_RS_LAUNCH(4) break;
   }
 #undef PKVMLA_RS_LAUNCH
+#undef PKVMLA_RS_LAUNCH2
 #undef PKVMLA_RS_ARGS
   *err = hipGetLastError();
   return true;

@@ -32,8 +32,9 @@ bool kernel_config_for(int num_heads, KernelConfig* cfg);
 struct DecodeParams {
   const uint16_t* q_nope;    // [B][H][512] bf16
   const uint16_t* q_pe;      // [B][H][64]  bf16
-  const uint16_t* ckv;       // [P][ps][512] bf16
-  const uint16_t* kpe;       // [P][ps][64]  bf16
+  const uint16_t* ckv;       // [P][ps] rows of 512 bf16, ckv_stride bytes apart
+  const uint16_t* kpe;       // [P][ps] rows of 64 bf16, kpe_stride bytes apart
+  int32_t ckv_stride, kpe_stride;  // row strides in bytes (1024 and 128 when contiguous)
   uint16_t* out;             // [B][H][512] bf16
   float* lse;                // [B][H]
   uint16_t* part_o;          // [slots][H][512] bf16 (normalized partial outputs)
@@ -64,6 +65,7 @@ struct GatherParams {
   const uint16_t* ckv;
   const uint16_t* kpe;
   uint16_t* rows;            // [n_rows][576]
+  int32_t ckv_stride, kpe_stride;  // cache row strides in bytes
   const int32_t* units;
   const int32_t* seq_indices;
   int32_t log2_ps;

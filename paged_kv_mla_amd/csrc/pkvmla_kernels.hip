@@ -83,7 +83,7 @@ template <bool BIG>
 __global__ void __launch_bounds__(kCopyWaves * 64)
 mla_gather_kernel(const uint16_t* __restrict__ ckv_cache, const uint16_t* __restrict__ kpe_cache,
                   uint16_t* __restrict__ rows, const int32_t* __restrict__ units_g,
-                  const int32_t* __restrict__ seq_indices_g, int log2_ps) {
+                  const int32_t* __restrict__ seq_indices_g, int log2_ps, int cs, int ks) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[kStageBytes];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
   const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
@@ -92,7 +92,7 @@ mla_gather_kernel(const uint16_t* __restrict__ ckv_cache, const uint16_t* __rest
   const char* ckv = reinterpret_cast<const char*>(ckv_cache);
   const char* kpe = reinterpret_cast<const char*>(kpe_cache);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // copy slot
-  const CopyLanes CL = copy_lanes(wave);
+  const CopyLanes CL = copy_lanes(wave, ks);
   idx_ptr rec = units + (size_t)blockIdx.x * kUnitInts;
   const int kv0 = rec[2], kv1 = rec[3], row0 = rec[5];
   TileStream ts;
@@ -102,12 +102,12 @@ mla_gather_kernel(const uint16_t* __restrict__ ckv_cache, const uint16_t* __rest
   stream_load_unit(ts, units, seq_indices);
   for (int tok0 = kv0; tok0 < kv1; tok0 += kTile) {
     __syncthreads();  // the previous tile has been read out
-    const TileCopy c = tile_copy(ts, ckv, kpe, log2_ps, smem_base, wave);
+    const TileCopy c = tile_copy(ts, ckv, kpe, log2_ps, smem_base, wave, cs, ks);
     if (BIG && c.full) {
 #pragma unroll
       for (int k = 0; k < kCopiesPerWave; ++k) tile_copy_part_full(c, wave, k, CL);
     } else {
-      tile_copy_slot<BIG>(c, ckv, kpe, wave, CL);
+      tile_copy_slot<BIG, true>(c, ckv, kpe, wave, CL);  // the gather reads packed caches
     }
     stream_advance(ts, units, seq_indices, log2_ps);
     wait_vmcnt<0>();
@@ -175,10 +175,12 @@ hipError_t launch_gather(const GatherParams& p, int n_units, hipStream_t stream)
   if (n_units <= 0) return hipSuccess;
   if (p.log2_ps >= 5)
     mla_gather_kernel<true><<<n_units, kCopyWaves * 64, 0, stream>>>(
-        p.ckv, p.kpe, p.rows, p.units, p.seq_indices, p.log2_ps);
+        p.ckv, p.kpe, p.rows, p.units, p.seq_indices, p.log2_ps, p.ckv_stride,
+        p.kpe_stride);
   else
     mla_gather_kernel<false><<<n_units, kCopyWaves * 64, 0, stream>>>(
-        p.ckv, p.kpe, p.rows, p.units, p.seq_indices, p.log2_ps);
+        p.ckv, p.kpe, p.rows, p.units, p.seq_indices, p.log2_ps, p.ckv_stride,
+        p.kpe_stride);
   return hipGetLastError();
 }
 

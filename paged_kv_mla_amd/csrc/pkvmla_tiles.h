@@ -71,19 +71,21 @@ struct TileCopy {
   int tok0, last, log2_ps;
   uint32_t st;            // LDS stage base
   // BIG, whole tiles (last == kTile - 1): this wave's two ckv row groups and
-  // its kpe block as ready scalar bases, so a copy needs no address arithmetic
+  // its kpe block as ready scalar bases, so a copy needs at most one scalar
+  // multiply-add (for a ckv row stride other than 1 KB)
   // (scalar ALU work between the MFMAs of the k-loop costs more than it looks:
   // about four clocks per instruction, in dependent chains)
   const char* g0;
   const char* g1;
   const char* kb;
   uint32_t row0;          // BIG: cache row of the tile's first token
+  int cs, ks;             // row strides of the ckv and kpe caches, bytes
   bool full;
 };
 
 __device__ __forceinline__ TileCopy tile_copy(const TileStream& s, const char* __restrict__ ckv,
                                               const char* __restrict__ kpe, int log2_ps,
-                                              uint32_t stage_base, int wave) {
+                                              uint32_t stage_base, int wave, int cs, int ks) {
   TileCopy c;
   c.tok0 = s.kv0 + s.tile * kTile;
   c.last = min(s.kv1 - 1 - c.tok0, kTile - 1);
@@ -92,12 +94,14 @@ __device__ __forceinline__ TileCopy tile_copy(const TileStream& s, const char* _
   c.st = stage_base;
   const int64_t rowbase = ((int64_t)(uint32_t)s.pid << log2_ps) + (c.tok0 & ((1 << log2_ps) - 1));
   c.row0 = (uint32_t)rowbase;
-  c.crow = ckv + rowbase * (kCkvDim * 2);
-  c.krow = kpe + rowbase * (kKpeDim * 2);
+  c.cs = cs;
+  c.ks = ks;
+  c.crow = ckv + rowbase * cs;
+  c.krow = kpe + rowbase * ks;
   c.full = c.last == kTile - 1;
-  c.g0 = c.crow + (4 * wave) * (kCkvDim * 2);
-  c.g1 = c.crow + (4 * wave + 16) * (kCkvDim * 2);
-  c.kb = c.krow + (8 * wave) * (kKpeDim * 2);
+  c.g0 = c.crow + (int64_t)(4 * wave) * cs;
+  c.g1 = c.crow + (int64_t)(4 * wave + 16) * cs;
+  c.kb = c.krow + (int64_t)(8 * wave) * ks;
   return c;
 }
 
@@ -128,7 +132,9 @@ struct CopyLanes {
   uint32_t vk;              // kpe block (the same for every wave)
 };
 
-__device__ __forceinline__ CopyLanes copy_lanes(int wave) {
+// ks: the kpe cache's row stride in bytes (128 for a [pages, page_size, 64]
+// tensor, 1152 for the kpe view of a combined [pages, page_size, 576] one).
+__device__ __forceinline__ CopyLanes copy_lanes(int wave, int ks) {
   const uint32_t lane = (uint32_t)lane_id_fresh();
   const uint32_t w4 = (uint32_t)(4 * wave);
   CopyLanes L;
@@ -137,7 +143,7 @@ __device__ __forceinline__ CopyLanes copy_lanes(int wave) {
   L.v2 = (lane ^ (w4 + 2u)) << 4;
   L.v3 = (lane ^ (w4 + 3u)) << 4;
   // token 8*wave + lane/8 (swz8 = lane/8), chunk lane % 8
-  L.vk = (lane >> 3) * (uint32_t)(kKpeDim * 2) + (((lane & 7u) ^ (lane >> 3)) << 4);
+  L.vk = (lane >> 3) * (uint32_t)ks + (((lane & 7u) ^ (lane >> 3)) << 4);
   return L;
 }
 
@@ -147,7 +153,9 @@ __device__ __forceinline__ CopyLanes copy_lanes(int wave) {
 // are resolved first, clamped to the last valid token, in one batch of scalar
 // page-id loads with one wait; then its 9 copies go out (M0 loaded three
 // times, as in the whole-tile path).
-template <bool BIG>
+// PACKED: the caches' rows are 1 KB (ckv) and 128 B (kpe) apart, so row
+// addresses are shifts; otherwise they take the runtime strides.
+template <bool BIG, bool PACKED>
 __device__ __forceinline__ void tile_copy_slot(const TileCopy& c, const char* __restrict__ ckv,
                                                const char* __restrict__ kpe, int wave,
                                                const CopyLanes& L) {
@@ -176,10 +184,11 @@ __device__ __forceinline__ void tile_copy_slot(const TileCopy& c, const char* __
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
     set_m0(c.st + (uint32_t)(4 * wave + 16 * g) * 1024u);
-    dma16_m0<0>(ckv + (size_t)rc[4 * g + 0] * (kCkvDim * 2), L.v0);
-    dma16_m0<1024>(ckv + (size_t)rc[4 * g + 1] * (kCkvDim * 2) - 1024, L.v1);
-    dma16_m0<2048>(ckv + (size_t)rc[4 * g + 2] * (kCkvDim * 2) - 2048, L.v2);
-    dma16_m0<3072>(ckv + (size_t)rc[4 * g + 3] * (kCkvDim * 2) - 3072, L.v3);
+    const size_t cs = PACKED ? (size_t)(kCkvDim * 2) : (size_t)c.cs;
+    dma16_m0<0>(ckv + (size_t)rc[4 * g + 0] * cs, L.v0);
+    dma16_m0<1024>(ckv + (size_t)rc[4 * g + 1] * cs - 1024, L.v1);
+    dma16_m0<2048>(ckv + (size_t)rc[4 * g + 2] * cs - 2048, L.v2);
+    dma16_m0<3072>(ckv + (size_t)rc[4 * g + 3] * cs - 3072, L.v3);
   }
   // kpe: lane group g8 = lane / 8 copies token 8*wave + g8 (chunk swizzle
   // g8, since 8*wave is a multiple of 8)
@@ -190,7 +199,7 @@ __device__ __forceinline__ void tile_copy_slot(const TileCopy& c, const char* __
 #pragma unroll
   for (int k = 1; k < 8; ++k) row = g8 == k ? rk[k] : row;
   const uint32_t kchunk = (uint32_t)(((lane & 7) ^ g8) << 4);
-  dma16_m0v(kpe + (size_t)row * (kKpeDim * 2) + kchunk);
+  dma16_m0v(kpe + (size_t)row * (PACKED ? (size_t)(kKpeDim * 2) : (size_t)c.ks) + kchunk);
 }
 
 // Part k of a whole tile's copies (BIG and full): ready bases, no clamping.
@@ -199,7 +208,9 @@ __device__ __forceinline__ void tile_copy_part_full(const TileCopy& c, int wave,
   if (k < 8) {
     const int j = k & 3;
     if (j == 0) set_m0(c.st + (uint32_t)(4 * wave + 16 * (k >> 2)) * 1024u);
-    const char* base = k < 4 ? c.g0 : c.g1;
+    // row 4*wave + 16*(k/4) + j sits j row strides past the group's base; the
+    // instruction offset adds j KB, so the base takes j * (stride - 1 KB)
+    const char* base = (k < 4 ? c.g0 : c.g1) + (int64_t)j * (c.cs - 1024);
     switch (j) {
       case 0: dma16_m0<0>(base, L.v0); break;
       case 1: dma16_m0<1024>(base, L.v1); break;

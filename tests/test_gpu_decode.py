@@ -247,3 +247,42 @@ def test_full_size_cascade():
     ref_o, ref_l = oracle_cascade(cas, reqs)
     st = compare(out, lse, ref_o, ref_l, requests=reqs, name="cascade")
     note(f"full cascade stats {st}")
+
+
+# ---------------------------------------- one combined [P, ps, 576] cache
+@pytest.mark.parametrize("H,ps", [(128, 64), (128, 32), (64, 16), (16, 1)])
+def test_combined_cache_views(H, ps):
+    """The ckv and kpe views of one [pages, page_size, 576] cache (row stride
+    576 for both) give the same bits as two packed caches, and match the
+    oracle."""
+    lens = {1: [1, 31, 70, 200], 16: [1, 17, 300, 513]}.get(ps, [1, 33, 100, 700, 2049])
+    inp = small(90 + ps, lens, H=H, ps=ps)
+    note(f"combined cache H={H} ps={ps}")
+    dev = Dev(inp)
+    plan = pk.plan_for(inp)
+    o1, l1 = run_gpu(plan, dev)
+    comb = torch.cat([dev.ckv, dev.kpe], dim=2).contiguous()
+    o2, l2 = plan.run(dev.q_nope, dev.q_pe, comb[..., :512], comb[..., 512:])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    ref_o, ref_l = oracle_flat(inp)
+    compare(o2, l2, ref_o, ref_l, name=f"combined H{H} ps{ps}")
+
+
+def test_combined_cache_cascade_and_bad_strides():
+    cas = make_cascade("cc", 95, 6, 64, 16, [32, 48], [1, 20, 0, 33, 5, 7], groups=2)
+    dev = Dev(cas)
+    plan = pk.plan_for(cas)
+    o1, l1 = run_gpu(plan, dev)
+    comb = torch.cat([dev.ckv, dev.kpe], dim=2).contiguous()
+    o2, l2 = plan.run(dev.q_nope, dev.q_pe, comb[..., :512], comb[..., 512:])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    out = torch.empty_like(o1)
+    lse = torch.empty_like(l1)
+    s = int(torch.cuda.current_stream().cuda_stream)
+    for cs, ks in [(500, 64), (512, 60), (516, 64), (576, 1 << 21)]:
+        rc = pk._lib.pkvmla_run_strided(plan._h, dev.q_nope.data_ptr(), dev.q_pe.data_ptr(),
+                                        dev.ckv.data_ptr(), dev.kpe.data_ptr(), cs, ks,
+                                        out.data_ptr(), lse.data_ptr(), s)
+        assert rc == pk.EINVAL, (cs, ks)
