@@ -131,3 +131,12 @@ def test_update_rejects_and_keeps_tables():
     torch.cuda.synchronize()
     o64, l64 = oracle_flat(A)
     compare(o, l, o64, l64, name="plain update")
+
+
+def test_update_of_cascade_plan_is_unsupported():
+    from mla_workloads import make_cascade
+    cas = make_cascade("gu", 212, 4, 16, 16, [32], [3, 0, 20, 7])
+    plan = pk.plan_for(cas)
+    with pytest.raises(pk.PkvmlaError) as e:
+        plan.update(cas.kv_indptr, cas.kv_indices, np.maximum(cas.kv_lens, 1))
+    assert e.value.code == pk.EUNSUPPORTED
