@@ -286,3 +286,31 @@ def test_combined_cache_cascade_and_bad_strides():
                                         dev.ckv.data_ptr(), dev.kpe.data_ptr(), cs, ks,
                                         out.data_ptr(), lse.data_ptr(), s)
         assert rc == pk.EINVAL, (cs, ks)
+
+
+# ------------------------------------------------------- extreme shapes
+def test_one_request_over_every_lane():
+    """One 131072-token request: the schedule splits it over every lane, so
+    the merge combines the largest number of partial states (one per lane)."""
+    inp = small(97, [131072], H=128, ps=64)
+    ex = pk.plan_for(inp).export()
+    n_split = int(ex.merges[0, 2])
+    note(f"one request, {n_split} partial states")
+    assert ex.merges.shape[0] == 1 and n_split == ex.grid >= 64
+    out, lse = run_gpu(pk.plan_for(inp), Dev(inp))
+    ref_o, ref_l = oracle_flat(inp)
+    compare(out, lse, ref_o, ref_l, name="one request")
+
+
+def test_many_tiny_requests():
+    """2048 requests of 1..8 tokens at page size 1: many units per lane, no
+    splits, every request written by the decode kernel directly."""
+    rng = np.random.default_rng(98)
+    lens = rng.integers(1, 9, size=2048).tolist()
+    inp = small(98, lens, H=16, ps=1)
+    ex = pk.plan_for(inp).export()
+    note(f"2048 tiny requests: {ex.units.shape[0]} units on {ex.grid} lanes")
+    assert ex.merges.shape[0] == 0
+    out, lse = run_gpu(pk.plan_for(inp), Dev(inp))
+    ref_o, ref_l = oracle_flat(inp)
+    compare(out, lse, ref_o, ref_l, name="tiny requests")
