@@ -17,7 +17,11 @@ namespace pkvmla {
 // log-sum-exp: lse = M + ln sum_i e^(lse_i - M), out = sum_i e^(lse_i - lse) o_i.
 // The partial outputs o_i are bf16 (each already normalized by its own row
 // sum), the combination runs in fp32.  Block: 4 heads x 64 lanes, 8 dims per
-// lane (one 16-byte load per partial row).
+// lane (one 16-byte load per partial row).  One pass: the states are read in
+// chunks of four (their loads in flight together) and folded into a running
+// (M, weight sum, weighted sum), so a request with at most four states costs
+// one round trip to memory (and the same bits as a max-first two-pass merge;
+// with more states, the rescaled sums round differently).
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) mla_merge_kernel(MergeParams p) {
   constexpr int kChunk = 4;  // partial states whose loads are in flight together
@@ -27,19 +31,12 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(MergeParams p) {
   const int H = p.num_heads;
   const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
   const int d0 = (threadIdx.x & 63) * 8;
-  // Chunks past the last state re-read the last one (valid memory) and carry
-  // weight 0 (a select, so they add exactly nothing).
-  float M = -INFINITY;
-  for (int i0 = 0; i0 < n; i0 += kChunk) {
-    float lv[kChunk];
-#pragma unroll
-    for (int j = 0; j < kChunk; ++j) lv[j] = p.part_lse[(size_t)(s0 + min(i0 + j, n - 1)) * H + h];
-#pragma unroll
-    for (int j = 0; j < kChunk; ++j) M = fmaxf(M, lv[j]);
-  }
+  constexpr float kLog2e = 1.4426950408889634f;
+  float M = -INFINITY, wsum = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
   for (int i0 = 0; i0 < n; i0 += kChunk) {
+    // chunk entries past the last state re-read the last one (valid memory)
+    // and carry weight 0 (a select, so they add exactly nothing)
     uint4 x[kChunk];
     float lv[kChunk];
 #pragma unroll
@@ -48,9 +45,19 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(MergeParams p) {
       lv[j] = p.part_lse[base];
       x[j] = *reinterpret_cast<const uint4*>(p.part_o + base * kCkvDim + d0);
     }
+    float cm = M;
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) cm = fmaxf(cm, lv[j]);
+    // rescale what is folded so far to the new maximum (the first chunk has
+    // nothing folded: factor 0 on zeros)
+    const float f = cm == M ? 1.f : __builtin_amdgcn_exp2f((M - cm) * kLog2e);
+    M = cm;
+    wsum *= f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] *= f;
 #pragma unroll
     for (int j = 0; j < kChunk; ++j) {
-      const float w = i0 + j < n ? __builtin_amdgcn_exp2f((lv[j] - M) * 1.4426950408889634f) : 0.f;
+      const float w = i0 + j < n ? __builtin_amdgcn_exp2f((lv[j] - M) * kLog2e) : 0.f;
       const uint32_t xw[4] = {x[j].x, x[j].y, x[j].z, x[j].w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
