@@ -98,3 +98,18 @@ def test_cascade_config_schedule():
     items = cascade_items(np.array([0, B]), np.array([prefix]), suffix)
     wg, units, merges = check_schedule(items, B, 256, kc["tile"], kc["fixed_cost"])
     assert len(merges) == B          # every request has prefix and suffix units
+
+
+def test_unit_page_fields_hand_case():
+    """Page fields worked out by hand: sequence 0 owns pages [7, 3], sequence 1
+    pages [9, 1, 4] (page size 16).  A unit of sequence 1 starting at token 32
+    begins in its third page, id 4; one of sequence 0 at token 16, in page 3."""
+    from oracle.schedule_ref import unit_page_fields
+    units = np.zeros((3, 8), np.int32)
+    units[0, :4] = (0, 0, 0, 16)
+    units[1, :4] = (1, 1, 32, 40)
+    units[2, :4] = (0, 0, 16, 20)
+    got = unit_page_fields(units, [0, 2, 5], [7, 3, 9, 1, 4], 16)
+    assert got[:, 6].tolist() == [0, 2, 0]
+    assert got[:, 7].tolist() == [7, 4, 3]
+    assert np.array_equal(got[:, :6], units[:, :6])   # the schedule fields are untouched
