@@ -147,3 +147,19 @@ def test_null_pointer_arguments_rejected():
     assert lib.pkvmla_plan_create(None, None, None, 1, 1, 16, 512, 64, 16, 0.0, None, None) == pk.EINVAL
     lib.pkvmla_plan_update.argtypes = [ctypes.c_void_p] * 5
     assert lib.pkvmla_plan_update(None, None, None, None, None) == pk.EINVAL
+
+
+def test_package_without_library_fails_loudly(tmp_path):
+    """No CPU or PyTorch fallback: the binding refuses to import without the
+    built HIP library."""
+    import shutil
+    import subprocess
+    import sys
+    pkg = tmp_path / "paged_kv_mla_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(ROOT, "paged_kv_mla_amd", "__init__.py"), pkg / "__init__.py")
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "try:\n    import paged_kv_mla_amd\nexcept ImportError as e:\n"
+            "    print('IMPORT_ERROR', e)\n") % str(tmp_path)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert "IMPORT_ERROR" in r.stdout and "no fallback" in r.stdout, r.stdout + r.stderr
