@@ -163,3 +163,39 @@ def test_package_without_library_fails_loudly(tmp_path):
             "    print('IMPORT_ERROR', e)\n") % str(tmp_path)
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert "IMPORT_ERROR" in r.stdout and "no fallback" in r.stdout, r.stdout + r.stderr
+
+
+def test_c_program_links_and_calls_host_entry_points(tmp_path):
+    """The header is plain C99, and a C program links against the library and
+    calls its host-only entry points (no GPU needed)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "abi.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include "pkvmla.h"
+int main(void) {
+  int32_t cfg[7];
+  if (pkvmla_kernel_config(128, cfg) != PKVMLA_OK) return 1;
+  if (pkvmla_kernel_config(8, cfg) != PKVMLA_EUNSUPPORTED) return 2;
+  int32_t items[6] = {0, 0, 100, 1, 1, 40};
+  int32_t wg[8], units[64], merges[16], counts[3];
+  if (pkvmla_schedule_host(items, 2, 2, 4, 32, 1, wg, 8, units, 64, merges, 16, counts)) return 3;
+  if (pkvmla_run(NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL) != PKVMLA_EINVAL) return 4;
+  printf("tile %d waves %d units %d %s\n", cfg[0], cfg[1], counts[1], pkvmla_last_error());
+  return 0;
+}
+''')
+    lib_dir = os.path.join(ROOT, "paged_kv_mla_amd")
+    exe = tmp_path / "abi"
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                        f"-I{os.path.join(ROOT, 'include')}", str(src), "-o", str(exe),
+                        f"-L{lib_dir}", "-lpkvmla", f"-Wl,-rpath,{lib_dir}"],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
+    assert r.stdout.startswith("tile 32 waves 8 units")
