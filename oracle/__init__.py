@@ -1,8 +1,8 @@
 """fp64 CPU oracle for batched paged-KV MLA decode (absorbed form).
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
-execute anything in this package: only the test suite, the smoke check of the
-graft entry point and the ``cpu_baseline`` leg of ``bench.py`` use it.  It
+execute anything in this package: only the test suite, the smoke check
+(``__graft_entry__.smoke``) and the ``cpu_baseline`` leg of ``bench.py`` use it.  It
 shares no code with the HIP library (``paged_kv_mla_amd``); both are fed from
 the seeded generators in ``mla_workloads``, which hold no attention arithmetic.
 
