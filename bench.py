@@ -4,20 +4,28 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload deepseek]
 
 A step is one pass of the whole decode path (fused decode kernel + split
-merge) over one batch.  The timed region runs K steps back to back, with no
-instrumentation inside it; every step
+merge) over one batch.  The timed region runs K steps back to back; every step
 reads a different copy ("layer") of the KV cache and query, cycling over
 enough copies to exceed the 256 MB last-level cache, so KV bytes come from HBM
 as they would across the layers of a real model.  Inputs are seeded synthetic
 bf16 (N(0,1)*0.5) with the workload's shapes; they are resident in HBM before
 the timed region starts.  Prints one JSON line.
 
+Timing.  The timed region is K steps back to back with a HIP event recorded
+after every step (events created without the system-scope fence, so a record
+adds no cache write-back); ms_per_step is the mean, and the median and p10/p90
+of the per-step intervals are reported beside it.  A second pass of K steps
+runs with the library's kernel timing on: a HIP event pair around every decode
+launch on its own stream, and the kernel's own span (earliest wave start to
+latest wave end on the GPU's 100 MHz real-time counter).  The event interval
+also holds the dispatch gap before the kernel; the span does not, and is what
+a rocprofv3 kernel trace reports as the kernel's duration.
+
 Roofline of the dominant kernel (the fused decode kernel): algorithmic bytes
-per launch = 1152 B per attended KV token + query (1152 B per head) + output
-(1024 B + 4 B lse per head) + page-table bytes, divided by the kernel's mean
-duration from HIP events recorded around that kernel (on its own stream) in a
-second run of K steps right after the timed region (the event records would
-otherwise add their own cost to the measured steps).
+per launch = 1152 B per unique KV token + query (1152 B per head) + output
+(1024 B + 4 B lse per head) + page-table bytes (flops: 2176 per attended token
+and head), divided by the kernel's mean span.  The line refuses to print if a
+decode kernel measured longer than the step that contains it.
 """
 
 from __future__ import annotations
@@ -49,6 +57,39 @@ WORKLOAD_DESC = {
                "8192-token shared prefix + suffix uniform [64,1024]",
     "tiny": "tiny decode: batch 4, 16 heads, 512/64, page_size 16, kv_len {1,17,64,200}",
 }
+
+
+class HipEvents:
+    """HIP events without the system-scope fence, through the HIP runtime that
+    torch has loaded (torch's own events record with the fence)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        import torch
+        self._c = ctypes
+        self._hip = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib",
+                                             "libamdhip64.so"))
+
+    def create(self):
+        e = self._c.c_void_p()
+        rc = self._hip.hipEventCreateWithFlags(self._c.byref(e), self.DISABLE_SYSTEM_FENCE)
+        assert rc == 0, rc
+        return e
+
+    def record(self, e, stream: int):
+        rc = self._hip.hipEventRecord(e, self._c.c_void_p(stream))
+        assert rc == 0, rc
+
+    def elapsed(self, a, b) -> float:
+        ms = self._c.c_float(0.0)
+        rc = self._hip.hipEventElapsedTime(self._c.byref(ms), a, b)
+        assert rc == 0, rc
+        return float(ms.value)
+
+    def destroy(self, e):
+        self._hip.hipEventDestroy(e)
 
 
 def kernel_source_hash() -> str:
@@ -134,7 +175,7 @@ def load_traffic(workload: str, launches_tokens: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="deepseek", choices=sorted(WORKLOAD_DESC))
     ap.add_argument("--layers", type=int, default=0,
@@ -202,28 +243,44 @@ def main():
         plan.run_ptrs(qns[k].data_ptr(), qps[k].data_ptr(), ckvs[k].data_ptr(),
                       kpes[k].data_ptr(), outs[k].data_ptr(), lses[k].data_ptr(), sh)
 
+    hip = HipEvents()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    total_ms = ev0.elapsed_time(ev1)
-    # the decode kernel's own duration: the same K steps again, with a HIP
-    # event pair around every decode launch
+
+    def timed_pass(first, n):
+        evs = [hip.create() for _ in range(n + 1)]
+        torch.cuda.synchronize()
+        hip.record(evs[0], sh)
+        for i in range(n):
+            step(first + i)
+            hip.record(evs[i + 1], sh)
+        torch.cuda.synchronize()
+        per = np.array([hip.elapsed(evs[i], evs[i + 1]) for i in range(n)])
+        total = hip.elapsed(evs[0], evs[-1])
+        for e in evs:
+            hip.destroy(e)
+        return total, per
+
+    total_ms, per_step = timed_pass(args.warmup, args.steps)
+    # percentiles over at least 50 steps (an extra pass when K is smaller)
+    stats_steps = max(args.steps, 50)
+    if stats_steps > args.steps:
+        _, per_step = timed_pass(args.warmup + args.steps, stats_steps)
+    # second pass: the decode kernel's event intervals and in-kernel spans (the
+    # library keeps the last 256 runs' records)
     plan.set_timing(True)
-    for i in range(args.steps):
-        step(args.warmup + args.steps + i)
-    torch.cuda.synchronize()
-    kern_ms, kern_n = plan.kernel_timing()
+    timing_steps = min(args.steps, 256)
+    total2_ms, per_step2 = timed_pass(args.warmup + 2 * stats_steps, timing_steps)
+    kern_ev_ms, kern_span_ms, kern_n = plan.kernel_timing()
     plan.set_timing(False)
     ms_per_step = total_ms / args.steps
-    kern_avg_ms = kern_ms / max(kern_n, 1)
+    kern_ev_avg = kern_ev_ms / max(kern_n, 1)
+    kern_avg_ms = kern_span_ms / max(kern_n, 1)
+    if kern_avg_ms > float(np.median(per_step2)) or kern_avg_ms <= 0.0:
+        print(f"inconsistent timing: decode kernel span {kern_avg_ms:.5f} ms against a step "
+              f"of {np.median(per_step2):.5f} ms", file=sys.stderr)
+        sys.exit(3)
 
     value = attended / (ms_per_step * 1e-3)
     tflops = alg_flops / (ms_per_step * 1e-3) / 1e12
@@ -264,7 +321,15 @@ def main():
                    "unique_kv_tokens": unique, "kv_copies_cycled": layers},
         "tflops": round(tflops, 2),
         "step_roofline_frac": round(max(t_hbm, t_mfma) / (ms_per_step * 1e-3), 4),
+        "ms_per_step_median": round(float(np.median(per_step)), 5),
+        "ms_per_step_p10": round(float(np.percentile(per_step, 10)), 5),
+        "ms_per_step_p90": round(float(np.percentile(per_step, 90)), 5),
+        "per_step_stats_steps": int(stats_steps),
         "decode_kernel_ms": round(kern_avg_ms, 5),
+        "decode_kernel_source": "in-kernel real-time stamps (earliest wave start to latest "
+                                "wave end), second pass of the same steps",
+        "decode_event_ms": round(kern_ev_avg, 5),
+        "ms_per_step_timing_pass": round(total2_ms / timing_steps, 5),
         "alg_bytes_per_step": int(alg_bytes),
         "alg_flops_per_step": alg_flops,
         "plan_host_ms": round(plan_ms, 2),

@@ -102,7 +102,11 @@ int pkvmla_plan_create_with_capacity(const int32_t* kv_indptr, const int32_t* kv
 
 /* Replace a flat plan's page table and lengths (same batch; host arrays as in
  * pkvmla_plan_create, read during the call only) and recompute its schedule,
- * in place: no allocation, no pointer or launch-shape change.  The new tables
+ * in place, without allocation.  A plan built with an index_capacity keeps
+ * every pointer and launch shape, so a graph captured around pkvmla_run stays
+ * valid.  An ordinary plan (index_capacity 0) accepts updates up to its first
+ * table's page count, but its launch shapes follow the new schedule: eager
+ * runs after the update are correct, a graph captured before it is not.  The new tables
  * are copied on `stream` and the call waits for that copy, so every run queued
  * earlier on `stream` has finished with the old tables and every later run
  * (eager, or a graph replayed on `stream`) sees the new ones; work on other
@@ -127,7 +131,11 @@ int pkvmla_plan_create_cascade(const int32_t* group_req_indptr, int32_t num_grou
                                int32_t page_size, float sm_scale, void* stream,
                                pkvmla_plan* out);
 
-/* Run the decode for one set of tensors (e.g. one layer) on `stream`.
+/* Run the decode for one set of tensors (e.g. one layer) on `stream`.  The
+ * plan-then-run split and the run's operands (q_nope, q_pe, the ckv and kpe
+ * caches in, output and log-sum-exp out) follow the decode-wrapper calls in
+ * the vLLM-metax page "[WIP] support flashinfer_mla" (the plan-argument and
+ * metadata reviews).
  * Asynchronous: only kernel launches on `stream`; no allocation, no host
  * synchronisation, no host<->device copies.  Device pointers are owned by the
  * caller and must stay valid until the stream reaches the end of the call;
@@ -155,18 +163,29 @@ int pkvmla_run_strided(pkvmla_plan plan, const void* q_nope, const void* q_pe,
                        int64_t kpe_row_stride, void* out, float* lse, void* stream);
 
 /* Kernel timing for benchmarks.  With enable != 0, every later pkvmla_run
- * records a HIP event pair on its stream around the fused decode kernel only
- * (events are created here, so run still allocates nothing); the counter is
- * reset.  pkvmla_plan_timing synchronises the device and returns the summed
- * duration of the last min(n, 256) timed runs' decode kernels and that count.
- * Timing must be off while a run is being captured into a HIP graph. */
+ * records a HIP event pair on its stream around the fused decode kernel, and
+ * the kernel itself records the earliest start and the latest end of its
+ * waves on the GPU's 100 MHz real-time counter (the kernel's own span, without
+ * the dispatch gap the events also contain).  The event and stamp buffers are
+ * created here, so run still allocates nothing; the run counter is reset.
+ * pkvmla_plan_timing synchronises the device and returns, over the last
+ * min(n, 256) timed runs, the summed event intervals (ms), the summed kernel
+ * spans (ms) and that count.  Timing must be off while a run is being
+ * captured into a HIP graph. */
 int pkvmla_plan_set_timing(pkvmla_plan plan, int32_t enable);
-int pkvmla_plan_timing(pkvmla_plan plan, double* total_ms, int64_t* n_runs);
+int pkvmla_plan_timing(pkvmla_plan plan, double* event_ms, double* span_ms, int64_t* n_runs);
 
-/* Free the plan's device buffers (synchronises the device first).  NULL is a no-op. */
+/* Free the plan's device buffers (synchronises the device first).  NULL is a
+ * no-op.  The plan is built once per batch of page tables and reused across
+ * runs (e.g. layers), as the metadata builder reviewed on the vLLM-metax page
+ * "[WIP] support flashinfer_mla" does; this ends that lifetime. */
 void pkvmla_plan_destroy(pkvmla_plan plan);
 
-/* Message of the calling thread's last failed call ("" if none). */
+/* Message of the calling thread's last failed call ("" if none).  Every
+ * unsupported request fails with a status and this message instead of falling
+ * back to another path: the backend-selection reviews on the vLLM-metax page
+ * "[WIP] support flashinfer_mla" ask for a hard error when the MLA backend
+ * cannot serve a configuration. */
 const char* pkvmla_last_error(void);
 
 /* Kernel configuration used for num_heads (values the schedule depends on):

@@ -24,6 +24,7 @@ from .generate import (  # noqa: F401
     make_config,
     config_lens,
     stress_variant,
+    stress_variant_cascade,
     poison_unreferenced,
     permute_pages,
     STRESS_KINDS,

@@ -338,18 +338,37 @@ def stress_variant(inp: FlatInputs, kind: str, seed: int = 1234) -> FlatInputs:
     return inp.replace(name=f"{inp.name}/{kind}", q_nope=q_nope, q_pe=q_pe, ckv=ckv, kpe=kpe)
 
 
-def poison_unreferenced(inp: FlatInputs) -> FlatInputs:
-    """Copy of ``inp`` where every pool slot that no request attends holds NaN bits:
-    unused pages, the tail slots of each last page and any extra trailing pages."""
+def _csr_rows(indptr, indices, length: int, i: int, page_size: int):
+    """(page, slot) of the first ``length`` tokens of page list i of a CSR table."""
+    t = np.arange(int(length))
+    return indices[int(indptr[i]) + t // page_size], t % page_size
+
+
+def _cascade_rows(cas: "CascadeInputs", b: int):
+    """(page, slot) of request b's tokens: its group's prefix, then its suffix."""
+    g = cas.group_of(b)
+    pp, ps_ = _csr_rows(cas.prefix_indptr, cas.prefix_indices, cas.prefix_lens[g], g,
+                        cas.page_size)
+    sp, ss = _csr_rows(cas.kv_indptr, cas.kv_indices, cas.kv_lens[b], b, cas.page_size)
+    return np.concatenate([pp, sp]), np.concatenate([ps_, ss])
+
+
+def poison_unreferenced(inp):
+    """Copy of ``inp`` (flat or cascade) where every pool slot that no request
+    attends holds NaN bits: unused pages, the tail slots of each last page and
+    any extra trailing pages."""
     used = np.zeros((inp.num_pages, inp.page_size), dtype=bool)
     for b in range(inp.batch):
-        pages, slots = _token_rows(inp, b)
+        if isinstance(inp, CascadeInputs):
+            pages, slots = _cascade_rows(inp, b)
+        else:
+            pages, slots = _token_rows(inp, b)
         used[pages, slots] = True
     ckv = inp.ckv.copy()
     kpe = inp.kpe.copy()
     ckv[~used] = 0x7FC0
     kpe[~used] = 0x7FC0
-    return inp.replace(name=inp.name + "/poison", ckv=ckv, kpe=kpe)
+    return dataclasses.replace(inp, name=inp.name + "/poison", ckv=ckv, kpe=kpe)
 
 
 def permute_pages(inp, seed: int = 99):
@@ -365,3 +384,72 @@ def permute_pages(inp, seed: int = 99):
     if isinstance(inp, CascadeInputs):
         kw["prefix_indices"] = pi[inp.prefix_indices]
     return dataclasses.replace(inp, **kw)
+
+
+def stress_variant_cascade(cas: CascadeInputs, kind: str, seed: int = 4321) -> CascadeInputs:
+    """Cascade counterpart of :func:`stress_variant`.  The prefix pages are
+    shared by a group's requests, so the structured rows follow the group:
+
+    qx8        q scaled by 8 (exact in bf16).
+    needle     request b (non-empty suffix) gets one suffix token whose rows are
+               a scaled copy of head b % H's query (logit near +20); each
+               group's prefix gets one such token for its first request.
+    increasing every request of group g shares a q_pe direction w_g; kpe rows
+               grow along the position (prefix, then suffix), so the largest
+               logit moves forward with every tile of both levels.
+    negative   kpe rows ~ -30 w_g everywhere: logits near -80.
+    """
+    rng = np.random.default_rng(seed)
+    scale = cas.sm_scale if cas.sm_scale is not None else 1.0 / math.sqrt(cas.ckv_dim + cas.kpe_dim)
+    q_nope, q_pe = cas.q_nope.copy(), cas.q_pe.copy()
+    ckv, kpe = cas.ckv.copy(), cas.kpe.copy()
+    ps = cas.page_size
+    G = cas.num_groups
+    if kind == "qx8":
+        q_nope = f32_to_bf16_bits(_bf16_bits_to_f32(q_nope) * np.float32(8))
+        q_pe = f32_to_bf16_bits(_bf16_bits_to_f32(q_pe) * np.float32(8))
+    elif kind == "needle":
+        def plant(b, h, page, slot):
+            qn = _bf16_bits_to_f32(q_nope[b, h]).astype(np.float64)
+            qp = _bf16_bits_to_f32(q_pe[b, h]).astype(np.float64)
+            beta = 20.0 / (scale * (qn @ qn + qp @ qp))
+            ckv[page, slot] = f32_to_bf16_bits((beta * qn).astype(np.float32))
+            kpe[page, slot] = f32_to_bf16_bits((beta * qp).astype(np.float32))
+        for g in range(G):
+            b0 = int(cas.group_req_indptr[g])
+            if cas.prefix_lens[g] > 0 and b0 < int(cas.group_req_indptr[g + 1]):
+                pp, sl = _csr_rows(cas.prefix_indptr, cas.prefix_indices, cas.prefix_lens[g], g, ps)
+                j = int(rng.integers(0, len(pp)))
+                plant(b0, 0, pp[j], sl[j])
+        for b in range(cas.batch):
+            if cas.kv_lens[b] > 0:
+                sp, sl = _csr_rows(cas.kv_indptr, cas.kv_indices, cas.kv_lens[b], b, ps)
+                j = int(rng.integers(0, len(sp)))
+                plant(b, b % cas.num_heads, sp[j], sl[j])
+    elif kind in ("increasing", "negative"):
+        for g in range(G):
+            w = rng.standard_normal(cas.kpe_dim).astype(np.float32)
+            reqs = range(int(cas.group_req_indptr[g]), int(cas.group_req_indptr[g + 1]))
+            P = int(cas.prefix_lens[g])
+            span = P + max([int(cas.kv_lens[b]) for b in reqs] or [0])
+
+            def rows_for(pos):
+                if kind == "increasing":
+                    coef = (30.0 / (scale * float(w @ w))) * (pos.astype(np.float32) / max(span, 1))
+                else:
+                    coef = np.full(len(pos), -80.0 / (scale * float(w @ w)), dtype=np.float32)
+                r = coef[:, None] * w[None, :] + rng.standard_normal((len(pos), cas.kpe_dim)).astype(np.float32) * 0.1
+                return f32_to_bf16_bits(r.astype(np.float32))
+            for b in reqs:
+                noise = rng.standard_normal((cas.num_heads, cas.kpe_dim)).astype(np.float32) * 0.05
+                q_pe[b] = f32_to_bf16_bits(w[None, :] + noise)
+                if cas.kv_lens[b] > 0:
+                    sp, sl = _csr_rows(cas.kv_indptr, cas.kv_indices, cas.kv_lens[b], b, ps)
+                    kpe[sp, sl] = rows_for(P + np.arange(len(sp)))
+            if P > 0:
+                pp, sl = _csr_rows(cas.prefix_indptr, cas.prefix_indices, P, g, ps)
+                kpe[pp, sl] = rows_for(np.arange(P))
+    else:
+        raise ValueError(kind)
+    return dataclasses.replace(cas, name=f"{cas.name}/{kind}", q_nope=q_nope, q_pe=q_pe,
+                               ckv=ckv, kpe=kpe)

@@ -57,11 +57,6 @@ def kernel_config(num_heads: int):
                 wg_per_cu=wg_per_cu, fixed_cost=fixed, head_groups=hg, tile=PLAN_TILE)
 
 
-def schedule_lanes(num_cu: int, num_heads: int) -> int:
-    kc = kernel_config(num_heads)
-    return max(1, num_cu * kc["wg_per_cu"] // kc["head_groups"])
-
-
 def flat_items(kv_lens):
     return [(b, b, int(L)) for b, L in enumerate(kv_lens)]
 

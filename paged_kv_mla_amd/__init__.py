@@ -62,7 +62,8 @@ _lib.pkvmla_plan_export.argtypes = [_vp, _i32p, ctypes.c_int64, _i64p]
 _lib.pkvmla_gather.argtypes = [_vp, _vp, _vp, _vp, _vp]
 _lib.pkvmla_gather_rows.argtypes = [_vp, _i64p]
 _lib.pkvmla_plan_set_timing.argtypes = [_vp, ctypes.c_int32]
-_lib.pkvmla_plan_timing.argtypes = [_vp, ctypes.POINTER(ctypes.c_double), _i64p]
+_lib.pkvmla_plan_timing.argtypes = [_vp, ctypes.POINTER(ctypes.c_double),
+                                    ctypes.POINTER(ctypes.c_double), _i64p]
 
 EXPORTED_SYMBOLS = (
     "pkvmla_plan_create", "pkvmla_plan_create_with_capacity", "pkvmla_plan_update",
@@ -103,6 +104,21 @@ def _stream_handle(stream) -> int:
     if stream is None:
         stream = torch.cuda.current_stream()
     return int(stream.cuda_stream)
+
+
+def _check_csr(what: str, indptr: np.ndarray, indices: np.ndarray, lens: np.ndarray) -> None:
+    """Array lengths the C layer trusts (it reads indptr[n] and indices[:indptr[n]])."""
+    if lens.ndim != 1 or indptr.ndim != 1 or indices.ndim != 1:
+        raise ValueError(f"{what}: indptr, indices and lengths must be 1-D")
+    if len(indptr) != len(lens) + 1:
+        raise ValueError(f"{what}: indptr needs {len(lens) + 1} entries (got {len(indptr)})")
+    if len(indptr) and indptr[-1] > len(indices):
+        raise ValueError(f"{what}: indptr[-1] = {indptr[-1]} exceeds the {len(indices)} indices")
+
+
+def _current_device() -> int:
+    import torch
+    return int(torch.cuda.current_device()) if torch.cuda.is_available() else 0
 
 
 def kernel_config(num_heads: int) -> dict:
@@ -159,10 +175,14 @@ class Plan:
     :func:`plan` or :func:`plan_cascade`; run it with :meth:`run` for every
     set of tensors (e.g. once per layer) that shares the page table."""
 
-    def __init__(self, handle: int, batch: int, num_heads: int):
+    def __init__(self, handle: int, batch: int, num_heads: int, page_size: int = 0,
+                 num_pages: int = 0, device: int = 0):
         self._h = ctypes.c_void_p(handle)
         self.batch = batch
         self.num_heads = num_heads
+        self.page_size = page_size
+        self.num_pages = num_pages
+        self.device = device
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -183,6 +203,8 @@ class Plan:
         given.  Asynchronous on `stream` (default: current stream)."""
         import torch
         B, H = self.batch, self.num_heads
+        # The C layer sees raw pointers only: every bound it cannot check
+        # (device, shape, dtype, pool size) is checked here, before a launch.
         for name, t, shape in (("q_nope", q_nope, (B, H, 512)), ("q_pe", q_pe, (B, H, 64))):
             if tuple(t.shape) != shape or t.dtype != torch.bfloat16 or not t.is_contiguous():
                 raise ValueError(f"{name} must be a contiguous bf16 tensor of shape {shape}")
@@ -193,11 +215,23 @@ class Plan:
             if not ok or t.stride(2) != 1 or t.stride(0) != t.shape[1] * S:
                 raise ValueError(f"{name} must be a bf16 [pages, page_size, {d}] tensor with "
                                  "unit stride in a row and packed rows")
+            if t.shape[0] < self.num_pages or t.shape[1] != self.page_size:
+                raise ValueError(f"{name} holds {t.shape[0]} pages of {t.shape[1]} slots; the "
+                                 f"plan needs >= {self.num_pages} pages of {self.page_size}")
             strides.append(S)
         if out is None:
             out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=q_nope.device)
+        elif tuple(out.shape) != (B, H, 512) or out.dtype != torch.bfloat16 or not out.is_contiguous():
+            raise ValueError(f"out must be a contiguous bf16 tensor of shape {(B, H, 512)}")
         if lse is None:
             lse = torch.empty((B, H), dtype=torch.float32, device=q_nope.device)
+        elif tuple(lse.shape) != (B, H) or lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise ValueError(f"lse must be a contiguous float32 tensor of shape {(B, H)}")
+        for name, t in (("q_nope", q_nope), ("q_pe", q_pe), ("ckv_cache", ckv_cache),
+                        ("kpe_cache", kpe_cache), ("out", out), ("lse", lse)):
+            if not t.is_cuda or t.device.index != self.device:
+                raise ValueError(f"{name} must live on cuda:{self.device}, the plan's device "
+                                 f"(got {t.device})")
         _check(_lib.pkvmla_run_strided(self._h, q_nope.data_ptr(), q_pe.data_ptr(),
                                        ckv_cache.data_ptr(), kpe_cache.data_ptr(), strides[0],
                                        strides[1], out.data_ptr(), lse.data_ptr(),
@@ -212,6 +246,7 @@ class Plan:
         ip, ix, ln = _i32(kv_indptr), _i32(kv_indices), _i32(kv_lens)
         if len(ln) != self.batch or len(ip) != self.batch + 1:
             raise ValueError(f"update needs batch {self.batch} (kv_lens) and batch + 1 (kv_indptr)")
+        _check_csr("kv", ip, ix, ln)
         if ix.size == 0:
             ix = np.zeros(1, np.int32)
         _check(_lib.pkvmla_plan_update(self._h, _ptr(ip), _ptr(ix), _ptr(ln),
@@ -227,11 +262,14 @@ class Plan:
         _check(_lib.pkvmla_plan_set_timing(self._h, 1 if enable else 0))
 
     def kernel_timing(self):
-        """(summed decode-kernel ms, number of timed runs), last 256 runs."""
+        """(summed decode-kernel event ms, summed in-kernel span ms, number of
+        timed runs), over the last 256 runs."""
         ms = ctypes.c_double(0.0)
+        span = ctypes.c_double(0.0)
         n = ctypes.c_int64(0)
-        _check(_lib.pkvmla_plan_timing(self._h, ctypes.byref(ms), ctypes.byref(n)))
-        return float(ms.value), int(n.value)
+        _check(_lib.pkvmla_plan_timing(self._h, ctypes.byref(ms), ctypes.byref(span),
+                                       ctypes.byref(n)))
+        return float(ms.value), float(span.value), int(n.value)
 
     def gather_rows(self) -> int:
         n = ctypes.c_int64(0)
@@ -274,6 +312,7 @@ def plan(kv_indptr, kv_indices, kv_lens, num_heads: int, page_size: int, num_pag
     :meth:`Plan.update` calls with up to that many page ids and fixes its
     launch shapes (for HIP-graph capture of :meth:`Plan.run`)."""
     ip, ix, ln = _i32(kv_indptr), _i32(kv_indices), _i32(kv_lens)
+    _check_csr("kv", ip, ix, ln)
     if ix.size == 0:
         ix = np.zeros(1, np.int32)
     h = ctypes.c_void_p()
@@ -281,7 +320,8 @@ def plan(kv_indptr, kv_indices, kv_lens, num_heads: int, page_size: int, num_pag
         _ptr(ip), _ptr(ix), _ptr(ln), int(len(ln)), int(num_pages), int(num_heads), int(ckv_dim),
         int(kpe_dim), int(page_size), float(sm_scale or 0.0), int(index_capacity),
         _stream_handle(stream) if stream else None, ctypes.byref(h)))
-    return Plan(h.value, int(len(ln)), int(num_heads))
+    return Plan(h.value, int(len(ln)), int(num_heads), int(page_size), int(num_pages),
+                _current_device())
 
 
 def plan_cascade(group_req_indptr, prefix_indptr, prefix_indices, prefix_lens,
@@ -292,6 +332,10 @@ def plan_cascade(group_req_indptr, prefix_indptr, prefix_indices, prefix_lens,
     own suffix list (kv_lens may be 0); states are merged by log-sum-exp."""
     g, pip, pix, pl = _i32(group_req_indptr), _i32(prefix_indptr), _i32(prefix_indices), _i32(prefix_lens)
     ip, ix, ln = _i32(kv_indptr), _i32(kv_indices), _i32(kv_lens)
+    if g.ndim != 1 or len(g) != len(pl) + 1:
+        raise ValueError("group_req_indptr needs num_groups + 1 entries")
+    _check_csr("prefix", pip, pix, pl)
+    _check_csr("suffix", ip, ix, ln)
     if pix.size == 0:
         pix = np.zeros(1, np.int32)
     if ix.size == 0:
@@ -301,7 +345,8 @@ def plan_cascade(group_req_indptr, prefix_indptr, prefix_indices, prefix_lens,
         _ptr(g), int(len(pl)), _ptr(pip), _ptr(pix), _ptr(pl), _ptr(ip), _ptr(ix), _ptr(ln),
         int(len(ln)), int(num_pages), int(num_heads), int(ckv_dim), int(kpe_dim), int(page_size),
         float(sm_scale or 0.0), _stream_handle(stream) if stream else None, ctypes.byref(h)))
-    return Plan(h.value, int(len(ln)), int(num_heads))
+    return Plan(h.value, int(len(ln)), int(num_heads), int(page_size), int(num_pages),
+                _current_device())
 
 
 def plan_for(inp, stream=None) -> Plan:

@@ -82,6 +82,7 @@ struct pkvmla_plan_s {
   // optional per-run timing of the decode kernel (events created up front)
   static constexpr int kTimingSlots = 256;
   hipEvent_t ev[2 * kTimingSlots] = {};
+  unsigned long long* d_stamps = nullptr;  // [kTimingSlots][2] kernel span stamps
   int timing = 0;
   int64_t timed_runs = 0;
 };
@@ -166,15 +167,15 @@ int build_plan_schedule(const pkvmla_plan_s* P, const std::vector<pkvmla::WorkIt
 // device tables (one copy on `stream`, then a wait for it: the host staging
 // buffer is local).  Entries past the live ones: wg_indptr repeats its last
 // value (empty lanes), merge records have count 0 (skipped).
-int upload_tables(pkvmla_plan_s* P, const std::vector<int32_t>& seq_indptr,
-                  const std::vector<int32_t>& seq_lens, const std::vector<int32_t>& seq_indices,
-                  hipStream_t stream) {
+int upload_tables(pkvmla_plan_s* P, const pkvmla::Schedule& sched,
+                  const std::vector<int32_t>& seq_indptr, const std::vector<int32_t>& seq_lens,
+                  const std::vector<int32_t>& seq_indices, hipStream_t stream) {
   std::vector<int32_t> host(P->table_ints, 0);
-  const std::vector<int32_t>& wg = P->sched.wg_indptr;
+  const std::vector<int32_t>& wg = sched.wg_indptr;
   for (int32_t l = 0; l <= P->cap_lanes; ++l)
     host[P->off_wg + l] = l < (int32_t)wg.size() ? wg[l] : wg.back();
-  std::copy(P->sched.units.begin(), P->sched.units.end(), host.begin() + P->off_units);
-  std::copy(P->sched.merges.begin(), P->sched.merges.end(), host.begin() + P->off_merges);
+  std::copy(sched.units.begin(), sched.units.end(), host.begin() + P->off_units);
+  std::copy(sched.merges.begin(), sched.merges.end(), host.begin() + P->off_merges);
   std::copy(seq_indptr.begin(), seq_indptr.end(), host.begin() + P->off_sip);
   std::copy(seq_lens.begin(), seq_lens.end(), host.begin() + P->off_sl);
   std::copy(seq_indices.begin(), seq_indices.end(), host.begin() + P->off_si);
@@ -224,7 +225,7 @@ int finish_plan(pkvmla_plan_s* P, const std::vector<pkvmla::WorkItem>& items,
   // (slots <= units)
   const size_t rows = (size_t)P->cap_units * P->num_heads;
   PKVMLA_HIP(hipMalloc(&P->d_part, rows * (pkvmla::kCkvDim * sizeof(uint16_t) + sizeof(float))));
-  return upload_tables(P, seq_indptr, seq_lens, seq_indices, stream);
+  return upload_tables(P, P->sched, seq_indptr, seq_lens, seq_indices, stream);
 }
 
 void free_plan(pkvmla_plan_s* P) {
@@ -233,6 +234,7 @@ void free_plan(pkvmla_plan_s* P) {
     if (e) (void)hipEventDestroy(e);
   if (P->d_tables) (void)hipFree(P->d_tables);
   if (P->d_part) (void)hipFree(P->d_part);
+  if (P->d_stamps) (void)hipFree(P->d_stamps);
   delete P;
 }
 
@@ -373,9 +375,10 @@ int pkvmla_plan_update(pkvmla_plan P, const int32_t* kv_indptr, const int32_t* k
   if ((int64_t)sched.units.size() > (int64_t)P->cap_units * pkvmla::kUnitRecordInts ||
       sched.grid > P->cap_lanes || sched.n_slots > P->cap_units)
     return fail(PKVMLA_EINVAL, "schedule exceeds the plan's capacities");
-  P->sched = std::move(sched);
-  rc = upload_tables(P, sip, sl, si, (hipStream_t)stream);
+  // the plan takes the new schedule only once its tables are on the device
+  rc = upload_tables(P, sched, sip, sl, si, (hipStream_t)stream);
   if (rc) return rc;
+  P->sched = std::move(sched);
   return ok();
 }
 
@@ -501,6 +504,7 @@ int pkvmla_run_strided(pkvmla_plan P, const void* q_nope, const void* q_pe,
   d.score_log2 = (float)((double)P->sm_scale * 1.4426950408889634);
   d.rescale_thr = (float)(8.0 / ((double)P->sm_scale * 1.4426950408889634));
   const int slot_ev = (int)(P->timed_runs % pkvmla_plan_s::kTimingSlots);
+  d.stamps = P->timing ? P->d_stamps + 2 * slot_ev : nullptr;
   if (P->timing) PKVMLA_HIP(hipEventRecord(P->ev[2 * slot_ev], s));
   PKVMLA_HIP(pkvmla::launch_decode(d, s));
   if (P->timing) {
@@ -541,22 +545,43 @@ int pkvmla_plan_set_timing(pkvmla_plan P, int32_t enable) {
     // interval and to the kernels that follow
     for (hipEvent_t& e : P->ev) PKVMLA_HIP(hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
   }
+  if (enable) {
+    // one {earliest start, latest end} pair per timed run, reset here (not per
+    // run: a reset launch would sit between the timed kernels)
+    const size_t n = 2 * (size_t)pkvmla_plan_s::kTimingSlots;
+    if (!P->d_stamps) PKVMLA_HIP(hipMalloc(&P->d_stamps, n * sizeof(unsigned long long)));
+    std::vector<unsigned long long> init(n);
+    for (size_t i = 0; i < n; i += 2) {
+      init[i] = ~0ull;
+      init[i + 1] = 0ull;
+    }
+    PKVMLA_HIP(hipDeviceSynchronize());
+    PKVMLA_HIP(hipMemcpy(P->d_stamps, init.data(), n * sizeof(unsigned long long),
+                         hipMemcpyHostToDevice));
+  }
   P->timing = enable ? 1 : 0;
   P->timed_runs = 0;
   return ok();
 }
 
-int pkvmla_plan_timing(pkvmla_plan P, double* total_ms, int64_t* n_runs) {
-  if (!P || !total_ms || !n_runs) return fail(PKVMLA_EINVAL, "null argument");
+int pkvmla_plan_timing(pkvmla_plan P, double* event_ms, double* span_ms, int64_t* n_runs) {
+  if (!P || !event_ms || !span_ms || !n_runs) return fail(PKVMLA_EINVAL, "null argument");
   PKVMLA_HIP(hipDeviceSynchronize());
   const int64_t n = std::min<int64_t>(P->timed_runs, pkvmla_plan_s::kTimingSlots);
-  double tot = 0.0;
+  double tot = 0.0, span = 0.0;
+  std::vector<unsigned long long> st(2 * (size_t)std::max<int64_t>(n, 1));
+  if (n > 0)
+    PKVMLA_HIP(hipMemcpy(st.data(), P->d_stamps, 2 * n * sizeof(unsigned long long),
+                         hipMemcpyDeviceToHost));
   for (int64_t i = 0; i < n; ++i) {
     float ms = 0.f;
     PKVMLA_HIP(hipEventElapsedTime(&ms, P->ev[2 * i], P->ev[2 * i + 1]));
     tot += ms;
+    // the real-time counter runs at 100 MHz: 1e-5 ms per tick
+    if (st[2 * i + 1] >= st[2 * i]) span += (double)(st[2 * i + 1] - st[2 * i]) * 1e-5;
   }
-  *total_ms = tot;
+  *event_ms = tot;
+  *span_ms = span;
   *n_runs = n;
   return ok();
 }

@@ -65,6 +65,11 @@ constexpr int kRsVAhead = 2;   // dim blocks between a V fragment's LDS read and
                                // (two: the register budget at ten waves, HB = 4)
 constexpr int kRsDBW = 8;      // output-dim blocks of 16 per PV wave (128 dims)
 static_assert(kCopyWaves == 2 * kRsCopyWaves, "each copy wave issues two copy slots' shares");
+// A copy wave keeps at most (kRsRing - 2) tiles of its two slots' copies in
+// flight.  The vmcnt counter of a wave holds at most 63 operations: with more
+// outstanding, an exact s_waitcnt (including the last one before the
+// workgroup retires) no longer covers every copy still writing LDS.
+static_assert((kRsRing - 2) * 2 * kCopiesPerWave < 64, "copies in flight exceed the vmcnt range");
 
 // LDS layout
 constexpr int kXpOff = kRsRing * kStageBytes;         // P^T exchange: [parity][hb] 1 KB blocks
@@ -112,7 +117,7 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
                      const int32_t* __restrict__ wg_indptr_g, const int32_t* __restrict__ units_g,
                      const int32_t* __restrict__ seq_indices_g, int H, int n_hg, int n_lanes,
                      int log2_ps, float sm_scale, float C, float thr, int cs_arg,
-                     int ks_arg) {
+                     int ks_arg, unsigned long long* stamps) {
   const int cs = PACKED ? kCkvDim * 2 : cs_arg;
   const int ks = PACKED ? kKpeDim * 2 : ks_arg;
   const idx_ptr wg_indptr = (idx_ptr)wg_indptr_g;
@@ -131,10 +136,14 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
   // apart, which the dispatcher places on the same XCD.
   const int hg = (int)(blockIdx.x >> 3) % n_hg;
   const int sl = (int)(blockIdx.x / (8 * n_hg)) * 8 + (int)(blockIdx.x & 7);
-  if (sl >= n_lanes) return;
+  const bool stamp_lane = stamps && (threadIdx.x & 63) == 0;
+  if (stamp_lane && wave == 0) stamp_start(stamps);
+  if (sl >= n_lanes || wg_indptr[sl] >= wg_indptr[sl + 1]) {
+    if (stamp_lane) stamp_end(stamps);
+    return;
+  }
   const int u_begin = wg_indptr[sl];
   const int u_end = wg_indptr[sl + 1];
-  if (u_begin >= u_end) return;
   const char* ckv = reinterpret_cast<const char*>(ckv_cache);
   const char* kpe = reinterpret_cast<const char*>(kpe_cache);
 
@@ -277,6 +286,7 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
       }
       lds_barrier();
     }
+    if (stamp_lane) stamp_end(stamps);
   } else if (wave < HB + kRsPvWaves) {
     // ======================= PV and epilogue role =======================
     const int lane0 = threadIdx.x & 63;
@@ -418,6 +428,7 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
     }
+    if (stamp_lane) stamp_end(stamps);
   } else {
     // ======================= copy role =======================
     // copy wave cw issues copy slots 2cw and 2cw+1 of every tile (18 copies;
@@ -473,6 +484,7 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
       lds_barrier();
     }
     wait_vmcnt<0>();
+    if (stamp_lane) stamp_end(stamps);
   }
 }
 
@@ -492,7 +504,7 @@ bool launch_decode_rs(const DecodeParams& p, hipStream_t stream, hipError_t* err
 #define PKVMLA_RS_ARGS                                                                   \
   p.q_nope, p.q_pe, p.ckv, p.kpe, p.out, p.lse, p.part_o, p.part_lse, p.wg_indptr, p.units, \
       p.seq_indices, p.num_heads, p.head_groups, p.n_lanes, p.log2_ps, p.sm_scale,     \
-      p.score_log2, p.rescale_thr, p.ckv_stride, p.kpe_stride
+      p.score_log2, p.rescale_thr, p.ckv_stride, p.kpe_stride, p.stamps
 #define PKVMLA_RS_LAUNCH2(HBV, PK)                                                             \
   if (big) mla_decode_rs_kernel<true, HBV, PK><<<grid, block, 0, stream>>>(PKVMLA_RS_ARGS);    \
   else mla_decode_rs_kernel<false, HBV, PK><<<grid, block, 0, stream>>>(PKVMLA_RS_ARGS);

@@ -143,6 +143,16 @@ __device__ __forceinline__ int lane_id_fresh() {
   return x;
 }
 
+// Kernel span stamps for timing runs (stamps != null): the earliest start and
+// the latest end over the launch's waves on the 100 MHz real-time counter.
+// One lane per caller; the atomics need no return value.
+__device__ __forceinline__ void stamp_start(unsigned long long* stamps) {
+  if (stamps) atomicMin(stamps, (unsigned long long)__builtin_amdgcn_s_memrealtime());
+}
+__device__ __forceinline__ void stamp_end(unsigned long long* stamps) {
+  if (stamps) atomicMax(stamps + 1, (unsigned long long)__builtin_amdgcn_s_memrealtime());
+}
+
 // Workgroup barrier that orders LDS traffic (every LDS access of this wave has
 // completed) without waiting for outstanding vector-memory loads: tile copies
 // in flight keep flying across it.  The memory clobber keeps the compiler from

@@ -50,6 +50,8 @@ struct DecodeParams {
   float sm_scale;
   float score_log2;          // sm_scale * log2(e)
   float rescale_thr;         // raw-score margin before the running max moves (8 / score_log2)
+  unsigned long long* stamps;  // null, or {earliest start, latest end} of the launch's
+                               // waves on the 100 MHz real-time clock (timing runs only)
 };
 
 struct MergeParams {

@@ -5,8 +5,6 @@
 
 #include <hip/hip_runtime.h>
 #include <math.h>
-#include <stdio.h>
-#include <stdlib.h>
 
 #include "pkvmla_tiles.h"
 
@@ -146,16 +144,6 @@ bool kernel_config_for(int num_heads, KernelConfig* cfg) {
     case 64: *cfg = KernelConfig{8, 16, 4, 1, 4, 1}; break;
     case 128: *cfg = KernelConfig{8, 16, 4, 1, 4, 2}; break;
     default: return false;
-  }
-  // Experiments only: PKVMLA_CONFIG="waves,heads_per_wave,stages,wg_per_cu,fixed,head_groups"
-  // overrides the table when the role-split kernel has that shape for num_heads.
-  if (const char* e = getenv("PKVMLA_CONFIG")) {
-    KernelConfig c{};
-    if (sscanf(e, "%d,%d,%d,%d,%d,%d", &c.waves, &c.heads_per_wave, &c.stages, &c.wg_per_cu,
-               &c.fixed_cost, &c.head_groups) == 6 &&
-        c.head_groups >= 1 && c.wg_per_cu >= 1 && c.fixed_cost >= 0 && c.stages == 4 &&
-        decode_rs_head_blocks(c.waves, c.heads_per_wave, num_heads, c.head_groups))
-      *cfg = c;
   }
   return true;
 }

@@ -7,8 +7,8 @@
 // after workgroup up to a cost cap; the cap is the smallest value at or above
 // the even share ceil(C / W) for which the walk needs at most W workgroups,
 // so the split overhead never piles up on the last workgroup.  Requests cut
-// into more than one unit write fp32 partial states into consecutive slots and
-// get one merge row.
+// into more than one unit write partial states (bf16 outputs normalized by
+// their own row sums, fp32 lse) into consecutive slots and get one merge row.
 #include <stdint.h>
 
 #include <algorithm>

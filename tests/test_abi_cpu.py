@@ -199,3 +199,69 @@ int main(void) {
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
     assert r.stdout.startswith("tile 32 waves 8 units")
+
+
+# ------------------------------------------- binding-side argument checks
+# The C layer sees raw pointers: sizes, devices and dtypes it cannot check are
+# checked by the binding before any call (no GPU needed to see them refused).
+@pytest.mark.parametrize("kw,msg", [
+    (dict(kv_indptr=[0, 2]), "indptr needs 3"),             # one entry short
+    (dict(kv_indptr=[0, 2, 3, 3]), "indptr needs 3"),       # one entry too many
+    (dict(kv_indices=[0, 1]), "exceeds the 2 indices"),     # indptr[-1] = 3 > 2 ids
+])
+def test_plan_rejects_short_arrays(kw, msg):
+    with pytest.raises(ValueError, match=msg):
+        pk.plan(**_flat_args(**kw))
+
+
+def test_plan_cascade_rejects_short_arrays():
+    base = dict(group_req_indptr=[0, 2], prefix_indptr=[0, 1], prefix_indices=[0],
+                prefix_lens=[16], kv_indptr=[0, 1, 1], kv_indices=[1], kv_lens=[3, 0],
+                num_heads=16, page_size=16, num_pages=4)
+    for kw, msg in [(dict(group_req_indptr=[0, 1, 2]), "num_groups"),
+                    (dict(prefix_indptr=[0, 2]), "exceeds"),
+                    (dict(kv_indptr=[0, 1]), "indptr needs"),
+                    (dict(kv_indices=[]), "exceeds")]:
+        a = dict(base)
+        a.update(kw)
+        with pytest.raises(ValueError, match=msg):
+            pk.plan_cascade(**a)
+
+
+def _fake_plan(B=2, H=16, ps=16, P=4):
+    # handle 0: never passed to the library (every check below fails first)
+    return pk.Plan(0, B, H, ps, P, 0)
+
+
+def _tensors(B=2, H=16, ps=16, P=4, **over):
+    import torch
+    t = dict(q_nope=torch.zeros(B, H, 512, dtype=torch.bfloat16),
+             q_pe=torch.zeros(B, H, 64, dtype=torch.bfloat16),
+             ckv_cache=torch.zeros(P, ps, 512, dtype=torch.bfloat16),
+             kpe_cache=torch.zeros(P, ps, 64, dtype=torch.bfloat16))
+    t.update(over)
+    return t
+
+
+def test_run_rejects_bad_tensors_before_launch():
+    import torch
+    plan = _fake_plan()
+    cases = [
+        (dict(q_nope=torch.zeros(2, 16, 512, dtype=torch.float16)), "q_nope"),
+        (dict(q_pe=torch.zeros(2, 8, 64, dtype=torch.bfloat16)), "q_pe"),
+        (dict(ckv_cache=torch.zeros(3, 16, 512, dtype=torch.bfloat16)), "pages"),   # pool too small
+        (dict(kpe_cache=torch.zeros(4, 8, 64, dtype=torch.bfloat16)), "pages"),     # page size
+        (dict(out=torch.zeros(2, 16, 256, dtype=torch.bfloat16)), "out"),
+        (dict(lse=torch.zeros(2, 16, dtype=torch.float16)), "lse"),
+        (dict(), "cuda"),                                                          # CPU tensors
+    ]
+    for over, msg in cases:
+        t = _tensors()
+        out, lse = over.pop("out", None), over.pop("lse", None)
+        t.update(over)
+        if out is None:
+            out = torch.zeros(2, 16, 512, dtype=torch.bfloat16)
+        if lse is None:
+            lse = torch.zeros(2, 16, dtype=torch.float32)
+        with pytest.raises(ValueError, match=msg):
+            plan.run(t["q_nope"], t["q_pe"], t["ckv_cache"], t["kpe_cache"], out=out, lse=lse)
