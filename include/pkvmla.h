@@ -162,6 +162,22 @@ int pkvmla_run_strided(pkvmla_plan plan, const void* q_nope, const void* q_pe,
                        const void* ckv_cache, const void* kpe_cache, int64_t ckv_row_stride,
                        int64_t kpe_row_stride, void* out, float* lse, void* stream);
 
+/* pkvmla_run for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * split workspace the decode and merge kernels use for partial outputs is a
+ * static device array of the library (64 MiB per device, held from the
+ * library's first use on a device until the process ends) instead of the
+ * plan's own buffer.  The call itself allocates nothing; its address lookup on
+ * a device happens once, at the first call on that device.  Arguments,
+ * layouts and results as pkvmla_run (packed caches), bitwise equal to
+ * pkvmla_run of the same plan and inputs.  Every call on one device shares
+ * that device's array: calls that overlap on one device (two streams, or two
+ * threads) race and must be ordered by the caller.  PKVMLA_EUNSUPPORTED when
+ * the plan's partial states (slots x num_heads x 1028 bytes) exceed 64 MiB. */
+int pkvmla_run_noalloc(pkvmla_plan plan, const void* q_nope, const void* q_pe,
+                       const void* ckv_cache, const void* kpe_cache, void* out, float* lse,
+                       void* stream);
+
 /* Kernel timing for benchmarks.  With enable != 0, every later pkvmla_run
  * records a HIP event pair on its stream around the fused decode kernel, and
  * the kernel itself records the earliest start and the latest end of its

@@ -49,6 +49,7 @@ _lib.pkvmla_plan_create_with_capacity.argtypes = [_i32p, _i32p, _i32p, ctypes.c_
                                                   ctypes.c_int64, _vp, ctypes.POINTER(_vp)]
 _lib.pkvmla_plan_update.argtypes = [_vp, _i32p, _i32p, _i32p, _vp]
 _lib.pkvmla_run.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.pkvmla_run_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.pkvmla_run_strided.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int64, ctypes.c_int64,
                                     _vp, _vp, _vp]
 _lib.pkvmla_plan_destroy.argtypes = [_vp]
@@ -70,6 +71,7 @@ EXPORTED_SYMBOLS = (
     "pkvmla_plan_create_cascade", "pkvmla_run", "pkvmla_run_strided", "pkvmla_plan_destroy",
     "pkvmla_last_error", "pkvmla_kernel_config", "pkvmla_schedule_host", "pkvmla_plan_export",
     "pkvmla_gather", "pkvmla_gather_rows", "pkvmla_plan_set_timing", "pkvmla_plan_timing",
+    "pkvmla_run_noalloc",
 )
 
 OK, EINVAL, EUNSUPPORTED, EHIP, ENOMEM = 0, 1, 2, 3, 4
@@ -256,6 +258,12 @@ class Plan:
                  stream: int) -> None:
         """Raw-pointer form of :meth:`run` (no checks beyond the library's)."""
         _check(_lib.pkvmla_run(self._h, q_nope, q_pe, ckv, kpe, out, lse, stream))
+
+    def run_noalloc_ptrs(self, q_nope: int, q_pe: int, ckv: int, kpe: int, out: int, lse: int,
+                         stream: int) -> None:
+        """Raw-pointer form of the allocation-free run (the split workspace is
+        the library's static per-device scratch; packed caches)."""
+        _check(_lib.pkvmla_run_noalloc(self._h, q_nope, q_pe, ckv, kpe, out, lse, stream))
 
     def set_timing(self, enable: bool = True) -> None:
         """Record HIP events around the decode kernel of every later run."""

@@ -452,9 +452,64 @@ int pkvmla_plan_create_cascade(const int32_t* group_req_indptr, int32_t num_grou
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+// Bytes of split workspace the plan's runs can touch: partial outputs (bf16)
+// and lse (fp32) for every partial slot a schedule of this plan can use.
+size_t workspace_bytes(const pkvmla_plan_s* P) {
+  const size_t slots = P->fixed_launch ? (size_t)P->cap_units : (size_t)P->sched.n_slots;
+  return slots * (size_t)P->num_heads * (pkvmla::kCkvDim * sizeof(uint16_t) + sizeof(float));
+}
+
+int run_impl(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* ckv_cache,
+             const void* kpe_cache, int64_t ckv_row_stride, int64_t kpe_row_stride, void* out,
+             float* lse, void* stream, void* workspace, size_t workspace_slots);
+
+}  // namespace
+
+extern "C" {
+
 int pkvmla_run_strided(pkvmla_plan P, const void* q_nope, const void* q_pe,
                        const void* ckv_cache, const void* kpe_cache, int64_t ckv_row_stride,
                        int64_t kpe_row_stride, void* out, float* lse, void* stream) {
+  if (!P) return fail(PKVMLA_EINVAL, "null plan");
+  return run_impl(P, q_nope, q_pe, ckv_cache, kpe_cache, ckv_row_stride, kpe_row_stride, out,
+                  lse, stream, P->d_part, (size_t)P->cap_units);
+}
+
+int pkvmla_run_noalloc(pkvmla_plan P, const void* q_nope, const void* q_pe,
+                       const void* ckv_cache, const void* kpe_cache, void* out, float* lse,
+                       void* stream) {
+  if (!P) return fail(PKVMLA_EINVAL, "null plan");
+  const size_t need = workspace_bytes(P);
+  if (need > pkvmla::kScratchBytes)
+    return fail(PKVMLA_EUNSUPPORTED,
+                "the plan's split workspace needs %zu bytes, more than the %zu bytes of static "
+                "scratch (use pkvmla_run)",
+                need, pkvmla::kScratchBytes);
+  int dev = -1;
+  PKVMLA_HIP(hipGetDevice(&dev));
+  if (dev != P->device)
+    return fail(PKVMLA_EINVAL, "plan was built on device %d, current device is %d", P->device,
+                dev);
+  void* ws = nullptr;
+  PKVMLA_HIP(pkvmla::scratch_address(dev, &ws));
+  // the scratch holds as many slots as fit; the plan's need is within that
+  const size_t slots = pkvmla::kScratchBytes /
+                       ((size_t)P->num_heads * (pkvmla::kCkvDim * sizeof(uint16_t) + sizeof(float)));
+  return run_impl(P, q_nope, q_pe, ckv_cache, kpe_cache, pkvmla::kCkvDim, pkvmla::kKpeDim, out,
+                  lse, stream, ws, slots);
+}
+
+}  // extern "C"
+
+namespace {
+
+int run_impl(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* ckv_cache,
+             const void* kpe_cache, int64_t ckv_row_stride, int64_t kpe_row_stride, void* out,
+             float* lse, void* stream, void* workspace, size_t workspace_slots) {
   if (!P) return fail(PKVMLA_EINVAL, "null plan");
   if (!q_nope || !q_pe || !ckv_cache || !kpe_cache || !out || !lse)
     return fail(PKVMLA_EINVAL, "null tensor pointer");
@@ -476,8 +531,9 @@ int pkvmla_run_strided(pkvmla_plan P, const void* q_nope, const void* q_pe,
     return fail(PKVMLA_EINVAL, "plan was built on device %d, current device is %d", P->device,
                 dev);
   hipStream_t s = (hipStream_t)stream;
-  const size_t part_o_elems = (size_t)P->cap_units * P->num_heads * pkvmla::kCkvDim;
-  uint16_t* part_o = static_cast<uint16_t*>(P->d_part);
+  // workspace layout: part_o bf16 [slots][H][512], then part_lse fp32 [slots][H]
+  const size_t part_o_elems = workspace_slots * P->num_heads * pkvmla::kCkvDim;
+  uint16_t* part_o = static_cast<uint16_t*>(workspace);
   pkvmla::DecodeParams d{};
   d.q_nope = static_cast<const uint16_t*>(q_nope);
   d.q_pe = static_cast<const uint16_t*>(q_pe);
@@ -528,6 +584,10 @@ int pkvmla_run_strided(pkvmla_plan P, const void* q_nope, const void* q_pe,
   }
   return ok();
 }
+
+}  // namespace
+
+extern "C" {
 
 int pkvmla_run(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* ckv_cache,
                const void* kpe_cache, void* out, float* lse, void* stream) {

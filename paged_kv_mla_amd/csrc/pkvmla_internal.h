@@ -73,6 +73,12 @@ struct GatherParams {
   int32_t log2_ps;
 };
 
+// Static split workspace of pkvmla_run_noalloc: its size, and its address on
+// a device (looked up once per device, with that device current).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+hipError_t scratch_address(int device, void** ptr);
+
 int decode_grid(int n_lanes, int head_groups);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 // Role-split kernel (16, 32 or 64 heads per workgroup, one or more head

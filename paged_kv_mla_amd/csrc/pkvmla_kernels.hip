@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <mutex>
+
 #include "pkvmla_tiles.h"
 
 namespace pkvmla {
@@ -146,6 +148,41 @@ bool kernel_config_for(int num_heads, KernelConfig* cfg) {
     default: return false;
   }
   return true;
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch for callers that cannot allocate.  pkvmla_run_noalloc keeps
+// the split workspace (partial outputs and their lse) here instead of in the
+// plan's own buffer.  Each device that loads the library holds one copy until
+// the process ends; runs on one device share it (calls that overlap on one
+// device race).  The host never passes `scratch` itself to a kernel: in host
+// code that name is a stand-in, not a device address.  Its address on each
+// device comes from hipGetSymbolAddress, once per device, with that device
+// current.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t scratch_address(int device, void** ptr) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != device) return hipErrorInvalidDevice;  // the caller makes it current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[device] = p;
+  }
+  *ptr = g_scratch_ptr[device];
+  return hipSuccess;
 }
 
 int decode_grid(int n_lanes, int head_groups) {
