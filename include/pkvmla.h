@@ -116,6 +116,28 @@ int pkvmla_plan_create_with_capacity(const int32_t* kv_indptr, const int32_t* kv
 int pkvmla_plan_update(pkvmla_plan plan, const int32_t* kv_indptr, const int32_t* kv_indices,
                        const int32_t* kv_lens, void* stream);
 
+/* Build a plan in which request b brings qo_len(b) = qo_indptr[b+1] - qo_indptr[b]
+ * new query tokens instead of one (speculative or multi-token decode, and the
+ * prefill/decode mixes of the "[V1][Core] FlashInfer attention backend for V1"
+ * page, where one batched wrapper serves requests with one and with several
+ * query tokens).  Attention is causal among a request's new tokens: the new
+ * tokens are the last qo_len(b) of its kv_lens[b] tokens, and query token j
+ * (0-based) sits at position kv_lens[b] - qo_len(b) + j and attends the tokens
+ * 0 .. that position.  With qo_len = 1 everywhere this is pkvmla_plan_create.
+ *   qo_indptr host int32[batch+1]: qo_indptr[0] == 0, qo_len(b) >= 1 and
+ *   qo_len(b) <= kv_lens[b].  Other arguments as pkvmla_plan_create.
+ * The run's query, output and lse tensors have one row per query token:
+ * q_nope [qo_indptr[batch], num_heads, 512], q_pe [.., 64], out [.., 512],
+ * lse [qo_indptr[batch], num_heads], row qo_indptr[b] + j for token j of b.
+ * Each row is scheduled as its own work item over request b's pages, so the
+ * rows of one request read its KV tiles once each (the rows of a request run
+ * on neighbouring lanes).  Plans of this kind take no page-table update
+ * (PKVMLA_EUNSUPPORTED). */
+int pkvmla_plan_create_qo(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                          const int32_t* kv_indices, const int32_t* kv_lens, int32_t batch,
+                          int32_t num_pages, int32_t num_heads, int32_t ckv_dim, int32_t kpe_dim,
+                          int32_t page_size, float sm_scale, void* stream, pkvmla_plan* out);
+
 /* Build a two-level (cascade) plan.  Requests are partitioned into
  * num_groups contiguous groups by group_req_indptr (host int32[G+1], from 0
  * to batch).  Group g's shared prefix is prefix_lens[g] tokens in pages
@@ -234,7 +256,8 @@ int pkvmla_schedule_host(const int32_t* items, int32_t n_items, int32_t batch,
  *            fixed_cost, grid, n_units, n_merges, n_slots
  *   [16..31] header 2: num_seqs, n_indices, num_cu, sm_scale (float bits),
  *            is_cascade, num_groups, head_groups, launched workgroups,
- *            fixed launch shapes (0/1), page-id capacity, 0...
+ *            fixed launch shapes (0/1), page-id capacity, several query tokens
+ *            per request (0/1), number of requests of such a plan, 0...
  *   then wg_indptr[grid+1], units[n_units*8], merges[n_merges*4],
  *   seq_indptr[num_seqs+1], seq_lens[num_seqs], seq_indices[n_indices].
  *   The unit records are those of pkvmla_schedule_host with their last two

@@ -21,6 +21,7 @@ from .generate import (  # noqa: F401
     f32_to_bf16_bits,
     make_flat,
     make_cascade,
+    make_qo,
     make_config,
     config_lens,
     stress_variant,

@@ -79,6 +79,8 @@ class FlatInputs:
     sm_scale: Optional[float] = None  # None -> 1/sqrt(512 + 64)
     ckv_dim: int = CKV_DIM
     kpe_dim: int = KPE_DIM
+    # several new query tokens per request: q rows qo_indptr[b] .. qo_indptr[b+1]
+    qo_indptr: Optional[np.ndarray] = None
 
     @property
     def total_tokens(self) -> int:
@@ -208,6 +210,24 @@ def make_flat(name: str, seed: int, batch: int, num_heads: int, page_size: int,
                       page_size=page_size, num_pages=num_pages, kv_lens=kv_lens,
                       kv_indptr=indptr, kv_indices=indices, q_nope=q_nope, q_pe=q_pe,
                       ckv=ckv, kpe=kpe, sm_scale=sm_scale)
+
+
+def make_qo(name: str, seed: int, batch: int, num_heads: int, page_size: int, lens,
+            qo_lens, pool_pages: Optional[int] = None,
+            sm_scale: Optional[float] = None) -> FlatInputs:
+    """Flat paged batch whose request b brings qo_lens[b] new query tokens
+    (its last qo_lens[b] tokens); q_nope/q_pe hold one row per query token."""
+    base = make_flat(name, seed, batch, num_heads, page_size, lens, pool_pages=pool_pages,
+                     sm_scale=sm_scale)
+    qo = np.asarray(qo_lens, dtype=np.int32)
+    assert qo.shape == (batch,) and np.all(qo >= 1) and np.all(qo <= base.kv_lens)
+    qo_indptr = np.zeros(batch + 1, dtype=np.int32)
+    qo_indptr[1:] = np.cumsum(qo)
+    rng = np.random.default_rng(seed + 7919)
+    T = int(qo_indptr[-1])
+    q_nope = _normal_bf16(rng, (T, num_heads, CKV_DIM))
+    q_pe = _normal_bf16(rng, (T, num_heads, KPE_DIM))
+    return base.replace(q_nope=q_nope, q_pe=q_pe, qo_indptr=qo_indptr)
 
 
 def make_cascade(name: str, seed: int, batch: int, num_heads: int, page_size: int,

@@ -25,6 +25,10 @@ Parity pins (all in tests/test_oracle_*.py, CPU only):
                               (L=1, equal rows, q=0), golden hand-derived values.
   merge_states              : split-then-merge equals unsplit; identity state.
   attend_cascade            : equals attend_flat on the concatenated page list.
+  attend_qo                 : torch fp64 SDPA with an explicit position mask,
+                              python-float fsum brute force, reduces to
+                              attend_flat for one query token, last query
+                              token equals full (unmasked) attention.
   gather_ref                : closed-form address walk vs an independent index
                               construction; permutation invariance.
   schedule_ref              : coverage/uniqueness invariants and hand-worked
@@ -42,6 +46,7 @@ from .mla_decode import (  # noqa: F401
     attend_flat_split,
     merge_states,
     attend_cascade,
+    attend_qo,
     EMPTY_LSE,
 )
 from .schedule_ref import schedule_ref, kernel_config, PLAN_TILE  # noqa: F401

@@ -168,3 +168,38 @@ def attend_cascade(q_nope, q_pe, ckv, kpe, page_size,
             s1 = attend_rows(q, k, v, scale)
             out[b], lse[b] = merge_states([s0, s1])
     return out, lse
+
+
+def attend_qo(q_nope, q_pe, ckv, kpe, qo_indptr, kv_indptr, kv_indices, kv_lens, page_size,
+              sm_scale=None):
+    """Several new query tokens per request, causal among them.
+
+    Request b brings n_b = qo_indptr[b+1] - qo_indptr[b] new query tokens; they
+    are the last n_b of its kv_lens[b] tokens.  Query row qo_indptr[b] + j sits
+    at position kv_lens[b] - n_b + j and attends exactly the tokens at positions
+    0 .. that position (scores of later positions masked to -inf before the
+    softmax).  q_nope [T, H, ckv_dim], q_pe [T, H, kpe_dim] with
+    T = qo_indptr[B].  Returns out float64 [T, H, ckv_dim] and lse [T, H]."""
+    T, H, dc = q_nope.shape
+    dr = q_pe.shape[2]
+    scale = default_sm_scale(dc, dr) if sm_scale is None else float(sm_scale)
+    out = np.zeros((T, H, dc))
+    lse = np.zeros((T, H))
+    for b in range(len(kv_lens)):
+        n = int(qo_indptr[b + 1]) - int(qo_indptr[b])
+        L = int(kv_lens[b])
+        pages, slots = token_pages(kv_indptr, kv_indices, L, b, page_size)
+        c = bf16_to_f64(ckv[pages, slots])
+        k = np.concatenate([c, bf16_to_f64(kpe[pages, slots])], axis=1)   # [L, 576]
+        positions = np.arange(L)
+        for j in range(n):
+            row = int(qo_indptr[b]) + j
+            q = np.concatenate([bf16_to_f64(q_nope[row]), bf16_to_f64(q_pe[row])], axis=1)
+            s = scale * (q @ k.T)                                           # [H, L]
+            s = np.where(positions[None, :] <= L - n + j, s, -np.inf)
+            m = s.max(axis=1)
+            e = np.exp(s - m[:, None])
+            z = e.sum(axis=1)
+            out[row] = (e @ c) / z[:, None]
+            lse[row] = m + np.log(z)
+    return out, lse

@@ -61,6 +61,18 @@ def flat_items(kv_lens):
     return [(b, b, int(L)) for b, L in enumerate(kv_lens)]
 
 
+def qo_items(qo_indptr, kv_lens):
+    """One item per query row of a plan with several new tokens per request:
+    row qo_indptr[b] + j over request b's pages, causal length
+    kv_lens[b] - n_b + 1 + j (its position plus one)."""
+    items = []
+    for b in range(len(kv_lens)):
+        n = int(qo_indptr[b + 1]) - int(qo_indptr[b])
+        for j in range(n):
+            items.append((int(qo_indptr[b]) + j, b, int(kv_lens[b]) - n + 1 + j))
+    return items
+
+
 def cascade_items(group_req_indptr, prefix_lens, kv_lens):
     G = len(prefix_lens)
     items = []

@@ -48,6 +48,9 @@ _lib.pkvmla_plan_create_with_capacity.argtypes = [_i32p, _i32p, _i32p, ctypes.c_
                                                   ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
                                                   ctypes.c_int64, _vp, ctypes.POINTER(_vp)]
 _lib.pkvmla_plan_update.argtypes = [_vp, _i32p, _i32p, _i32p, _vp]
+_lib.pkvmla_plan_create_qo.argtypes = [_i32p, _i32p, _i32p, _i32p, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_float, _vp, ctypes.POINTER(_vp)]
 _lib.pkvmla_run.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.pkvmla_run_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.pkvmla_run_strided.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int64, ctypes.c_int64,
@@ -71,7 +74,7 @@ EXPORTED_SYMBOLS = (
     "pkvmla_plan_create_cascade", "pkvmla_run", "pkvmla_run_strided", "pkvmla_plan_destroy",
     "pkvmla_last_error", "pkvmla_kernel_config", "pkvmla_schedule_host", "pkvmla_plan_export",
     "pkvmla_gather", "pkvmla_gather_rows", "pkvmla_plan_set_timing", "pkvmla_plan_timing",
-    "pkvmla_run_noalloc",
+    "pkvmla_run_noalloc", "pkvmla_plan_create_qo",
 )
 
 OK, EINVAL, EUNSUPPORTED, EHIP, ENOMEM = 0, 1, 2, 3, 4
@@ -332,6 +335,29 @@ def plan(kv_indptr, kv_indices, kv_lens, num_heads: int, page_size: int, num_pag
                 _current_device())
 
 
+def plan_qo(qo_indptr, kv_indptr, kv_indices, kv_lens, num_heads: int, page_size: int,
+            num_pages: int, ckv_dim: int = 512, kpe_dim: int = 64,
+            sm_scale: Optional[float] = None, stream=None) -> Plan:
+    """Plan with qo_indptr[b+1] - qo_indptr[b] new query tokens for request b,
+    causal among them (they are the request's last tokens).  The run takes and
+    returns one row per query token ([qo_indptr[-1], H, ...]); the Plan's
+    ``batch`` is that row count."""
+    qi = _i32(qo_indptr)
+    ip, ix, ln = _i32(kv_indptr), _i32(kv_indices), _i32(kv_lens)
+    _check_csr("kv", ip, ix, ln)
+    if qi.ndim != 1 or len(qi) != len(ln) + 1:
+        raise ValueError(f"qo_indptr needs {len(ln) + 1} entries (got {len(qi)})")
+    if ix.size == 0:
+        ix = np.zeros(1, np.int32)
+    h = ctypes.c_void_p()
+    _check(_lib.pkvmla_plan_create_qo(
+        _ptr(qi), _ptr(ip), _ptr(ix), _ptr(ln), int(len(ln)), int(num_pages), int(num_heads),
+        int(ckv_dim), int(kpe_dim), int(page_size), float(sm_scale or 0.0),
+        _stream_handle(stream) if stream else None, ctypes.byref(h)))
+    return Plan(h.value, int(qi[-1]), int(num_heads), int(page_size), int(num_pages),
+                _current_device())
+
+
 def plan_cascade(group_req_indptr, prefix_indptr, prefix_indices, prefix_lens,
                  kv_indptr, kv_indices, kv_lens, num_heads: int, page_size: int,
                  num_pages: int, ckv_dim: int = 512, kpe_dim: int = 64,
@@ -359,6 +385,9 @@ def plan_cascade(group_req_indptr, prefix_indptr, prefix_indices, prefix_lens,
 
 def plan_for(inp, stream=None) -> Plan:
     """Plan for an input bundle from mla_workloads (flat or cascade)."""
+    if getattr(inp, "qo_indptr", None) is not None:
+        return plan_qo(inp.qo_indptr, inp.kv_indptr, inp.kv_indices, inp.kv_lens, inp.num_heads,
+                       inp.page_size, inp.num_pages, sm_scale=inp.sm_scale, stream=stream)
     if hasattr(inp, "prefix_lens"):
         return plan_cascade(inp.group_req_indptr, inp.prefix_indptr, inp.prefix_indices,
                             inp.prefix_lens, inp.kv_indptr, inp.kv_indices, inp.kv_lens,

@@ -52,6 +52,8 @@ struct pkvmla_plan_s {
   int32_t ckv_dim = 0, kpe_dim = 0, num_pages = 0;
   float sm_scale = 0.f;
   int32_t is_cascade = 0, num_groups = 0, num_cu = 0;
+  int32_t num_requests = 0;  // requests of a plan with several query tokens per request
+  int32_t is_qo = 0;
   pkvmla::KernelConfig cfg{};
   pkvmla::Schedule sched;
   int32_t num_seqs = 0;
@@ -340,6 +342,65 @@ int pkvmla_plan_create_with_capacity(const int32_t* kv_indptr, const int32_t* kv
   return ok();
 }
 
+int pkvmla_plan_create_qo(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                          const int32_t* kv_indices, const int32_t* kv_lens, int32_t batch,
+                          int32_t num_pages, int32_t num_heads, int32_t ckv_dim, int32_t kpe_dim,
+                          int32_t page_size, float sm_scale, void* stream, pkvmla_plan* out) {
+  if (!out) return fail(PKVMLA_EINVAL, "null plan output pointer");
+  *out = nullptr;
+  int32_t log2_ps;
+  float scale;
+  int rc = check_shape(batch, num_pages, num_heads, ckv_dim, kpe_dim, page_size, sm_scale,
+                       &log2_ps, &scale);
+  if (rc) return rc;
+  rc = check_pages("kv", kv_indptr, kv_indices, kv_lens, batch, num_pages, page_size, 1);
+  if (rc) return rc;
+  if (!qo_indptr) return fail(PKVMLA_EINVAL, "null qo_indptr");
+  if (qo_indptr[0] != 0) return fail(PKVMLA_EINVAL, "qo_indptr[0] must be 0");
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t n = (int64_t)qo_indptr[b + 1] - qo_indptr[b];
+    if (n < 1) return fail(PKVMLA_EINVAL, "request %d has %lld query tokens (>= 1 needed)", b, (long long)n);
+    if (n > kv_lens[b])
+      return fail(PKVMLA_EINVAL, "request %d: %lld query tokens but kv_len %d (the new tokens are part "
+                  "of the KV)", b, (long long)n, kv_lens[b]);
+  }
+  const int32_t rows = qo_indptr[batch];
+  pkvmla_plan_s* P = new pkvmla_plan_s();
+  P->batch = rows;  // one query row per (request, new token)
+  P->num_requests = batch;
+  P->is_qo = 1;
+  P->num_heads = num_heads;
+  P->page_size = page_size;
+  P->log2_ps = log2_ps;
+  P->ckv_dim = ckv_dim;
+  P->kpe_dim = kpe_dim;
+  P->num_pages = num_pages;
+  P->sm_scale = scale;
+  pkvmla::kernel_config_for(num_heads, &P->cfg);
+  // Query row r = qo_indptr[b] + j sits at position kv_len - qo_len + j and
+  // attends tokens 0 .. that position of request b's page list (causal among
+  // the request's new tokens, every earlier token visible): one work item of
+  // that length over sequence b.
+  std::vector<pkvmla::WorkItem> items((size_t)rows);
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t n = qo_indptr[b + 1] - qo_indptr[b];
+    for (int32_t j = 0; j < n; ++j)
+      items[qo_indptr[b] + j] = pkvmla::WorkItem{qo_indptr[b] + j, b, kv_lens[b] - n + 1 + j};
+  }
+  std::vector<int32_t> sip(kv_indptr, kv_indptr + batch + 1);
+  std::vector<int32_t> sl(kv_lens, kv_lens + batch);
+  std::vector<int32_t> si(kv_indices, kv_indices + kv_indptr[batch]);
+  rc = finish_plan(P, items, sip, sl, si, (hipStream_t)stream);
+  if (rc) {
+    std::string msg = g_last_error;
+    free_plan(P);
+    g_last_error = msg;
+    return rc;
+  }
+  *out = P;
+  return ok();
+}
+
 int pkvmla_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
                        const int32_t* kv_lens, int32_t batch, int32_t num_pages,
                        int32_t num_heads, int32_t ckv_dim, int32_t kpe_dim, int32_t page_size,
@@ -353,6 +414,7 @@ int pkvmla_plan_update(pkvmla_plan P, const int32_t* kv_indptr, const int32_t* k
                        const int32_t* kv_lens, void* stream) {
   if (!P) return fail(PKVMLA_EINVAL, "null plan");
   if (P->is_cascade) return fail(PKVMLA_EUNSUPPORTED, "update of a cascade plan");
+  if (P->is_qo) return fail(PKVMLA_EUNSUPPORTED, "update of a plan with several query tokens per request");
   int rc = check_pages("kv", kv_indptr, kv_indices, kv_lens, P->batch, P->num_pages,
                        P->page_size, 1);
   if (rc) return rc;
@@ -683,6 +745,8 @@ int pkvmla_plan_export(pkvmla_plan P, int32_t* buf, int64_t cap, int64_t* used) 
                                 P->cfg.head_groups);
   buf[24] = P->fixed_launch;
   buf[25] = (int32_t)std::min<int64_t>(P->cap_indices, INT32_MAX);
+  buf[26] = P->is_qo;
+  buf[27] = P->num_requests;
   int32_t* dst = buf + 32;
   auto pull = [&](const int32_t* src, int64_t n) -> hipError_t {
     hipError_t e = n ? hipMemcpy(dst, src, n * sizeof(int32_t), hipMemcpyDeviceToHost) : hipSuccess;

@@ -82,6 +82,12 @@ def oracle_cascade(inp, requests=None):
     return np.stack(outs), np.stack(lses)
 
 
+def oracle_qo(inp):
+    """fp64 oracle for inputs with several new query tokens per request."""
+    return oracle.attend_qo(inp.q_nope, inp.q_pe, inp.ckv, inp.kpe, inp.qo_indptr, inp.kv_indptr,
+                            inp.kv_indices, inp.kv_lens, inp.page_size, sm_scale=inp.sm_scale)
+
+
 def compare(out_gpu: torch.Tensor, lse_gpu: torch.Tensor, out_ref, lse_ref, requests=None,
             name=""):
     """Element-wise comparison at the acceptance bar; returns the error stats."""

@@ -265,3 +265,27 @@ def test_run_rejects_bad_tensors_before_launch():
             lse = torch.zeros(2, 16, dtype=torch.float32)
         with pytest.raises(ValueError, match=msg):
             plan.run(t["q_nope"], t["q_pe"], t["ckv_cache"], t["kpe_cache"], out=out, lse=lse)
+
+
+@pytest.mark.parametrize("qo,code", [
+    ([1, 2, 3], pk.EINVAL),            # qo_indptr[0] != 0
+    ([0, 0, 1], pk.EINVAL),            # a request without query tokens
+    ([0, 21, 22], pk.EINVAL),          # more query tokens than kv_len (20)
+])
+def test_plan_qo_rejects(qo, code):
+    with pytest.raises(pk.PkvmlaError) as e:
+        pk.plan_qo(qo, [0, 2, 3], [0, 1, 2], [20, 5], 16, 16, 4)
+    assert e.value.code == code
+
+
+def test_plan_qo_rejects_short_indptr():
+    with pytest.raises(ValueError, match="qo_indptr"):
+        pk.plan_qo([0, 1], [0, 2, 3], [0, 1, 2], [20, 5], 16, 16, 4)
+
+
+def test_schedule_host_matches_reference_qo():
+    from oracle.schedule_ref import qo_items
+    qo = np.array([0, 2, 6, 7, 11])
+    lens = np.array([40, 300, 1, 2000])
+    _compare(qo_items(qo, lens), int(qo[-1]), 128, 32, 4)
+    _compare(qo_items(qo, lens), int(qo[-1]), 7, 32, 2)

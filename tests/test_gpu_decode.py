@@ -13,12 +13,13 @@ import pytest
 import torch
 
 import oracle
-from oracle.schedule_ref import (schedule_ref, flat_items, cascade_items, kernel_config,
-                                 unit_page_fields)
-from mla_workloads import (make_flat, make_cascade, make_config, stress_variant,
+from oracle.schedule_ref import (schedule_ref, flat_items, cascade_items, qo_items,
+                                 kernel_config, unit_page_fields)
+from mla_workloads import (make_flat, make_cascade, make_config, make_qo, stress_variant,
                            stress_variant_cascade, poison_unreferenced, permute_pages,
                            STRESS_KINDS)
-from gpu_helpers import Dev, run_gpu, oracle_flat, oracle_cascade, compare, bits_of, dev_bf16
+from gpu_helpers import (Dev, run_gpu, oracle_flat, oracle_cascade, oracle_qo, compare, bits_of,
+                         dev_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -365,3 +366,43 @@ def test_many_tiny_requests():
     out, lse = run_gpu(pk.plan_for(inp), Dev(inp))
     ref_o, ref_l = oracle_flat(inp)
     compare(out, lse, ref_o, ref_l, name="tiny requests")
+
+
+# ------------------------------------- several new query tokens per request
+QO_CASES = {
+    "h16_qo2_ps16": lambda: make_qo("q1", 131, 5, 16, 16, [2, 17, 64, 200, 777], [2] * 5),
+    "h16_qo4_ps1": lambda: make_qo("q2", 132, 4, 16, 1, [4, 31, 33, 300], [4] * 4),
+    "h128_qo2_ps64": lambda: make_qo("q3", 133, 4, 128, 64, [2, 65, 700, 2049], [2] * 4),
+    "h128_qo4_ps64": lambda: make_qo("q4", 134, 4, 128, 64, [4, 100, 1025, 3000], [4] * 4),
+    "h32_mixed_ps8": lambda: make_qo("q5", 135, 6, 32, 8, [1, 5, 40, 9, 250, 16], [1, 5, 3, 2, 4, 16]),
+    "h64_mixed_ps16": lambda: make_qo("q6", 136, 5, 64, 16, [3, 48, 513, 7, 90], [3, 1, 4, 7, 2]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(QO_CASES))
+def test_qo_decode(name):
+    inp = QO_CASES[name]()
+    note(f"qo {name}: {int(inp.qo_indptr[-1])} query rows")
+    out, lse = run_gpu(pk.plan_for(inp), Dev(inp))
+    ref_o, ref_l = oracle_qo(inp)
+    compare(out, lse, ref_o, ref_l, name=f"qo {name}")
+
+
+@pytest.mark.parametrize("H,ps", [(16, 16), (128, 64)])
+def test_qo_stress_and_export(H, ps):
+    inp = stress_variant(make_qo("qs", 137 + H, 4, H, ps, [4, 70, 300, 1500], [4, 2, 3, 4]), "qx8")
+    note(f"qo stress H{H} ps{ps}")
+    plan = pk.plan_for(inp)
+    out, lse = run_gpu(plan, Dev(inp))
+    compare(out, lse, *oracle_qo(inp), name=f"qo qx8 H{H}")
+    # the uploaded schedule is the rule's, one item per query row
+    ex = plan.export()
+    kc = kernel_config(H)
+    lanes = max(1, ex.num_cu * kc["wg_per_cu"] // kc["head_groups"])
+    wg, units, merges = schedule_ref(qo_items(inp.qo_indptr, inp.kv_lens), int(inp.qo_indptr[-1]),
+                                     lanes, kc["tile"], kc["fixed_cost"])
+    units = unit_page_fields(units, inp.kv_indptr, inp.kv_indices, ps)
+    assert int(ex.header[26]) == 1 and int(ex.header[27]) == inp.batch
+    np.testing.assert_array_equal(ex.wg_indptr, wg)
+    np.testing.assert_array_equal(ex.units, units)
+    np.testing.assert_array_equal(ex.merges, merges)
