@@ -184,6 +184,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for HBM counter calibration)")
+    ap.add_argument("--gemm-calibration", action="store_true",
+                    help="only time a plain bf16 GEMM (8192^3, the PyTorch/hipBLASLt "
+                         "library path): the dense MFMA rate a library reaches on this GPU")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -205,6 +208,29 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n, "launches": 3}))
+        return
+
+    if args.gemm_calibration:
+        n = 8192
+        a = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
+        b = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
+        for _ in range(5):
+            c = a @ b
+        torch.cuda.synchronize()
+        hip = HipEvents()
+        e0, e1 = hip.create(), hip.create()
+        sh = int(torch.cuda.current_stream().cuda_stream)
+        reps = 50
+        hip.record(e0, sh)
+        for _ in range(reps):
+            c = a @ b
+        hip.record(e1, sh)
+        torch.cuda.synchronize()
+        ms = hip.elapsed(e0, e1) / reps
+        tfs = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+        del c
+        print(json.dumps({"gemm": "bf16 8192x8192x8192 (torch.matmul)", "ms": round(ms, 4),
+                          "tflops": round(tfs, 1), "frac_of_peak": round(tfs / MFMA_BF16_PEAK_TFS, 4)}))
         return
 
     import paged_kv_mla_amd as pk
@@ -262,11 +288,26 @@ def main():
             hip.destroy(e)
         return total, per
 
-    total_ms, per_step = timed_pass(args.warmup, args.steps)
-    # percentiles over at least 50 steps (an extra pass when K is smaller)
+    def timed_total(first, n):
+        # the K timed steps, with one event before and one after them: an
+        # event recorded between two steps delays the next step's dispatch
+        e0, e1 = hip.create(), hip.create()
+        torch.cuda.synchronize()
+        hip.record(e0, sh)
+        for i in range(n):
+            step(first + i)
+        hip.record(e1, sh)
+        torch.cuda.synchronize()
+        t = hip.elapsed(e0, e1)
+        hip.destroy(e0)
+        hip.destroy(e1)
+        return t
+
+    total_ms = timed_total(args.warmup, args.steps)
+    # per-step distribution: a separate pass of at least 50 steps with an event
+    # after every step (those events add their own delay to each step)
     stats_steps = max(args.steps, 50)
-    if stats_steps > args.steps:
-        _, per_step = timed_pass(args.warmup + args.steps, stats_steps)
+    _, per_step = timed_pass(args.warmup + args.steps, stats_steps)
     # second pass: the decode kernel's event intervals and in-kernel spans (the
     # library keeps the last 256 runs' records)
     plan.set_timing(True)
@@ -325,6 +366,7 @@ def main():
         "ms_per_step_p10": round(float(np.percentile(per_step, 10)), 5),
         "ms_per_step_p90": round(float(np.percentile(per_step, 90)), 5),
         "per_step_stats_steps": int(stats_steps),
+        "per_step_stats_source": "separate pass, HIP event after every step",
         "decode_kernel_ms": round(kern_avg_ms, 5),
         "decode_kernel_source": "in-kernel real-time stamps (earliest wave start to latest "
                                 "wave end), second pass of the same steps",

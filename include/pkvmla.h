@@ -143,7 +143,14 @@ int pkvmla_plan_create_qo(const int32_t* qo_indptr, const int32_t* kv_indptr,
  * to batch).  Group g's shared prefix is prefix_lens[g] tokens in pages
  * prefix_indices[prefix_indptr[g] ...] (host arrays).  kv_indptr, kv_indices
  * and kv_lens describe each request's own suffix as in a flat plan, except
- * that kv_lens[b] may be 0.  prefix_lens[g] + kv_lens[b] >= 1 for every b. */
+ * that kv_lens[b] may be 0.  prefix_lens[g] + kv_lens[b] >= 1 for every b.
+ * The two levels follow the cascade attention of the vLLM page "[V1][Core]
+ * FlashInfer attention backend for V1" (shared-prefix level, per-request
+ * level, merged; it must equal normal attention).  A run launches level 0
+ * (each group's query rows b * H + head, 64 to a workgroup, several requests
+ * per workgroup below 64 heads, scoring the group's prefix tiles: see
+ * pkvmla_schedule_rows_host), then level 1 (each suffix, split like a flat
+ * plan), then the log-sum-exp merge of every request's states. */
 int pkvmla_plan_create_cascade(const int32_t* group_req_indptr, int32_t num_groups,
                                const int32_t* prefix_indptr, const int32_t* prefix_indices,
                                const int32_t* prefix_lens,
@@ -249,6 +256,24 @@ int pkvmla_schedule_host(const int32_t* items, int32_t n_items, int32_t batch,
                          int32_t* units, int64_t cap_units,
                          int32_t* merges, int64_t cap_merges, int32_t* counts);
 
+/* The level-0 schedule of a cascade plan, computed on the host exactly as
+ * pkvmla_plan_create_cascade does (no GPU needed).  Query rows rho = b * H +
+ * head; group g owns rows [group_req_indptr[g] * H, group_req_indptr[g+1] * H),
+ * cut into blocks of max(64, H) rows (groups with an empty prefix have none).
+ * With nb blocks on num_wg lanes: nb <= num_wg cuts every block's prefix into
+ * S = num_wg / nb token pieces (at most its tile count; piece p of T tiles
+ * covers tiles [p*T/P, (p+1)*T/P) of P pieces) with piece p of block k on
+ * lane k*S + p; nb > num_wg puts block k whole on lane k mod num_wg.  Unit
+ * records (row0, group, kv_begin, kv_end, slot offset, row_end, 0, 0): slots
+ * are numbered from 0 in lane order, one per request of a unit's rows, and
+ * the offset is (first slot) * H - row0, so row rho's partial state is row
+ * rho + offset of the partial-state rows.  counts[0..2] = grid, n_units,
+ * n_slots.  A plan uses num_wg = CUs / max(1, H / 64). */
+int pkvmla_schedule_rows_host(const int32_t* group_req_indptr, int32_t num_groups,
+                              const int32_t* prefix_lens, int32_t num_heads, int32_t num_wg,
+                              int32_t tile, int32_t* wg_indptr, int64_t cap_wg,
+                              int32_t* units, int64_t cap_units, int32_t* counts);
+
 /* Copy the plan's uploaded device tables back to the host, for bit-exact
  * checking.  Layout of host int32 buf (cap elements):
  *   [0..15]  header: version(1), batch, num_heads, page_size, ckv_dim,
@@ -257,9 +282,16 @@ int pkvmla_schedule_host(const int32_t* items, int32_t n_items, int32_t batch,
  *   [16..31] header 2: num_seqs, n_indices, num_cu, sm_scale (float bits),
  *            is_cascade, num_groups, head_groups, launched workgroups,
  *            fixed launch shapes (0/1), page-id capacity, several query tokens
- *            per request (0/1), number of requests of such a plan, 0...
+ *            per request (0/1), number of requests of such a plan,
+ *            cascade level 0: grid0, n_units0, slot-list length, head groups
  *   then wg_indptr[grid+1], units[n_units*8], merges[n_merges*4],
- *   seq_indptr[num_seqs+1], seq_lens[num_seqs], seq_indices[n_indices].
+ *   seq_indptr[num_seqs+1], seq_lens[num_seqs], seq_indices[n_indices],
+ *   and for a cascade plan wg_indptr0[grid0+1], units0[n_units0*8] (the
+ *   records of pkvmla_schedule_rows_host with the page fields filled), the
+ *   slot list.  A cascade plan's units are its suffixes', every one with a
+ *   partial slot numbered after level 0's (in emission order), and its merge
+ *   records are (request, first slot-list entry, count, 1): the request's
+ *   level-0 slots in level-0 emission order, then its suffix slots.
  *   The unit records are those of pkvmla_schedule_host with their last two
  *   fields filled: page_base = seq_indptr[sequence] and first_page =
  *   seq_indices[page_base + kv_begin / page_size].
@@ -271,7 +303,9 @@ int pkvmla_plan_export(pkvmla_plan plan, int32_t* buf, int64_t cap, int64_t* use
  * kernel: rows (device bf16 [sum of attended tokens, 576]) receives, for every
  * work unit of the plan in request order and then token order, the ckv row
  * followed by the kpe row of each token.  For a flat plan this is
- * [sum(kv_lens), 576] in (request, token) order.  Bit-exact copy. */
+ * [sum(kv_lens), 576] in (request, token) order.  For a cascade plan: the
+ * level-0 units (prefix token ranges, in level-0 emission order), then the
+ * suffix units.  Bit-exact copy. */
 int pkvmla_gather(pkvmla_plan plan, const void* ckv_cache, const void* kpe_cache,
                   void* rows, void* stream);
 

@@ -7,9 +7,9 @@ checked bit for bit.  It shares no code with the C implementation.
 
 Rule (all integers):
   * Work items are (request b, sequence s, length L): a flat plan has one item
-    per request with s = b; a cascade plan has, per request, the group prefix
-    (s = group id, L = prefix length) then the request's own suffix
-    (s = G + b, L = suffix length).  Items with L = 0 are skipped.
+    per request with s = b; a cascade plan's level 1 has one per request for
+    its own suffix (s = G + b, L = suffix length; sequences 0..G-1 are the
+    groups' prefixes).  Items with L = 0 are skipped.
   * tiles(L) = ceil(L / TILE).  Every segment also costs FIXED tiles.
     C = sum over items of (tiles(L) + FIXED); W is the workgroup budget
     (compute units x workgroups per CU).
@@ -73,15 +73,101 @@ def qo_items(qo_indptr, kv_lens):
     return items
 
 
-def cascade_items(group_req_indptr, prefix_lens, kv_lens):
-    G = len(prefix_lens)
-    items = []
-    for g in range(G):
-        for b in range(int(group_req_indptr[g]), int(group_req_indptr[g + 1])):
-            items.append((b, g, int(prefix_lens[g])))
-            items.append((b, G + b, int(kv_lens[b])))
-    items.sort(key=lambda it: it[0])  # stable: prefix before suffix per request
-    return items
+def suffix_items(num_groups: int, kv_lens):
+    """Level-1 items of a cascade plan: request b over its suffix (sequence
+    G + b)."""
+    return [(b, num_groups + b, int(L)) for b, L in enumerate(kv_lens)]
+
+
+def row_schedule_ref(group_req_indptr, prefix_lens, num_heads: int, num_wg: int,
+                     tile: int = PLAN_TILE):
+    """Level 0 of a cascade plan (its shared prefixes), restated from the rule:
+
+    * query rows rho = b * H + h; group g owns rows [gi[g] * H, gi[g+1] * H);
+      each group with a non-empty prefix has blocks of R = max(64, H) rows
+      starting at its first row (the last one may be short), in group order;
+    * nb blocks, W lanes.  nb <= W: S = W // nb pieces per block, P = min(S,
+      tiles) of them for a prefix of `tiles` tiles, piece p covering tiles
+      p*tiles//P .. (p+1)*tiles//P - 1 (tokens clipped to the prefix length),
+      on lane k*S + p for block k; grid = nb * S.  nb > W: block k whole on
+      lane k % W; grid = W;
+    * units in lane order (a lane's in block order): (row0, g, kv_begin,
+      kv_end, offset, row_end, 0, 0), slots counted from 0 in that order, a
+      unit taking (row_end - row0) / H of them, offset = first slot * H - row0.
+
+    Returns (wg_indptr [grid+1], units [n, 8], n_slots)."""
+    H = int(num_heads)
+    R = max(64, H)
+    blocks = []
+    for g in range(len(prefix_lens)):
+        L = int(prefix_lens[g])
+        if L <= 0:
+            continue
+        lo, hi = int(group_req_indptr[g]) * H, int(group_req_indptr[g + 1]) * H
+        r = lo
+        while r < hi:
+            blocks.append((g, r, min(r + R, hi), L))
+            r += R
+    nb = len(blocks)
+    if nb == 0:
+        return np.zeros(1, np.int32), np.zeros((0, UNIT_INTS), np.int32), 0
+    if nb <= num_wg:
+        S = num_wg // nb
+        grid = nb * S
+        lanes = [[] for _ in range(grid)]
+        for k, (g, r0, r1, L) in enumerate(blocks):
+            T = -(-L // tile)
+            P = min(S, T)
+            for p in range(P):
+                t0, t1 = p * T // P, (p + 1) * T // P
+                lanes[k * S + p].append((k, t0 * tile, min(t1 * tile, L)))
+    else:
+        grid = num_wg
+        lanes = [[] for _ in range(grid)]
+        for k, (g, r0, r1, L) in enumerate(blocks):
+            lanes[k % num_wg].append((k, 0, L))
+    units, wg = [], [0]
+    slot = 0
+    for lane in lanes:
+        for (k, k0, k1) in lane:
+            g, r0, r1, _ = blocks[k]
+            units.append((r0, g, k0, k1, slot * H - r0, r1, 0, 0))
+            slot += (r1 - r0) // H
+        wg.append(len(units))
+    return (np.asarray(wg, np.int32), np.asarray(units, np.int32).reshape(-1, UNIT_INTS), slot)
+
+
+def cascade_plan_ref(group_req_indptr, prefix_lens, kv_lens, num_heads: int, num_wg: int,
+                     num_wg0: int, tile: int = PLAN_TILE, fixed: int = 1):
+    """The two schedules of a cascade plan and its merge lists.
+
+    Level 1 is the split-KV walk over the suffix items with every unit given a
+    partial slot, numbered after level 0's in emission order.  Request b's
+    merge lists its level-0 slots (each level-0 unit whose rows hold b, in
+    level-0 emission order: the unit's first slot + b - row0 / H) and then its
+    level-1 slots; merge records are (b, first list entry, count, 1).
+
+    Returns dict(wg0, units0, wg, units, merges, slot_list)."""
+    H = int(num_heads)
+    wg0, units0, n0 = row_schedule_ref(group_req_indptr, prefix_lens, H, num_wg0, tile)
+    B = len(kv_lens)
+    wg, units, _ = schedule_ref(suffix_items(len(prefix_lens), kv_lens), B, num_wg, tile, fixed)
+    units = units.copy()
+    units[:, 4] = n0 + np.arange(units.shape[0])
+    per = [[] for _ in range(B)]
+    for u in units0:
+        first = (int(u[4]) + int(u[0])) // H
+        for b in range(int(u[0]) // H, int(u[5]) // H):
+            per[b].append(first + b - int(u[0]) // H)
+    for u in units:
+        per[int(u[0])].append(int(u[4]))
+    merges, slot_list = [], []
+    for b in range(B):
+        merges.append((b, len(slot_list), len(per[b]), 1))
+        slot_list.extend(per[b])
+    return dict(wg0=wg0, units0=units0, wg=wg, units=units,
+                merges=np.asarray(merges, np.int32).reshape(-1, MERGE_INTS),
+                slot_list=np.asarray(slot_list, np.int32))
 
 
 def schedule_ref(items, batch: int, num_wg: int, tile: int = PLAN_TILE, fixed: int = 1):

@@ -62,6 +62,9 @@ _lib.pkvmla_kernel_config.argtypes = [ctypes.c_int32, _i32p]
 _lib.pkvmla_schedule_host.argtypes = [_i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_int32, ctypes.c_int32, _i32p, ctypes.c_int64,
                                       _i32p, ctypes.c_int64, _i32p, ctypes.c_int64, _i32p]
+_lib.pkvmla_schedule_rows_host.argtypes = [_i32p, ctypes.c_int32, _i32p, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_int32, _i32p, ctypes.c_int64,
+                                           _i32p, ctypes.c_int64, _i32p]
 _lib.pkvmla_plan_export.argtypes = [_vp, _i32p, ctypes.c_int64, _i64p]
 _lib.pkvmla_gather.argtypes = [_vp, _vp, _vp, _vp, _vp]
 _lib.pkvmla_gather_rows.argtypes = [_vp, _i64p]
@@ -74,7 +77,7 @@ EXPORTED_SYMBOLS = (
     "pkvmla_plan_create_cascade", "pkvmla_run", "pkvmla_run_strided", "pkvmla_plan_destroy",
     "pkvmla_last_error", "pkvmla_kernel_config", "pkvmla_schedule_host", "pkvmla_plan_export",
     "pkvmla_gather", "pkvmla_gather_rows", "pkvmla_plan_set_timing", "pkvmla_plan_timing",
-    "pkvmla_run_noalloc", "pkvmla_plan_create_qo",
+    "pkvmla_run_noalloc", "pkvmla_plan_create_qo", "pkvmla_schedule_rows_host",
 )
 
 OK, EINVAL, EUNSUPPORTED, EHIP, ENOMEM = 0, 1, 2, 3, 4
@@ -151,6 +154,26 @@ def schedule_host(items, batch: int, num_wg: int, tile: int, fixed_cost: int):
     return wg[:grid + 1].copy(), units[:8 * nu].reshape(nu, 8).copy(), merges[:4 * nm].reshape(nm, 4).copy()
 
 
+def schedule_rows_host(group_req_indptr, prefix_lens, num_heads: int, num_wg: int,
+                       tile: int = 32):
+    """The library's level-0 (shared-prefix) schedule of a cascade plan,
+    computed on the host.  Returns (wg_indptr, units [n, 8], n_slots)."""
+    gi, pl = _i32(group_req_indptr), _i32(prefix_lens)
+    if gi.ndim != 1 or pl.ndim != 1 or len(gi) != len(pl) + 1:
+        raise ValueError("group_req_indptr needs len(prefix_lens) + 1 entries")
+    rows = int(gi[-1]) * int(num_heads)
+    n_blocks = rows // 64 + len(pl) + 1
+    cap_u = 8 * (n_blocks + 1) * max(1, int(num_wg))
+    wg = np.zeros(int(num_wg) + 1, np.int32)
+    units = np.zeros(cap_u, np.int32)
+    counts = np.zeros(3, np.int32)
+    _check(_lib.pkvmla_schedule_rows_host(_ptr(gi), len(pl), _ptr(pl), int(num_heads),
+                                          int(num_wg), int(tile), _ptr(wg), wg.size, _ptr(units),
+                                          units.size, _ptr(counts)))
+    grid, nu, ns = (int(c) for c in counts)
+    return wg[:grid + 1].copy(), units[:8 * nu].reshape(nu, 8).copy(), ns
+
+
 @dataclass
 class PlanExport:
     header: np.ndarray
@@ -161,6 +184,9 @@ class PlanExport:
     seq_indptr: np.ndarray
     seq_lens: np.ndarray
     seq_indices: np.ndarray
+    wg_indptr0: np.ndarray = None   # cascade level 0 (empty for other plans)
+    units0: np.ndarray = None
+    slot_list: np.ndarray = None
 
     @property
     def grid(self) -> int:
@@ -191,7 +217,8 @@ class Plan:
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h is not None and h.value:
+        # (at interpreter exit the module globals may already be gone)
+        if h is not None and h.value and _lib is not None:
             _lib.pkvmla_plan_destroy(h)
             self._h = None
 
@@ -303,15 +330,18 @@ class Plan:
         _check(_lib.pkvmla_plan_export(self._h, _ptr(buf), buf.size, ctypes.byref(used)))
         hdr = buf[:32].copy()
         grid, nu, nm, ns, ni = int(hdr[12]), int(hdr[13]), int(hdr[14]), int(hdr[16]), int(hdr[17])
+        g0, nu0, nsl = int(hdr[28]), int(hdr[29]), int(hdr[30])
         o = 32
         parts = []
-        for n in (grid + 1, 8 * nu, 4 * nm, ns + 1, ns, ni):
+        for n in (grid + 1, 8 * nu, 4 * nm, ns + 1, ns, ni,
+                  (g0 + 1) if int(hdr[20]) else 0, 8 * nu0, nsl):
             parts.append(buf[o:o + n].copy())
             o += n
         return PlanExport(header=hdr, sm_scale=float(hdr[19:20].view(np.float32)[0]),
                           wg_indptr=parts[0], units=parts[1].reshape(nu, 8),
                           merges=parts[2].reshape(nm, 4), seq_indptr=parts[3],
-                          seq_lens=parts[4], seq_indices=parts[5])
+                          seq_lens=parts[4], seq_indices=parts[5], wg_indptr0=parts[6],
+                          units0=parts[7].reshape(nu0, 8), slot_list=parts[8])
 
 
 def plan(kv_indptr, kv_indices, kv_lens, num_heads: int, page_size: int, num_pages: int,

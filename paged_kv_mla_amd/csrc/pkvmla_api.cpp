@@ -70,7 +70,15 @@ struct pkvmla_plan_s {
   // is split) or, for a plan built with a capacity, fixed at the capacities so
   // that the kernels a captured graph replays stay right after updates.
   int fixed_launch = 0;
+  int32_t cap_slots = 0;     // partial-state slots of the split workspace
+  // cascade plans: level 0, row blocks of each group's query rows over its
+  // shared prefix (a launch of its own before the suffixes), and the merge's
+  // slot lists
+  pkvmla::KernelConfig cfg0{};
+  pkvmla::RowSchedule sched0;
+  std::vector<int32_t> slot_list;
   size_t off_wg = 0, off_units = 0, off_merges = 0, off_sip = 0, off_sl = 0, off_si = 0;
+  size_t off_wg0 = 0, off_units0 = 0, off_list = 0;
   // device tables (one allocation) and split workspace
   int32_t* d_tables = nullptr;
   int32_t* d_wg_indptr = nullptr;
@@ -79,6 +87,9 @@ struct pkvmla_plan_s {
   int32_t* d_seq_indptr = nullptr;
   int32_t* d_seq_lens = nullptr;
   int32_t* d_seq_indices = nullptr;
+  int32_t* d_wg0 = nullptr;
+  int32_t* d_units0 = nullptr;
+  int32_t* d_slot_list = nullptr;
   void* d_part = nullptr;  // part_o bf16 [slots][H][512] then part_lse fp32 [slots][H]
   size_t table_ints = 0;
   // optional per-run timing of the decode kernel (events created up front)
@@ -145,6 +156,18 @@ int check_pages(const char* what, const int32_t* indptr, const int32_t* indices,
   return PKVMLA_OK;
 }
 
+// The page fields of unit records: the sequence's page-list start and the page
+// of the unit's first token.
+void fill_page_fields(std::vector<int32_t>* units, const std::vector<int32_t>& seq_indptr,
+                      const std::vector<int32_t>& seq_indices, int32_t page_size) {
+  for (size_t i = 0; i < units->size(); i += pkvmla::kUnitRecordInts) {
+    int32_t* u = &(*units)[i];
+    const int32_t base = seq_indptr[u[1]];
+    u[6] = base;
+    u[7] = seq_indices[(size_t)base + (size_t)(u[2] / page_size)];
+  }
+}
+
 // Build the schedule for `items` into *sched, with the page fields of its unit
 // records (the sequence's page-list start and the page of the unit's first
 // token, so a workgroup's first copies need one dependent load, the record,
@@ -156,12 +179,7 @@ int build_plan_schedule(const pkvmla_plan_s* P, const std::vector<pkvmla::WorkIt
                               sched))
     return fail(PKVMLA_EINVAL, "schedule construction failed");
   if (sched->total_rows > INT32_MAX) return fail(PKVMLA_EUNSUPPORTED, "too many tokens");
-  for (size_t i = 0; i < sched->units.size(); i += pkvmla::kUnitRecordInts) {
-    int32_t* u = &sched->units[i];
-    const int32_t base = seq_indptr[u[1]];
-    u[6] = base;
-    u[7] = seq_indices[(size_t)base + (size_t)(u[2] / P->page_size)];
-  }
+  fill_page_fields(&sched->units, seq_indptr, seq_indices, P->page_size);
   return PKVMLA_OK;
 }
 
@@ -181,6 +199,11 @@ int upload_tables(pkvmla_plan_s* P, const pkvmla::Schedule& sched,
   std::copy(seq_indptr.begin(), seq_indptr.end(), host.begin() + P->off_sip);
   std::copy(seq_lens.begin(), seq_lens.end(), host.begin() + P->off_sl);
   std::copy(seq_indices.begin(), seq_indices.end(), host.begin() + P->off_si);
+  if (P->is_cascade) {
+    std::copy(P->sched0.wg_indptr.begin(), P->sched0.wg_indptr.end(), host.begin() + P->off_wg0);
+    std::copy(P->sched0.units.begin(), P->sched0.units.end(), host.begin() + P->off_units0);
+    std::copy(P->slot_list.begin(), P->slot_list.end(), host.begin() + P->off_list);
+  }
   PKVMLA_HIP(hipMemcpyAsync(P->d_tables, host.data(), P->table_ints * sizeof(int32_t),
                             hipMemcpyHostToDevice, stream));
   PKVMLA_HIP(hipStreamSynchronize(stream));
@@ -189,10 +212,21 @@ int upload_tables(pkvmla_plan_s* P, const pkvmla::Schedule& sched,
   return PKVMLA_OK;
 }
 
+// Level 0 of a cascade plan (its groups and prefix lengths).
+struct Level0Groups {
+  const int32_t* group_req_indptr;
+  int32_t num_groups;
+  const int32_t* prefix_lens;
+};
+
 // Fix the capacities, build the schedule, allocate and upload the device tables.
+// With `l0` (cascade plans) the items are the suffixes; the level-0 row-block
+// schedule is built beside them, every suffix unit writes a partial state
+// after the level-0 slots, and each request's merge lists all of its states.
 int finish_plan(pkvmla_plan_s* P, const std::vector<pkvmla::WorkItem>& items,
                 const std::vector<int32_t>& seq_indptr, const std::vector<int32_t>& seq_lens,
-                const std::vector<int32_t>& seq_indices, hipStream_t stream) {
+                const std::vector<int32_t>& seq_indices, hipStream_t stream,
+                const Level0Groups* l0 = nullptr) {
   PKVMLA_HIP(hipGetDevice(&P->device));
   PKVMLA_HIP(hipDeviceGetAttribute(&P->num_cu, hipDeviceAttributeMultiprocessorCount, P->device));
   // the schedule's lanes: each lane's token ranges are replicated over the head groups
@@ -203,13 +237,32 @@ int finish_plan(pkvmla_plan_s* P, const std::vector<pkvmla::WorkItem>& items,
   P->cap_indices = std::max<int64_t>((int64_t)seq_indices.size(), P->index_capacity_request);
   int rc = build_plan_schedule(P, items, seq_indptr, seq_indices, &P->sched);
   if (rc) return rc;
+  P->cap_slots = P->cap_units;
+  if (l0) {
+    const int32_t lanes0 = std::max(1, P->num_cu / P->cfg0.head_groups);
+    if (!pkvmla::build_row_schedule(l0->group_req_indptr, l0->num_groups, l0->prefix_lens,
+                                    P->num_heads, lanes0, pkvmla::kTile, &P->sched0))
+      return fail(PKVMLA_EUNSUPPORTED, "level-0 schedule construction failed (too many rows)");
+    fill_page_fields(&P->sched0.units, seq_indptr, seq_indices, P->page_size);
+    int64_t slot = P->sched0.n_slots;
+    for (size_t i = 0; i < P->sched.units.size(); i += pkvmla::kUnitRecordInts)
+      P->sched.units[i + 4] = (int32_t)slot++;
+    if (slot > INT32_MAX / 2) return fail(PKVMLA_EUNSUPPORTED, "too many partial states");
+    P->sched.n_slots = (int32_t)slot;
+    pkvmla::build_cascade_merges(P->sched0, P->sched.units, P->batch, P->num_heads,
+                                 &P->sched.merges, &P->slot_list);
+    P->cap_slots = (int32_t)slot;
+  }
 
   // 64-int aligned sub-buffers inside one allocation
   auto pad = [](size_t n) { return (n + 63) & ~size_t(63); };
   P->off_wg = 0;
   P->off_units = P->off_wg + pad((size_t)P->cap_lanes + 1);
   P->off_merges = P->off_units + pad((size_t)P->cap_units * pkvmla::kUnitRecordInts);
-  P->off_sip = P->off_merges + pad((size_t)P->cap_merges * pkvmla::kMergeRecordInts);
+  P->off_wg0 = P->off_merges + pad((size_t)P->cap_merges * pkvmla::kMergeRecordInts);
+  P->off_units0 = P->off_wg0 + pad(P->sched0.wg_indptr.size());
+  P->off_list = P->off_units0 + pad(P->sched0.units.size());
+  P->off_sip = P->off_list + pad(P->slot_list.size());
   P->off_sl = P->off_sip + pad(seq_indptr.size());
   P->off_si = P->off_sl + pad(seq_lens.size());
   // every page-id read of the kernels lies inside its sequence's list (tile
@@ -223,9 +276,12 @@ int finish_plan(pkvmla_plan_s* P, const std::vector<pkvmla::WorkItem>& items,
   P->d_seq_indptr = P->d_tables + P->off_sip;
   P->d_seq_lens = P->d_tables + P->off_sl;
   P->d_seq_indices = P->d_tables + P->off_si;
+  P->d_wg0 = P->d_tables + P->off_wg0;
+  P->d_units0 = P->d_tables + P->off_units0;
+  P->d_slot_list = P->d_tables + P->off_list;
   // split workspace for the largest slot count any schedule can need
-  // (slots <= units)
-  const size_t rows = (size_t)P->cap_units * P->num_heads;
+  // (flat plans: slots <= units)
+  const size_t rows = (size_t)P->cap_slots * P->num_heads;
   PKVMLA_HIP(hipMalloc(&P->d_part, rows * (pkvmla::kCkvDim * sizeof(uint16_t) + sizeof(float))));
   return upload_tables(P, P->sched, seq_indptr, seq_lens, seq_indices, stream);
 }
@@ -292,6 +348,35 @@ int pkvmla_schedule_host(const int32_t* items, int32_t n_items, int32_t batch, i
   std::copy(s.wg_indptr.begin(), s.wg_indptr.end(), wg_indptr);
   std::copy(s.units.begin(), s.units.end(), units);
   std::copy(s.merges.begin(), s.merges.end(), merges);
+  return ok();
+}
+
+int pkvmla_schedule_rows_host(const int32_t* group_req_indptr, int32_t num_groups,
+                               const int32_t* prefix_lens, int32_t num_heads, int32_t num_wg,
+                               int32_t tile, int32_t* wg_indptr, int64_t cap_wg, int32_t* units,
+                               int64_t cap_units, int32_t* counts) {
+  if (!group_req_indptr || !prefix_lens || !counts || num_groups < 1)
+    return fail(PKVMLA_EINVAL, "null argument or num_groups < 1");
+  if (num_wg < 1 || tile < 1 || num_heads < 16 || num_heads % 16)
+    return fail(PKVMLA_EINVAL, "num_wg, tile must be >= 1, num_heads a multiple of 16");
+  if (group_req_indptr[0] != 0) return fail(PKVMLA_EINVAL, "group_req_indptr[0] must be 0");
+  for (int32_t g = 0; g < num_groups; ++g)
+    if (group_req_indptr[g + 1] < group_req_indptr[g] || prefix_lens[g] < 0)
+      return fail(PKVMLA_EINVAL, "group %d: decreasing indptr or negative prefix length", g);
+  pkvmla::RowSchedule s;
+  if (!pkvmla::build_row_schedule(group_req_indptr, num_groups, prefix_lens, num_heads, num_wg,
+                                  tile, &s))
+    return fail(PKVMLA_EINVAL, "row schedule construction failed");
+  counts[0] = s.grid;
+  counts[1] = (int32_t)(s.units.size() / pkvmla::kUnitRecordInts);
+  counts[2] = s.n_slots;
+  if ((int64_t)s.wg_indptr.size() > cap_wg || (int64_t)s.units.size() > cap_units)
+    return fail(PKVMLA_EINVAL, "output capacity too small (need %zu, %zu)", s.wg_indptr.size(),
+                s.units.size());
+  if (!s.wg_indptr.empty() && !wg_indptr) return fail(PKVMLA_EINVAL, "null wg_indptr");
+  if (!s.units.empty() && !units) return fail(PKVMLA_EINVAL, "null units");
+  std::copy(s.wg_indptr.begin(), s.wg_indptr.end(), wg_indptr);
+  std::copy(s.units.begin(), s.units.end(), units);
   return ok();
 }
 
@@ -487,6 +572,9 @@ int pkvmla_plan_create_cascade(const int32_t* group_req_indptr, int32_t num_grou
   P->is_cascade = 1;
   P->num_groups = num_groups;
   pkvmla::kernel_config_for(num_heads, &P->cfg);
+  // level 0: 64 query rows per workgroup (four head blocks), a whole request
+  // per lane above 64 heads (its head groups)
+  P->cfg0 = pkvmla::KernelConfig{8, 16, 4, 1, 4, num_heads > 64 ? num_heads / 64 : 1};
   // sequences: G prefix lists, then one suffix list per request
   std::vector<int32_t> sip, sl, si;
   sip.reserve(num_groups + batch + 1);
@@ -496,14 +584,13 @@ int pkvmla_plan_create_cascade(const int32_t* group_req_indptr, int32_t num_grou
   for (int32_t b = 0; b < batch; ++b) sl.push_back(kv_lens[b]);
   si.assign(prefix_indices, prefix_indices + prefix_indptr[num_groups]);
   si.insert(si.end(), kv_indices, kv_indices + kv_indptr[batch]);
+  // level 1: each request's suffix (empty ones have no unit)
   std::vector<pkvmla::WorkItem> items;
-  items.reserve(2 * (size_t)batch);
-  for (int32_t g = 0; g < num_groups; ++g)
-    for (int32_t b = group_req_indptr[g]; b < group_req_indptr[g + 1]; ++b) {
-      items.push_back(pkvmla::WorkItem{b, g, prefix_lens[g]});
-      items.push_back(pkvmla::WorkItem{b, num_groups + b, kv_lens[b]});
-    }
-  rc = finish_plan(P, items, sip, sl, si, (hipStream_t)stream);
+  items.reserve((size_t)batch);
+  for (int32_t b = 0; b < batch; ++b)
+    items.push_back(pkvmla::WorkItem{b, num_groups + b, kv_lens[b]});
+  const Level0Groups l0{group_req_indptr, num_groups, prefix_lens};
+  rc = finish_plan(P, items, sip, sl, si, (hipStream_t)stream, &l0);
   if (rc) {
     std::string msg = g_last_error;
     free_plan(P);
@@ -521,7 +608,7 @@ namespace {
 // Bytes of split workspace the plan's runs can touch: partial outputs (bf16)
 // and lse (fp32) for every partial slot a schedule of this plan can use.
 size_t workspace_bytes(const pkvmla_plan_s* P) {
-  const size_t slots = P->fixed_launch ? (size_t)P->cap_units : (size_t)P->sched.n_slots;
+  const size_t slots = P->fixed_launch ? (size_t)P->cap_slots : (size_t)P->sched.n_slots;
   return slots * (size_t)P->num_heads * (pkvmla::kCkvDim * sizeof(uint16_t) + sizeof(float));
 }
 
@@ -538,7 +625,7 @@ int pkvmla_run_strided(pkvmla_plan P, const void* q_nope, const void* q_pe,
                        int64_t kpe_row_stride, void* out, float* lse, void* stream) {
   if (!P) return fail(PKVMLA_EINVAL, "null plan");
   return run_impl(P, q_nope, q_pe, ckv_cache, kpe_cache, ckv_row_stride, kpe_row_stride, out,
-                  lse, stream, P->d_part, (size_t)P->cap_units);
+                  lse, stream, P->d_part, (size_t)P->cap_slots);
 }
 
 int pkvmla_run_noalloc(pkvmla_plan P, const void* q_nope, const void* q_pe,
@@ -624,6 +711,19 @@ int run_impl(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* ck
   const int slot_ev = (int)(P->timed_runs % pkvmla_plan_s::kTimingSlots);
   d.stamps = P->timing ? P->d_stamps + 2 * slot_ev : nullptr;
   if (P->timing) PKVMLA_HIP(hipEventRecord(P->ev[2 * slot_ev], s));
+  if (P->is_cascade && P->sched0.grid > 0) {
+    // level 0: the groups' query rows over their shared prefixes
+    pkvmla::DecodeParams d0 = d;
+    d0.wg_indptr = P->d_wg0;
+    d0.units = P->d_units0;
+    d0.head_groups = P->cfg0.head_groups;
+    d0.n_lanes = P->sched0.grid;
+    d0.waves = P->cfg0.waves;
+    d0.heads_per_wave = P->cfg0.heads_per_wave;
+    d0.stages = P->cfg0.stages;
+    d0.row_blocks = 1;
+    PKVMLA_HIP(pkvmla::launch_decode(d0, s));
+  }
   PKVMLA_HIP(pkvmla::launch_decode(d, s));
   if (P->timing) {
     PKVMLA_HIP(hipEventRecord(P->ev[2 * slot_ev + 1], s));
@@ -639,6 +739,7 @@ int run_impl(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* ck
     m.part_o = d.part_o;
     m.part_lse = d.part_lse;
     m.merges = P->d_merges;
+    m.slot_list = P->d_slot_list;
     m.out = d.out;
     m.lse = lse;
     m.num_heads = P->num_heads;
@@ -713,7 +814,11 @@ int pkvmla_plan_export(pkvmla_plan P, int32_t* buf, int64_t cap, int64_t* used) 
   const int64_t n_wg = (int64_t)P->sched.wg_indptr.size();
   const int64_t n_u = (int64_t)P->sched.units.size();
   const int64_t n_m = (int64_t)P->sched.merges.size();
-  const int64_t need = 32 + n_wg + n_u + n_m + (P->num_seqs + 1) + P->num_seqs + P->n_indices;
+  const int64_t n_wg0 = (int64_t)P->sched0.wg_indptr.size();
+  const int64_t n_u0 = (int64_t)P->sched0.units.size();
+  const int64_t n_sl = (int64_t)P->slot_list.size();
+  const int64_t need = 32 + n_wg + n_u + n_m + (P->num_seqs + 1) + P->num_seqs + P->n_indices +
+                       n_wg0 + n_u0 + n_sl;
   *used = need;
   if (!buf || cap < need) return fail(PKVMLA_EINVAL, "buffer too small: need %lld int32", (long long)need);
   PKVMLA_HIP(hipDeviceSynchronize());
@@ -747,6 +852,10 @@ int pkvmla_plan_export(pkvmla_plan P, int32_t* buf, int64_t cap, int64_t* used) 
   buf[25] = (int32_t)std::min<int64_t>(P->cap_indices, INT32_MAX);
   buf[26] = P->is_qo;
   buf[27] = P->num_requests;
+  buf[28] = P->sched0.grid;
+  buf[29] = (int32_t)(n_u0 / pkvmla::kUnitRecordInts);
+  buf[30] = (int32_t)n_sl;
+  buf[31] = P->cfg0.head_groups;
   int32_t* dst = buf + 32;
   auto pull = [&](const int32_t* src, int64_t n) -> hipError_t {
     hipError_t e = n ? hipMemcpy(dst, src, n * sizeof(int32_t), hipMemcpyDeviceToHost) : hipSuccess;
@@ -759,12 +868,18 @@ int pkvmla_plan_export(pkvmla_plan P, int32_t* buf, int64_t cap, int64_t* used) 
   PKVMLA_HIP(pull(P->d_seq_indptr, P->num_seqs + 1));
   PKVMLA_HIP(pull(P->d_seq_lens, P->num_seqs));
   PKVMLA_HIP(pull(P->d_seq_indices, P->n_indices));
+  PKVMLA_HIP(pull(P->d_wg0, n_wg0));
+  PKVMLA_HIP(pull(P->d_units0, n_u0));
+  PKVMLA_HIP(pull(P->d_slot_list, n_sl));
   return ok();
 }
 
 int pkvmla_gather_rows(pkvmla_plan P, int64_t* n_rows) {
   if (!P || !n_rows) return fail(PKVMLA_EINVAL, "null argument");
-  *n_rows = P->sched.total_rows;
+  int64_t n = P->sched.total_rows;
+  for (size_t i = 0; i < P->sched0.units.size(); i += pkvmla::kUnitRecordInts)
+    n += P->sched0.units[i + 3] - P->sched0.units[i + 2];
+  *n_rows = n;
   return ok();
 }
 
@@ -790,7 +905,36 @@ int pkvmla_gather(pkvmla_plan P, const void* ckv_cache, const void* kpe_cache, v
   g.ckv_stride = pkvmla::kCkvDim * 2;
   g.kpe_stride = pkvmla::kKpeDim * 2;
   const int n_units = (int)(P->sched.units.size() / pkvmla::kUnitRecordInts);
-  PKVMLA_HIP(pkvmla::launch_gather(g, n_units, (hipStream_t)stream));
+  if (!P->is_cascade) {
+    PKVMLA_HIP(pkvmla::launch_gather(g, n_units, (hipStream_t)stream));
+    return ok();
+  }
+  // cascade: the level-0 pieces (prefix tokens, once per row-block piece)
+  // then the suffix units, as gather records (request field unused, row =
+  // tokens before); a temporary table, and a wait before it is freed
+  std::vector<int32_t> gu;
+  int64_t row = 0;
+  auto add = [&](const std::vector<int32_t>& us) {
+    for (size_t i = 0; i < us.size(); i += pkvmla::kUnitRecordInts) {
+      gu.insert(gu.end(), {0, us[i + 1], us[i + 2], us[i + 3], -1, (int32_t)row, us[i + 6], us[i + 7]});
+      row += us[i + 3] - us[i + 2];
+    }
+  };
+  add(P->sched0.units);
+  add(P->sched.units);
+  if (gu.empty()) return ok();
+  if (row > INT32_MAX) return fail(PKVMLA_EUNSUPPORTED, "too many rows");
+  int32_t* d_gu = nullptr;
+  PKVMLA_HIP(hipMalloc(&d_gu, gu.size() * sizeof(int32_t)));
+  hipError_t e = hipMemcpy(d_gu, gu.data(), gu.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+  if (e == hipSuccess) {
+    g.units = d_gu;
+    e = pkvmla::launch_gather(g, (int)(gu.size() / pkvmla::kUnitRecordInts), (hipStream_t)stream);
+  }
+  const hipError_t e2 = hipStreamSynchronize((hipStream_t)stream);
+  (void)hipFree(d_gu);
+  PKVMLA_HIP(e);
+  PKVMLA_HIP(e2);
   return ok();
 }
 

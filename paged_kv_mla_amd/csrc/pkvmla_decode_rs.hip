@@ -39,6 +39,15 @@
 // shares (36 operations) in flight: the vmcnt counter holds at most 63, and a
 // wave with more outstanding cannot wait for them exactly.
 //
+// Row-block units (the level-0 launch of a cascade plan).  The 64 rows of a
+// workgroup are then not the heads of one request but 64 consecutive query
+// rows rho = b * H + head of a prefix group (four requests at 16 heads, two at
+// 32, one at 64, half of one at 128), all scoring the same shared-prefix tile
+// from LDS.  Such a unit's record holds the block's first row, the offset of
+// its rows in the partial-state rows (rho + offset) and the end of the
+// group's rows in place of request, slot and gathered-row index; its rows
+// always write partial states, which the merge combines with the suffix's.
+//
 // Masking.  Only the last tile of a unit can be partial.  Its ckv slots past
 // kv_end copy the last valid row (finite data), its kpe slots the page's own
 // rows; the QK waves set those slots' scores to -inf (a select) before the
@@ -78,12 +87,14 @@ constexpr int kXlOff = kXaOff + 2 * 64 * 4;        // unit row sums:   [parity][
 constexpr int kRsLds = kXlOff + 2 * 64 * 4;
 static_assert(kRsLds <= 160 * 1024, "LDS budget");
 
-// Unit cursor: the unit and tile a role is at, with the unit's fields.
+// Unit cursor: the unit and tile a role is at, with the unit's fields.  For
+// a row-block unit, b is its first query row, slot the offset of its rows in
+// the partial-state rows, and rend the end of its group's rows.
 struct UnitCursor {
   int u;        // unit index
   int tile;     // tile index within the unit
   int ntiles;   // tiles in the unit
-  int b, kv0, kv1, slot;
+  int b, kv0, kv1, slot, rend;
 };
 
 __device__ __forceinline__ void cursor_load(UnitCursor& c, idx_ptr units) {
@@ -92,6 +103,7 @@ __device__ __forceinline__ void cursor_load(UnitCursor& c, idx_ptr units) {
   c.kv0 = rec[2];
   c.kv1 = rec[3];
   c.slot = rec[4];
+  c.rend = rec[5];
   c.ntiles = (c.kv1 - c.kv0 + kTile - 1) / kTile;
   c.tile = 0;
 }
@@ -107,8 +119,8 @@ __device__ __forceinline__ void cursor_next(UnitCursor& c, idx_ptr units, int u_
 // PACKED: the caches are packed [pages, page_size, 512] and [.., 64] tensors
 // (row strides 1 KB and 128 B, compile-time constants); otherwise the row
 // strides cs_arg and ks_arg (bytes) apply, e.g. the two views of one
-// [pages, page_size, 576] cache.
-template <bool BIG, int HB, bool PACKED>
+// [pages, page_size, 576] cache.  ROWS: the units are row blocks (above).
+template <bool BIG, int HB, bool PACKED, bool ROWS>
 __global__ void __launch_bounds__(rs_threads(HB), 1)
 mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
                      const uint16_t* __restrict__ ckv_cache, const uint16_t* __restrict__ kpe_cache,
@@ -160,6 +172,11 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
     const int g = lane >> 4;
     const int li = lane & 15;
     const int head = hg * HEADS + r * 16 + li;
+    // the query row of this lane in a unit (rows past a row block's group
+    // load the group's last row and write nothing)
+    auto q_row = [&](int b, int rend) -> int {
+      return ROWS ? min(b + hg * HEADS + r * 16 + li, rend - 1) : b * H + head;
+    };
     int offA[2], offK[2];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
@@ -171,9 +188,9 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
     cursor_load(cq, units);
     // the unit's query: lane (g, li) holds Q[head][ks*32 + g*8 .. +7]
     bf16x8_t q[18];
-    auto load_q = [&](int b) {
-      const char* qn = reinterpret_cast<const char*>(q_nope + ((size_t)b * H + head) * kCkvDim);
-      const char* qp = reinterpret_cast<const char*>(q_pe + ((size_t)b * H + head) * kKpeDim);
+    auto load_q = [&](int row) {
+      const char* qn = reinterpret_cast<const char*>(q_nope + (size_t)row * kCkvDim);
+      const char* qp = reinterpret_cast<const char*>(q_pe + (size_t)row * kKpeDim);
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks)
         q[ks] = *reinterpret_cast<const bf16x8_t*>(qn + (ks * 32 + g * 8) * 2);
@@ -184,7 +201,7 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
     // the query loads go out after the copy waves have issued tile 0, so that
     // tile's copies do not queue behind them in the memory pipeline
     lds_barrier();
-    load_q(cq.b);
+    load_q(q_row(cq.b, cq.rend));
     float m_run = -INFINITY, l_run = 0.f;
 
     lds_barrier();  // tile 0 has landed
@@ -233,7 +250,10 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
         __builtin_amdgcn_s_setprio(0);
         // Q of the next unit goes out once the last k-step has read this
         // unit's, so its latency hides behind the softmax and the barrier
-        if (cq.tile == cq.ntiles - 1 && cq.u + 1 < u_end) load_q(units[(size_t)(cq.u + 1) * kUnitInts]);
+        if (cq.tile == cq.ntiles - 1 && cq.u + 1 < u_end) {
+          idx_ptr nrec = units + (size_t)(cq.u + 1) * kUnitInts;
+          load_q(q_row(nrec[0], ROWS ? nrec[5] : 0));
+        }
         // ---- softmax of this tile: lane (g, li) holds tokens tb*16 + g*4 + k ----
         const int valid = min(cq.kv1 - (cq.kv0 + cq.tile * kTile), kTile);
         float sv[8];
@@ -278,8 +298,14 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
           const float lse = m_run * sm_scale + __builtin_amdgcn_logf(l) * 0.69314718055994531f;
           if (g == 0) {
             *(LDS_AS float*)(smem + kXlOff + (par * 64 + li * 4 + r) * 4) = l;
-            if (cq.slot < 0) lse_out[(size_t)cq.b * H + head] = lse;
-            else part_lse[(size_t)cq.slot * H + head] = lse;
+            if (ROWS) {
+              const int row = cq.b + hg * HEADS + r * 16 + li;
+              if (row < cq.rend) part_lse[cq.slot + row] = lse;
+            } else if (cq.slot < 0) {
+              lse_out[(size_t)cq.b * H + head] = lse;
+            } else {
+              part_lse[(size_t)cq.slot * H + head] = lse;
+            }
           }
         }
         cursor_next(cq, units, u_end);
@@ -400,11 +426,15 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
         const uint32_t col = (uint32_t)(lie * kCkvDim + r * (kRsDBW * 16) + (ge >> 1) * 8);
         // a whole request's rows go to out, a split unit's to its partial slot
         // (both bf16)
+        // (a row block's rows: partial-state rows from its first row plus
+        // the unit's offset; head blocks past its group's rows store nothing)
         char* obase = reinterpret_cast<char*>(
-            cp.slot < 0 ? out + ((size_t)cp.b * H + hg * HEADS) * kCkvDim
-                        : part_o + ((size_t)cp.slot * H + hg * HEADS) * kCkvDim);
+            ROWS ? part_o + (size_t)(cp.slot + cp.b + hg * HEADS) * kCkvDim
+            : cp.slot < 0 ? out + ((size_t)cp.b * H + hg * HEADS) * kCkvDim
+                          : part_o + ((size_t)cp.slot * H + hg * HEADS) * kCkvDim);
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) {
+          if (ROWS && cp.b + hg * HEADS + hb * 16 >= cp.rend) break;
           const uint32_t row = col + (uint32_t)hb * 16 * kCkvDim;
 #pragma unroll
           for (int dp = 0; dp < kRsDBW / 2; ++dp) {
@@ -496,7 +526,10 @@ int decode_rs_head_blocks(int waves, int heads_per_wave, int num_heads, int head
 }
 
 bool launch_decode_rs(const DecodeParams& p, hipStream_t stream, hipError_t* err) {
-  const int hb = decode_rs_head_blocks(p.waves, p.heads_per_wave, p.num_heads, p.head_groups);
+  // row-block units: 64 rows per workgroup at every head count
+  const int hb = p.row_blocks ? (p.waves == 4 + kRsPvWaves && p.heads_per_wave == 16 ? 4 : 0)
+                              : decode_rs_head_blocks(p.waves, p.heads_per_wave, p.num_heads,
+                                                      p.head_groups);
   if (!hb) return false;
   const bool big = p.log2_ps >= 5;
   const bool packed = p.ckv_stride == kCkvDim * 2 && p.kpe_stride == kKpeDim * 2;
@@ -505,16 +538,20 @@ bool launch_decode_rs(const DecodeParams& p, hipStream_t stream, hipError_t* err
   p.q_nope, p.q_pe, p.ckv, p.kpe, p.out, p.lse, p.part_o, p.part_lse, p.wg_indptr, p.units, \
       p.seq_indices, p.num_heads, p.head_groups, p.n_lanes, p.log2_ps, p.sm_scale,     \
       p.score_log2, p.rescale_thr, p.ckv_stride, p.kpe_stride, p.stamps
-#define PKVMLA_RS_LAUNCH2(HBV, PK)                                                             \
-  if (big) mla_decode_rs_kernel<true, HBV, PK><<<grid, block, 0, stream>>>(PKVMLA_RS_ARGS);    \
-  else mla_decode_rs_kernel<false, HBV, PK><<<grid, block, 0, stream>>>(PKVMLA_RS_ARGS);
-#define PKVMLA_RS_LAUNCH(HBV)                 \
-  if (packed) { PKVMLA_RS_LAUNCH2(HBV, true) } \
-  else { PKVMLA_RS_LAUNCH2(HBV, false) }
-  switch (hb) {
-    case 1: PKVMLA_RS_LAUNCH(1) break;
-    case 2: PKVMLA_RS_LAUNCH(2) break;
-    default: PKVMLA_RS_LAUNCH(4) break;
+#define PKVMLA_RS_LAUNCH2(HBV, PK, RB)                                                           \
+  if (big) mla_decode_rs_kernel<true, HBV, PK, RB><<<grid, block, 0, stream>>>(PKVMLA_RS_ARGS);  \
+  else mla_decode_rs_kernel<false, HBV, PK, RB><<<grid, block, 0, stream>>>(PKVMLA_RS_ARGS);
+#define PKVMLA_RS_LAUNCH(HBV, RB)                 \
+  if (packed) { PKVMLA_RS_LAUNCH2(HBV, true, RB) } \
+  else { PKVMLA_RS_LAUNCH2(HBV, false, RB) }
+  if (p.row_blocks) {
+    PKVMLA_RS_LAUNCH(4, true)
+  } else {
+    switch (hb) {
+      case 1: PKVMLA_RS_LAUNCH(1, false) break;
+      case 2: PKVMLA_RS_LAUNCH(2, false) break;
+      default: PKVMLA_RS_LAUNCH(4, false) break;
+    }
   }
 #undef PKVMLA_RS_LAUNCH
 #undef PKVMLA_RS_LAUNCH2

@@ -13,7 +13,7 @@ constexpr int kTile = 32;           // KV tokens per tile
 constexpr int kUnitInts = 8;        // b, seq, kv_begin, kv_end, slot, row, page_base, first_page
                                     // (page_base: start of seq's page list in seq_indices;
                                     //  first_page: the page of token kv_begin)
-constexpr int kMergeInts = 4;       // b, first_slot, count, 0
+constexpr int kMergeInts = 4;       // b, first_slot (or first list entry), count, kind
 constexpr int kStageBytes = kTile * kCkvDim * 2 + kTile * kKpeDim * 2;  // 36864
 constexpr int kIndexPad = 64;       // margin of valid page ids after the device index table
 
@@ -47,6 +47,7 @@ struct DecodeParams {
   int32_t n_lanes;           // schedule lanes (workgroups per head group)
   int32_t waves, heads_per_wave, stages;
   int32_t log2_ps;
+  int32_t row_blocks;        // units are row blocks of a cascade plan's level 0
   float sm_scale;
   float score_log2;          // sm_scale * log2(e)
   float rescale_thr;         // raw-score margin before the running max moves (8 / score_log2)
@@ -57,7 +58,9 @@ struct DecodeParams {
 struct MergeParams {
   const uint16_t* part_o;    // [slots][H][512] bf16
   const float* part_lse;
-  const int32_t* merges;     // [n_merges][4]
+  const int32_t* merges;     // [n_merges][4]: b, first, count, kind (0: slots first ..
+                             // first + count - 1; 1: slots slot_list[first .. first + count - 1])
+  const int32_t* slot_list;
   uint16_t* out;
   float* lse;
   int32_t num_heads;

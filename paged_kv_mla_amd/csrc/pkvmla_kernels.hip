@@ -28,6 +28,9 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(MergeParams p) {
   const int32_t* mr = p.merges + (size_t)blockIdx.x * kMergeInts;
   const int b = mr[0], s0 = mr[1], n = mr[2];
   if (n <= 0) return;  // an unused record slot of a plan with fixed launches
+  // kind 1: the request's slots are listed (a cascade plan's prefix states
+  // sit in its level-0 row blocks' slots)
+  const int32_t* list = mr[3] == 1 ? p.slot_list + s0 : nullptr;
   const int H = p.num_heads;
   const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
   const int d0 = (threadIdx.x & 63) * 8;
@@ -41,7 +44,8 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(MergeParams p) {
     float lv[kChunk];
 #pragma unroll
     for (int j = 0; j < kChunk; ++j) {
-      const size_t base = (size_t)(s0 + min(i0 + j, n - 1)) * H + h;
+      const int e = min(i0 + j, n - 1);
+      const size_t base = (size_t)(list ? list[e] : s0 + e) * H + h;
       lv[j] = p.part_lse[base];
       x[j] = *reinterpret_cast<const uint4*>(p.part_o + base * kCkvDim + d0);
     }

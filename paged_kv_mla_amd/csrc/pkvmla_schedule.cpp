@@ -12,6 +12,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <array>
 #include <vector>
 
 #include "pkvmla_schedule.h"
@@ -109,6 +110,95 @@ bool build_schedule(const std::vector<WorkItem>& items, int32_t batch, int32_t n
   s->n_slots = slot;
   s->total_rows = row;
   return true;
+}
+
+// Level-0 schedule.  Blocks: for each group with a non-empty prefix, its rows
+// [first request * H, end request * H) cut into blocks of row_block_rows(H).
+// With nb blocks on W lanes:
+//   nb <= W: every block is cut into S = floor(W / nb) token pieces (never
+//     more pieces than the prefix has tiles), piece s of block k on lane
+//     k * S + s.  Lanes are placed round-robin on the eight XCDs (lane l on
+//     XCD l mod 8): with S = 1 every lane walks its prefix from the first
+//     tile at the same time, so the workgroups of one XCD read each tile from
+//     its L2 after the first; with S a multiple of 8 each XCD streams only
+//     its own pieces of every prefix.
+//   nb > W: block k goes whole to lane k mod W.
+// Piece s of a prefix of T tiles covers tiles [s*T/P, (s+1)*T/P) (P pieces).
+bool build_row_schedule(const int32_t* group_req_indptr, int32_t num_groups,
+                        const int32_t* prefix_lens, int32_t num_heads, int32_t num_wg,
+                        int32_t tile, RowSchedule* s) {
+  if (num_wg < 1 || tile < 1 || num_heads < 1 || num_groups < 0) return false;
+  struct Block {
+    int32_t g, row0, row_end, len;
+  };
+  std::vector<Block> blocks;
+  const int32_t rb = row_block_rows(num_heads);
+  for (int32_t g = 0; g < num_groups; ++g) {
+    if (prefix_lens[g] <= 0) continue;
+    const int64_t r0 = (int64_t)group_req_indptr[g] * num_heads;
+    const int64_t r1 = (int64_t)group_req_indptr[g + 1] * num_heads;
+    for (int64_t r = r0; r < r1; r += rb)
+      blocks.push_back(Block{g, (int32_t)r, (int32_t)std::min<int64_t>(r + rb, r1), prefix_lens[g]});
+  }
+  const int64_t nb = (int64_t)blocks.size();
+  std::vector<std::vector<std::array<int32_t, 4>>> lane_units;  // block, kv_begin, kv_end
+  if (nb == 0) {
+    s->grid = 0;
+  } else if (nb <= num_wg) {
+    const int64_t S = num_wg / nb;
+    s->grid = (int32_t)(nb * S);
+    lane_units.assign((size_t)s->grid, {});
+    for (int64_t k = 0; k < nb; ++k) {
+      const int64_t T = ceil_div(blocks[k].len, tile);
+      const int64_t P = std::min<int64_t>(S, T);
+      for (int64_t p = 0; p < P; ++p) {
+        const int64_t t0 = p * T / P, t1 = (p + 1) * T / P;
+        lane_units[(size_t)(k * S + p)].push_back(
+            {(int32_t)k, (int32_t)(t0 * tile), (int32_t)std::min<int64_t>(t1 * tile, blocks[k].len), 0});
+      }
+    }
+  } else {
+    s->grid = num_wg;
+    lane_units.assign((size_t)num_wg, {});
+    for (int64_t k = 0; k < nb; ++k)
+      lane_units[(size_t)(k % num_wg)].push_back({(int32_t)k, 0, blocks[k].len, 0});
+  }
+  s->wg_indptr.assign((size_t)s->grid + 1, 0);
+  s->units.clear();
+  int64_t slot = 0;
+  for (int32_t l = 0; l < s->grid; ++l) {
+    for (const auto& u : lane_units[(size_t)l]) {
+      const Block& b = blocks[(size_t)u[0]];
+      const int64_t off = slot * num_heads - b.row0;
+      if (off < INT32_MIN || off > INT32_MAX) return false;
+      s->units.insert(s->units.end(), {b.row0, b.g, u[1], u[2], (int32_t)off, b.row_end, 0, 0});
+      slot += (b.row_end - b.row0) / num_heads;
+    }
+    s->wg_indptr[(size_t)l + 1] = (int32_t)(s->units.size() / kUnitRecordInts);
+  }
+  if (slot > INT32_MAX) return false;
+  s->n_slots = (int32_t)slot;
+  return true;
+}
+
+void build_cascade_merges(const RowSchedule& l0, const std::vector<int32_t>& l1_units,
+                          int32_t batch, int32_t num_heads, std::vector<int32_t>* merges,
+                          std::vector<int32_t>* slot_list) {
+  std::vector<std::vector<int32_t>> per(batch);
+  for (size_t i = 0; i < l0.units.size(); i += kUnitRecordInts) {
+    const int32_t* u = &l0.units[i];
+    const int32_t first = (u[4] + u[0]) / num_heads;  // slot of the block's first request
+    for (int32_t b = u[0] / num_heads; b < u[5] / num_heads; ++b)
+      per[b].push_back(first + (b - u[0] / num_heads));
+  }
+  for (size_t i = 0; i < l1_units.size(); i += kUnitRecordInts)
+    per[l1_units[i]].push_back(l1_units[i + 4]);
+  merges->clear();
+  slot_list->clear();
+  for (int32_t b = 0; b < batch; ++b) {
+    merges->insert(merges->end(), {b, (int32_t)slot_list->size(), (int32_t)per[b].size(), 1});
+    slot_list->insert(slot_list->end(), per[b].begin(), per[b].end());
+  }
 }
 
 }  // namespace pkvmla

@@ -31,6 +31,32 @@ struct Schedule {
 bool build_schedule(const std::vector<WorkItem>& items, int32_t batch, int32_t num_wg,
                     int32_t tile, int32_t fixed, Schedule* s);
 
+// Level 0 of a cascade plan: the shared prefix of each group scored by row
+// blocks of its query rows (rho = b * H + head).  Unit records:
+// row0, group, kv_begin, kv_end, slot offset (first slot * H - row0), row_end,
+// then the two page fields the plan fills.  Slots 0 .. n_slots - 1, each
+// unit taking one per request of its rows, in emission order.
+struct RowSchedule {
+  int32_t grid = 0;
+  int32_t n_slots = 0;
+  std::vector<int32_t> wg_indptr;  // grid + 1
+  std::vector<int32_t> units;      // n_units * 8
+};
+
+// Rows per block at a head count (64, or a whole request above 64 heads).
+inline int32_t row_block_rows(int32_t num_heads) { return num_heads > 64 ? num_heads : 64; }
+
+bool build_row_schedule(const int32_t* group_req_indptr, int32_t num_groups,
+                        const int32_t* prefix_lens, int32_t num_heads, int32_t num_wg,
+                        int32_t tile, RowSchedule* s);
+
+// Merge records (b, first list entry, count, 1) and the slot list of a
+// cascade plan: per request its level-0 slots (level-0 emission order) then
+// its level-1 slots (the `l1` units' slot fields, emission order).
+void build_cascade_merges(const RowSchedule& l0, const std::vector<int32_t>& l1_units,
+                          int32_t batch, int32_t num_heads, std::vector<int32_t>* merges,
+                          std::vector<int32_t>* slot_list);
+
 }  // namespace pkvmla
 
 #endif  // PKVMLA_SCHEDULE_H_

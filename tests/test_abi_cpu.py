@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 
 import paged_kv_mla_amd as pk
-from oracle.schedule_ref import schedule_ref, flat_items, cascade_items, kernel_config
+from oracle.schedule_ref import (schedule_ref, flat_items, suffix_items, row_schedule_ref,
+                                 kernel_config)
 from mla_workloads import config_lens, CONFIGS
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -64,10 +65,41 @@ def test_schedule_host_matches_reference(name, num_cu):
 def test_schedule_host_matches_reference_cascade():
     prefix, suffix = config_lens("cascade")
     B = len(suffix)
-    items = cascade_items(np.array([0, B]), np.array([prefix]), suffix)
-    _compare(items, B, 256, 32, 2)
-    items = cascade_items(np.array([0, 2, 5]), np.array([64, 0]), np.array([3, 0, 40, 0, 1]))
-    _compare(items, 5, 512, 32, 1)
+    _compare(suffix_items(1, suffix), B, 128, 32, 4)
+    _compare(suffix_items(2, np.array([3, 0, 40, 0, 1])), 5, 512, 32, 1)
+
+
+def _compare_rows(gi, pl, H, W):
+    w1, u1, n1 = pk.schedule_rows_host(gi, pl, H, W)
+    w2, u2, n2 = row_schedule_ref(gi, pl, H, W)
+    np.testing.assert_array_equal(w1, w2)
+    np.testing.assert_array_equal(u1, u2)
+    assert n1 == n2
+
+
+def test_row_schedule_host_matches_reference():
+    prefix, suffix = config_lens("cascade")
+    for H in (16, 32, 64, 128):
+        for W in (256 // max(1, H // 64), 7, 1, 300):
+            _compare_rows([0, len(suffix)], [prefix], H, W)
+    _compare_rows([0, 2, 5], [64, 0], 16, 512)
+    _compare_rows([0, 3], [100], 128, 2)
+    rng = np.random.default_rng(11)
+    for _ in range(150):
+        G = int(rng.integers(1, 6))
+        sizes = rng.integers(0, 9, size=G)
+        gi = np.concatenate([[0], np.cumsum(sizes)])
+        pl = rng.integers(0, 5000, size=G)
+        _compare_rows(gi, pl, int(rng.choice([16, 32, 64, 128])), int(rng.integers(1, 400)))
+
+
+def test_row_schedule_host_rejects():
+    with pytest.raises(pk.PkvmlaError):
+        pk.schedule_rows_host([1, 2], [10], 16, 8)          # indptr[0] != 0
+    with pytest.raises(pk.PkvmlaError):
+        pk.schedule_rows_host([0, 2], [-1], 16, 8)          # negative prefix
+    with pytest.raises(pk.PkvmlaError):
+        pk.schedule_rows_host([0, 2], [10], 24, 8)          # heads not a multiple of 16
 
 
 def test_schedule_host_random_cases():

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from oracle.schedule_ref import (schedule_ref, flat_items, cascade_items, qo_items,
+from oracle.schedule_ref import (schedule_ref, flat_items, cascade_plan_ref, qo_items,
                                  kernel_config, unit_page_fields)
 from mla_workloads import (make_flat, make_cascade, make_config, make_qo, stress_variant,
                            stress_variant_cascade, poison_unreferenced, permute_pages,
@@ -73,10 +73,22 @@ def test_gather_bit_exact(name):
 def test_gather_bit_exact_cascade():
     cas = make_cascade("cg", 64, 5, 16, 16, [32, 48], [1, 20, 0, 33, 5], groups=2)
     note("gather cascade")
-    rows = pk.plan_for(cas).gather(dev_bf16(cas.ckv), dev_bf16(cas.kpe))
-    flat = cas.flat_view()
-    ref = oracle.gather_ref(flat.ckv, flat.kpe, flat.kv_indptr, flat.kv_indices, flat.kv_lens,
-                            flat.page_size)
+    plan = pk.plan_for(cas)
+    rows = plan.gather(dev_bf16(cas.ckv), dev_bf16(cas.kpe))
+    # expected: each level-0 piece's prefix tokens, then each suffix unit's
+    # tokens (the token ranges from the oracle's own schedule re-derivation)
+    ex = plan.export()
+    r = cascade_plan_ref(cas.group_req_indptr, cas.prefix_lens, cas.kv_lens, 16,
+                         max(1, ex.num_cu // ex.head_groups), ex.num_cu, 32, int(ex.header[11]))
+    G = cas.num_groups
+    seq_indptr = np.concatenate([cas.prefix_indptr, cas.prefix_indptr[G] + cas.kv_indptr[1:]])
+    seq_indices = np.concatenate([cas.prefix_indices[:cas.prefix_indptr[G]], cas.kv_indices])
+    seq_lens = np.concatenate([cas.prefix_lens, cas.kv_lens])
+    full = oracle.gather_ref(cas.ckv, cas.kpe, seq_indptr, seq_indices, seq_lens, cas.page_size)
+    start = np.concatenate([[0], np.cumsum(seq_lens)])
+    ref = [full[start[u[1]] + u[2]:start[u[1]] + u[3]]
+           for u in np.concatenate([r["units0"], r["units"]])]
+    ref = np.concatenate(ref) if ref else np.zeros((0, 576), np.uint16)
     assert np.array_equal(bits_of(rows), ref)
 
 
@@ -111,22 +123,29 @@ def test_plan_export_bit_exact(name):
     assert ex.sm_scale == np.float32(1.0 / math.sqrt(576))
 
 
-def test_plan_export_cascade():
-    cas = make_cascade("ce", 65, 6, 64, 16, [32, 48], [1, 20, 0, 33, 5, 7], groups=2)
-    note("export cascade")
+@pytest.mark.parametrize("H", [16, 64, 128])
+def test_plan_export_cascade(H):
+    cas = make_cascade("ce", 65 + H, 6, H, 16, [32, 48], [1, 20, 0, 33, 5, 7], groups=2)
+    note(f"export cascade H{H}")
     ex = pk.plan_for(cas).export()
-    kc = kernel_config(64)
+    kc = kernel_config(H)
     hdr = ex.header
-    items = cascade_items(cas.group_req_indptr, cas.prefix_lens, cas.kv_lens)
     lanes = max(1, ex.num_cu * int(hdr[10]) // ex.head_groups)
-    wg, units, merges = schedule_ref(items, cas.batch, lanes, kc["tile"], int(hdr[11]))
+    hg0 = max(1, H // 64)
+    assert int(hdr[31]) == hg0
+    r = cascade_plan_ref(cas.group_req_indptr, cas.prefix_lens, cas.kv_lens, H, lanes,
+                         max(1, ex.num_cu // hg0), kc["tile"], int(hdr[11]))
     G = cas.num_groups
     seq_indptr = np.concatenate([cas.prefix_indptr, cas.prefix_indptr[G] + cas.kv_indptr[1:]])
     seq_indices = np.concatenate([cas.prefix_indices[:cas.prefix_indptr[G]], cas.kv_indices])
-    units = unit_page_fields(units, seq_indptr, seq_indices, cas.page_size)
-    np.testing.assert_array_equal(ex.units, units)
-    np.testing.assert_array_equal(ex.merges, merges)
-    np.testing.assert_array_equal(ex.wg_indptr, wg)
+    np.testing.assert_array_equal(ex.units, unit_page_fields(r["units"], seq_indptr, seq_indices,
+                                                             cas.page_size))
+    np.testing.assert_array_equal(ex.units0, unit_page_fields(r["units0"], seq_indptr,
+                                                              seq_indices, cas.page_size))
+    np.testing.assert_array_equal(ex.merges, r["merges"])
+    np.testing.assert_array_equal(ex.slot_list, r["slot_list"])
+    np.testing.assert_array_equal(ex.wg_indptr, r["wg"])
+    np.testing.assert_array_equal(ex.wg_indptr0, r["wg0"])
     np.testing.assert_array_equal(ex.seq_lens, np.concatenate([cas.prefix_lens, cas.kv_lens]))
     np.testing.assert_array_equal(ex.seq_indptr, seq_indptr)
     np.testing.assert_array_equal(ex.seq_indices, seq_indices)

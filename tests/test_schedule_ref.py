@@ -4,7 +4,7 @@ structural invariants that hold for any valid schedule)."""
 import numpy as np
 import pytest
 
-from oracle.schedule_ref import schedule_ref, flat_items, cascade_items, kernel_config
+from oracle.schedule_ref import schedule_ref, flat_items, kernel_config
 from mla_workloads import config_lens, CONFIGS
 
 
@@ -82,22 +82,59 @@ def test_deepseek_balance():
     assert cost.max() <= cost.mean() * 1.15
 
 
-def test_cascade_items_and_schedule():
-    items = cascade_items(np.array([0, 2, 5]), np.array([64, 0]), np.array([3, 0, 40, 0, 1]))
-    assert items == [(0, 0, 64), (0, 2, 3), (1, 0, 64), (1, 3, 0), (2, 1, 0), (2, 4, 40),
-                     (3, 1, 0), (3, 5, 0), (4, 1, 0), (4, 6, 1)]
-    wg, units, merges = check_schedule(items, 5, 512, 32, 1)
-    # request 3 has no tokens at all in this hand-made table: it gets no unit
-    assert 3 not in set(units[:, 0].tolist())
+def test_row_schedule_hand_cases():
+    """Level-0 schedules worked out by hand from the rule."""
+    from oracle.schedule_ref import row_schedule_ref
+    # one group of two requests at 16 heads (32 rows, one block), 64-token
+    # prefix (2 tiles), 512 lanes: S = 512 pieces asked, 2 tiles give 2 pieces
+    wg, units, ns = row_schedule_ref([0, 2, 5], [64, 0], 16, 512)
+    assert len(wg) == 513 and wg[1] == 1 and wg[2] == 2 and wg[-1] == 2
+    assert units.tolist() == [[0, 0, 0, 32, 0, 32, 0, 0], [0, 0, 32, 64, 32, 32, 0, 0]]
+    assert ns == 4     # two requests per piece
+    # three requests at 128 heads (a block each), 2 lanes: blocks 0 and 2 on
+    # lane 0, block 1 on lane 1; slots in lane order 0, 1 | 2
+    wg, units, ns = row_schedule_ref([0, 3], [100], 128, 2)
+    assert wg.tolist() == [0, 2, 3]
+    assert units.tolist() == [[0, 0, 0, 100, 0, 128, 0, 0], [256, 0, 0, 100, -128, 384, 0, 0],
+                              [128, 0, 0, 100, 128, 256, 0, 0]]
+    assert ns == 3
+    # 32 heads, 5 requests: rows 0..159 -> blocks of 64, 64, 32 rows; 7 lanes:
+    # S = 2 pieces each of a 3-tile prefix: tiles [0,1) and [1,3)
+    wg, units, ns = row_schedule_ref([0, 5], [70], 32, 7)
+    assert wg.tolist() == [0, 1, 2, 3, 4, 5, 6]
+    assert [u[:6] for u in units.tolist()] == [
+        [0, 0, 0, 32, 0, 64], [0, 0, 32, 70, 64, 64],
+        [64, 0, 0, 32, 64, 128], [64, 0, 32, 70, 128, 128],
+        [128, 0, 0, 32, 128, 160], [128, 0, 32, 70, 160, 160]]
+    assert ns == 10
+
+
+def test_cascade_plan_merge_lists_hand_case():
+    """Two groups ([0, 2) with a 64-token prefix, [2, 5) with none), suffixes
+    3, 0, 40, 2, 1 at 16 heads; 512 level-0 lanes, 512 level-1 lanes."""
+    from oracle.schedule_ref import cascade_plan_ref
+    r = cascade_plan_ref([0, 2, 5], [64, 0], [3, 0, 40, 2, 1], 16, 512, 512, 32, 1)
+    # level 0: piece 0 (lane 0) holds slots 0, 1 (requests 0, 1), piece 1
+    # (lane 1) slots 2, 3.  Level 1: cost 2 + 3 + 2 + 2 = 9 on 512 lanes gives
+    # the minimum cap 2, one tile per unit: request 2's 40 tokens take two
+    # units.  Slots 4..8 in emission order.
+    assert r["units"][:, :5].tolist() == [[0, 2, 0, 3, 4], [2, 4, 0, 32, 5], [2, 4, 32, 40, 6],
+                                          [3, 5, 0, 2, 7], [4, 6, 0, 1, 8]]
+    assert r["merges"].tolist() == [[0, 0, 3, 1], [1, 3, 2, 1], [2, 5, 2, 1], [3, 7, 1, 1],
+                                    [4, 8, 1, 1]]
+    assert r["slot_list"].tolist() == [0, 2, 4, 1, 3, 5, 6, 7, 8]
 
 
 def test_cascade_config_schedule():
+    from oracle.schedule_ref import cascade_plan_ref
     prefix, suffix = config_lens("cascade")
     B = len(suffix)
     kc = kernel_config(128)
-    items = cascade_items(np.array([0, B]), np.array([prefix]), suffix)
-    wg, units, merges = check_schedule(items, B, 256, kc["tile"], kc["fixed_cost"])
-    assert len(merges) == B          # every request has prefix and suffix units
+    r = cascade_plan_ref([0, B], [prefix], suffix, 128, 128, 128, kc["tile"], kc["fixed_cost"])
+    # one lane per request, each walking the whole prefix from its first tile
+    assert len(r["wg0"]) == B + 1 and r["units0"].shape[0] == B
+    assert (r["units0"][:, 2] == 0).all() and (r["units0"][:, 3] == prefix).all()
+    assert r["merges"][:, 2].min() >= 2      # a prefix state and at least one suffix state
 
 
 def test_unit_page_fields_hand_case():
