@@ -112,7 +112,8 @@ int pkvmla_plan_create_with_capacity(const int32_t* kv_indptr, const int32_t* kv
  * (eager, or a graph replayed on `stream`) sees the new ones; work on other
  * streams must be ordered by the caller.  PKVMLA_EINVAL when the arrays are
  * malformed or kv_indptr[batch] exceeds the plan's page-id capacity (the
- * plan is then unchanged); PKVMLA_EUNSUPPORTED for a cascade plan. */
+ * plan is then unchanged, as it is for a cascade plan, which takes
+ * pkvmla_plan_update_cascade). */
 int pkvmla_plan_update(pkvmla_plan plan, const int32_t* kv_indptr, const int32_t* kv_indices,
                        const int32_t* kv_lens, void* stream);
 
@@ -159,6 +160,33 @@ int pkvmla_plan_create_cascade(const int32_t* group_req_indptr, int32_t num_grou
                                int32_t num_heads, int32_t ckv_dim, int32_t kpe_dim,
                                int32_t page_size, float sm_scale, void* stream,
                                pkvmla_plan* out);
+
+/* pkvmla_plan_create_cascade with device tables, split workspace and launch
+ * shapes sized once (index_capacity > 0: page ids of prefixes and suffixes
+ * together) for later pkvmla_plan_update_cascade calls, so that a HIP graph
+ * captured around pkvmla_run stays valid across them.  The vLLM page "[WIP]
+ * [Kernel] Flashinfer MLA support" names graph capture of the decode path as
+ * the part that did not yet work there.  Every level-0 and level-1 lane and
+ * every merge record is launched on each run (empty ones return at once).
+ * index_capacity 0 is pkvmla_plan_create_cascade. */
+int pkvmla_plan_create_cascade_with_capacity(
+    const int32_t* group_req_indptr, int32_t num_groups, const int32_t* prefix_indptr,
+    const int32_t* prefix_indices, const int32_t* prefix_lens, const int32_t* kv_indptr,
+    const int32_t* kv_indices, const int32_t* kv_lens, int32_t batch, int32_t num_pages,
+    int32_t num_heads, int32_t ckv_dim, int32_t kpe_dim, int32_t page_size, float sm_scale,
+    int64_t index_capacity, void* stream, pkvmla_plan* out);
+
+/* Replace a cascade plan's groups (same num_groups and batch), prefixes and
+ * suffixes (arrays as in pkvmla_plan_create_cascade, read during the call
+ * only) and recompute both levels' schedules and the merge lists, in place,
+ * without allocation.  Ordering and graph validity as for
+ * pkvmla_plan_update.  PKVMLA_EINVAL when the arrays are malformed, a flat
+ * plan is given, or the page ids exceed the plan's capacity (the plan is then
+ * unchanged). */
+int pkvmla_plan_update_cascade(pkvmla_plan plan, const int32_t* group_req_indptr,
+                               const int32_t* prefix_indptr, const int32_t* prefix_indices,
+                               const int32_t* prefix_lens, const int32_t* kv_indptr,
+                               const int32_t* kv_indices, const int32_t* kv_lens, void* stream);
 
 /* Run the decode for one set of tensors (e.g. one layer) on `stream`.  The
  * plan-then-run split and the run's operands (q_nope, q_pe, the ckv and kpe

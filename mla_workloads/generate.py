@@ -232,9 +232,12 @@ def make_qo(name: str, seed: int, batch: int, num_heads: int, page_size: int, le
 
 def make_cascade(name: str, seed: int, batch: int, num_heads: int, page_size: int,
                  prefix_len, suffix, groups: int = 1,
-                 sm_scale: Optional[float] = None) -> CascadeInputs:
+                 sm_scale: Optional[float] = None,
+                 pool_pages: Optional[int] = None) -> CascadeInputs:
     """Shared-prefix batch.  ``prefix_len`` is an int (same for all groups) or a list;
-    ``suffix`` is (lo, hi) for uniform suffix lengths or an explicit list."""
+    ``suffix`` is (lo, hi) for uniform suffix lengths or an explicit list.
+    ``pool_pages`` fixes the pool size (at least the pages needed; the tables
+    take the first pages of a permutation of the whole pool)."""
     rng = np.random.default_rng(seed)
     if isinstance(suffix, tuple):
         kv_lens = rng.integers(suffix[0], suffix[1], size=batch, endpoint=True).astype(np.int32)
@@ -250,6 +253,10 @@ def make_cascade(name: str, seed: int, batch: int, num_heads: int, page_size: in
     ppages = (prefix_lens.astype(np.int64) + page_size - 1) // page_size
     spages = (kv_lens.astype(np.int64) + page_size - 1) // page_size
     num_pages = int(ppages.sum() + spages.sum())
+    if pool_pages is not None:
+        if pool_pages < num_pages:
+            raise ValueError(f"pool of {pool_pages} pages is below the {num_pages} needed")
+        num_pages = int(pool_pages)
     perm = rng.permutation(num_pages).astype(np.int32)
     prefix_indptr = np.zeros(groups + 1, dtype=np.int32)
     prefix_indptr[1:] = np.cumsum(ppages)

@@ -43,6 +43,12 @@ _lib.pkvmla_plan_create_cascade.argtypes = [_i32p, ctypes.c_int32, _i32p, _i32p,
                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, ctypes.c_float, _vp,
                                             ctypes.POINTER(_vp)]
+_lib.pkvmla_plan_create_cascade_with_capacity.argtypes = [
+    _i32p, ctypes.c_int32, _i32p, _i32p, _i32p, _i32p, _i32p, _i32p, ctypes.c_int32,
+    ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+    ctypes.c_float, ctypes.c_int64, _vp, ctypes.POINTER(_vp)]
+_lib.pkvmla_plan_update_cascade.argtypes = [_vp, _i32p, _i32p, _i32p, _i32p, _i32p, _i32p, _i32p,
+                                            _vp]
 _lib.pkvmla_plan_create_with_capacity.argtypes = [_i32p, _i32p, _i32p, ctypes.c_int32,
                                                   ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                   ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
@@ -78,6 +84,7 @@ EXPORTED_SYMBOLS = (
     "pkvmla_last_error", "pkvmla_kernel_config", "pkvmla_schedule_host", "pkvmla_plan_export",
     "pkvmla_gather", "pkvmla_gather_rows", "pkvmla_plan_set_timing", "pkvmla_plan_timing",
     "pkvmla_run_noalloc", "pkvmla_plan_create_qo", "pkvmla_schedule_rows_host",
+    "pkvmla_plan_create_cascade_with_capacity", "pkvmla_plan_update_cascade",
 )
 
 OK, EINVAL, EUNSUPPORTED, EHIP, ENOMEM = 0, 1, 2, 3, 4
@@ -284,6 +291,20 @@ class Plan:
         _check(_lib.pkvmla_plan_update(self._h, _ptr(ip), _ptr(ix), _ptr(ln),
                                        _stream_handle(stream)))
 
+    def update_cascade(self, group_req_indptr, prefix_indptr, prefix_indices, prefix_lens,
+                       kv_indptr, kv_indices, kv_lens, stream=None) -> None:
+        """Replace a cascade plan's groups, prefixes and suffixes in place (same
+        number of groups and batch), as :meth:`update` does for flat plans."""
+        g, pip, pix, pl, ip, ix, ln = _cascade_arrays(group_req_indptr, prefix_indptr,
+                                                      prefix_indices, prefix_lens, kv_indptr,
+                                                      kv_indices, kv_lens)
+        if len(ln) != self.batch or len(pl) != getattr(self, "num_groups", -1):
+            raise ValueError(f"update_cascade needs batch {self.batch} and the plan's "
+                             f"{getattr(self, 'num_groups', None)} groups")
+        _check(_lib.pkvmla_plan_update_cascade(self._h, _ptr(g), _ptr(pip), _ptr(pix), _ptr(pl),
+                                               _ptr(ip), _ptr(ix), _ptr(ln),
+                                               _stream_handle(stream)))
+
     def run_ptrs(self, q_nope: int, q_pe: int, ckv: int, kpe: int, out: int, lse: int,
                  stream: int) -> None:
         """Raw-pointer form of :meth:`run` (no checks beyond the library's)."""
@@ -388,13 +409,10 @@ def plan_qo(qo_indptr, kv_indptr, kv_indices, kv_lens, num_heads: int, page_size
                 _current_device())
 
 
-def plan_cascade(group_req_indptr, prefix_indptr, prefix_indices, prefix_lens,
-                 kv_indptr, kv_indices, kv_lens, num_heads: int, page_size: int,
-                 num_pages: int, ckv_dim: int = 512, kpe_dim: int = 64,
-                 sm_scale: Optional[float] = None, stream=None) -> Plan:
-    """Two-level plan: per group a shared prefix page list, per request its
-    own suffix list (kv_lens may be 0); states are merged by log-sum-exp."""
-    g, pip, pix, pl = _i32(group_req_indptr), _i32(prefix_indptr), _i32(prefix_indices), _i32(prefix_lens)
+def _cascade_arrays(group_req_indptr, prefix_indptr, prefix_indices, prefix_lens, kv_indptr,
+                    kv_indices, kv_lens):
+    g, pip, pix, pl = (_i32(group_req_indptr), _i32(prefix_indptr), _i32(prefix_indices),
+                       _i32(prefix_lens))
     ip, ix, ln = _i32(kv_indptr), _i32(kv_indices), _i32(kv_lens)
     if g.ndim != 1 or len(g) != len(pl) + 1:
         raise ValueError("group_req_indptr needs num_groups + 1 entries")
@@ -404,13 +422,30 @@ def plan_cascade(group_req_indptr, prefix_indptr, prefix_indices, prefix_lens,
         pix = np.zeros(1, np.int32)
     if ix.size == 0:
         ix = np.zeros(1, np.int32)
+    return g, pip, pix, pl, ip, ix, ln
+
+
+def plan_cascade(group_req_indptr, prefix_indptr, prefix_indices, prefix_lens,
+                 kv_indptr, kv_indices, kv_lens, num_heads: int, page_size: int,
+                 num_pages: int, ckv_dim: int = 512, kpe_dim: int = 64,
+                 sm_scale: Optional[float] = None, stream=None, index_capacity: int = 0) -> Plan:
+    """Two-level plan: per group a shared prefix page list, per request its
+    own suffix list (kv_lens may be 0); states are merged by log-sum-exp.
+    index_capacity > 0 sizes the plan for later :meth:`Plan.update_cascade`
+    calls (prefix and suffix page ids together) and fixes its launch shapes."""
+    g, pip, pix, pl, ip, ix, ln = _cascade_arrays(group_req_indptr, prefix_indptr,
+                                                  prefix_indices, prefix_lens, kv_indptr,
+                                                  kv_indices, kv_lens)
     h = ctypes.c_void_p()
-    _check(_lib.pkvmla_plan_create_cascade(
+    _check(_lib.pkvmla_plan_create_cascade_with_capacity(
         _ptr(g), int(len(pl)), _ptr(pip), _ptr(pix), _ptr(pl), _ptr(ip), _ptr(ix), _ptr(ln),
         int(len(ln)), int(num_pages), int(num_heads), int(ckv_dim), int(kpe_dim), int(page_size),
-        float(sm_scale or 0.0), _stream_handle(stream) if stream else None, ctypes.byref(h)))
-    return Plan(h.value, int(len(ln)), int(num_heads), int(page_size), int(num_pages),
-                _current_device())
+        float(sm_scale or 0.0), int(index_capacity),
+        _stream_handle(stream) if stream else None, ctypes.byref(h)))
+    p = Plan(h.value, int(len(ln)), int(num_heads), int(page_size), int(num_pages),
+             _current_device())
+    p.num_groups = int(len(pl))
+    return p
 
 
 def plan_for(inp, stream=None) -> Plan:

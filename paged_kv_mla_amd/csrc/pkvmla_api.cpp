@@ -77,6 +77,7 @@ struct pkvmla_plan_s {
   pkvmla::KernelConfig cfg0{};
   pkvmla::RowSchedule sched0;
   std::vector<int32_t> slot_list;
+  int32_t cap_lanes0 = 0, cap_units0 = 0, cap_list = 0;
   size_t off_wg = 0, off_units = 0, off_merges = 0, off_sip = 0, off_sl = 0, off_si = 0;
   size_t off_wg0 = 0, off_units0 = 0, off_list = 0;
   // device tables (one allocation) and split workspace
@@ -189,7 +190,9 @@ int build_plan_schedule(const pkvmla_plan_s* P, const std::vector<pkvmla::WorkIt
 // value (empty lanes), merge records have count 0 (skipped).
 int upload_tables(pkvmla_plan_s* P, const pkvmla::Schedule& sched,
                   const std::vector<int32_t>& seq_indptr, const std::vector<int32_t>& seq_lens,
-                  const std::vector<int32_t>& seq_indices, hipStream_t stream) {
+                  const std::vector<int32_t>& seq_indices, hipStream_t stream,
+                  const pkvmla::RowSchedule* sched0 = nullptr,
+                  const std::vector<int32_t>* slot_list = nullptr) {
   std::vector<int32_t> host(P->table_ints, 0);
   const std::vector<int32_t>& wg = sched.wg_indptr;
   for (int32_t l = 0; l <= P->cap_lanes; ++l)
@@ -199,10 +202,12 @@ int upload_tables(pkvmla_plan_s* P, const pkvmla::Schedule& sched,
   std::copy(seq_indptr.begin(), seq_indptr.end(), host.begin() + P->off_sip);
   std::copy(seq_lens.begin(), seq_lens.end(), host.begin() + P->off_sl);
   std::copy(seq_indices.begin(), seq_indices.end(), host.begin() + P->off_si);
-  if (P->is_cascade) {
-    std::copy(P->sched0.wg_indptr.begin(), P->sched0.wg_indptr.end(), host.begin() + P->off_wg0);
-    std::copy(P->sched0.units.begin(), P->sched0.units.end(), host.begin() + P->off_units0);
-    std::copy(P->slot_list.begin(), P->slot_list.end(), host.begin() + P->off_list);
+  if (sched0) {
+    const std::vector<int32_t>& wg0 = sched0->wg_indptr;
+    for (int32_t l = 0; l <= P->cap_lanes0; ++l)
+      host[P->off_wg0 + l] = l < (int32_t)wg0.size() ? wg0[l] : wg0.back();
+    std::copy(sched0->units.begin(), sched0->units.end(), host.begin() + P->off_units0);
+    std::copy(slot_list->begin(), slot_list->end(), host.begin() + P->off_list);
   }
   PKVMLA_HIP(hipMemcpyAsync(P->d_tables, host.data(), P->table_ints * sizeof(int32_t),
                             hipMemcpyHostToDevice, stream));
@@ -218,6 +223,81 @@ struct Level0Groups {
   int32_t num_groups;
   const int32_t* prefix_lens;
 };
+
+// A cascade plan's schedules: level 1 over the suffix items (every unit
+// writing a partial state numbered after level 0's), level 0 over the row
+// blocks, the merge records and slot list.
+int build_cascade_schedules(const pkvmla_plan_s* P, const Level0Groups& l0,
+                            const std::vector<pkvmla::WorkItem>& items,
+                            const std::vector<int32_t>& seq_indptr,
+                            const std::vector<int32_t>& seq_indices, pkvmla::Schedule* sched,
+                            pkvmla::RowSchedule* sched0, std::vector<int32_t>* slot_list) {
+  int rc = build_plan_schedule(P, items, seq_indptr, seq_indices, sched);
+  if (rc) return rc;
+  if (!pkvmla::build_row_schedule(l0.group_req_indptr, l0.num_groups, l0.prefix_lens,
+                                  P->num_heads, P->cap_lanes0, pkvmla::kTile, sched0))
+    return fail(PKVMLA_EUNSUPPORTED, "level-0 schedule construction failed (too many rows)");
+  fill_page_fields(&sched0->units, seq_indptr, seq_indices, P->page_size);
+  int64_t slot = sched0->n_slots;
+  for (size_t i = 0; i < sched->units.size(); i += pkvmla::kUnitRecordInts)
+    sched->units[i + 4] = (int32_t)slot++;
+  if (slot > INT32_MAX / 2) return fail(PKVMLA_EUNSUPPORTED, "too many partial states");
+  sched->n_slots = (int32_t)slot;
+  pkvmla::build_cascade_merges(*sched0, sched->units, P->batch, P->num_heads, &sched->merges,
+                               slot_list);
+  return PKVMLA_OK;
+}
+
+// The host tables of a cascade plan, as the caller passes them.
+struct CascadeTables {
+  const int32_t* group_req_indptr;
+  int32_t num_groups;
+  const int32_t* prefix_indptr;
+  const int32_t* prefix_indices;
+  const int32_t* prefix_lens;
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  const int32_t* kv_lens;
+  int32_t batch;
+};
+
+int check_cascade(const CascadeTables& t, int32_t num_pages, int32_t page_size) {
+  if (t.num_groups < 1 || !t.group_req_indptr)
+    return fail(PKVMLA_EINVAL, "num_groups must be >= 1 with a group_req_indptr");
+  if (t.group_req_indptr[0] != 0 || t.group_req_indptr[t.num_groups] != t.batch)
+    return fail(PKVMLA_EINVAL, "group_req_indptr must run from 0 to batch");
+  for (int32_t g = 0; g < t.num_groups; ++g)
+    if (t.group_req_indptr[g + 1] < t.group_req_indptr[g])
+      return fail(PKVMLA_EINVAL, "group_req_indptr must be non-decreasing (at %d)", g);
+  int rc = check_pages("prefix", t.prefix_indptr, t.prefix_indices, t.prefix_lens, t.num_groups,
+                       num_pages, page_size, 0);
+  if (rc) return rc;
+  rc = check_pages("suffix", t.kv_indptr, t.kv_indices, t.kv_lens, t.batch, num_pages, page_size,
+                   0);
+  if (rc) return rc;
+  for (int32_t g = 0; g < t.num_groups; ++g)
+    for (int32_t b = t.group_req_indptr[g]; b < t.group_req_indptr[g + 1]; ++b)
+      if (t.prefix_lens[g] + t.kv_lens[b] < 1)
+        return fail(PKVMLA_EINVAL, "request %d attends no token (prefix and suffix empty)", b);
+  return PKVMLA_OK;
+}
+
+// Sequences (G prefix lists, then one suffix list per request) and the
+// level-1 items (each request over its suffix; empty ones get no unit).
+void cascade_sequences(const CascadeTables& t, std::vector<int32_t>* sip, std::vector<int32_t>* sl,
+                       std::vector<int32_t>* si, std::vector<pkvmla::WorkItem>* items) {
+  const int32_t G = t.num_groups, B = t.batch;
+  sip->clear();
+  sl->clear();
+  for (int32_t g = 0; g <= G; ++g) sip->push_back(t.prefix_indptr[g]);
+  for (int32_t b = 1; b <= B; ++b) sip->push_back(t.prefix_indptr[G] + t.kv_indptr[b]);
+  for (int32_t g = 0; g < G; ++g) sl->push_back(t.prefix_lens[g]);
+  for (int32_t b = 0; b < B; ++b) sl->push_back(t.kv_lens[b]);
+  si->assign(t.prefix_indices, t.prefix_indices + t.prefix_indptr[G]);
+  si->insert(si->end(), t.kv_indices, t.kv_indices + t.kv_indptr[B]);
+  items->clear();
+  for (int32_t b = 0; b < B; ++b) items->push_back(pkvmla::WorkItem{b, G + b, t.kv_lens[b]});
+}
 
 // Fix the capacities, build the schedule, allocate and upload the device tables.
 // With `l0` (cascade plans) the items are the suffixes; the level-0 row-block
@@ -235,24 +315,30 @@ int finish_plan(pkvmla_plan_s* P, const std::vector<pkvmla::WorkItem>& items,
   P->cap_units = (int32_t)items.size() + P->cap_lanes;
   P->cap_merges = P->batch;
   P->cap_indices = std::max<int64_t>((int64_t)seq_indices.size(), P->index_capacity_request);
-  int rc = build_plan_schedule(P, items, seq_indptr, seq_indices, &P->sched);
-  if (rc) return rc;
+  int rc;
   P->cap_slots = P->cap_units;
   if (l0) {
-    const int32_t lanes0 = std::max(1, P->num_cu / P->cfg0.head_groups);
-    if (!pkvmla::build_row_schedule(l0->group_req_indptr, l0->num_groups, l0->prefix_lens,
-                                    P->num_heads, lanes0, pkvmla::kTile, &P->sched0))
-      return fail(PKVMLA_EUNSUPPORTED, "level-0 schedule construction failed (too many rows)");
-    fill_page_fields(&P->sched0.units, seq_indptr, seq_indices, P->page_size);
-    int64_t slot = P->sched0.n_slots;
-    for (size_t i = 0; i < P->sched.units.size(); i += pkvmla::kUnitRecordInts)
-      P->sched.units[i + 4] = (int32_t)slot++;
-    if (slot > INT32_MAX / 2) return fail(PKVMLA_EUNSUPPORTED, "too many partial states");
-    P->sched.n_slots = (int32_t)slot;
-    pkvmla::build_cascade_merges(P->sched0, P->sched.units, P->batch, P->num_heads,
-                                 &P->sched.merges, &P->slot_list);
-    P->cap_slots = (int32_t)slot;
+    // level-0 capacities, for any groups and prefixes of this batch and head
+    // count: nb <= lanes gives one unit per lane (at most 64 / H requests,
+    // at least one, per unit), nb > lanes one unit per block (blocks <=
+    // rows / 64 + groups, one slot per request)
+    const int64_t H = P->num_heads, B = P->batch;
+    P->cap_lanes0 = std::max(1, P->num_cu / P->cfg0.head_groups);
+    const int64_t blocks = (B * H + 63) / 64 + l0->num_groups;
+    const int64_t u0 = std::max<int64_t>(P->cap_lanes0, blocks);
+    const int64_t s0 = std::max<int64_t>((int64_t)P->cap_lanes0 * std::max<int64_t>(1, 64 / H), B);
+    const int64_t slots = s0 + B + P->cap_lanes;
+    if (u0 > INT32_MAX / pkvmla::kUnitRecordInts || slots > INT32_MAX / 2)
+      return fail(PKVMLA_EUNSUPPORTED, "too many query rows for a cascade plan");
+    P->cap_units0 = (int32_t)u0;
+    P->cap_slots = (int32_t)slots;
+    P->cap_list = (int32_t)slots;
+    rc = build_cascade_schedules(P, *l0, items, seq_indptr, seq_indices, &P->sched, &P->sched0,
+                                 &P->slot_list);
+  } else {
+    rc = build_plan_schedule(P, items, seq_indptr, seq_indices, &P->sched);
   }
+  if (rc) return rc;
 
   // 64-int aligned sub-buffers inside one allocation
   auto pad = [](size_t n) { return (n + 63) & ~size_t(63); };
@@ -260,9 +346,9 @@ int finish_plan(pkvmla_plan_s* P, const std::vector<pkvmla::WorkItem>& items,
   P->off_units = P->off_wg + pad((size_t)P->cap_lanes + 1);
   P->off_merges = P->off_units + pad((size_t)P->cap_units * pkvmla::kUnitRecordInts);
   P->off_wg0 = P->off_merges + pad((size_t)P->cap_merges * pkvmla::kMergeRecordInts);
-  P->off_units0 = P->off_wg0 + pad(P->sched0.wg_indptr.size());
-  P->off_list = P->off_units0 + pad(P->sched0.units.size());
-  P->off_sip = P->off_list + pad(P->slot_list.size());
+  P->off_units0 = P->off_wg0 + pad(l0 ? (size_t)P->cap_lanes0 + 1 : 0);
+  P->off_list = P->off_units0 + pad((size_t)P->cap_units0 * pkvmla::kUnitRecordInts);
+  P->off_sip = P->off_list + pad((size_t)P->cap_list);
   P->off_sl = P->off_sip + pad(seq_indptr.size());
   P->off_si = P->off_sl + pad(seq_lens.size());
   // every page-id read of the kernels lies inside its sequence's list (tile
@@ -283,7 +369,8 @@ int finish_plan(pkvmla_plan_s* P, const std::vector<pkvmla::WorkItem>& items,
   // (flat plans: slots <= units)
   const size_t rows = (size_t)P->cap_slots * P->num_heads;
   PKVMLA_HIP(hipMalloc(&P->d_part, rows * (pkvmla::kCkvDim * sizeof(uint16_t) + sizeof(float))));
-  return upload_tables(P, P->sched, seq_indptr, seq_lens, seq_indices, stream);
+  return upload_tables(P, P->sched, seq_indptr, seq_lens, seq_indices, stream,
+                       l0 ? &P->sched0 : nullptr, l0 ? &P->slot_list : nullptr);
 }
 
 void free_plan(pkvmla_plan_s* P) {
@@ -498,7 +585,7 @@ int pkvmla_plan_create(const int32_t* kv_indptr, const int32_t* kv_indices,
 int pkvmla_plan_update(pkvmla_plan P, const int32_t* kv_indptr, const int32_t* kv_indices,
                        const int32_t* kv_lens, void* stream) {
   if (!P) return fail(PKVMLA_EINVAL, "null plan");
-  if (P->is_cascade) return fail(PKVMLA_EUNSUPPORTED, "update of a cascade plan");
+  if (P->is_cascade) return fail(PKVMLA_EINVAL, "a cascade plan is updated with pkvmla_plan_update_cascade");
   if (P->is_qo) return fail(PKVMLA_EUNSUPPORTED, "update of a plan with several query tokens per request");
   int rc = check_pages("kv", kv_indptr, kv_indices, kv_lens, P->batch, P->num_pages,
                        P->page_size, 1);
@@ -529,13 +616,12 @@ int pkvmla_plan_update(pkvmla_plan P, const int32_t* kv_indptr, const int32_t* k
   return ok();
 }
 
-int pkvmla_plan_create_cascade(const int32_t* group_req_indptr, int32_t num_groups,
-                               const int32_t* prefix_indptr, const int32_t* prefix_indices,
-                               const int32_t* prefix_lens, const int32_t* kv_indptr,
-                               const int32_t* kv_indices, const int32_t* kv_lens, int32_t batch,
-                               int32_t num_pages, int32_t num_heads, int32_t ckv_dim,
-                               int32_t kpe_dim, int32_t page_size, float sm_scale, void* stream,
-                               pkvmla_plan* out) {
+int pkvmla_plan_create_cascade_with_capacity(
+    const int32_t* group_req_indptr, int32_t num_groups, const int32_t* prefix_indptr,
+    const int32_t* prefix_indices, const int32_t* prefix_lens, const int32_t* kv_indptr,
+    const int32_t* kv_indices, const int32_t* kv_lens, int32_t batch, int32_t num_pages,
+    int32_t num_heads, int32_t ckv_dim, int32_t kpe_dim, int32_t page_size, float sm_scale,
+    int64_t index_capacity, void* stream, pkvmla_plan* out) {
   if (!out) return fail(PKVMLA_EINVAL, "null plan output pointer");
   *out = nullptr;
   int32_t log2_ps;
@@ -543,22 +629,15 @@ int pkvmla_plan_create_cascade(const int32_t* group_req_indptr, int32_t num_grou
   int rc = check_shape(batch, num_pages, num_heads, ckv_dim, kpe_dim, page_size, sm_scale,
                        &log2_ps, &scale);
   if (rc) return rc;
-  if (num_groups < 1 || !group_req_indptr)
-    return fail(PKVMLA_EINVAL, "num_groups must be >= 1 with a group_req_indptr");
-  if (group_req_indptr[0] != 0 || group_req_indptr[num_groups] != batch)
-    return fail(PKVMLA_EINVAL, "group_req_indptr must run from 0 to batch");
-  for (int32_t g = 0; g < num_groups; ++g)
-    if (group_req_indptr[g + 1] < group_req_indptr[g])
-      return fail(PKVMLA_EINVAL, "group_req_indptr must be non-decreasing (at %d)", g);
-  rc = check_pages("prefix", prefix_indptr, prefix_indices, prefix_lens, num_groups, num_pages,
-                   page_size, 0);
+  const CascadeTables t{group_req_indptr, num_groups, prefix_indptr, prefix_indices, prefix_lens,
+                        kv_indptr, kv_indices, kv_lens, batch};
+  rc = check_cascade(t, num_pages, page_size);
   if (rc) return rc;
-  rc = check_pages("suffix", kv_indptr, kv_indices, kv_lens, batch, num_pages, page_size, 0);
-  if (rc) return rc;
-  for (int32_t g = 0; g < num_groups; ++g)
-    for (int32_t b = group_req_indptr[g]; b < group_req_indptr[g + 1]; ++b)
-      if (prefix_lens[g] + kv_lens[b] < 1)
-        return fail(PKVMLA_EINVAL, "request %d attends no token (prefix and suffix empty)", b);
+  if (index_capacity < 0) return fail(PKVMLA_EINVAL, "index_capacity must be >= 0");
+  const int64_t n_ids = (int64_t)prefix_indptr[num_groups] + kv_indptr[batch];
+  if (index_capacity > 0 && index_capacity < n_ids)
+    return fail(PKVMLA_EINVAL, "index_capacity %lld is below the tables' %lld page ids",
+                (long long)index_capacity, (long long)n_ids);
 
   pkvmla_plan_s* P = new pkvmla_plan_s();
   P->batch = batch;
@@ -571,24 +650,15 @@ int pkvmla_plan_create_cascade(const int32_t* group_req_indptr, int32_t num_grou
   P->sm_scale = scale;
   P->is_cascade = 1;
   P->num_groups = num_groups;
+  P->index_capacity_request = index_capacity;
+  P->fixed_launch = index_capacity > 0 ? 1 : 0;
   pkvmla::kernel_config_for(num_heads, &P->cfg);
   // level 0: 64 query rows per workgroup (four head blocks), a whole request
   // per lane above 64 heads (its head groups)
   P->cfg0 = pkvmla::KernelConfig{8, 16, 4, 1, 4, num_heads > 64 ? num_heads / 64 : 1};
-  // sequences: G prefix lists, then one suffix list per request
   std::vector<int32_t> sip, sl, si;
-  sip.reserve(num_groups + batch + 1);
-  for (int32_t g = 0; g <= num_groups; ++g) sip.push_back(prefix_indptr[g]);
-  for (int32_t b = 1; b <= batch; ++b) sip.push_back(prefix_indptr[num_groups] + kv_indptr[b]);
-  for (int32_t g = 0; g < num_groups; ++g) sl.push_back(prefix_lens[g]);
-  for (int32_t b = 0; b < batch; ++b) sl.push_back(kv_lens[b]);
-  si.assign(prefix_indices, prefix_indices + prefix_indptr[num_groups]);
-  si.insert(si.end(), kv_indices, kv_indices + kv_indptr[batch]);
-  // level 1: each request's suffix (empty ones have no unit)
   std::vector<pkvmla::WorkItem> items;
-  items.reserve((size_t)batch);
-  for (int32_t b = 0; b < batch; ++b)
-    items.push_back(pkvmla::WorkItem{b, num_groups + b, kv_lens[b]});
+  cascade_sequences(t, &sip, &sl, &si, &items);
   const Level0Groups l0{group_req_indptr, num_groups, prefix_lens};
   rc = finish_plan(P, items, sip, sl, si, (hipStream_t)stream, &l0);
   if (rc) {
@@ -598,6 +668,61 @@ int pkvmla_plan_create_cascade(const int32_t* group_req_indptr, int32_t num_grou
     return rc;
   }
   *out = P;
+  return ok();
+}
+
+int pkvmla_plan_create_cascade(const int32_t* group_req_indptr, int32_t num_groups,
+                               const int32_t* prefix_indptr, const int32_t* prefix_indices,
+                               const int32_t* prefix_lens, const int32_t* kv_indptr,
+                               const int32_t* kv_indices, const int32_t* kv_lens, int32_t batch,
+                               int32_t num_pages, int32_t num_heads, int32_t ckv_dim,
+                               int32_t kpe_dim, int32_t page_size, float sm_scale, void* stream,
+                               pkvmla_plan* out) {
+  return pkvmla_plan_create_cascade_with_capacity(
+      group_req_indptr, num_groups, prefix_indptr, prefix_indices, prefix_lens, kv_indptr,
+      kv_indices, kv_lens, batch, num_pages, num_heads, ckv_dim, kpe_dim, page_size, sm_scale, 0,
+      stream, out);
+}
+
+int pkvmla_plan_update_cascade(pkvmla_plan P, const int32_t* group_req_indptr,
+                               const int32_t* prefix_indptr, const int32_t* prefix_indices,
+                               const int32_t* prefix_lens, const int32_t* kv_indptr,
+                               const int32_t* kv_indices, const int32_t* kv_lens, void* stream) {
+  if (!P) return fail(PKVMLA_EINVAL, "null plan");
+  if (!P->is_cascade) return fail(PKVMLA_EINVAL, "not a cascade plan (use pkvmla_plan_update)");
+  const CascadeTables t{group_req_indptr, P->num_groups, prefix_indptr, prefix_indices,
+                        prefix_lens, kv_indptr, kv_indices, kv_lens, P->batch};
+  int rc = check_cascade(t, P->num_pages, P->page_size);
+  if (rc) return rc;
+  const int64_t n_ids = (int64_t)prefix_indptr[P->num_groups] + kv_indptr[P->batch];
+  if (n_ids > P->cap_indices)
+    return fail(PKVMLA_EINVAL, "%lld page ids exceed the plan's capacity of %lld",
+                (long long)n_ids, (long long)P->cap_indices);
+  int dev = -1;
+  PKVMLA_HIP(hipGetDevice(&dev));
+  if (dev != P->device)
+    return fail(PKVMLA_EINVAL, "plan was built on device %d, current device is %d", P->device,
+                dev);
+  std::vector<int32_t> sip, sl, si;
+  std::vector<pkvmla::WorkItem> items;
+  cascade_sequences(t, &sip, &sl, &si, &items);
+  pkvmla::Schedule sched;
+  pkvmla::RowSchedule sched0;
+  std::vector<int32_t> list;
+  const Level0Groups l0{group_req_indptr, P->num_groups, prefix_lens};
+  rc = build_cascade_schedules(P, l0, items, sip, si, &sched, &sched0, &list);
+  if (rc) return rc;
+  if ((int64_t)sched.units.size() > (int64_t)P->cap_units * pkvmla::kUnitRecordInts ||
+      sched.grid > P->cap_lanes || sched0.grid > P->cap_lanes0 ||
+      (int64_t)sched0.units.size() > (int64_t)P->cap_units0 * pkvmla::kUnitRecordInts ||
+      sched.n_slots > P->cap_slots || (int64_t)list.size() > P->cap_list)
+    return fail(PKVMLA_EINVAL, "schedule exceeds the plan's capacities");
+  // the plan takes the new schedules only once its tables are on the device
+  rc = upload_tables(P, sched, sip, sl, si, (hipStream_t)stream, &sched0, &list);
+  if (rc) return rc;
+  P->sched = std::move(sched);
+  P->sched0 = std::move(sched0);
+  P->slot_list = std::move(list);
   return ok();
 }
 
@@ -711,13 +836,13 @@ int run_impl(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* ck
   const int slot_ev = (int)(P->timed_runs % pkvmla_plan_s::kTimingSlots);
   d.stamps = P->timing ? P->d_stamps + 2 * slot_ev : nullptr;
   if (P->timing) PKVMLA_HIP(hipEventRecord(P->ev[2 * slot_ev], s));
-  if (P->is_cascade && P->sched0.grid > 0) {
+  if (P->is_cascade && (P->sched0.grid > 0 || P->fixed_launch)) {
     // level 0: the groups' query rows over their shared prefixes
     pkvmla::DecodeParams d0 = d;
     d0.wg_indptr = P->d_wg0;
     d0.units = P->d_units0;
     d0.head_groups = P->cfg0.head_groups;
-    d0.n_lanes = P->sched0.grid;
+    d0.n_lanes = P->fixed_launch ? P->cap_lanes0 : P->sched0.grid;
     d0.waves = P->cfg0.waves;
     d0.heads_per_wave = P->cfg0.heads_per_wave;
     d0.stages = P->cfg0.stages;

@@ -134,10 +134,73 @@ def test_update_rejects_and_keeps_tables():
     compare(o, l, o64, l64, name="plain update")
 
 
-def test_update_of_cascade_plan_is_unsupported():
+def test_update_of_cascade_plan_needs_the_cascade_call():
     from mla_workloads import make_cascade
     cas = make_cascade("gu", 212, 4, 16, 16, [32], [3, 0, 20, 7])
     plan = pk.plan_for(cas)
     with pytest.raises(pk.PkvmlaError) as e:
         plan.update(cas.kv_indptr, cas.kv_indices, np.maximum(cas.kv_lens, 1))
-    assert e.value.code == pk.EUNSUPPORTED
+    assert e.value.code == pk.EINVAL and "cascade" in str(e.value)
+    flat = tables(213, [10, 20], 16, 16)
+    fplan = pk.plan(flat.kv_indptr, flat.kv_indices, flat.kv_lens, 16, 16, POOL)
+    fplan.num_groups = 1
+    with pytest.raises(pk.PkvmlaError) as e:
+        fplan.update_cascade([0, 2], [0, 2], cas.prefix_indices[:2], [32], flat.kv_indptr,
+                             flat.kv_indices, flat.kv_lens)
+    assert e.value.code == pk.EINVAL
+
+
+@pytest.mark.parametrize("H,ps", [(128, 64), (16, 16), (32, 1)])
+def test_graph_replay_and_update_cascade(H, ps):
+    """A captured cascade run (level 0, level 1, merge) across in-place
+    updates of groups' prefixes and requests' suffixes."""
+    from mla_workloads import make_cascade
+    from gpu_helpers import oracle_cascade
+    specs = [([500, 64], [1, 40, 0, 300, 7, 64]), ([0, 1000], [30, 3, 9, 64, 1, 5]),
+             ([33, 33], [5, 5, 5, 5, 5, 5])]
+    if ps == 1:
+        specs = [([50, 20], [1, 4, 0, 30, 7, 6]), ([0, 100], [3, 3, 9, 6, 1, 5]),
+                 ([33, 33], [5, 5, 5, 5, 5, 5])]
+    bundles = [make_cascade(f"gc{i}", 220 + i, 6, H, ps, pre, suf, groups=2, pool_pages=POOL)
+               for i, (pre, suf) in enumerate(specs)]
+    cap = max(len(b.prefix_indices) + len(b.kv_indices) for b in bundles) + 7
+    A = bundles[0]
+    note(f"graph cascade H={H} ps={ps} cap={cap}")
+
+    def args(c):
+        return (c.group_req_indptr, c.prefix_indptr, c.prefix_indices, c.prefix_lens,
+                c.kv_indptr, c.kv_indices, c.kv_lens)
+
+    plan = pk.plan_cascade(*args(A), H, ps, POOL, index_capacity=cap)
+    assert plan.export().header[24] == 1
+    dev = Dev(A)
+    out = torch.empty((A.batch, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((A.batch, H), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    ref_o, ref_l = eager(plan, dev, out, lse, side)
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        plan.run(dev.q_nope, dev.q_pe, dev.ckv, dev.kpe, out=out, lse=lse, stream=side)
+    torch.cuda.synchronize()
+
+    for step, inp in enumerate(bundles + [A]):
+        if step > 0:
+            plan.update_cascade(*args(inp), stream=side)
+            load_into(dev, inp)
+            torch.cuda.synchronize()
+            ref_o, ref_l = eager(plan, dev, out, lse, side)
+            fresh = pk.plan_cascade(*args(inp), H, ps, POOL)
+            fo, fl = eager(fresh, dev, torch.empty_like(out), torch.empty_like(lse), side)
+            assert torch.equal(fo, ref_o) and torch.equal(fl, ref_l)
+            o64, l64 = oracle_cascade(inp)
+            compare(ref_o, ref_l, o64, l64, name=f"cascade update {step}")
+        for rep in range(3):
+            out.fill_(7.0)
+            lse.fill_(-1.0)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref_o), (step, rep)
+            assert torch.equal(lse, ref_l), (step, rep)
+        note(f"graph cascade step {step}: 3 replays bit-identical")
