@@ -29,4 +29,5 @@ from .generate import (  # noqa: F401
     poison_unreferenced,
     permute_pages,
     STRESS_KINDS,
+    quantize_kv_fp8,
 )

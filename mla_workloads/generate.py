@@ -81,6 +81,11 @@ class FlatInputs:
     kpe_dim: int = KPE_DIM
     # several new query tokens per request: q rows qo_indptr[b] .. qo_indptr[b+1]
     qo_indptr: Optional[np.ndarray] = None
+    # fp8 KV caches (quantize_kv_fp8): E4M3 codes and per-tensor scales
+    ckv8: Optional[np.ndarray] = None   # uint8 [P, ps, 512]
+    kpe8: Optional[np.ndarray] = None   # uint8 [P, ps, 64]
+    ckv_scale: Optional[float] = None
+    kpe_scale: Optional[float] = None
 
     @property
     def total_tokens(self) -> int:
@@ -116,6 +121,10 @@ class CascadeInputs:
     ckv: np.ndarray
     kpe: np.ndarray
     sm_scale: Optional[float] = None
+    ckv8: Optional[np.ndarray] = None   # fp8 KV caches (quantize_kv_fp8)
+    kpe8: Optional[np.ndarray] = None
+    ckv_scale: Optional[float] = None
+    kpe_scale: Optional[float] = None
     ckv_dim: int = CKV_DIM
     kpe_dim: int = KPE_DIM
 
@@ -480,3 +489,29 @@ def stress_variant_cascade(cas: CascadeInputs, kind: str, seed: int = 4321) -> C
         raise ValueError(kind)
     return dataclasses.replace(cas, name=f"{cas.name}/{kind}", q_nope=q_nope, q_pe=q_pe,
                                ckv=ckv, kpe=kpe)
+
+
+def _e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """float32 values (|x| <= 448 or NaN) to OCP E4M3 codes, round to nearest
+    even (PyTorch's float8_e4m3fn cast on the CPU)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+
+
+def quantize_kv_fp8(inp, ckv_scale: Optional[float] = None, kpe_scale: Optional[float] = None):
+    """The same bundle with E4M3 copies of its KV caches: code = RNE(value /
+    scale), one scale per cache (default: its largest finite magnitude / 448,
+    so no value overflows; NaN poison stays NaN).  Input preparation only: the
+    attention side decodes the codes itself."""
+    def f32(bits):
+        return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+    c, k = f32(inp.ckv), f32(inp.kpe)
+
+    def auto(x):
+        m = float(np.nanmax(np.abs(x))) if np.isfinite(x).any() else 1.0
+        return np.float32(m / 448.0) if m > 0 else np.float32(1.0)
+    sc = np.float32(ckv_scale) if ckv_scale is not None else auto(c)
+    sk = np.float32(kpe_scale) if kpe_scale is not None else auto(k)
+    return dataclasses.replace(inp, ckv8=_e4m3_codes(c / sc), kpe8=_e4m3_codes(k / sk),
+                               ckv_scale=float(sc), kpe_scale=float(sk))

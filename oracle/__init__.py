@@ -29,6 +29,12 @@ Parity pins (all in tests/test_oracle_*.py, CPU only):
                               python-float fsum brute force, reduces to
                               attend_flat for one query token, last query
                               token equals full (unmasked) attention.
+  e4m3_to_f64               : hand-listed OCP E4M3 values (tests/golden), all 256
+                              codes against torch's float8_e4m3fn widening,
+                              monotone positive codes, sign symmetry.
+  kv_scales (fp8 caches)    : power-of-two scales reduce to the bf16 oracle
+                              on the same values; torch fp64 SDPA on the
+                              dequantized rows; cascade = flat.
   gather_ref                : closed-form address walk vs an independent index
                               construction; permutation invariance.
   schedule_ref              : coverage/uniqueness invariants and hand-worked
@@ -38,6 +44,7 @@ Parity pins (all in tests/test_oracle_*.py, CPU only):
 
 from .mla_decode import (  # noqa: F401
     bf16_to_f64,
+    e4m3_to_f64,
     default_sm_scale,
     token_pages,
     gather_ref,

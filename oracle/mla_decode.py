@@ -19,6 +19,23 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
+def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    """Exact value of OCP 8-bit floating point E4M3 codes (uint8), float64.
+
+    The format (OCP "8-bit Floating Point Specification (OFP8)", E4M3): sign
+    bit, 4 exponent bits with bias 7, 3 mantissa bits.  Exponent field 0 is
+    subnormal, (-1)^s * 2^-6 * m/8; otherwise (-1)^s * 2^(e-7) * (1 + m/8).
+    There is no infinity: exponent field 15 with mantissa 7 is NaN, so the
+    largest finite magnitude is 1.75 * 2^8 = 448."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (c & 0x7 == 7), np.nan, mag)
+    return sign * mag
+
+
 def default_sm_scale(ckv_dim: int, kpe_dim: int) -> float:
     """Softmax scale the flashinfer_mla plan review asks for:
     1/sqrt(kv_lora_rank + qk_rope_head_dim)  (1/24 for 512 + 64)."""
@@ -68,25 +85,34 @@ def attend_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, sm_scale: float):
 
 
 def _request_qkv(q_nope, q_pe, ckv, kpe, kv_indptr, kv_indices, kv_len, b, page_size,
-                 t0=0, t1=None):
+                 t0=0, t1=None, kv_scales=None):
     """Absorbed-form operands of request b over tokens [t0, t1):
     query [q_nope | q_pe] (H x 576), key [ckv | kpe] (L x 576), value ckv (L x 512).
-    All H heads share the one latent KV row per token."""
+    All H heads share the one latent KV row per token.  kv_scales None: the
+    caches hold bf16 bits; (ckv_scale, kpe_scale): they hold E4M3 codes and a
+    row's value is its scale times the code's value."""
     pages, slots = token_pages(kv_indptr, kv_indices, kv_len, b, page_size)
     t1 = int(kv_len) if t1 is None else t1
     pages, slots = pages[t0:t1], slots[t0:t1]
-    c = bf16_to_f64(ckv[pages, slots])
-    r = bf16_to_f64(kpe[pages, slots])
+    if kv_scales is None:
+        c = bf16_to_f64(ckv[pages, slots])
+        r = bf16_to_f64(kpe[pages, slots])
+    else:
+        c = float(kv_scales[0]) * e4m3_to_f64(ckv[pages, slots])
+        r = float(kv_scales[1]) * e4m3_to_f64(kpe[pages, slots])
     q = np.concatenate([bf16_to_f64(q_nope[b]), bf16_to_f64(q_pe[b])], axis=1)
     k = np.concatenate([c, r], axis=1)
     return q, k, c
 
 
 def attend_flat(q_nope, q_pe, ckv, kpe, kv_indptr, kv_indices, kv_lens, page_size,
-                sm_scale=None):
+                sm_scale=None, kv_scales=None):
     """Batched decode: for every request b and head h,
     score_t = sm_scale (q_nope[b,h].ckv_t + q_pe[b,h].kpe_t) over the kv_lens[b]
     tokens of b's pages (non-causal, one query token), out = softmax . ckv.
+    kv_scales (ckv_scale, kpe_scale): ckv and kpe hold E4M3 codes, dequantized
+    to scale * value before the products (bf16 queries, as in the fp8 KV-cache
+    limitation the V1 FlashInfer backend page lists for cascade).
     Returns out float64 [B, H, ckv_dim] and lse float64 [B, H]."""
     B, H, dc = q_nope.shape
     dr = q_pe.shape[2]
@@ -95,7 +121,7 @@ def attend_flat(q_nope, q_pe, ckv, kpe, kv_indptr, kv_indices, kv_lens, page_siz
     lse = np.zeros((B, H))
     for b in range(B):
         q, k, v = _request_qkv(q_nope, q_pe, ckv, kpe, kv_indptr, kv_indices,
-                               kv_lens[b], b, page_size)
+                               kv_lens[b], b, page_size, kv_scales=kv_scales)
         out[b], lse[b] = attend_rows(q, k, v, scale)
     return out, lse
 
@@ -143,7 +169,7 @@ def attend_flat_split(q_nope, q_pe, ckv, kpe, kv_indptr, kv_indices, kv_lens, pa
 
 def attend_cascade(q_nope, q_pe, ckv, kpe, page_size,
                    group_req_indptr, prefix_indptr, prefix_indices, prefix_lens,
-                   kv_indptr, kv_indices, kv_lens, sm_scale=None):
+                   kv_indptr, kv_indices, kv_lens, sm_scale=None, kv_scales=None):
     """Two-level (cascade) attention: level 0 attends every request of group g to
     the group's shared prefix pages, level 1 attends request b to its own suffix
     pages, and the two states are merged by log-sum-exp.  Equals flat attention
@@ -159,12 +185,12 @@ def attend_cascade(q_nope, q_pe, ckv, kpe, page_size,
         for b in range(int(group_req_indptr[g]), int(group_req_indptr[g + 1])):
             # level 0: shared prefix of group g (its own page list)
             q, k, v = _request_qkv(q_nope, q_pe, ckv, kpe, prefix_indptr, prefix_indices,
-                                   prefix_lens[g], g, page_size)
+                                   prefix_lens[g], g, page_size, kv_scales=kv_scales)
             q = np.concatenate([bf16_to_f64(q_nope[b]), bf16_to_f64(q_pe[b])], axis=1)
             s0 = attend_rows(q, k, v, scale)
             # level 1: request b's suffix
             q, k, v = _request_qkv(q_nope, q_pe, ckv, kpe, kv_indptr, kv_indices,
-                                   kv_lens[b], b, page_size)
+                                   kv_lens[b], b, page_size, kv_scales=kv_scales)
             s1 = attend_rows(q, k, v, scale)
             out[b], lse[b] = merge_states([s0, s1])
     return out, lse

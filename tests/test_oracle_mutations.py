@@ -11,15 +11,19 @@ import oracle.mla_decode as od
 from oracle_pins import ALL_PINS
 
 
-def _drop_kpe(q_nope, q_pe, ckv, kpe, kv_indptr, kv_indices, kv_len, b, page_size, t0=0, t1=None):
-    q, k, c = _orig_qkv(q_nope, q_pe, ckv, kpe, kv_indptr, kv_indices, kv_len, b, page_size, t0, t1)
+def _drop_kpe(q_nope, q_pe, ckv, kpe, kv_indptr, kv_indices, kv_len, b, page_size, t0=0, t1=None,
+              kv_scales=None):
+    q, k, c = _orig_qkv(q_nope, q_pe, ckv, kpe, kv_indptr, kv_indices, kv_len, b, page_size, t0, t1,
+                        kv_scales=kv_scales)
     k = k.copy()
     k[:, 512:] = 0.0
     return q, k, c
 
 
-def _value_includes_kpe(q_nope, q_pe, ckv, kpe, kv_indptr, kv_indices, kv_len, b, page_size, t0=0, t1=None):
-    q, k, c = _orig_qkv(q_nope, q_pe, ckv, kpe, kv_indptr, kv_indices, kv_len, b, page_size, t0, t1)
+def _value_includes_kpe(q_nope, q_pe, ckv, kpe, kv_indptr, kv_indices, kv_len, b, page_size, t0=0,
+                        t1=None, kv_scales=None):
+    q, k, c = _orig_qkv(q_nope, q_pe, ckv, kpe, kv_indptr, kv_indices, kv_len, b, page_size, t0, t1,
+                        kv_scales=kv_scales)
     c = c + np.pad(k[:, 512:], ((0, 0), (0, 448)))
     return q, k, c
 
