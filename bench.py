@@ -100,8 +100,9 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def workload_counts(inp):
-    """Attended tokens, unique KV rows and algorithmic bytes/flops of one step."""
+def workload_counts(inp, kv_row_bytes: int = 1152):
+    """Attended tokens, unique KV rows and algorithmic bytes/flops of one step
+    (kv_row_bytes: one token's ckv + kpe row, 1152 in bf16, 576 in fp8)."""
     H = inp.num_heads
     B = inp.batch
     if hasattr(inp, "prefix_lens"):
@@ -111,7 +112,7 @@ def workload_counts(inp):
     else:
         attended = unique = inp.total_tokens
         idx_bytes = 4 * len(inp.kv_indices) + 8 * B
-    alg_bytes = unique * 1152 + idx_bytes + B * H * (1152 + 1024 + 4)
+    alg_bytes = unique * kv_row_bytes + idx_bytes + B * H * (1152 + 1024 + 4)
     alg_flops = 2176.0 * H * attended
     return attended, unique, alg_bytes, alg_flops
 
@@ -131,22 +132,26 @@ def cpu_baseline(inp, budget_s: float = 12.0):
     b = 0
     while True:
         sl = slice(b, b + 1)
+        sc = (inp.ckv_scale, inp.kpe_scale) if inp.ckv8 is not None else None
+        ckv, kpe = (inp.ckv8, inp.kpe8) if sc else (inp.ckv, inp.kpe)
         if is_cas:
             g = inp.group_of(b)
             oracle.attend_cascade(
-                inp.q_nope[sl], inp.q_pe[sl], inp.ckv, inp.kpe, inp.page_size,
+                inp.q_nope[sl], inp.q_pe[sl], ckv, kpe, inp.page_size,
                 np.array([0, 1], np.int32),
                 np.array([0, inp.prefix_indptr[g + 1] - inp.prefix_indptr[g]], np.int32),
                 inp.prefix_indices[inp.prefix_indptr[g]:inp.prefix_indptr[g + 1]],
                 inp.prefix_lens[g:g + 1],
                 np.array([0, inp.kv_indptr[b + 1] - inp.kv_indptr[b]], np.int32),
-                inp.kv_indices[inp.kv_indptr[b]:inp.kv_indptr[b + 1]], inp.kv_lens[sl])
+                inp.kv_indices[inp.kv_indptr[b]:inp.kv_indptr[b + 1]], inp.kv_lens[sl],
+                kv_scales=sc)
             done_tokens += int(inp.prefix_lens[g]) + int(inp.kv_lens[b])
         else:
             ip = np.array([0, inp.kv_indptr[b + 1] - inp.kv_indptr[b]], np.int32)
-            oracle.attend_flat(inp.q_nope[sl], inp.q_pe[sl], inp.ckv, inp.kpe, ip,
+            oracle.attend_flat(inp.q_nope[sl], inp.q_pe[sl], ckv, kpe, ip,
                                inp.kv_indices[inp.kv_indptr[b]:inp.kv_indptr[b + 1]],
-                               inp.kv_lens[sl], inp.page_size, sm_scale=inp.sm_scale)
+                               inp.kv_lens[sl], inp.page_size, sm_scale=inp.sm_scale,
+                               kv_scales=sc)
             done_tokens += int(inp.kv_lens[b])
         reqs += 1
         b = (b + 1) % inp.batch
@@ -159,10 +164,11 @@ def cpu_baseline(inp, budget_s: float = 12.0):
                       f"{el:.1f} s wall"}
 
 
-def load_traffic(workload: str, launches_tokens: int):
+def load_traffic(workload: str, launches_tokens: int, kv: str = "bf16"):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_decode_{workload}.json")
+    suffix = "" if kv == "bf16" else "_" + kv
+    path = os.path.join(ROOT, "profiles", f"traffic_decode_{workload}{suffix}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -180,6 +186,9 @@ def main():
     ap.add_argument("--workload", default="deepseek", choices=sorted(WORKLOAD_DESC))
     ap.add_argument("--layers", type=int, default=0,
                     help="KV copies cycled over (0: enough to exceed the last-level cache)")
+    ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
+                    help="KV-cache element type: bf16, or OCP E4M3 codes with per-tensor "
+                         "scales (queries and outputs stay bf16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -234,19 +243,25 @@ def main():
         return
 
     import paged_kv_mla_amd as pk
-    from mla_workloads import make_config
+    from mla_workloads import make_config, quantize_kv_fp8
 
+    fp8 = args.kv == "fp8"
     t0 = time.perf_counter()
     inp = make_config(args.workload)
+    if fp8:
+        inp = quantize_kv_fp8(inp)
     gen_s = time.perf_counter() - t0
-    attended, unique, alg_bytes, alg_flops = workload_counts(inp)
+    attended, unique, alg_bytes, alg_flops = workload_counts(inp, 576 if fp8 else 1152)
 
     def dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda")
 
-    pool_bytes = inp.ckv.nbytes + inp.kpe.nbytes
+    def dev8(codes):
+        return torch.from_numpy(np.ascontiguousarray(codes)).to("cuda")
+
+    pool_bytes = (inp.ckv8.nbytes + inp.kpe8.nbytes) if fp8 else (inp.ckv.nbytes + inp.kpe.nbytes)
     layers = args.layers or max(2, math.ceil(3 * MALL_BYTES / pool_bytes))
-    ckv0, kpe0 = dev(inp.ckv), dev(inp.kpe)
+    ckv0, kpe0 = (dev8(inp.ckv8), dev8(inp.kpe8)) if fp8 else (dev(inp.ckv), dev(inp.kpe))
     qn0, qp0 = dev(inp.q_nope), dev(inp.q_pe)
     ckvs = [ckv0] + [ckv0.clone() for _ in range(layers - 1)]
     kpes = [kpe0] + [kpe0.clone() for _ in range(layers - 1)]
@@ -266,8 +281,13 @@ def main():
 
     def step(i):
         k = i % layers
-        plan.run_ptrs(qns[k].data_ptr(), qps[k].data_ptr(), ckvs[k].data_ptr(),
-                      kpes[k].data_ptr(), outs[k].data_ptr(), lses[k].data_ptr(), sh)
+        if fp8:
+            plan.run_fp8_ptrs(qns[k].data_ptr(), qps[k].data_ptr(), ckvs[k].data_ptr(),
+                              kpes[k].data_ptr(), 512, 64, inp.ckv_scale, inp.kpe_scale,
+                              outs[k].data_ptr(), lses[k].data_ptr(), sh)
+        else:
+            plan.run_ptrs(qns[k].data_ptr(), qps[k].data_ptr(), ckvs[k].data_ptr(),
+                          kpes[k].data_ptr(), outs[k].data_ptr(), lses[k].data_ptr(), sh)
 
     hip = HipEvents()
     for i in range(args.warmup):
@@ -338,7 +358,7 @@ def main():
         achieved = alg_flops / (kern_avg_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4)}
-    roof["traffic"] = load_traffic(args.workload, attended)
+    roof["traffic"] = load_traffic(args.workload, attended, args.kv)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -355,10 +375,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16 queries, fp8 e4m3 KV (per-tensor scales)" if fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": WORKLOAD_DESC[args.workload], "batch": B, "num_heads": H,
-                   "page_size": inp.page_size, "attended_kv_tokens": attended,
+                   "page_size": inp.page_size, "kv_cache": args.kv,
+                   "attended_kv_tokens": attended,
                    "unique_kv_tokens": unique, "kv_copies_cycled": layers},
         "tflops": round(tflops, 2),
         "step_roofline_frac": round(max(t_hbm, t_mfma) / (ms_per_step * 1e-3), 4),

@@ -161,6 +161,26 @@ int pkvmla_plan_create_cascade(const int32_t* group_req_indptr, int32_t num_grou
                                int32_t page_size, float sm_scale, void* stream,
                                pkvmla_plan* out);
 
+/* pkvmla_run_strided for fp8 KV caches: ckv_cache and kpe_cache hold OCP
+ * E4M3 codes (one byte per element, the format of the OCP 8-bit floating
+ * point specification: bias 7, no infinity, S.1111.111 NaN), a token's ckv
+ * value being ckv_scale times its code's value and its kpe value kpe_scale
+ * times its code's (per-tensor scales, finite and > 0).  Queries, out and lse
+ * are as in pkvmla_run.  The vLLM page "[V1][Core] FlashInfer attention
+ * backend for V1" lists a KV-cache dtype other than the query dtype as the
+ * limitation of its cascade path; here both flat and cascade plans take fp8
+ * caches with bf16 queries.  The codes are widened exactly to bf16 and the
+ * scales applied in fp32 (scores: ckv part + kpe_scale / ckv_scale times the
+ * kpe part, times sm_scale * ckv_scale; outputs times ckv_scale).  Row
+ * strides are in BYTES: ckv >= 512 and a multiple of 16, kpe >= 64 and a
+ * multiple of 8 (packed caches: 512 and 64; the two views of one
+ * [pages, page_size, 576] fp8 cache: 576 and 576).  ckv_cache 16-byte, kpe_cache
+ * 8-byte aligned.  Errors as pkvmla_run, PKVMLA_EINVAL for bad scales. */
+int pkvmla_run_fp8(pkvmla_plan plan, const void* q_nope, const void* q_pe,
+                   const void* ckv_cache, const void* kpe_cache, int64_t ckv_row_stride,
+                   int64_t kpe_row_stride, float ckv_scale, float kpe_scale, void* out,
+                   float* lse, void* stream);
+
 /* pkvmla_plan_create_cascade with device tables, split workspace and launch
  * shapes sized once (index_capacity > 0: page ids of prefixes and suffixes
  * together) for later pkvmla_plan_update_cascade calls, so that a HIP graph

@@ -513,5 +513,11 @@ def quantize_kv_fp8(inp, ckv_scale: Optional[float] = None, kpe_scale: Optional[
         return np.float32(m / 448.0) if m > 0 else np.float32(1.0)
     sc = np.float32(ckv_scale) if ckv_scale is not None else auto(c)
     sk = np.float32(kpe_scale) if kpe_scale is not None else auto(k)
-    return dataclasses.replace(inp, ckv8=_e4m3_codes(c / sc), kpe8=_e4m3_codes(k / sk),
-                               ckv_scale=float(sc), kpe_scale=float(sk))
+    codes = []
+    for name, x, s in (("ckv", c, sc), ("kpe", k, sk)):
+        q = _e4m3_codes(x / s)
+        if np.any(np.isfinite(x) & ((q & 0x7F) == 0x7F)):     # a finite value overflowed
+            raise ValueError(f"{name} scale {s} lets values pass the E4M3 maximum 448")
+        codes.append(q)
+    return dataclasses.replace(inp, ckv8=codes[0], kpe8=codes[1], ckv_scale=float(sc),
+                               kpe_scale=float(sk))

@@ -61,6 +61,8 @@ _lib.pkvmla_run.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.pkvmla_run_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.pkvmla_run_strided.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int64, ctypes.c_int64,
                                     _vp, _vp, _vp]
+_lib.pkvmla_run_fp8.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int64, ctypes.c_int64,
+                                ctypes.c_float, ctypes.c_float, _vp, _vp, _vp]
 _lib.pkvmla_plan_destroy.argtypes = [_vp]
 _lib.pkvmla_plan_destroy.restype = None
 _lib.pkvmla_last_error.restype = ctypes.c_char_p
@@ -84,7 +86,7 @@ EXPORTED_SYMBOLS = (
     "pkvmla_last_error", "pkvmla_kernel_config", "pkvmla_schedule_host", "pkvmla_plan_export",
     "pkvmla_gather", "pkvmla_gather_rows", "pkvmla_plan_set_timing", "pkvmla_plan_timing",
     "pkvmla_run_noalloc", "pkvmla_plan_create_qo", "pkvmla_schedule_rows_host",
-    "pkvmla_plan_create_cascade_with_capacity", "pkvmla_plan_update_cascade",
+    "pkvmla_plan_create_cascade_with_capacity", "pkvmla_plan_update_cascade", "pkvmla_run_fp8",
 )
 
 OK, EINVAL, EUNSUPPORTED, EHIP, ENOMEM = 0, 1, 2, 3, 4
@@ -232,16 +234,22 @@ class Plan:
     def destroy(self) -> None:
         self.__del__()
 
-    def run(self, q_nope, q_pe, ckv_cache, kpe_cache, out=None, lse=None, stream=None):
+    def run(self, q_nope, q_pe, ckv_cache, kpe_cache, out=None, lse=None, stream=None,
+            kv_scales=None):
         """Decode on the device.  q_nope [B,H,512], q_pe [B,H,64] are
         contiguous bf16 CUDA tensors; ckv_cache [P,ps,512] and kpe_cache
         [P,ps,64] are bf16 with unit stride inside a row and packed rows within
         a page (row stride S, page stride ps*S): contiguous tensors, or the two
-        views [..., :512] and [..., 512:] of one [P,ps,576] cache.  Returns
-        (out bf16 [B,H,512], lse fp32 [B,H]); out/lse are allocated when not
-        given.  Asynchronous on `stream` (default: current stream)."""
+        views [..., :512] and [..., 512:] of one [P,ps,576] cache.  With
+        kv_scales = (ckv_scale, kpe_scale) the caches hold OCP E4M3 codes
+        (uint8 or float8_e4m3fn tensors of the same shapes) and a value is its
+        scale times its code's value.  Returns (out bf16 [B,H,512], lse fp32
+        [B,H]); out/lse are allocated when not given.  Asynchronous on
+        `stream` (default: current stream)."""
         import torch
         B, H = self.batch, self.num_heads
+        fp8 = kv_scales is not None
+        kv_dtypes = (torch.uint8, torch.float8_e4m3fn) if fp8 else (torch.bfloat16,)
         # The C layer sees raw pointers only: every bound it cannot check
         # (device, shape, dtype, pool size) is checked here, before a launch.
         for name, t, shape in (("q_nope", q_nope, (B, H, 512)), ("q_pe", q_pe, (B, H, 64))):
@@ -249,11 +257,12 @@ class Plan:
                 raise ValueError(f"{name} must be a contiguous bf16 tensor of shape {shape}")
         strides = []
         for name, t, d in (("ckv_cache", ckv_cache, 512), ("kpe_cache", kpe_cache, 64)):
-            ok = t.dim() == 3 and t.shape[2] == d and t.dtype == torch.bfloat16
+            ok = t.dim() == 3 and t.shape[2] == d and t.dtype in kv_dtypes
             S = t.stride(1) if ok else 0
             if not ok or t.stride(2) != 1 or t.stride(0) != t.shape[1] * S:
-                raise ValueError(f"{name} must be a bf16 [pages, page_size, {d}] tensor with "
-                                 "unit stride in a row and packed rows")
+                raise ValueError(f"{name} must be a {'fp8' if fp8 else 'bf16'} "
+                                 f"[pages, page_size, {d}] tensor with unit stride in a row "
+                                 "and packed rows")
             if t.shape[0] < self.num_pages or t.shape[1] != self.page_size:
                 raise ValueError(f"{name} holds {t.shape[0]} pages of {t.shape[1]} slots; the "
                                  f"plan needs >= {self.num_pages} pages of {self.page_size}")
@@ -271,10 +280,16 @@ class Plan:
             if not t.is_cuda or t.device.index != self.device:
                 raise ValueError(f"{name} must live on cuda:{self.device}, the plan's device "
                                  f"(got {t.device})")
-        _check(_lib.pkvmla_run_strided(self._h, q_nope.data_ptr(), q_pe.data_ptr(),
+        if fp8:
+            _check(_lib.pkvmla_run_fp8(self._h, q_nope.data_ptr(), q_pe.data_ptr(),
                                        ckv_cache.data_ptr(), kpe_cache.data_ptr(), strides[0],
-                                       strides[1], out.data_ptr(), lse.data_ptr(),
-                                       _stream_handle(stream)))
+                                       strides[1], float(kv_scales[0]), float(kv_scales[1]),
+                                       out.data_ptr(), lse.data_ptr(), _stream_handle(stream)))
+        else:
+            _check(_lib.pkvmla_run_strided(self._h, q_nope.data_ptr(), q_pe.data_ptr(),
+                                           ckv_cache.data_ptr(), kpe_cache.data_ptr(),
+                                           strides[0], strides[1], out.data_ptr(),
+                                           lse.data_ptr(), _stream_handle(stream)))
         return out, lse
 
     def update(self, kv_indptr, kv_indices, kv_lens, stream=None) -> None:
@@ -309,6 +324,14 @@ class Plan:
                  stream: int) -> None:
         """Raw-pointer form of :meth:`run` (no checks beyond the library's)."""
         _check(_lib.pkvmla_run(self._h, q_nope, q_pe, ckv, kpe, out, lse, stream))
+
+    def run_fp8_ptrs(self, q_nope: int, q_pe: int, ckv: int, kpe: int, ckv_row_stride: int,
+                     kpe_row_stride: int, ckv_scale: float, kpe_scale: float, out: int, lse: int,
+                     stream: int) -> None:
+        """Raw-pointer form of :meth:`run` for fp8 caches (row strides in bytes)."""
+        _check(_lib.pkvmla_run_fp8(self._h, q_nope, q_pe, ckv, kpe, int(ckv_row_stride),
+                                   int(kpe_row_stride), float(ckv_scale), float(kpe_scale), out,
+                                   lse, stream))
 
     def run_noalloc_ptrs(self, q_nope: int, q_pe: int, ckv: int, kpe: int, out: int, lse: int,
                          stream: int) -> None:

@@ -737,9 +737,17 @@ size_t workspace_bytes(const pkvmla_plan_s* P) {
   return slots * (size_t)P->num_heads * (pkvmla::kCkvDim * sizeof(uint16_t) + sizeof(float));
 }
 
+// KV cache element type of a run: bf16, or OCP E4M3 codes with per-tensor
+// scales (a value is scale * code value).
+struct KvFormat {
+  int fp8;
+  float ckv_scale, kpe_scale;
+};
+
 int run_impl(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* ckv_cache,
              const void* kpe_cache, int64_t ckv_row_stride, int64_t kpe_row_stride, void* out,
-             float* lse, void* stream, void* workspace, size_t workspace_slots);
+             float* lse, void* stream, void* workspace, size_t workspace_slots,
+             KvFormat kv = KvFormat{0, 1.f, 1.f});
 
 }  // namespace
 
@@ -777,27 +785,52 @@ int pkvmla_run_noalloc(pkvmla_plan P, const void* q_nope, const void* q_pe,
                   lse, stream, ws, slots);
 }
 
+int pkvmla_run_fp8(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* ckv_cache,
+                   const void* kpe_cache, int64_t ckv_row_stride, int64_t kpe_row_stride,
+                   float ckv_scale, float kpe_scale, void* out, float* lse, void* stream) {
+  if (!P) return fail(PKVMLA_EINVAL, "null plan");
+  if (!(std::isfinite(ckv_scale) && ckv_scale > 0.f && std::isfinite(kpe_scale) &&
+        kpe_scale > 0.f))
+    return fail(PKVMLA_EINVAL, "fp8 cache scales must be finite and > 0 (got %g, %g)",
+                (double)ckv_scale, (double)kpe_scale);
+  // strides in bytes: ckv rows in 16-byte loads, kpe rows in 8-byte loads
+  if (ckv_row_stride < pkvmla::kCkvDim || kpe_row_stride < pkvmla::kKpeDim ||
+      (ckv_row_stride & 15) || (kpe_row_stride & 7) || ckv_row_stride > (1 << 20) ||
+      kpe_row_stride > (1 << 20))
+    return fail(PKVMLA_EINVAL,
+                "fp8 row strides (bytes) must be >= 512 and a multiple of 16 (ckv), >= 64 and "
+                "a multiple of 8 (kpe), <= 2^20 (got %lld, %lld)",
+                (long long)ckv_row_stride, (long long)kpe_row_stride);
+  if ((reinterpret_cast<uintptr_t>(kpe_cache) & 7u))
+    return fail(PKVMLA_EINVAL, "the fp8 kpe cache must be 8-byte aligned");
+  return run_impl(P, q_nope, q_pe, ckv_cache, kpe_cache, ckv_row_stride, kpe_row_stride, out,
+                  lse, stream, P->d_part, (size_t)P->cap_slots,
+                  KvFormat{1, ckv_scale, kpe_scale});
+}
+
 }  // extern "C"
 
 namespace {
 
 int run_impl(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* ckv_cache,
              const void* kpe_cache, int64_t ckv_row_stride, int64_t kpe_row_stride, void* out,
-             float* lse, void* stream, void* workspace, size_t workspace_slots) {
+             float* lse, void* stream, void* workspace, size_t workspace_slots, KvFormat kv) {
   if (!P) return fail(PKVMLA_EINVAL, "null plan");
   if (!q_nope || !q_pe || !ckv_cache || !kpe_cache || !out || !lse)
     return fail(PKVMLA_EINVAL, "null tensor pointer");
-  // strides in bf16 elements: whole 16-byte chunks, at least one row, and
+  // bf16 strides in elements: whole 16-byte chunks, at least one row, and
   // every row offset (pages x page_size rows) inside 32-bit row arithmetic
-  if (ckv_row_stride < pkvmla::kCkvDim || kpe_row_stride < pkvmla::kKpeDim ||
-      (ckv_row_stride & 7) || (kpe_row_stride & 7) || ckv_row_stride > (1 << 20) ||
-      kpe_row_stride > (1 << 20))
+  // (fp8 strides, in bytes, are checked by pkvmla_run_fp8)
+  if (!kv.fp8 && (ckv_row_stride < pkvmla::kCkvDim || kpe_row_stride < pkvmla::kKpeDim ||
+                  (ckv_row_stride & 7) || (kpe_row_stride & 7) || ckv_row_stride > (1 << 20) ||
+                  kpe_row_stride > (1 << 20)))
     return fail(PKVMLA_EINVAL,
                 "row strides must be multiples of 8 elements, >= 512 (ckv) and >= 64 (kpe), "
                 "<= 2^20 (got %lld, %lld)",
                 (long long)ckv_row_stride, (long long)kpe_row_stride);
-  if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(ckv_cache) || !aligned16(kpe_cache) ||
-      !aligned16(out) || (reinterpret_cast<uintptr_t>(lse) & 3u))
+  if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(ckv_cache) ||
+      (!kv.fp8 && !aligned16(kpe_cache)) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u))
     return fail(PKVMLA_EINVAL, "device pointers must be 16-byte aligned (lse 4-byte)");
   int dev = -1;
   PKVMLA_HIP(hipGetDevice(&dev));
@@ -813,8 +846,9 @@ int run_impl(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* ck
   d.q_pe = static_cast<const uint16_t*>(q_pe);
   d.ckv = static_cast<const uint16_t*>(ckv_cache);
   d.kpe = static_cast<const uint16_t*>(kpe_cache);
-  d.ckv_stride = (int32_t)(ckv_row_stride * 2);
-  d.kpe_stride = (int32_t)(kpe_row_stride * 2);
+  const int64_t esize = kv.fp8 ? 1 : 2;  // bytes per cache element
+  d.ckv_stride = (int32_t)(ckv_row_stride * esize);
+  d.kpe_stride = (int32_t)(kpe_row_stride * esize);
   d.out = static_cast<uint16_t*>(out);
   d.lse = lse;
   d.part_o = part_o;
@@ -830,9 +864,15 @@ int run_impl(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* ck
   d.heads_per_wave = P->cfg.heads_per_wave;
   d.stages = P->cfg.stages;
   d.log2_ps = P->log2_ps;
-  d.sm_scale = P->sm_scale;
-  d.score_log2 = (float)((double)P->sm_scale * 1.4426950408889634);
-  d.rescale_thr = (float)(8.0 / ((double)P->sm_scale * 1.4426950408889634));
+  // fp8: the ckv scale multiplies every score (the kpe part is rescaled by
+  // kpe_ratio in the kernel) and every output row
+  const double eff_scale = (double)P->sm_scale * (kv.fp8 ? (double)kv.ckv_scale : 1.0);
+  d.sm_scale = (float)eff_scale;
+  d.score_log2 = (float)(eff_scale * 1.4426950408889634);
+  d.rescale_thr = (float)(8.0 / (eff_scale * 1.4426950408889634));
+  d.fp8 = kv.fp8;
+  d.v_scale = kv.ckv_scale;
+  d.kpe_ratio = kv.fp8 ? (float)((double)kv.kpe_scale / (double)kv.ckv_scale) : 1.f;
   const int slot_ev = (int)(P->timed_runs % pkvmla_plan_s::kTimingSlots);
   d.stamps = P->timing ? P->d_stamps + 2 * slot_ev : nullptr;
   if (P->timing) PKVMLA_HIP(hipEventRecord(P->ev[2 * slot_ev], s));

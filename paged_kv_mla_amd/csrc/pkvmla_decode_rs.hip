@@ -67,7 +67,12 @@ namespace {
 constexpr int kRsPvWaves = 4;
 constexpr int kRsCopyWaves = 2;
 constexpr int kRsMaxHB = 4;
-__host__ __device__ constexpr int rs_threads(int hb) { return (hb + kRsPvWaves + kRsCopyWaves) * 64; }
+// fp8 caches: four copy waves (one per SIMD: their loads, widening and LDS
+// stores are VALU work), one copy slot each
+constexpr int kRsCopyWavesFp8 = 4;
+__host__ __device__ constexpr int rs_threads(int hb, bool fp8 = false) {
+  return (hb + kRsPvWaves + (fp8 ? kRsCopyWavesFp8 : kRsCopyWaves)) * 64;
+}
 constexpr int kRsRing = 4;     // LDS stages: PV tile, QK tile, two tiles in flight
 constexpr int kRsAhead = 2;    // k-steps between a K fragment's LDS read and its MFMA
 constexpr int kRsVAhead = 2;   // dim blocks between a V fragment's LDS read and its MFMAs
@@ -120,8 +125,12 @@ __device__ __forceinline__ void cursor_next(UnitCursor& c, idx_ptr units, int u_
 // (row strides 1 KB and 128 B, compile-time constants); otherwise the row
 // strides cs_arg and ks_arg (bytes) apply, e.g. the two views of one
 // [pages, page_size, 576] cache.  ROWS: the units are row blocks (above).
-template <bool BIG, int HB, bool PACKED, bool ROWS>
-__global__ void __launch_bounds__(rs_threads(HB), 1)
+// FP8: the caches hold OCP E4M3 codes (row strides in bytes); the copy waves
+// widen each tile to bf16 in LDS, the score is ckv part + kpe_ratio * kpe
+// part (kpe_ratio = kpe scale / ckv scale; the ckv scale is folded into
+// sm_scale by the host) and the output rows take v_scale (the ckv scale).
+template <bool BIG, int HB, bool PACKED, bool ROWS, bool FP8>
+__global__ void __launch_bounds__(rs_threads(HB, FP8), 1)
 mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
                      const uint16_t* __restrict__ ckv_cache, const uint16_t* __restrict__ kpe_cache,
                      uint16_t* __restrict__ out, float* __restrict__ lse_out,
@@ -129,7 +138,7 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
                      const int32_t* __restrict__ wg_indptr_g, const int32_t* __restrict__ units_g,
                      const int32_t* __restrict__ seq_indices_g, int H, int n_hg, int n_lanes,
                      int log2_ps, float sm_scale, float C, float thr, int cs_arg,
-                     int ks_arg, unsigned long long* stamps) {
+                     int ks_arg, unsigned long long* stamps, float v_scale, float kpe_ratio) {
   const int cs = PACKED ? kCkvDim * 2 : cs_arg;
   const int ks = PACKED ? kKpeDim * 2 : ks_arg;
   const idx_ptr wg_indptr = (idx_ptr)wg_indptr_g;
@@ -236,6 +245,8 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
           A[pp][1] = ldA(pp, 1);
         }
         f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+        // (FP8: the two kpe k-steps accumulate apart, to take their own scale)
+        f32x4_t acck[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int ks = 0; ks < 18; ++ks) {
           if (ks + AH < 18) {
@@ -243,8 +254,12 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
             A[(ks + AH) % (AH + 1)][1] = ldA(ks + AH, 1);
           }
 #pragma unroll
-          for (int tb = 0; tb < 2; ++tb)
-            acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ks % (AH + 1)][tb], q[ks], acc[tb], 0, 0, 0);
+          for (int tb = 0; tb < 2; ++tb) {
+            if (FP8 && ks >= 16)
+              acck[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ks % (AH + 1)][tb], q[ks], acck[tb], 0, 0, 0);
+            else
+              acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ks % (AH + 1)][tb], q[ks], acc[tb], 0, 0, 0);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_setprio(0);
@@ -260,7 +275,7 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-          for (int k = 0; k < 4; ++k) sv[tb * 4 + k] = acc[tb][k];
+          for (int k = 0; k < 4; ++k) sv[tb * 4 + k] = FP8 ? fmaf(kpe_ratio, acck[tb][k], acc[tb][k]) : acc[tb][k];
         if (valid < kTile) {  // a unit's partial last tile (uniform branch)
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb)
@@ -416,7 +431,7 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
         const f32x4_t l4 = *(const LDS_AS f32x4_t*)(smem + kXlOff + (par * 64 + lie * 4) * 4);
         float linv[HB];
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb) linv[hb] = __builtin_amdgcn_rcpf(l4[hb]);
+        for (int hb = 0; hb < HB; ++hb) linv[hb] = __builtin_amdgcn_rcpf(l4[hb]) * (FP8 ? v_scale : 1.f);
         // Lane (g, li) holds dims r*128 + db*16 + g*4 .. +3 of head hb*16 + li.
         // For a pair of dim blocks (2dp, 2dp+1) one row swap (rows 0<->1 and
         // 2<->3, v_permlane16_swap) gives every lane 8 consecutive dims: even
@@ -457,6 +472,64 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
+    }
+    if (stamp_lane) stamp_end(stamps);
+  } else if constexpr (FP8) {
+    // ================= copy role, fp8 caches =================
+    // copy wave cw loads copy slot cw of every tile into registers (five
+    // loads), widens it to bf16 and stores it to the tile's LDS stage.  Two
+    // register buffers alternate by tile parity: at step i the loads of tile
+    // i+2 go out, then tile i+1 (loaded one step earlier) is widened and
+    // stored, and the barrier publishes it once the wave's LDS stores have
+    // completed.  The compiler waits for the loads a store uses; no wait here
+    // covers the loads still in flight.
+    const int cw = wave - (HB + kRsPvWaves);
+    const Fp8Lanes FL = fp8_lanes(cw, cs, ks);
+    TileStream ts;
+    ts.u = u_begin;
+    ts.u_end = u_end;
+    ts.g = 0;
+    stream_load_unit(ts, units, seq_indices);
+    Fp8Slot b0, b1;
+    // Every step loads a tile: once the stream is exhausted, the last tile's
+    // rows again (valid memory, never stored).  With no branch around the
+    // loads of a step, the compiler's wait before a store counts exactly the
+    // five loads issued after that buffer's.
+    TileCopy keep;
+    auto load_tile = [&](Fp8Slot& buf) __attribute__((always_inline)) {
+      const bool more = ts.u < ts.u_end;
+      if (more) keep = tile_copy(ts, ckv, kpe, log2_ps, 0u, cw, cs, ks);
+      if (BIG && keep.full) fp8_slot_load_full(keep, FL, buf);
+      else fp8_slot_load<BIG>(keep, ckv, kpe, cw, buf);
+      if (more) stream_advance(ts, units, seq_indices, log2_ps);
+    };
+    auto store_tile = [&](const Fp8Slot& buf, int g) __attribute__((always_inline)) {
+      fp8_slot_store(smem + (g % kRsRing) * kStageBytes, FL, buf);
+    };
+    // this wave's LDS stores are complete, then the workgroup barrier (no
+    // fence: loads of the next tile stay in flight across it)
+    auto publish = [&]() __attribute__((always_inline)) {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt left open
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    load_tile(b0);  // tile 0
+    publish();      // the QK waves load their queries from here on
+    load_tile(b1);  // tile 1
+    store_tile(b0, 0);
+    publish();
+    // steps s = 0 .. G (one barrier each), two per pass: step s loads tile
+    // s+2 into the buffer of tile s (stored at step s-1) and stores tile s+1
+    for (int i = 0;; i += 2) {
+      load_tile(b0);
+      if (i + 1 < G) store_tile(b1, i + 1);
+      publish();
+      if (i >= G) break;
+      load_tile(b1);
+      if (i + 2 < G) store_tile(b0, i + 2);
+      publish();
+      if (i + 1 >= G) break;
     }
     if (stamp_lane) stamp_end(stamps);
   } else {
@@ -533,17 +606,20 @@ bool launch_decode_rs(const DecodeParams& p, hipStream_t stream, hipError_t* err
   if (!hb) return false;
   const bool big = p.log2_ps >= 5;
   const bool packed = p.ckv_stride == kCkvDim * 2 && p.kpe_stride == kKpeDim * 2;
-  const dim3 grid(decode_grid(p.n_lanes, p.head_groups)), block(rs_threads(hb));
+  const dim3 grid(decode_grid(p.n_lanes, p.head_groups)), block(rs_threads(hb, p.fp8 != 0));
 #define PKVMLA_RS_ARGS                                                                   \
   p.q_nope, p.q_pe, p.ckv, p.kpe, p.out, p.lse, p.part_o, p.part_lse, p.wg_indptr, p.units, \
       p.seq_indices, p.num_heads, p.head_groups, p.n_lanes, p.log2_ps, p.sm_scale,     \
-      p.score_log2, p.rescale_thr, p.ckv_stride, p.kpe_stride, p.stamps
-#define PKVMLA_RS_LAUNCH2(HBV, PK, RB)                                                           \
-  if (big) mla_decode_rs_kernel<true, HBV, PK, RB><<<grid, block, 0, stream>>>(PKVMLA_RS_ARGS);  \
-  else mla_decode_rs_kernel<false, HBV, PK, RB><<<grid, block, 0, stream>>>(PKVMLA_RS_ARGS);
-#define PKVMLA_RS_LAUNCH(HBV, RB)                 \
-  if (packed) { PKVMLA_RS_LAUNCH2(HBV, true, RB) } \
-  else { PKVMLA_RS_LAUNCH2(HBV, false, RB) }
+      p.score_log2, p.rescale_thr, p.ckv_stride, p.kpe_stride, p.stamps, p.v_scale,    \
+      p.kpe_ratio
+#define PKVMLA_RS_LAUNCH3(HBV, PK, RB, F8)                                                     \
+  if (big) mla_decode_rs_kernel<true, HBV, PK, RB, F8><<<grid, block, 0, stream>>>(PKVMLA_RS_ARGS); \
+  else mla_decode_rs_kernel<false, HBV, PK, RB, F8><<<grid, block, 0, stream>>>(PKVMLA_RS_ARGS);
+  // fp8 caches always take the runtime row strides
+#define PKVMLA_RS_LAUNCH(HBV, RB)                                   \
+  if (p.fp8) { PKVMLA_RS_LAUNCH3(HBV, false, RB, true) }            \
+  else if (packed) { PKVMLA_RS_LAUNCH3(HBV, true, RB, false) }      \
+  else { PKVMLA_RS_LAUNCH3(HBV, false, RB, false) }
   if (p.row_blocks) {
     PKVMLA_RS_LAUNCH(4, true)
   } else {
@@ -554,7 +630,7 @@ bool launch_decode_rs(const DecodeParams& p, hipStream_t stream, hipError_t* err
     }
   }
 #undef PKVMLA_RS_LAUNCH
-#undef PKVMLA_RS_LAUNCH2
+#undef PKVMLA_RS_LAUNCH3
 #undef PKVMLA_RS_ARGS
   *err = hipGetLastError();
   return true;

@@ -53,6 +53,9 @@ struct DecodeParams {
   float rescale_thr;         // raw-score margin before the running max moves (8 / score_log2)
   unsigned long long* stamps;  // null, or {earliest start, latest end} of the launch's
                                // waves on the 100 MHz real-time clock (timing runs only)
+  int32_t fp8;               // caches hold OCP E4M3 codes (ckv, kpe as bytes)
+  float v_scale;             // fp8: ckv scale (output rows); else unused
+  float kpe_ratio;           // fp8: kpe scale / ckv scale; else unused
 };
 
 struct MergeParams {

@@ -155,27 +155,38 @@ __device__ __forceinline__ CopyLanes copy_lanes(int wave, int ks) {
 // times, as in the whole-tile path).
 // PACKED: the caches' rows are 1 KB (ckv) and 128 B (kpe) apart, so row
 // addresses are shifts; otherwise they take the runtime strides.
-template <bool BIG, bool PACKED>
-__device__ __forceinline__ void tile_copy_slot(const TileCopy& c, const char* __restrict__ ckv,
-                                               const char* __restrict__ kpe, int wave,
-                                               const CopyLanes& L) {
-  // slot tokens: ckv rows 4*wave + j, 4*wave + 16 + j; kpe tokens 8*wave + k
-  auto tok_of = [&](int i) { return i < 4 ? 4 * wave + i : i < 8 ? 4 * wave + 12 + i : 8 * wave + i - 8; };
-  uint32_t rows[16];
+// Slot tokens: ckv rows 4*wave + j and 4*wave + 16 + j (i = 0..7), kpe tokens
+// 8*wave + k (i = 8..15).
+__device__ __forceinline__ int slot_token(int wave, int i) {
+  return i < 4 ? 4 * wave + i : i < 8 ? 4 * wave + 12 + i : 8 * wave + i - 8;
+}
+
+// Cache rows of a slot's 16 tokens, clamped to the tile's last valid token.
+template <bool BIG>
+__device__ __forceinline__ void slot_rows(const TileCopy& c, int wave, uint32_t* rows) {
   if constexpr (BIG) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) rows[i] = c.row0 + (uint32_t)min(tok_of(i), c.last);  // one page
+    for (int i = 0; i < 16; ++i) rows[i] = c.row0 + (uint32_t)min(slot_token(wave, i), c.last);  // one page
   } else {
     // all 16 page-id loads go out before the first use (one wait, not 16)
     const int ps_mask = (1 << c.log2_ps) - 1;
     uint32_t pid[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) pid[i] = (uint32_t)c.pages[(c.tok0 + min(tok_of(i), c.last)) >> c.log2_ps];
+    for (int i = 0; i < 16; ++i)
+      pid[i] = (uint32_t)c.pages[(c.tok0 + min(slot_token(wave, i), c.last)) >> c.log2_ps];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      rows[i] = (pid[i] << c.log2_ps) + (uint32_t)((c.tok0 + min(tok_of(i), c.last)) & ps_mask);
+      rows[i] = (pid[i] << c.log2_ps) + (uint32_t)((c.tok0 + min(slot_token(wave, i), c.last)) & ps_mask);
   }
+}
+
+template <bool BIG, bool PACKED>
+__device__ __forceinline__ void tile_copy_slot(const TileCopy& c, const char* __restrict__ ckv,
+                                               const char* __restrict__ kpe, int wave,
+                                               const CopyLanes& L) {
+  uint32_t rows[16];
+  slot_rows<BIG>(c, wave, rows);
   const uint32_t* rc = rows;
   const uint32_t* rk = rows + 8;
   // ckv: the source of row t is its row address; the copy's instruction
@@ -221,6 +232,115 @@ __device__ __forceinline__ void tile_copy_part_full(const TileCopy& c, int wave,
     set_m0(c.st + kTile * 1024 + (uint32_t)wave * 1024u);
     dma16_m0<0>(c.kb, L.vk);
   }
+}
+
+// ---------------------------------------------------------------------------
+// fp8 (OCP E4M3) caches: a slot's share of a tile goes HBM -> registers ->
+// bf16 -> LDS, into the same swizzled bf16 layout as the direct copies, so
+// the QK and PV waves read the tile unchanged.  Every E4M3 value is exactly a
+// bf16 value (3 mantissa bits, exponents 2^-9 .. 2^8), so the widening is
+// exact; the caches' scales are applied in fp32 by the consumers.
+// A slot's registers: its 8 ckv rows as four 16-byte loads (lanes 0..31 and
+// 32..63 take rows 2i and 2i+1 of the slot, 16 codes each: bf16 chunks 2c
+// and 2c+1 of the row) and its 8 kpe rows as one 8-byte load (lane l: token
+// 8*wave + l/8, chunk l%8).  Row strides cs and ks are in bytes.
+// ---------------------------------------------------------------------------
+struct Fp8Slot {
+  u32x4_t c[4];
+  uint32_t k[2];
+};
+
+// Loads through the global address space: a generic (flat) load would also
+// count on lgkmcnt, so the LDS-store wait before each barrier would wait for
+// the next tile's loads too.
+#define PKVMLA_GLOBAL_AS __attribute__((address_space(1)))
+typedef const PKVMLA_GLOBAL_AS char* gchar_ptr;
+__device__ __forceinline__ u32x4_t gload16(gchar_ptr p) {
+  return *reinterpret_cast<const PKVMLA_GLOBAL_AS u32x4_t*>(p);
+}
+typedef uint32_t u32x2_t __attribute__((__vector_size__(8)));
+__device__ __forceinline__ u32x2_t gload8(gchar_ptr p) {
+  return *reinterpret_cast<const PKVMLA_GLOBAL_AS u32x2_t*>(p);
+}
+
+template <bool BIG>
+__device__ __forceinline__ void fp8_slot_load(const TileCopy& c, const char* __restrict__ ckv,
+                                              const char* __restrict__ kpe, int wave, Fp8Slot& r) {
+  uint32_t rows[16];
+  slot_rows<BIG>(c, wave, rows);
+  const int lane = lane_id_fresh();
+  const int half = lane >> 5, cl = lane & 31;
+  const gchar_ptr gc = (gchar_ptr)ckv;
+  const gchar_ptr gk = (gchar_ptr)kpe;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t row = half ? rows[2 * i + 1] : rows[2 * i];
+    r.c[i] = gload16(gc + (size_t)row * c.cs + cl * 16);
+  }
+  const int g8 = lane >> 3;
+  uint32_t row = rows[8];
+#pragma unroll
+  for (int k = 1; k < 8; ++k) row = g8 == k ? rows[8 + k] : row;
+  const u32x2_t kv = gload8(gk + (size_t)row * c.ks + (lane & 7) * 8);
+  r.k[0] = kv[0];
+  r.k[1] = kv[1];
+}
+
+// Per-lane constants of one copy slot: the byte offsets of its loads from
+// the tile's first ckv and kpe rows (whole tiles of one page: rows t at
+// t * stride) and the LDS offsets (within a stage) of its bf16 chunks.
+struct Fp8Lanes {
+  uint32_t gc[4], gk;
+  uint32_t lc[8], lk;
+};
+
+__device__ __forceinline__ Fp8Lanes fp8_lanes(int wave, int cs, int ks) {
+  const int lane = lane_id_fresh();
+  const int half = lane >> 5, cl = lane & 31;
+  Fp8Lanes L;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = slot_token(wave, 2 * i + half);
+    L.gc[i] = (uint32_t)(t * cs + cl * 16);
+    L.lc[2 * i] = (uint32_t)lds_ckv_off(t, 2 * cl);
+    L.lc[2 * i + 1] = (uint32_t)lds_ckv_off(t, 2 * cl + 1);
+  }
+  const int t = 8 * wave + (lane >> 3);
+  L.gk = (uint32_t)(t * ks + (lane & 7) * 8);
+  L.lk = (uint32_t)lds_kpe_off(t, lane & 7);
+  return L;
+}
+
+// A whole tile of one page (BIG and full): scalar row bases plus the lane
+// offsets, no clamping.
+__device__ __forceinline__ void fp8_slot_load_full(const TileCopy& c, const Fp8Lanes& L, Fp8Slot& r) {
+  const gchar_ptr crow = (gchar_ptr)to_sgpr(c.crow);
+  const gchar_ptr krow = (gchar_ptr)to_sgpr(c.krow);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.c[i] = gload16(crow + L.gc[i]);
+  const u32x2_t kv = gload8(krow + L.gk);
+  r.k[0] = kv[0];
+  r.k[1] = kv[1];
+}
+
+// Four codes (one dword) to four bf16 (two dwords), exactly.
+__device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t v) {
+  const auto lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, false);
+  const auto hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, true);
+  return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+}
+
+__device__ __forceinline__ void fp8_slot_store(LDS_AS char* stage, const Fp8Lanes& L,
+                                               const Fp8Slot& r) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint2 a = fp8x4_to_bf16x4(r.c[i][0]), b = fp8x4_to_bf16x4(r.c[i][1]);
+    const uint2 d = fp8x4_to_bf16x4(r.c[i][2]), e = fp8x4_to_bf16x4(r.c[i][3]);
+    *(LDS_AS u32x4_t*)(stage + L.lc[2 * i]) = u32x4_t{a.x, a.y, b.x, b.y};
+    *(LDS_AS u32x4_t*)(stage + L.lc[2 * i + 1]) = u32x4_t{d.x, d.y, e.x, e.y};
+  }
+  const uint2 a = fp8x4_to_bf16x4(r.k[0]), b = fp8x4_to_bf16x4(r.k[1]);
+  *(LDS_AS u32x4_t*)(stage + L.lk) = u32x4_t{a.x, a.y, b.x, b.y};
 }
 
 }  // namespace pkvmla

@@ -31,52 +31,70 @@ def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
 
 
 class Dev:
-    """Device copies of one input bundle."""
+    """Device copies of one input bundle (fp8=True: its E4M3 caches, from
+    mla_workloads.quantize_kv_fp8, instead of the bf16 ones)."""
 
-    def __init__(self, inp):
+    def __init__(self, inp, fp8: bool = False):
         self.inp = inp
         self.q_nope = dev_bf16(inp.q_nope)
         self.q_pe = dev_bf16(inp.q_pe)
-        self.ckv = dev_bf16(inp.ckv)
-        self.kpe = dev_bf16(inp.kpe)
+        self.fp8 = fp8
+        if fp8:
+            self.ckv = torch.from_numpy(np.ascontiguousarray(inp.ckv8)).to("cuda")
+            self.kpe = torch.from_numpy(np.ascontiguousarray(inp.kpe8)).to("cuda")
+            self.kv_scales = (inp.ckv_scale, inp.kpe_scale)
+        else:
+            self.ckv = dev_bf16(inp.ckv)
+            self.kpe = dev_bf16(inp.kpe)
+            self.kv_scales = None
 
 
 def run_gpu(plan, dev: Dev, out=None, lse=None):
-    o, l = plan.run(dev.q_nope, dev.q_pe, dev.ckv, dev.kpe, out=out, lse=lse)
+    o, l = plan.run(dev.q_nope, dev.q_pe, dev.ckv, dev.kpe, out=out, lse=lse,
+                    kv_scales=dev.kv_scales)
     torch.cuda.synchronize()
     return o, l
 
 
-def oracle_flat(inp, requests=None):
-    """fp64 oracle out/lse for all (or the listed) requests of flat inputs."""
+def _kv(inp, fp8):
+    return ((inp.ckv8, inp.kpe8, (inp.ckv_scale, inp.kpe_scale)) if fp8
+            else (inp.ckv, inp.kpe, None))
+
+
+def oracle_flat(inp, requests=None, fp8: bool = False):
+    """fp64 oracle out/lse for all (or the listed) requests of flat inputs
+    (fp8: of its E4M3 caches and scales)."""
     reqs = range(inp.batch) if requests is None else requests
     outs, lses = [], []
     for b in reqs:
         sl = slice(b, b + 1)
         ip = np.array([0, inp.kv_indptr[b + 1] - inp.kv_indptr[b]], np.int32)
         ix = inp.kv_indices[inp.kv_indptr[b]:inp.kv_indptr[b + 1]]
-        o, l = oracle.attend_flat(inp.q_nope[sl], inp.q_pe[sl], inp.ckv, inp.kpe, ip, ix,
-                                  inp.kv_lens[sl], inp.page_size, sm_scale=inp.sm_scale)
+        ckv, kpe, sc = _kv(inp, fp8)
+        o, l = oracle.attend_flat(inp.q_nope[sl], inp.q_pe[sl], ckv, kpe, ip, ix,
+                                  inp.kv_lens[sl], inp.page_size, sm_scale=inp.sm_scale,
+                                  kv_scales=sc)
         outs.append(o[0])
         lses.append(l[0])
     return np.stack(outs), np.stack(lses)
 
 
-def oracle_cascade(inp, requests=None):
+def oracle_cascade(inp, requests=None, fp8: bool = False):
     reqs = range(inp.batch) if requests is None else requests
     outs, lses = [], []
+    ckv, kpe, sc = _kv(inp, fp8)
     for b in reqs:
         g = inp.group_of(b)
         sl = slice(b, b + 1)
         o, l = oracle.attend_cascade(
-            inp.q_nope[sl], inp.q_pe[sl], inp.ckv, inp.kpe, inp.page_size,
+            inp.q_nope[sl], inp.q_pe[sl], ckv, kpe, inp.page_size,
             np.array([0, 1], np.int32),
             np.array([0, inp.prefix_indptr[g + 1] - inp.prefix_indptr[g]], np.int32),
             inp.prefix_indices[inp.prefix_indptr[g]:inp.prefix_indptr[g + 1]],
             inp.prefix_lens[g:g + 1],
             np.array([0, inp.kv_indptr[b + 1] - inp.kv_indptr[b]], np.int32),
             inp.kv_indices[inp.kv_indptr[b]:inp.kv_indptr[b + 1]], inp.kv_lens[sl],
-            sm_scale=inp.sm_scale)
+            sm_scale=inp.sm_scale, kv_scales=sc)
         outs.append(o[0])
         lses.append(l[0])
     return np.stack(outs), np.stack(lses)
