@@ -322,6 +322,26 @@ int pkvmla_schedule_rows_host(const int32_t* group_req_indptr, int32_t num_group
                               int32_t tile, int32_t* wg_indptr, int64_t cap_wg,
                               int32_t* units, int64_t cap_units, int32_t* counts);
 
+/* The one-launch cascade schedule, computed on the host exactly as
+ * pkvmla_plan_create_cascade does for an ordinary plan with num_heads >= 64
+ * and every prefix non-empty (no GPU needed).  Request b of group g is one
+ * block over g's prefix, cut over num_wg lanes as in
+ * pkvmla_schedule_rows_host (batch <= num_wg: S = num_wg / batch pieces,
+ * piece p on lane b*S + p; else request b whole on lane b mod num_wg).  Its
+ * non-empty suffix (sequence num_groups + b, tokens 0 .. kv_lens[b]) follows
+ * its last piece on that lane, and that piece's slot field is INT32_MIN: the
+ * softmax state carries into the suffix unit.  A request with one piece
+ * writes out directly (slot -1); otherwise each of its states takes the next
+ * slot (emission order) and it gets a merge record (b, first list entry,
+ * count, 1).  Unit records: (b, sequence, kv_begin, kv_end, slot, 0, 0, 0).
+ * counts[0..3] = grid, n_units, n_merges, slot-list length. */
+int pkvmla_schedule_chain_host(const int32_t* group_req_indptr, int32_t num_groups,
+                               const int32_t* prefix_lens, const int32_t* kv_lens,
+                               int32_t batch, int32_t num_wg, int32_t tile, int32_t* wg_indptr,
+                               int64_t cap_wg, int32_t* units, int64_t cap_units,
+                               int32_t* merges, int64_t cap_merges, int32_t* slot_list,
+                               int64_t cap_list, int32_t* counts);
+
 /* Copy the plan's uploaded device tables back to the host, for bit-exact
  * checking.  Layout of host int32 buf (cap elements):
  *   [0..15]  header: version(1), batch, num_heads, page_size, ckv_dim,
@@ -331,7 +351,9 @@ int pkvmla_schedule_rows_host(const int32_t* group_req_indptr, int32_t num_group
  *            is_cascade, num_groups, head_groups, launched workgroups,
  *            fixed launch shapes (0/1), page-id capacity, several query tokens
  *            per request (0/1), number of requests of such a plan,
- *            cascade level 0: grid0, n_units0, slot-list length, head groups
+ *            cascade level 0: grid0, n_units0, slot-list length, and 1 when the
+ *            cascade runs in one launch (level-0 table: requests' prefix
+ *            pieces with their suffixes chained; no level-1 units), else 0
  *   then wg_indptr[grid+1], units[n_units*8], merges[n_merges*4],
  *   seq_indptr[num_seqs+1], seq_lens[num_seqs], seq_indices[n_indices],
  *   and for a cascade plan wg_indptr0[grid0+1], units0[n_units0*8] (the

@@ -137,6 +137,77 @@ def row_schedule_ref(group_req_indptr, prefix_lens, num_heads: int, num_wg: int,
     return (np.asarray(wg, np.int32), np.asarray(units, np.int32).reshape(-1, UNIT_INTS), slot)
 
 
+CHAIN_NEXT = -(2 ** 31)   # slot field: the unit's state carries into the next unit
+
+
+def cascade_chain_ref(group_req_indptr, prefix_lens, kv_lens, num_wg: int, tile: int = PLAN_TILE):
+    """A cascade in one launch (64 heads or more, every prefix non-empty).
+
+    Request b (in group g) is one block over the g prefix of L tiles' tokens.
+    B requests on W lanes: B <= W gives S = W // B pieces per request (P =
+    min(S, tiles) of them; piece p covers tiles p*T//P .. (p+1)*T//P - 1, on
+    lane b*S + p); B > W puts request b whole on lane b % W.  Right after the
+    last piece of b, on its lane, comes b's suffix (sequence G + b, tokens
+    0 .. kv_lens[b]) when it is non-empty; that piece's slot field is
+    CHAIN_NEXT (its state carries into the suffix unit).  A request with one
+    piece writes out directly (slot -1); otherwise every state (each earlier
+    piece, and the last piece or its chain) takes the next slot in emission
+    order, and the request gets a merge record (b, first list entry, count, 1)
+    listing its slots.  Unit records: (b, seq, kv_begin, kv_end, slot, 0, page
+    fields 0, 0).  Returns dict(wg0, units0, merges, slot_list, n_slots)."""
+    G = len(prefix_lens)
+    B = len(kv_lens)
+    grp = np.zeros(B, np.int64)
+    for g in range(G):
+        assert int(prefix_lens[g]) > 0
+        grp[int(group_req_indptr[g]):int(group_req_indptr[g + 1])] = g
+    if B <= num_wg:
+        S = num_wg // B
+        grid = B * S
+        lanes = [[] for _ in range(grid)]
+        P = []
+        for b in range(B):
+            L = int(prefix_lens[grp[b]])
+            T = -(-L // tile)
+            n = min(S, T)
+            P.append(n)
+            for p in range(n):
+                t0, t1 = p * T // n, (p + 1) * T // n
+                lanes[b * S + p].append((b, t0 * tile, min(t1 * tile, L), p == n - 1))
+    else:
+        grid = num_wg
+        lanes = [[] for _ in range(grid)]
+        P = [1] * B
+        for b in range(B):
+            lanes[b % num_wg].append((b, 0, int(prefix_lens[grp[b]]), True))
+    units, wg, per = [], [0], [[] for _ in range(B)]
+    slot = 0
+    for lane in lanes:
+        for (b, k0, k1, last) in lane:
+            chain = last and int(kv_lens[b]) > 0
+
+            def take():
+                nonlocal slot
+                if P[b] == 1:
+                    return -1
+                per[b].append(slot)
+                slot += 1
+                return slot - 1
+            units.append((b, int(grp[b]), k0, k1, CHAIN_NEXT if chain else take(), 0, 0, 0))
+            if chain:
+                units.append((b, G + b, 0, int(kv_lens[b]), take(), 0, 0, 0))
+        wg.append(len(units))
+    merges, slot_list = [], []
+    for b in range(B):
+        if per[b]:
+            merges.append((b, len(slot_list), len(per[b]), 1))
+            slot_list.extend(per[b])
+    return dict(wg0=np.asarray(wg, np.int32),
+                units0=np.asarray(units, np.int64).astype(np.int32).reshape(-1, UNIT_INTS),
+                merges=np.asarray(merges, np.int32).reshape(-1, MERGE_INTS),
+                slot_list=np.asarray(slot_list, np.int32), n_slots=slot)
+
+
 def cascade_plan_ref(group_req_indptr, prefix_lens, kv_lens, num_heads: int, num_wg: int,
                      num_wg0: int, tile: int = PLAN_TILE, fixed: int = 1):
     """The two schedules of a cascade plan and its merge lists.

@@ -73,6 +73,10 @@ _lib.pkvmla_schedule_host.argtypes = [_i32p, ctypes.c_int32, ctypes.c_int32, cty
 _lib.pkvmla_schedule_rows_host.argtypes = [_i32p, ctypes.c_int32, _i32p, ctypes.c_int32,
                                            ctypes.c_int32, ctypes.c_int32, _i32p, ctypes.c_int64,
                                            _i32p, ctypes.c_int64, _i32p]
+_lib.pkvmla_schedule_chain_host.argtypes = [_i32p, ctypes.c_int32, _i32p, _i32p, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_int32, _i32p, ctypes.c_int64,
+                                            _i32p, ctypes.c_int64, _i32p, ctypes.c_int64, _i32p,
+                                            ctypes.c_int64, _i32p]
 _lib.pkvmla_plan_export.argtypes = [_vp, _i32p, ctypes.c_int64, _i64p]
 _lib.pkvmla_gather.argtypes = [_vp, _vp, _vp, _vp, _vp]
 _lib.pkvmla_gather_rows.argtypes = [_vp, _i64p]
@@ -87,6 +91,7 @@ EXPORTED_SYMBOLS = (
     "pkvmla_gather", "pkvmla_gather_rows", "pkvmla_plan_set_timing", "pkvmla_plan_timing",
     "pkvmla_run_noalloc", "pkvmla_plan_create_qo", "pkvmla_schedule_rows_host",
     "pkvmla_plan_create_cascade_with_capacity", "pkvmla_plan_update_cascade", "pkvmla_run_fp8",
+    "pkvmla_schedule_chain_host",
 )
 
 OK, EINVAL, EUNSUPPORTED, EHIP, ENOMEM = 0, 1, 2, 3, 4
@@ -181,6 +186,28 @@ def schedule_rows_host(group_req_indptr, prefix_lens, num_heads: int, num_wg: in
                                           units.size, _ptr(counts)))
     grid, nu, ns = (int(c) for c in counts)
     return wg[:grid + 1].copy(), units[:8 * nu].reshape(nu, 8).copy(), ns
+
+
+def schedule_chain_host(group_req_indptr, prefix_lens, kv_lens, num_wg: int, tile: int = 32):
+    """The library's one-launch cascade schedule, computed on the host.
+    Returns (wg_indptr, units [n, 8], merges [m, 4], slot_list)."""
+    gi, pl, kl = _i32(group_req_indptr), _i32(prefix_lens), _i32(kv_lens)
+    if gi.ndim != 1 or len(gi) != len(pl) + 1:
+        raise ValueError("group_req_indptr needs len(prefix_lens) + 1 entries")
+    B = len(kl)
+    cap = 2 * (B + int(num_wg)) + 8
+    wg = np.zeros(int(num_wg) + 1, np.int32)
+    units = np.zeros(8 * cap, np.int32)
+    merges = np.zeros(4 * (B + 1), np.int32)
+    lst = np.zeros(cap, np.int32)
+    counts = np.zeros(4, np.int32)
+    _check(_lib.pkvmla_schedule_chain_host(_ptr(gi), len(pl), _ptr(pl), _ptr(kl), B, int(num_wg),
+                                           int(tile), _ptr(wg), wg.size, _ptr(units), units.size,
+                                           _ptr(merges), merges.size, _ptr(lst), lst.size,
+                                           _ptr(counts)))
+    grid, nu, nm, nl = (int(c) for c in counts)
+    return (wg[:grid + 1].copy(), units[:8 * nu].reshape(nu, 8).copy(),
+            merges[:4 * nm].reshape(nm, 4).copy(), lst[:nl].copy())
 
 
 @dataclass

@@ -78,6 +78,9 @@ struct pkvmla_plan_s {
   pkvmla::RowSchedule sched0;
   std::vector<int32_t> slot_list;
   int32_t cap_lanes0 = 0, cap_units0 = 0, cap_list = 0;
+  // cascade in one launch: each request's suffix chained after its prefix
+  // piece (64 heads or more, every prefix non-empty, ordinary plans)
+  int32_t cascade_chain = 0;
   size_t off_wg = 0, off_units = 0, off_merges = 0, off_sip = 0, off_sl = 0, off_si = 0;
   size_t off_wg0 = 0, off_units0 = 0, off_list = 0;
   // device tables (one allocation) and split workspace
@@ -299,6 +302,34 @@ void cascade_sequences(const CascadeTables& t, std::vector<int32_t>* sip, std::v
   for (int32_t b = 0; b < B; ++b) items->push_back(pkvmla::WorkItem{b, G + b, t.kv_lens[b]});
 }
 
+static_assert(pkvmla::kChainNext == pkvmla::kChainNextSlot, "chained-unit slot marker");
+
+// The one-launch (chained) cascade schedule, in the plan's tables: its units
+// in the level-0 table, no level-1 units.
+int build_chain_tables(const pkvmla_plan_s* P, const Level0Groups& l0, const int32_t* kv_lens,
+                       const std::vector<int32_t>& seq_indptr,
+                       const std::vector<int32_t>& seq_indices, pkvmla::Schedule* sched,
+                       pkvmla::RowSchedule* sched0, std::vector<int32_t>* slot_list) {
+  if (!pkvmla::build_chain_schedule(l0.group_req_indptr, l0.num_groups, l0.prefix_lens, kv_lens,
+                                    P->batch, P->cap_lanes0, pkvmla::kTile, sched0,
+                                    &sched->merges, slot_list))
+    return fail(PKVMLA_EUNSUPPORTED, "chained cascade schedule construction failed");
+  fill_page_fields(&sched0->units, seq_indptr, seq_indices, P->page_size);
+  sched->grid = 0;
+  sched->wg_indptr.assign(1, 0);
+  sched->units.clear();
+  sched->n_slots = sched0->n_slots;
+  sched->total_rows = 0;
+  return PKVMLA_OK;
+}
+
+bool chain_eligible(const pkvmla_plan_s* P, const Level0Groups& l0) {
+  if (P->fixed_launch || P->num_heads < 64) return false;
+  for (int32_t g = 0; g < l0.num_groups; ++g)
+    if (l0.prefix_lens[g] <= 0) return false;
+  return true;
+}
+
 // Fix the capacities, build the schedule, allocate and upload the device tables.
 // With `l0` (cascade plans) the items are the suffixes; the level-0 row-block
 // schedule is built beside them, every suffix unit writes a partial state
@@ -333,8 +364,21 @@ int finish_plan(pkvmla_plan_s* P, const std::vector<pkvmla::WorkItem>& items,
     P->cap_units0 = (int32_t)u0;
     P->cap_slots = (int32_t)slots;
     P->cap_list = (int32_t)slots;
-    rc = build_cascade_schedules(P, *l0, items, seq_indptr, seq_indices, &P->sched, &P->sched0,
-                                 &P->slot_list);
+    P->cascade_chain = chain_eligible(P, *l0) ? 1 : 0;
+    if (P->cascade_chain) {
+      // pieces: at most one per lane (batch <= lanes) or one per request;
+      // plus a suffix unit per request; a slot per piece or chain at most
+      const int64_t pieces = std::max<int64_t>(P->cap_lanes0, B);
+      P->cap_units0 = (int32_t)std::max<int64_t>(u0, pieces + B);
+      P->cap_slots = (int32_t)std::max<int64_t>(slots, pieces + B);
+      P->cap_list = P->cap_slots;
+      std::vector<int32_t> kvl(seq_lens.begin() + l0->num_groups, seq_lens.end());
+      rc = build_chain_tables(P, *l0, kvl.data(), seq_indptr, seq_indices, &P->sched,
+                              &P->sched0, &P->slot_list);
+    } else {
+      rc = build_cascade_schedules(P, *l0, items, seq_indptr, seq_indices, &P->sched,
+                                   &P->sched0, &P->slot_list);
+    }
   } else {
     rc = build_plan_schedule(P, items, seq_indptr, seq_indices, &P->sched);
   }
@@ -464,6 +508,44 @@ int pkvmla_schedule_rows_host(const int32_t* group_req_indptr, int32_t num_group
   if (!s.units.empty() && !units) return fail(PKVMLA_EINVAL, "null units");
   std::copy(s.wg_indptr.begin(), s.wg_indptr.end(), wg_indptr);
   std::copy(s.units.begin(), s.units.end(), units);
+  return ok();
+}
+
+int pkvmla_schedule_chain_host(const int32_t* group_req_indptr, int32_t num_groups,
+                                const int32_t* prefix_lens, const int32_t* kv_lens, int32_t batch,
+                                int32_t num_wg, int32_t tile, int32_t* wg_indptr, int64_t cap_wg,
+                                int32_t* units, int64_t cap_units, int32_t* merges,
+                                int64_t cap_merges, int32_t* slot_list, int64_t cap_list,
+                                int32_t* counts) {
+  if (!group_req_indptr || !prefix_lens || !kv_lens || !counts || num_groups < 1 || batch < 1)
+    return fail(PKVMLA_EINVAL, "null argument, num_groups < 1 or batch < 1");
+  if (num_wg < 1 || tile < 1) return fail(PKVMLA_EINVAL, "num_wg and tile must be >= 1");
+  if (group_req_indptr[0] != 0 || group_req_indptr[num_groups] != batch)
+    return fail(PKVMLA_EINVAL, "group_req_indptr must run from 0 to batch");
+  for (int32_t g = 0; g < num_groups; ++g)
+    if (group_req_indptr[g + 1] < group_req_indptr[g] || prefix_lens[g] < 1)
+      return fail(PKVMLA_EINVAL, "group %d: decreasing indptr or empty prefix", g);
+  for (int32_t b = 0; b < batch; ++b)
+    if (kv_lens[b] < 0) return fail(PKVMLA_EINVAL, "negative suffix length at %d", b);
+  pkvmla::RowSchedule s;
+  std::vector<int32_t> m, l;
+  if (!pkvmla::build_chain_schedule(group_req_indptr, num_groups, prefix_lens, kv_lens, batch,
+                                    num_wg, tile, &s, &m, &l))
+    return fail(PKVMLA_EINVAL, "chain schedule construction failed");
+  counts[0] = s.grid;
+  counts[1] = (int32_t)(s.units.size() / pkvmla::kUnitRecordInts);
+  counts[2] = (int32_t)(m.size() / pkvmla::kMergeRecordInts);
+  counts[3] = (int32_t)l.size();
+  if ((int64_t)s.wg_indptr.size() > cap_wg || (int64_t)s.units.size() > cap_units ||
+      (int64_t)m.size() > cap_merges || (int64_t)l.size() > cap_list)
+    return fail(PKVMLA_EINVAL, "output capacity too small");
+  if (!wg_indptr || (!s.units.empty() && !units) || (!m.empty() && !merges) ||
+      (!l.empty() && !slot_list))
+    return fail(PKVMLA_EINVAL, "null output");
+  std::copy(s.wg_indptr.begin(), s.wg_indptr.end(), wg_indptr);
+  std::copy(s.units.begin(), s.units.end(), units);
+  std::copy(m.begin(), m.end(), merges);
+  std::copy(l.begin(), l.end(), slot_list);
   return ok();
 }
 
@@ -710,7 +792,16 @@ int pkvmla_plan_update_cascade(pkvmla_plan P, const int32_t* group_req_indptr,
   pkvmla::RowSchedule sched0;
   std::vector<int32_t> list;
   const Level0Groups l0{group_req_indptr, P->num_groups, prefix_lens};
-  rc = build_cascade_schedules(P, l0, items, sip, si, &sched, &sched0, &list);
+  if (P->cascade_chain) {
+    // a plan in the one-launch layout keeps it (an update that would need the
+    // two-level layout, an empty prefix, is refused: its launches differ)
+    if (!chain_eligible(P, l0))
+      return fail(PKVMLA_EUNSUPPORTED, "this plan runs its cascade in one launch, which needs "
+                  "every prefix non-empty (build it with an index_capacity to update freely)");
+    rc = build_chain_tables(P, l0, kv_lens, sip, si, &sched, &sched0, &list);
+  } else {
+    rc = build_cascade_schedules(P, l0, items, sip, si, &sched, &sched0, &list);
+  }
   if (rc) return rc;
   if ((int64_t)sched.units.size() > (int64_t)P->cap_units * pkvmla::kUnitRecordInts ||
       sched.grid > P->cap_lanes || sched0.grid > P->cap_lanes0 ||
@@ -886,7 +977,7 @@ int run_impl(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* ck
     d0.waves = P->cfg0.waves;
     d0.heads_per_wave = P->cfg0.heads_per_wave;
     d0.stages = P->cfg0.stages;
-    d0.row_blocks = 1;
+    d0.row_blocks = P->cascade_chain ? 0 : 1;
     PKVMLA_HIP(pkvmla::launch_decode(d0, s));
   }
   PKVMLA_HIP(pkvmla::launch_decode(d, s));
@@ -1020,7 +1111,7 @@ int pkvmla_plan_export(pkvmla_plan P, int32_t* buf, int64_t cap, int64_t* used) 
   buf[28] = P->sched0.grid;
   buf[29] = (int32_t)(n_u0 / pkvmla::kUnitRecordInts);
   buf[30] = (int32_t)n_sl;
-  buf[31] = P->cfg0.head_groups;
+  buf[31] = P->cascade_chain;
   int32_t* dst = buf + 32;
   auto pull = [&](const int32_t* src, int64_t n) -> hipError_t {
     hipError_t e = n ? hipMemcpy(dst, src, n * sizeof(int32_t), hipMemcpyDeviceToHost) : hipSuccess;

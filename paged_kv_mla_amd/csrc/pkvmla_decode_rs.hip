@@ -94,12 +94,16 @@ static_assert(kRsLds <= 160 * 1024, "LDS budget");
 
 // Unit cursor: the unit and tile a role is at, with the unit's fields.  For
 // a row-block unit, b is its first query row, slot the offset of its rows in
-// the partial-state rows, and rend the end of its group's rows.
+// the partial-state rows, and rend the end of its group's rows.  A unit whose
+// slot is kChainNext hands its softmax state to the next unit of the list
+// (the same request's rows over another sequence): it writes nothing, and the
+// next unit (cont) starts from its running max, row sums and outputs.
 struct UnitCursor {
   int u;        // unit index
   int tile;     // tile index within the unit
   int ntiles;   // tiles in the unit
   int b, kv0, kv1, slot, rend;
+  bool cont;    // this unit continues the previous one's state
 };
 
 __device__ __forceinline__ void cursor_load(UnitCursor& c, idx_ptr units) {
@@ -115,6 +119,7 @@ __device__ __forceinline__ void cursor_load(UnitCursor& c, idx_ptr units) {
 
 __device__ __forceinline__ void cursor_next(UnitCursor& c, idx_ptr units, int u_end) {
   if (++c.tile >= c.ntiles) {
+    c.cont = c.slot == kChainNext;
     if (++c.u < u_end) cursor_load(c, units);
   }
 }
@@ -194,6 +199,7 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
     }
     UnitCursor cq;
     cq.u = u_begin;
+    cq.cont = false;
     cursor_load(cq, units);
     // the unit's query: lane (g, li) holds Q[head][ks*32 + g*8 .. +7]
     bf16x8_t q[18];
@@ -218,7 +224,7 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
       if (i < G) {
         const int stage = i % kRsRing;
         const int par = i & 1;
-        if (cq.tile == 0) {
+        if (cq.tile == 0 && !cq.cont) {
           m_run = -INFINITY;
           l_run = 0.f;
         }
@@ -265,7 +271,7 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
         __builtin_amdgcn_s_setprio(0);
         // Q of the next unit goes out once the last k-step has read this
         // unit's, so its latency hides behind the softmax and the barrier
-        if (cq.tile == cq.ntiles - 1 && cq.u + 1 < u_end) {
+        if (cq.tile == cq.ntiles - 1 && cq.u + 1 < u_end && cq.slot != kChainNext) {
           idx_ptr nrec = units + (size_t)(cq.u + 1) * kUnitInts;
           load_q(q_row(nrec[0], ROWS ? nrec[5] : 0));
         }
@@ -305,7 +311,7 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
         l_run = l_run * alpha + ps;
         *(LDS_AS bf16x8_t*)(smem + kXpOff + (par * kRsMaxHB + r) * 1024 + lane * 16) = pT;
         if (g == 0) *(LDS_AS float*)(smem + kXaOff + (par * 64 + li * 4 + r) * 4) = alpha;
-        if (cq.tile == cq.ntiles - 1) {
+        if (cq.tile == cq.ntiles - 1 && cq.slot != kChainNext) {
           // unit done: row sums for the PV waves, lse for the output
           float l = l_run;
           l += __shfl_xor(l, 16);
@@ -345,6 +351,7 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
 
     UnitCursor cp;
     cp.u = u_begin;
+    cp.cont = false;
     cursor_load(cp, units);
     // O (128 VGPRs, MFMAs in VGPR form) starts at zero once.  A tile whose
     // rescale factors are not all 1 multiplies O by them before its MFMAs
@@ -424,7 +431,7 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
         vn0 = ldV(so1, 0, 0);
         vn1 = ldV(so1, 0, 1);
       }
-      if (cp.tile == cp.ntiles - 1) {
+      if (cp.tile == cp.ntiles - 1 && cp.slot != kChainNext) {
         // ---- epilogue: this wave's 128 dims of the unit's 64 heads ----
         const int le = lane_id_fresh();
         const int ge = le >> 4, lie = le & 15;

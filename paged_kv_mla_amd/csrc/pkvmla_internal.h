@@ -14,6 +14,10 @@ constexpr int kUnitInts = 8;        // b, seq, kv_begin, kv_end, slot, row, page
                                     // (page_base: start of seq's page list in seq_indices;
                                     //  first_page: the page of token kv_begin)
 constexpr int kMergeInts = 4;       // b, first_slot (or first list entry), count, kind
+// Slot field of a unit that hands its softmax state to the next unit of its
+// workgroup's list instead of writing it (a chained cascade request: its last
+// prefix piece, then its suffix).
+constexpr int32_t kChainNext = INT32_MIN;
 constexpr int kStageBytes = kTile * kCkvDim * 2 + kTile * kKpeDim * 2;  // 36864
 constexpr int kIndexPad = 64;       // margin of valid page ids after the device index table
 

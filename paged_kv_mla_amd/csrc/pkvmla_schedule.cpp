@@ -181,6 +181,80 @@ bool build_row_schedule(const int32_t* group_req_indptr, int32_t num_groups,
   return true;
 }
 
+bool build_chain_schedule(const int32_t* group_req_indptr, int32_t num_groups,
+                          const int32_t* prefix_lens, const int32_t* kv_lens, int32_t batch,
+                          int32_t num_wg, int32_t tile, RowSchedule* s,
+                          std::vector<int32_t>* merges, std::vector<int32_t>* slot_list) {
+  if (num_wg < 1 || tile < 1 || batch < 1 || num_groups < 1) return false;
+  std::vector<int32_t> group(batch, -1);
+  for (int32_t g = 0; g < num_groups; ++g) {
+    if (prefix_lens[g] <= 0) return false;  // every request needs a prefix block
+    for (int32_t b = group_req_indptr[g]; b < group_req_indptr[g + 1]; ++b) group[b] = g;
+  }
+  // per lane: (request, kv_begin, kv_end, is_last_piece)
+  std::vector<std::vector<std::array<int32_t, 4>>> lanes;
+  std::vector<int32_t> pieces(batch, 0);
+  if (batch <= num_wg) {
+    const int64_t S = num_wg / batch;
+    s->grid = (int32_t)(batch * S);
+    lanes.assign((size_t)s->grid, {});
+    for (int32_t b = 0; b < batch; ++b) {
+      const int64_t L = prefix_lens[group[b]];
+      const int64_t T = ceil_div(L, tile);
+      const int64_t P = std::min<int64_t>(S, T);
+      pieces[b] = (int32_t)P;
+      for (int64_t p = 0; p < P; ++p) {
+        const int64_t t0 = p * T / P, t1 = (p + 1) * T / P;
+        lanes[(size_t)(b * S + p)].push_back(
+            {b, (int32_t)(t0 * tile), (int32_t)std::min<int64_t>(t1 * tile, L), p == P - 1});
+      }
+    }
+  } else {
+    s->grid = num_wg;
+    lanes.assign((size_t)num_wg, {});
+    for (int32_t b = 0; b < batch; ++b) {
+      pieces[b] = 1;
+      lanes[(size_t)(b % num_wg)].push_back({b, 0, prefix_lens[group[b]], 1});
+    }
+  }
+  std::vector<std::vector<int32_t>> per(batch);
+  s->wg_indptr.assign((size_t)s->grid + 1, 0);
+  s->units.clear();
+  int32_t slot = 0;
+  for (int32_t l = 0; l < s->grid; ++l) {
+    for (const auto& u : lanes[(size_t)l]) {
+      const int32_t b = u[0];
+      const bool chain = u[3] && kv_lens[b] > 0;
+      int32_t sl = -1;
+      if (chain) {
+        sl = kChainNextSlot;
+      } else if (pieces[b] > 1) {
+        per[b].push_back(slot);
+        sl = slot++;
+      }
+      s->units.insert(s->units.end(), {b, group[b], u[1], u[2], sl, 0, 0, 0});
+      if (chain) {
+        int32_t sl2 = -1;
+        if (pieces[b] > 1) {
+          per[b].push_back(slot);
+          sl2 = slot++;
+        }
+        s->units.insert(s->units.end(), {b, num_groups + b, 0, kv_lens[b], sl2, 0, 0, 0});
+      }
+    }
+    s->wg_indptr[(size_t)l + 1] = (int32_t)(s->units.size() / kUnitRecordInts);
+  }
+  s->n_slots = slot;
+  merges->clear();
+  slot_list->clear();
+  for (int32_t b = 0; b < batch; ++b) {
+    if (per[b].empty()) continue;
+    merges->insert(merges->end(), {b, (int32_t)slot_list->size(), (int32_t)per[b].size(), 1});
+    slot_list->insert(slot_list->end(), per[b].begin(), per[b].end());
+  }
+  return true;
+}
+
 void build_cascade_merges(const RowSchedule& l0, const std::vector<int32_t>& l1_units,
                           int32_t batch, int32_t num_heads, std::vector<int32_t>* merges,
                           std::vector<int32_t>* slot_list) {

@@ -12,6 +12,9 @@ namespace pkvmla {
 // leaves the last two 0, the plan fills them from the page tables
 constexpr int kUnitRecordInts = 8;
 constexpr int kMergeRecordInts = 4;  // req, first_slot, count, 0
+// slot field of a unit whose state carries into the next unit (the kernels'
+// kChainNext)
+constexpr int32_t kChainNextSlot = INT32_MIN;
 
 struct WorkItem {
   int32_t req;  // request whose query heads attend
@@ -49,6 +52,21 @@ inline int32_t row_block_rows(int32_t num_heads) { return num_heads > 64 ? num_h
 bool build_row_schedule(const int32_t* group_req_indptr, int32_t num_groups,
                         const int32_t* prefix_lens, int32_t num_heads, int32_t num_wg,
                         int32_t tile, RowSchedule* s);
+
+// A cascade in one launch (num_heads >= 64, every group's prefix non-empty):
+// each request's rows are one block, cut over the lanes as in
+// build_row_schedule, and the request's suffix (if any) follows the block's
+// last piece on that lane, chained to it (kChainNext in the piece's slot
+// field: the state carries into the suffix unit).  Unit records are flat
+// ones: request, sequence (group g for a prefix piece, G + b for a suffix),
+// kv_begin, kv_end, slot, 0, then the two page fields the plan fills.  A
+// request with one state (one piece) writes out directly (slot -1); one with
+// several pieces gets a partial slot per state (slots numbered in emission
+// order) and a merge record (b, first list entry, count, 1) over its slots.
+bool build_chain_schedule(const int32_t* group_req_indptr, int32_t num_groups,
+                          const int32_t* prefix_lens, const int32_t* kv_lens, int32_t batch,
+                          int32_t num_wg, int32_t tile, RowSchedule* s,
+                          std::vector<int32_t>* merges, std::vector<int32_t>* slot_list);
 
 // Merge records (b, first list entry, count, 1) and the slot list of a
 // cascade plan: per request its level-0 slots (level-0 emission order) then

@@ -93,6 +93,31 @@ def test_row_schedule_host_matches_reference():
         _compare_rows(gi, pl, int(rng.choice([16, 32, 64, 128])), int(rng.integers(1, 400)))
 
 
+def _compare_chain(gi, pl, kl, W):
+    from oracle.schedule_ref import cascade_chain_ref
+    w1, u1, m1, l1 = pk.schedule_chain_host(gi, pl, kl, W)
+    r = cascade_chain_ref(gi, pl, kl, W)
+    np.testing.assert_array_equal(w1, r["wg0"])
+    np.testing.assert_array_equal(u1, r["units0"])
+    np.testing.assert_array_equal(m1, r["merges"])
+    np.testing.assert_array_equal(l1, r["slot_list"])
+
+
+def test_chain_schedule_host_matches_reference():
+    prefix, suffix = config_lens("cascade")
+    for W in (128, 256, 64, 7, 1, 300):
+        _compare_chain([0, len(suffix)], [prefix], suffix, W)
+    rng = np.random.default_rng(12)
+    for _ in range(150):
+        G = int(rng.integers(1, 5))
+        sizes = rng.integers(0, 7, size=G)
+        sizes[0] = max(1, sizes[0])
+        gi = np.concatenate([[0], np.cumsum(sizes)])
+        pl = rng.integers(1, 3000, size=G)
+        kl = rng.integers(0, 600, size=int(gi[-1]))
+        _compare_chain(gi, pl, kl, int(rng.integers(1, 300)))
+
+
 def test_row_schedule_host_rejects():
     with pytest.raises(pk.PkvmlaError):
         pk.schedule_rows_host([1, 2], [10], 16, 8)          # indptr[0] != 0

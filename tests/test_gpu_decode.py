@@ -13,8 +13,8 @@ import pytest
 import torch
 
 import oracle
-from oracle.schedule_ref import (schedule_ref, flat_items, cascade_plan_ref, qo_items,
-                                 kernel_config, unit_page_fields)
+from oracle.schedule_ref import (schedule_ref, flat_items, cascade_plan_ref, cascade_chain_ref,
+                                 qo_items, kernel_config, unit_page_fields)
 from mla_workloads import (make_flat, make_cascade, make_config, make_qo, stress_variant,
                            stress_variant_cascade, poison_unreferenced, permute_pages,
                            STRESS_KINDS)
@@ -132,19 +132,26 @@ def test_plan_export_cascade(H):
     hdr = ex.header
     lanes = max(1, ex.num_cu * int(hdr[10]) // ex.head_groups)
     hg0 = max(1, H // 64)
-    assert int(hdr[31]) == hg0
-    r = cascade_plan_ref(cas.group_req_indptr, cas.prefix_lens, cas.kv_lens, H, lanes,
-                         max(1, ex.num_cu // hg0), kc["tile"], int(hdr[11]))
     G = cas.num_groups
     seq_indptr = np.concatenate([cas.prefix_indptr, cas.prefix_indptr[G] + cas.kv_indptr[1:]])
     seq_indices = np.concatenate([cas.prefix_indices[:cas.prefix_indptr[G]], cas.kv_indices])
-    np.testing.assert_array_equal(ex.units, unit_page_fields(r["units"], seq_indptr, seq_indices,
-                                                             cas.page_size))
+    # 64 heads or more with every prefix non-empty: one launch, suffixes chained
+    chained = H >= 64 and (cas.prefix_lens > 0).all()
+    assert int(hdr[31]) == int(chained)
+    if chained:
+        r = cascade_chain_ref(cas.group_req_indptr, cas.prefix_lens, cas.kv_lens,
+                              max(1, ex.num_cu // hg0), kc["tile"])
+        assert ex.units.shape[0] == 0 and ex.wg_indptr.tolist() == [0]
+    else:
+        r = cascade_plan_ref(cas.group_req_indptr, cas.prefix_lens, cas.kv_lens, H, lanes,
+                             max(1, ex.num_cu // hg0), kc["tile"], int(hdr[11]))
+        np.testing.assert_array_equal(ex.units, unit_page_fields(r["units"], seq_indptr,
+                                                                 seq_indices, cas.page_size))
+        np.testing.assert_array_equal(ex.wg_indptr, r["wg"])
     np.testing.assert_array_equal(ex.units0, unit_page_fields(r["units0"], seq_indptr,
                                                               seq_indices, cas.page_size))
     np.testing.assert_array_equal(ex.merges, r["merges"])
     np.testing.assert_array_equal(ex.slot_list, r["slot_list"])
-    np.testing.assert_array_equal(ex.wg_indptr, r["wg"])
     np.testing.assert_array_equal(ex.wg_indptr0, r["wg0"])
     np.testing.assert_array_equal(ex.seq_lens, np.concatenate([cas.prefix_lens, cas.kv_lens]))
     np.testing.assert_array_equal(ex.seq_indptr, seq_indptr)

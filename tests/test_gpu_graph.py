@@ -192,9 +192,15 @@ def test_graph_replay_and_update_cascade(H, ps):
             ref_o, ref_l = eager(plan, dev, out, lse, side)
             fresh = pk.plan_cascade(*args(inp), H, ps, POOL)
             fo, fl = eager(fresh, dev, torch.empty_like(out), torch.empty_like(lse), side)
-            assert torch.equal(fo, ref_o) and torch.equal(fl, ref_l)
             o64, l64 = oracle_cascade(inp)
             compare(ref_o, ref_l, o64, l64, name=f"cascade update {step}")
+            if fresh.export().header[31] == 0:
+                # the same two-level layout: the same bits
+                assert torch.equal(fo, ref_o) and torch.equal(fl, ref_l)
+            else:
+                # an ordinary plan may run the cascade in one launch (chained
+                # suffixes): other rounding, the same attention
+                compare(fo, fl, o64, l64, name=f"cascade fresh one-launch {step}")
         for rep in range(3):
             out.fill_(7.0)
             lse.fill_(-1.0)

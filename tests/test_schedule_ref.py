@@ -125,6 +125,30 @@ def test_cascade_plan_merge_lists_hand_case():
     assert r["slot_list"].tolist() == [0, 2, 4, 1, 3, 5, 6, 7, 8]
 
 
+def test_chain_schedule_hand_cases():
+    """One-launch cascade schedules worked out by hand from the rule."""
+    from oracle.schedule_ref import cascade_chain_ref, CHAIN_NEXT
+    # two requests, one group, 100-token prefix (4 tiles), suffixes 10 and 0,
+    # 4 lanes: S = 2 pieces each; tiles [0,2) and [2,4) of 4
+    r = cascade_chain_ref([0, 2], [100], [10, 0], 4)
+    assert r["wg0"].tolist() == [0, 1, 3, 4, 5]
+    assert [u[:5] for u in r["units0"].tolist()] == [
+        [0, 0, 0, 64, 0],               # request 0 piece 0: slot 0
+        [0, 0, 64, 100, CHAIN_NEXT],    # piece 1, state carried into ...
+        [0, 1, 0, 10, 1],               # ... its suffix (sequence G + 0): slot 1
+        [1, 0, 0, 64, 2],               # request 1 (empty suffix): pieces in slots 2, 3
+        [1, 0, 64, 100, 3]]
+    assert r["merges"].tolist() == [[0, 0, 2, 1], [1, 2, 2, 1]]
+    assert r["slot_list"].tolist() == [0, 1, 2, 3]
+    # three requests on 2 lanes: whole requests round robin, one state each
+    r = cascade_chain_ref([0, 3], [40], [5, 6, 0], 2)
+    assert r["wg0"].tolist() == [0, 3, 5]
+    assert [u[:5] for u in r["units0"].tolist()] == [
+        [0, 0, 0, 40, CHAIN_NEXT], [0, 1, 0, 5, -1], [2, 0, 0, 40, -1],
+        [1, 0, 0, 40, CHAIN_NEXT], [1, 2, 0, 6, -1]]
+    assert r["merges"].shape == (0, 4)
+
+
 def test_cascade_config_schedule():
     from oracle.schedule_ref import cascade_plan_ref
     prefix, suffix = config_lens("cascade")
