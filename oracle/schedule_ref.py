@@ -73,6 +73,93 @@ def qo_items(qo_indptr, kv_lens):
     return items
 
 
+QO_BLOCK_ROWS = 64            # query rows per row block of a qo plan
+QO_ROWS_DIRECT = -(2 ** 31) + 1   # slot field of a row block that writes out and lse itself
+QO_ROWS_FIXED = 4             # fixed cost per segment of the 64-row kernel (its config)
+
+
+def qo_uses_rows(qo_indptr, num_heads: int) -> bool:
+    """Layout rule of a plan with several new tokens per request.  Request b's
+    query rows are rho = t * H + h for its tokens t = qo_indptr[b] ..
+    qo_indptr[b+1] - 1; cut into blocks of 64 rows they give
+    ceil(n_b * H / 64) blocks.  Row blocks are used when H is 16 or 32 and
+    the blocks are on average more than half full: total rows > 32 x blocks.
+    Otherwise the plan has one work item per query token (qo_items)."""
+    H = int(num_heads)
+    if H > 32:
+        return False
+    rows, blocks = 0, 0
+    for b in range(len(qo_indptr) - 1):
+        n = int(qo_indptr[b + 1]) - int(qo_indptr[b])
+        rows += n * H
+        blocks += -(-(n * H) // QO_BLOCK_ROWS)
+    return 2 * rows > QO_BLOCK_ROWS * blocks
+
+
+def qo_rows_ref(qo_indptr, kv_lens, num_heads: int, num_wg: int, tile: int = PLAN_TILE,
+                fixed: int = QO_ROWS_FIXED, pages=None):
+    """Row-block schedule of a plan with several new tokens per request
+    (H = 16 or 32), restated from its rule:
+
+    * request b's rows [qo_indptr[b] * H, qo_indptr[b+1] * H) are cut into
+      blocks of 64 (the last may be short), in request order; block k of
+      request b is a work item (k, b, kv_lens[b]) of the flat walk
+      (schedule_ref, batch = number of blocks, the 64-row kernel's fixed cost):
+      every block attends its whole sequence, the causal bound is per row;
+    * each walk unit (k, b, kv_begin, kv_end, slot) becomes the record
+      (row0, c_b, kv_begin, kv_end, slot field, row_end, page fields) with
+      c_b = kv_lens[b] - n_b + 1 - qo_indptr[b], so that token t
+      (rows t * H ..) sees the positions below t + c_b; slot field
+      QO_ROWS_DIRECT for a block the walk left whole, else
+      walk slot * 64 - row0 (partial row = walk slot * 64 + rho - row0, so
+      walk slot s holds partial slots s * 64/H .. of H rows each);
+    * each walk merge (k, first, count) gives, for every token t of block k
+      in order, the merge record (t, list position, count, 1) and the list
+      entries (first + i) * 64/H + (t - row0 / H), i = 0 .. count - 1;
+    * page fields (optional `pages` = (kv_indptr, kv_indices, page_size)):
+      those of unit_page_fields for sequence b.
+
+    Returns (wg_indptr, units [n, 8], merges [m, 4], slot_list, n_slots) with
+    n_slots in slots of H rows."""
+    H = int(num_heads)
+    assert H in (16, 32)
+    per = QO_BLOCK_ROWS // H
+    blocks = []   # (b, row0, row_end)
+    for b in range(len(kv_lens)):
+        lo, hi = int(qo_indptr[b]) * H, int(qo_indptr[b + 1]) * H
+        for r in range(lo, hi, QO_BLOCK_ROWS):
+            blocks.append((b, r, min(r + QO_BLOCK_ROWS, hi)))
+    items = [(k, b, int(kv_lens[b])) for k, (b, _, _) in enumerate(blocks)]
+    wg, fu, fm = schedule_ref(items, len(blocks), num_wg, tile, fixed)
+    units = np.zeros_like(fu)
+    walk_slots = 0
+    for i in range(fu.shape[0]):
+        k, b, k0, k1, sl = (int(x) for x in fu[i, :5])
+        _, r0, r1 = blocks[k]
+        n = int(qo_indptr[b + 1]) - int(qo_indptr[b])
+        c = int(kv_lens[b]) - n + 1 - int(qo_indptr[b])
+        if sl < 0:
+            field = QO_ROWS_DIRECT
+        else:
+            field = sl * QO_BLOCK_ROWS - r0
+            walk_slots = max(walk_slots, sl + 1)
+        units[i, :6] = (r0, c, k0, k1, field, r1)
+    merges, slot_list = [], []
+    for (k, first, count, _) in fm:
+        _, r0, r1 = blocks[int(k)]
+        for j in range((r1 - r0) // H):
+            merges.append((r0 // H + j, len(slot_list), int(count), 1))
+            slot_list.extend((int(first) + i) * per + j for i in range(int(count)))
+    if pages is not None:
+        kv_indptr, kv_indices, page_size = pages
+        withseq = units.copy()
+        withseq[:, 1] = [blocks[int(fu[i, 0])][0] for i in range(fu.shape[0])]
+        filled = unit_page_fields(withseq, kv_indptr, kv_indices, page_size)
+        units[:, 6:] = filled[:, 6:]
+    return (wg, units, np.asarray(merges, np.int32).reshape(-1, MERGE_INTS),
+            np.asarray(slot_list, np.int32), walk_slots * per)
+
+
 def suffix_items(num_groups: int, kv_lens):
     """Level-1 items of a cascade plan: request b over its suffix (sequence
     G + b)."""

@@ -174,3 +174,81 @@ def test_unit_page_fields_hand_case():
     assert got[:, 6].tolist() == [0, 2, 0]
     assert got[:, 7].tolist() == [7, 4, 3]
     assert np.array_equal(got[:, :6], units[:, :6])   # the schedule fields are untouched
+
+
+def test_qo_rows_layout_rule_hand_cases():
+    """Row blocks when H <= 32 and the 64-row blocks average more than half full."""
+    from oracle.schedule_ref import qo_uses_rows
+    assert not qo_uses_rows([0, 2], 16)          # 32 rows in one block: exactly half
+    assert qo_uses_rows([0, 3], 16)              # 48 rows in one block
+    assert not qo_uses_rows([0, 1], 32)          # 32 rows in one block
+    assert qo_uses_rows([0, 2], 32)              # one full block
+    assert not qo_uses_rows([0, 4], 64)          # 64 heads or more: one item per token
+    assert not qo_uses_rows([0, 1, 2, 3, 8], 16)  # 128 rows in 5 blocks (< 160)
+    assert qo_uses_rows([0, 1, 2, 10], 16)       # 160 rows in 4 blocks (> 128)
+
+
+def test_qo_rows_schedule_hand_case():
+    """H = 16, requests with 5 and 2 new tokens, kv_lens 100 and 40, 8 lanes.
+    Blocks: rows [0, 64) and [64, 80) of request 0, [80, 112) of request 1;
+    items of 4, 4 and 2 tiles at fixed cost 4, C = 22.  cap 5 (one tile per
+    unit) needs 10 lanes, cap 6 (two tiles) needs 5: request 0's blocks are cut
+    at token 64 into walk slots 0, 1 and 2, 3; the last block stays whole.
+    Causal offsets: 100 - 5 + 1 - 0 = 96 and 40 - 2 + 1 - 5 = 34."""
+    from oracle.schedule_ref import qo_rows_ref, QO_ROWS_DIRECT
+    wg, units, merges, slot_list, n_slots = qo_rows_ref([0, 5, 7], [100, 40], 16, 8)
+    assert wg.tolist() == [0, 1, 2, 3, 4, 5]
+    assert [u[:6] for u in units.tolist()] == [
+        [0, 96, 0, 64, 0, 64], [0, 96, 64, 100, 64, 64],
+        [64, 96, 0, 64, 64, 80], [64, 96, 64, 100, 128, 80],
+        [80, 34, 0, 40, QO_ROWS_DIRECT, 112]]
+    # four 16-row slots per walk slot: token t of block 0 sits in slots t and
+    # 4 + t; token 4 (block 1, rows 64..79) in walk slots 2 and 3's first
+    assert merges.tolist() == [[0, 0, 2, 1], [1, 2, 2, 1], [2, 4, 2, 1], [3, 6, 2, 1],
+                               [4, 8, 2, 1]]
+    assert slot_list.tolist() == [0, 4, 1, 5, 2, 6, 3, 7, 8, 12]
+    assert n_slots == 16
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_qo_rows_schedule_invariants(seed):
+    """Any qo row-block schedule: each token's causal range [0, t + c) lies
+    inside its block's token cover, which the block's pieces tile exactly
+    once; every partial row is written by exactly one (piece, token) and read
+    by that token's merge alone; whole blocks have no merge."""
+    from oracle.schedule_ref import qo_rows_ref, QO_ROWS_DIRECT
+    rng = np.random.default_rng(seed)
+    H = int(rng.choice([16, 32]))
+    B = int(rng.integers(1, 7))
+    qo = rng.integers(1, 20, size=B)
+    kv = np.maximum(qo, rng.integers(1, 3000, size=B))
+    qo_indptr = np.concatenate([[0], np.cumsum(qo)]).astype(np.int32)
+    W = int(rng.integers(1, 300))
+    wg, units, merges, slot_list, n_slots = qo_rows_ref(qo_indptr, kv, H, W)
+    assert 0 < len(wg) - 1 <= W and np.all(np.diff(wg) >= 1)
+    cover, writers = {}, {}
+    for u in units.tolist():
+        r0, c, k0, k1, sl, r1 = u[:6]
+        assert 0 <= k0 < k1 and r0 % H == 0 and r1 % H == 0 and 0 < r1 - r0 <= 64
+        cover.setdefault(r0, []).append((k0, k1, sl))
+        for t in range(r0 // H, r1 // H):
+            b = int(np.searchsorted(qo_indptr, t, side="right")) - 1
+            n = int(qo[b])
+            assert t + c == int(kv[b]) - n + 1 + (t - int(qo_indptr[b]))   # causal limit
+            if sl != QO_ROWS_DIRECT:
+                s = (sl + t * H) // H
+                assert (sl + t * H) % H == 0 and 0 <= s < n_slots
+                assert s not in writers
+                writers[s] = t
+    for r0, pieces in cover.items():
+        pieces.sort()
+        b = int(np.searchsorted(qo_indptr * H, r0, side="right")) - 1
+        assert pieces[0][0] == 0 and pieces[-1][1] == int(kv[b])
+        assert all(pieces[i][1] == pieces[i + 1][0] for i in range(len(pieces) - 1))
+        assert (len(pieces) == 1) == (pieces[0][2] == QO_ROWS_DIRECT)
+    merged = {}
+    for (t, pos, cnt, kind) in merges.tolist():
+        assert kind == 1 and t not in merged
+        merged[t] = slot_list[pos:pos + cnt].tolist()
+        assert all(writers[s] == t for s in merged[t])
+    assert sorted(s for v in merged.values() for s in v) == sorted(writers)
