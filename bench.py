@@ -56,6 +56,8 @@ WORKLOAD_DESC = {
     "cascade": "cascade shared-prefix decode: batch 128, 128 heads, 512/64, page_size 64, "
                "8192-token shared prefix + suffix uniform [64,1024]",
     "tiny": "tiny decode: batch 4, 16 heads, 512/64, page_size 16, kv_len {1,17,64,200}",
+    "qo": "several query tokens per request: batch 64, 4 new tokens each (causal among them), "
+          "16 heads, 512/64, page_size 64, kv_len uniform [1024,4096]",
 }
 
 
@@ -101,18 +103,28 @@ def kernel_source_hash() -> str:
 
 
 def workload_counts(inp, kv_row_bytes: int = 1152):
-    """Attended tokens, unique KV rows and algorithmic bytes/flops of one step
-    (kv_row_bytes: one token's ckv + kpe row, 1152 in bf16, 576 in fp8)."""
+    """Attended tokens (per query token, summed), unique KV rows and
+    algorithmic bytes/flops of one step (kv_row_bytes: one token's ckv + kpe
+    row, 1152 in bf16, 576 in fp8)."""
     H = inp.num_heads
     B = inp.batch
+    rows = B   # query rows of H heads
     if hasattr(inp, "prefix_lens"):
         attended = inp.attended_tokens()
         unique = inp.unique_tokens()
         idx_bytes = 4 * (len(inp.prefix_indices) + len(inp.kv_indices)) + 8 * B
+    elif getattr(inp, "qo_indptr", None) is not None:
+        # query token j of n sees kv_len - n + 1 + j tokens; the cache is read once
+        n = np.diff(inp.qo_indptr).astype(np.int64)
+        L = inp.kv_lens.astype(np.int64)
+        attended = int(np.sum(n * (L - n + 1) + n * (n - 1) // 2))
+        unique = int(L.sum())
+        rows = int(inp.qo_indptr[-1])
+        idx_bytes = 4 * len(inp.kv_indices) + 12 * B
     else:
         attended = unique = inp.total_tokens
         idx_bytes = 4 * len(inp.kv_indices) + 8 * B
-    alg_bytes = unique * kv_row_bytes + idx_bytes + B * H * (1152 + 1024 + 4)
+    alg_bytes = unique * kv_row_bytes + idx_bytes + rows * H * (1152 + 1024 + 4)
     alg_flops = 2176.0 * H * attended
     return attended, unique, alg_bytes, alg_flops
 
@@ -126,6 +138,7 @@ def cpu_baseline(inp, budget_s: float = 12.0):
     except Exception:
         threads = len(os.sched_getaffinity(0))
     is_cas = hasattr(inp, "prefix_lens")
+    is_qo = getattr(inp, "qo_indptr", None) is not None
     done_tokens = 0
     reqs = 0
     t0 = time.perf_counter()
@@ -146,6 +159,16 @@ def cpu_baseline(inp, budget_s: float = 12.0):
                 inp.kv_indices[inp.kv_indptr[b]:inp.kv_indptr[b + 1]], inp.kv_lens[sl],
                 kv_scales=sc)
             done_tokens += int(inp.prefix_lens[g]) + int(inp.kv_lens[b])
+        elif is_qo:
+            q0, q1 = int(inp.qo_indptr[b]), int(inp.qo_indptr[b + 1])
+            ip = np.array([0, inp.kv_indptr[b + 1] - inp.kv_indptr[b]], np.int32)
+            oracle.attend_qo(inp.q_nope[q0:q1], inp.q_pe[q0:q1], ckv, kpe,
+                             np.array([0, q1 - q0], np.int32), ip,
+                             inp.kv_indices[inp.kv_indptr[b]:inp.kv_indptr[b + 1]],
+                             inp.kv_lens[sl], inp.page_size, sm_scale=inp.sm_scale,
+                             kv_scales=sc)
+            n, L = q1 - q0, int(inp.kv_lens[b])
+            done_tokens += n * (L - n + 1) + n * (n - 1) // 2
         else:
             ip = np.array([0, inp.kv_indptr[b + 1] - inp.kv_indptr[b]], np.int32)
             oracle.attend_flat(inp.q_nope[sl], inp.q_pe[sl], ckv, kpe, ip,
@@ -268,8 +291,9 @@ def main():
     qns = [qn0] + [qn0.clone() for _ in range(layers - 1)]
     qps = [qp0] + [qp0.clone() for _ in range(layers - 1)]
     B, H = inp.batch, inp.num_heads
-    outs = [torch.empty((B, H, 512), dtype=torch.bfloat16, device="cuda") for _ in range(layers)]
-    lses = [torch.empty((B, H), dtype=torch.float32, device="cuda") for _ in range(layers)]
+    R = int(inp.qo_indptr[-1]) if getattr(inp, "qo_indptr", None) is not None else B
+    outs = [torch.empty((R, H, 512), dtype=torch.bfloat16, device="cuda") for _ in range(layers)]
+    lses = [torch.empty((R, H), dtype=torch.float32, device="cuda") for _ in range(layers)]
     torch.cuda.synchronize()
 
     t0 = time.perf_counter()
@@ -378,6 +402,7 @@ def main():
         "dtype": "bf16 queries, fp8 e4m3 KV (per-tensor scales)" if fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": WORKLOAD_DESC[args.workload], "batch": B, "num_heads": H,
+                   "query_rows": R,
                    "page_size": inp.page_size, "kv_cache": args.kv,
                    "attended_kv_tokens": attended,
                    "unique_kv_tokens": unique, "kv_copies_cycled": layers},

@@ -130,14 +130,46 @@ int pkvmla_plan_update(pkvmla_plan plan, const int32_t* kv_indptr, const int32_t
  * The run's query, output and lse tensors have one row per query token:
  * q_nope [qo_indptr[batch], num_heads, 512], q_pe [.., 64], out [.., 512],
  * lse [qo_indptr[batch], num_heads], row qo_indptr[b] + j for token j of b.
- * Each row is scheduled as its own work item over request b's pages, so the
- * rows of one request read its KV tiles once each (the rows of a request run
- * on neighbouring lanes).  Plans of this kind take no page-table update
+ * The layout is chosen as pkvmla_plan_create_qo_layout does with
+ * PKVMLA_QO_AUTO.  Plans of this kind take no page-table update
  * (PKVMLA_EUNSUPPORTED). */
 int pkvmla_plan_create_qo(const int32_t* qo_indptr, const int32_t* kv_indptr,
                           const int32_t* kv_indices, const int32_t* kv_lens, int32_t batch,
                           int32_t num_pages, int32_t num_heads, int32_t ckv_dim, int32_t kpe_dim,
                           int32_t page_size, float sm_scale, void* stream, pkvmla_plan* out);
+
+/* Work layouts of a plan with several query tokens per request. */
+enum {
+  PKVMLA_QO_AUTO = 0,        /* row blocks when the rule below picks them, else tokens */
+  PKVMLA_QO_TOKENS = 1,      /* one work item per query token (any head count) */
+  PKVMLA_QO_ROW_BLOCKS = 2   /* 16 or 32 heads: blocks of 64 query rows */
+};
+
+/* pkvmla_plan_create_qo with an explicit layout (same semantics and results,
+ * up to rounding).
+ *   PKVMLA_QO_TOKENS: each query token is its own work item over request b's
+ *   pages, of its causal length; the tokens of a request read its KV tiles
+ *   once each.
+ *   PKVMLA_QO_ROW_BLOCKS (num_heads 16 or 32, else PKVMLA_EUNSUPPORTED): the
+ *   query rows t * H + h of request b's tokens are cut into blocks of 64 rows
+ *   (64 / H tokens each, the last block possibly short); a block is one work
+ *   item over the request's whole sequence, split over lanes like a flat
+ *   request, and every 64-row workgroup scores each KV tile once for all of
+ *   its tokens, each row masked at its own causal bound.  A block left whole
+ *   writes out and lse itself; a split one writes a partial state per token
+ *   and piece, merged per token (see pkvmla_schedule_qo_rows_host).
+ *   PKVMLA_QO_AUTO: row blocks when num_heads is 16 or 32 and some request
+ *   brings more than one query token (qo_indptr[batch] > batch), else tokens
+ *   (a 64-row workgroup costs about what a 16- or 32-head one does per KV
+ *   tile, so blocks gain as soon as one tile serves two tokens).
+ * pkvmla_plan_export reports the layout in header word 26 (1: tokens, 2: row
+ * blocks; the blocks' units, slot list and merges are in the level-0 fields).
+ * PKVMLA_EINVAL for an unknown layout. */
+int pkvmla_plan_create_qo_layout(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                                 const int32_t* kv_indices, const int32_t* kv_lens, int32_t batch,
+                                 int32_t num_pages, int32_t num_heads, int32_t ckv_dim,
+                                 int32_t kpe_dim, int32_t page_size, float sm_scale,
+                                 int32_t layout, void* stream, pkvmla_plan* out);
 
 /* Build a two-level (cascade) plan.  Requests are partitioned into
  * num_groups contiguous groups by group_req_indptr (host int32[G+1], from 0
@@ -342,6 +374,30 @@ int pkvmla_schedule_chain_host(const int32_t* group_req_indptr, int32_t num_grou
                                int32_t* merges, int64_t cap_merges, int32_t* slot_list,
                                int64_t cap_list, int32_t* counts);
 
+/* The row-block schedule of a plan with several query tokens per request
+ * (PKVMLA_QO_ROW_BLOCKS), computed on the host exactly as the plan does (no
+ * GPU needed; a plan uses num_wg = CUs, fixed_cost = 4, tile = 32).  Request
+ * b's rows [qo_indptr[b] * H, qo_indptr[b+1] * H) are cut into blocks of 64
+ * rows in request order; block k is the work item (k, b, kv_lens[b]) of
+ * pkvmla_schedule_host's walk.  Each walk unit becomes the record
+ * (row0, c_b, kv_begin, kv_end, slot field, row_end, 0, 0) with
+ * c_b = kv_lens[b] - qo_len(b) + 1 - qo_indptr[b] (query token t, rows
+ * t * H .. t * H + H - 1, attends the positions below t + c_b) and slot field
+ * INT32_MIN + 1 for a block the walk left whole (it writes out and lse), else
+ * walk slot * 64 - row0 (row rho's partial state is partial row
+ * field + rho; partial slots hold H rows).  A split block's walk merge
+ * (k, first, count) becomes, for each of its tokens t in order, the merge
+ * record (t, first slot-list entry, count, 1) whose list holds the token's
+ * slot (first + i) * 64 / H + (t - row0 / H) of every piece i.
+ * counts[0..5] = grid, n_units, n_merges, slot-list length, partial slots
+ * (of H rows), and 1 when PKVMLA_QO_AUTO would pick row blocks, else 0. */
+int pkvmla_schedule_qo_rows_host(const int32_t* qo_indptr, const int32_t* kv_lens,
+                                 int32_t batch, int32_t num_heads, int32_t num_wg, int32_t tile,
+                                 int32_t fixed_cost, int32_t* wg_indptr, int64_t cap_wg,
+                                 int32_t* units, int64_t cap_units, int32_t* merges,
+                                 int64_t cap_merges, int32_t* slot_list, int64_t cap_list,
+                                 int32_t* counts);
+
 /* Copy the plan's uploaded device tables back to the host, for bit-exact
  * checking.  Layout of host int32 buf (cap elements):
  *   [0..15]  header: version(1), batch, num_heads, page_size, ckv_dim,
@@ -350,7 +406,8 @@ int pkvmla_schedule_chain_host(const int32_t* group_req_indptr, int32_t num_grou
  *   [16..31] header 2: num_seqs, n_indices, num_cu, sm_scale (float bits),
  *            is_cascade, num_groups, head_groups, launched workgroups,
  *            fixed launch shapes (0/1), page-id capacity, several query tokens
- *            per request (0/1), number of requests of such a plan,
+ *            per request (0: no, 1: one item per token, 2: row blocks),
+ *            number of requests of such a plan,
  *            cascade level 0: grid0, n_units0, slot-list length, and 1 when the
  *            cascade runs in one launch (level-0 table: requests' prefix
  *            pieces with their suffixes chained; no level-1 units), else 0
@@ -358,7 +415,9 @@ int pkvmla_schedule_chain_host(const int32_t* group_req_indptr, int32_t num_grou
  *   seq_indptr[num_seqs+1], seq_lens[num_seqs], seq_indices[n_indices],
  *   and for a cascade plan wg_indptr0[grid0+1], units0[n_units0*8] (the
  *   records of pkvmla_schedule_rows_host with the page fields filled), the
- *   slot list.  A cascade plan's units are its suffixes', every one with a
+ *   slot list; a row-block plan of several query tokens has the same three
+ *   (records of pkvmla_schedule_qo_rows_host with the page fields of request
+ *   b's pages) and its merges in the merge field, with no level-1 units.  A cascade plan's units are its suffixes', every one with a
  *   partial slot numbered after level 0's (in emission order), and its merge
  *   records are (request, first slot-list entry, count, 1): the request's
  *   level-0 slots in level-0 emission order, then its suffix slots.

@@ -29,8 +29,12 @@ CONFIGS = {
                    lens=("lognormal", 1024.0, 1.0, 1, 16384), pool_pages=None),
     "cascade": dict(kind="cascade", batch=128, num_heads=128, page_size=64,
                     prefix_len=8192, suffix=(64, 1024)),
+    # several new tokens per request (e.g. speculative decode with 3 draft
+    # tokens) on a 16-head share: 4 query tokens each, causal among them
+    "qo": dict(kind="qo", batch=64, num_heads=16, page_size=64,
+               lens=("uniform", 1024, 4096), pool_pages=None, qo_len=4),
 }
-CONFIG_SEEDS = {"tiny": 0, "deepseek": 1, "long": 2, "ragged": 3, "cascade": 4}
+CONFIG_SEEDS = {"tiny": 0, "deepseek": 1, "long": 2, "ragged": 3, "cascade": 4, "qo": 5}
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -293,6 +297,9 @@ def make_config(name: str, seed: Optional[int] = None):
     if kind == "flat":
         return make_flat(name, seed, cfg["batch"], cfg["num_heads"], cfg["page_size"],
                          cfg["lens"], cfg["pool_pages"])
+    if kind == "qo":
+        return make_qo(name, seed, cfg["batch"], cfg["num_heads"], cfg["page_size"],
+                       cfg["lens"], [cfg["qo_len"]] * cfg["batch"], cfg["pool_pages"])
     return make_cascade(name, seed, cfg["batch"], cfg["num_heads"], cfg["page_size"],
                         cfg["prefix_len"], cfg["suffix"])
 
@@ -304,7 +311,7 @@ def config_lens(name: str, seed: Optional[int] = None):
     cfg = CONFIGS[name]
     seed = CONFIG_SEEDS[name] if seed is None else seed
     rng = np.random.default_rng(seed)
-    if cfg["kind"] == "flat":
+    if cfg["kind"] in ("flat", "qo"):
         return _draw_lens(rng, cfg["batch"], cfg["lens"])
     lo, hi = cfg["suffix"]
     return cfg["prefix_len"], rng.integers(lo, hi, size=cfg["batch"], endpoint=True).astype(np.int32)

@@ -197,7 +197,7 @@ def attend_cascade(q_nope, q_pe, ckv, kpe, page_size,
 
 
 def attend_qo(q_nope, q_pe, ckv, kpe, qo_indptr, kv_indptr, kv_indices, kv_lens, page_size,
-              sm_scale=None):
+              sm_scale=None, kv_scales=None):
     """Several new query tokens per request, causal among them.
 
     Request b brings n_b = qo_indptr[b+1] - qo_indptr[b] new query tokens; they
@@ -205,7 +205,8 @@ def attend_qo(q_nope, q_pe, ckv, kpe, qo_indptr, kv_indptr, kv_indices, kv_lens,
     at position kv_lens[b] - n_b + j and attends exactly the tokens at positions
     0 .. that position (scores of later positions masked to -inf before the
     softmax).  q_nope [T, H, ckv_dim], q_pe [T, H, kpe_dim] with
-    T = qo_indptr[B].  Returns out float64 [T, H, ckv_dim] and lse [T, H]."""
+    T = qo_indptr[B].  kv_scales as in attend_flat.  Returns out float64
+    [T, H, ckv_dim] and lse [T, H]."""
     T, H, dc = q_nope.shape
     dr = q_pe.shape[2]
     scale = default_sm_scale(dc, dr) if sm_scale is None else float(sm_scale)
@@ -215,8 +216,13 @@ def attend_qo(q_nope, q_pe, ckv, kpe, qo_indptr, kv_indptr, kv_indices, kv_lens,
         n = int(qo_indptr[b + 1]) - int(qo_indptr[b])
         L = int(kv_lens[b])
         pages, slots = token_pages(kv_indptr, kv_indices, L, b, page_size)
-        c = bf16_to_f64(ckv[pages, slots])
-        k = np.concatenate([c, bf16_to_f64(kpe[pages, slots])], axis=1)   # [L, 576]
+        if kv_scales is None:
+            c = bf16_to_f64(ckv[pages, slots])
+            r = bf16_to_f64(kpe[pages, slots])
+        else:
+            c = float(kv_scales[0]) * e4m3_to_f64(ckv[pages, slots])
+            r = float(kv_scales[1]) * e4m3_to_f64(kpe[pages, slots])
+        k = np.concatenate([c, r], axis=1)                                 # [L, 576]
         positions = np.arange(L)
         for j in range(n):
             row = int(qo_indptr[b]) + j

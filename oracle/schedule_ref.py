@@ -79,21 +79,12 @@ QO_ROWS_FIXED = 4             # fixed cost per segment of the 64-row kernel (its
 
 
 def qo_uses_rows(qo_indptr, num_heads: int) -> bool:
-    """Layout rule of a plan with several new tokens per request.  Request b's
-    query rows are rho = t * H + h for its tokens t = qo_indptr[b] ..
-    qo_indptr[b+1] - 1; cut into blocks of 64 rows they give
-    ceil(n_b * H / 64) blocks.  Row blocks are used when H is 16 or 32 and
-    the blocks are on average more than half full: total rows > 32 x blocks.
-    Otherwise the plan has one work item per query token (qo_items)."""
-    H = int(num_heads)
-    if H > 32:
-        return False
-    rows, blocks = 0, 0
-    for b in range(len(qo_indptr) - 1):
-        n = int(qo_indptr[b + 1]) - int(qo_indptr[b])
-        rows += n * H
-        blocks += -(-(n * H) // QO_BLOCK_ROWS)
-    return 2 * rows > QO_BLOCK_ROWS * blocks
+    """Layout rule of a plan with several new tokens per request: row blocks
+    (qo_rows_ref) when H is 16 or 32 and some request brings more than one
+    query token (qo_indptr[B] > B); otherwise one work item per query token
+    (qo_items)."""
+    B = len(qo_indptr) - 1
+    return int(num_heads) in (16, 32) and int(qo_indptr[B]) > B
 
 
 def qo_rows_ref(qo_indptr, kv_lens, num_heads: int, num_wg: int, tile: int = PLAN_TILE,

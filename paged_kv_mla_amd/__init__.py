@@ -57,6 +57,15 @@ _lib.pkvmla_plan_update.argtypes = [_vp, _i32p, _i32p, _i32p, _vp]
 _lib.pkvmla_plan_create_qo.argtypes = [_i32p, _i32p, _i32p, _i32p, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_float, _vp, ctypes.POINTER(_vp)]
+_lib.pkvmla_plan_create_qo_layout.argtypes = [_i32p, _i32p, _i32p, _i32p, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                                              ctypes.c_int32, _vp, ctypes.POINTER(_vp)]
+_lib.pkvmla_schedule_qo_rows_host.argtypes = [_i32p, _i32p, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                              _i32p, ctypes.c_int64, _i32p, ctypes.c_int64,
+                                              _i32p, ctypes.c_int64, _i32p, ctypes.c_int64,
+                                              _i32p]
 _lib.pkvmla_run.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.pkvmla_run_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.pkvmla_run_strided.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int64, ctypes.c_int64,
@@ -91,8 +100,11 @@ EXPORTED_SYMBOLS = (
     "pkvmla_gather", "pkvmla_gather_rows", "pkvmla_plan_set_timing", "pkvmla_plan_timing",
     "pkvmla_run_noalloc", "pkvmla_plan_create_qo", "pkvmla_schedule_rows_host",
     "pkvmla_plan_create_cascade_with_capacity", "pkvmla_plan_update_cascade", "pkvmla_run_fp8",
-    "pkvmla_schedule_chain_host",
+    "pkvmla_schedule_chain_host", "pkvmla_plan_create_qo_layout", "pkvmla_schedule_qo_rows_host",
 )
+
+# work layouts of a plan with several query tokens per request
+QO_AUTO, QO_TOKENS, QO_ROW_BLOCKS = 0, 1, 2
 
 OK, EINVAL, EUNSUPPORTED, EHIP, ENOMEM = 0, 1, 2, 3, 4
 _NAMES = {EINVAL: "EINVAL", EUNSUPPORTED: "EUNSUPPORTED", EHIP: "EHIP", ENOMEM: "ENOMEM"}
@@ -210,6 +222,32 @@ def schedule_chain_host(group_req_indptr, prefix_lens, kv_lens, num_wg: int, til
             merges[:4 * nm].reshape(nm, 4).copy(), lst[:nl].copy())
 
 
+def schedule_qo_rows_host(qo_indptr, kv_lens, num_heads: int, num_wg: int, tile: int = 32,
+                          fixed_cost: int = 4):
+    """The library's row-block schedule of several query tokens per request,
+    computed on the host.  Returns (wg_indptr, units [n, 8], merges [m, 4],
+    slot_list, n_slots, auto_picks_rows)."""
+    qi, kl = _i32(qo_indptr), _i32(kv_lens)
+    if qi.ndim != 1 or len(qi) != len(kl) + 1:
+        raise ValueError("qo_indptr needs len(kv_lens) + 1 entries")
+    B = len(kl)
+    blocks = int(sum(-(-int(qi[b + 1] - qi[b]) * int(num_heads) // 64) for b in range(B)))
+    ucap = blocks + int(num_wg) + 8
+    tokens = int(qi[-1])
+    wg = np.zeros(int(num_wg) + 1, np.int32)
+    units = np.zeros(8 * ucap, np.int32)
+    merges = np.zeros(4 * (tokens + 1), np.int32)
+    lst = np.zeros(ucap * 4 + 8, np.int32)
+    counts = np.zeros(6, np.int32)
+    _check(_lib.pkvmla_schedule_qo_rows_host(_ptr(qi), _ptr(kl), B, int(num_heads), int(num_wg),
+                                             int(tile), int(fixed_cost), _ptr(wg), wg.size,
+                                             _ptr(units), units.size, _ptr(merges), merges.size,
+                                             _ptr(lst), lst.size, _ptr(counts)))
+    grid, nu, nm, nl, ns, auto = (int(c) for c in counts)
+    return (wg[:grid + 1].copy(), units[:8 * nu].reshape(nu, 8).copy(),
+            merges[:4 * nm].reshape(nm, 4).copy(), lst[:nl].copy(), ns, bool(auto))
+
+
 @dataclass
 class PlanExport:
     header: np.ndarray
@@ -220,7 +258,8 @@ class PlanExport:
     seq_indptr: np.ndarray
     seq_lens: np.ndarray
     seq_indices: np.ndarray
-    wg_indptr0: np.ndarray = None   # cascade level 0 (empty for other plans)
+    wg_indptr0: np.ndarray = None   # cascade level 0, or the row blocks of several
+                                    # query tokens per request (empty for other plans)
     units0: np.ndarray = None
     slot_list: np.ndarray = None
 
@@ -405,7 +444,7 @@ class Plan:
         o = 32
         parts = []
         for n in (grid + 1, 8 * nu, 4 * nm, ns + 1, ns, ni,
-                  (g0 + 1) if int(hdr[20]) else 0, 8 * nu0, nsl):
+                  (g0 + 1) if (int(hdr[20]) or int(hdr[26]) == 2) else 0, 8 * nu0, nsl):
             parts.append(buf[o:o + n].copy())
             o += n
         return PlanExport(header=hdr, sm_scale=float(hdr[19:20].view(np.float32)[0]),
@@ -438,11 +477,13 @@ def plan(kv_indptr, kv_indices, kv_lens, num_heads: int, page_size: int, num_pag
 
 def plan_qo(qo_indptr, kv_indptr, kv_indices, kv_lens, num_heads: int, page_size: int,
             num_pages: int, ckv_dim: int = 512, kpe_dim: int = 64,
-            sm_scale: Optional[float] = None, stream=None) -> Plan:
+            sm_scale: Optional[float] = None, stream=None, layout: int = QO_AUTO) -> Plan:
     """Plan with qo_indptr[b+1] - qo_indptr[b] new query tokens for request b,
     causal among them (they are the request's last tokens).  The run takes and
     returns one row per query token ([qo_indptr[-1], H, ...]); the Plan's
-    ``batch`` is that row count."""
+    ``batch`` is that row count.  ``layout``: QO_AUTO, QO_TOKENS (a work item
+    per token) or QO_ROW_BLOCKS (16 or 32 heads: blocks of 64 query rows that
+    score each KV tile once for several tokens)."""
     qi = _i32(qo_indptr)
     ip, ix, ln = _i32(kv_indptr), _i32(kv_indices), _i32(kv_lens)
     _check_csr("kv", ip, ix, ln)
@@ -451,9 +492,9 @@ def plan_qo(qo_indptr, kv_indptr, kv_indices, kv_lens, num_heads: int, page_size
     if ix.size == 0:
         ix = np.zeros(1, np.int32)
     h = ctypes.c_void_p()
-    _check(_lib.pkvmla_plan_create_qo(
+    _check(_lib.pkvmla_plan_create_qo_layout(
         _ptr(qi), _ptr(ip), _ptr(ix), _ptr(ln), int(len(ln)), int(num_pages), int(num_heads),
-        int(ckv_dim), int(kpe_dim), int(page_size), float(sm_scale or 0.0),
+        int(ckv_dim), int(kpe_dim), int(page_size), float(sm_scale or 0.0), int(layout),
         _stream_handle(stream) if stream else None, ctypes.byref(h)))
     return Plan(h.value, int(qi[-1]), int(num_heads), int(page_size), int(num_pages),
                 _current_device())
@@ -498,11 +539,13 @@ def plan_cascade(group_req_indptr, prefix_indptr, prefix_indices, prefix_lens,
     return p
 
 
-def plan_for(inp, stream=None) -> Plan:
-    """Plan for an input bundle from mla_workloads (flat or cascade)."""
+def plan_for(inp, stream=None, qo_layout: int = QO_AUTO) -> Plan:
+    """Plan for an input bundle from mla_workloads (flat, several query
+    tokens per request, or cascade)."""
     if getattr(inp, "qo_indptr", None) is not None:
         return plan_qo(inp.qo_indptr, inp.kv_indptr, inp.kv_indices, inp.kv_lens, inp.num_heads,
-                       inp.page_size, inp.num_pages, sm_scale=inp.sm_scale, stream=stream)
+                       inp.page_size, inp.num_pages, sm_scale=inp.sm_scale, stream=stream,
+                       layout=qo_layout)
     if hasattr(inp, "prefix_lens"):
         return plan_cascade(inp.group_req_indptr, inp.prefix_indptr, inp.prefix_indices,
                             inp.prefix_lens, inp.kv_indptr, inp.kv_indices, inp.kv_lens,

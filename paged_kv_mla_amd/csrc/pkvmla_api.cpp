@@ -162,11 +162,14 @@ int check_pages(const char* what, const int32_t* indptr, const int32_t* indices,
 
 // The page fields of unit records: the sequence's page-list start and the page
 // of the unit's first token.
+// The sequence is the record's second field, or seq_of[unit] when given (row
+// blocks of several query tokens keep their causal offset there).
 void fill_page_fields(std::vector<int32_t>* units, const std::vector<int32_t>& seq_indptr,
-                      const std::vector<int32_t>& seq_indices, int32_t page_size) {
+                      const std::vector<int32_t>& seq_indices, int32_t page_size,
+                      const std::vector<int32_t>* seq_of = nullptr) {
   for (size_t i = 0; i < units->size(); i += pkvmla::kUnitRecordInts) {
     int32_t* u = &(*units)[i];
-    const int32_t base = seq_indptr[u[1]];
+    const int32_t base = seq_indptr[seq_of ? (*seq_of)[i / pkvmla::kUnitRecordInts] : u[1]];
     u[6] = base;
     u[7] = seq_indices[(size_t)base + (size_t)(u[2] / page_size)];
   }
@@ -323,6 +326,15 @@ int build_chain_tables(const pkvmla_plan_s* P, const Level0Groups& l0, const int
   return PKVMLA_OK;
 }
 
+// A plan with several new tokens per request, laid out in row blocks.
+struct QoRows {
+  const int32_t* qo_indptr;
+  const int32_t* kv_lens;
+  int32_t num_requests;
+};
+
+static_assert(pkvmla::kRowsDirect == pkvmla::kRowsDirectSlot, "direct row-block slot marker");
+
 bool chain_eligible(const pkvmla_plan_s* P, const Level0Groups& l0) {
   if (P->fixed_launch || P->num_heads < 64) return false;
   for (int32_t g = 0; g < l0.num_groups; ++g)
@@ -337,7 +349,7 @@ bool chain_eligible(const pkvmla_plan_s* P, const Level0Groups& l0) {
 int finish_plan(pkvmla_plan_s* P, const std::vector<pkvmla::WorkItem>& items,
                 const std::vector<int32_t>& seq_indptr, const std::vector<int32_t>& seq_lens,
                 const std::vector<int32_t>& seq_indices, hipStream_t stream,
-                const Level0Groups* l0 = nullptr) {
+                const Level0Groups* l0 = nullptr, const QoRows* qo = nullptr) {
   PKVMLA_HIP(hipGetDevice(&P->device));
   PKVMLA_HIP(hipDeviceGetAttribute(&P->num_cu, hipDeviceAttributeMultiprocessorCount, P->device));
   // the schedule's lanes: each lane's token ranges are replicated over the head groups
@@ -379,6 +391,26 @@ int finish_plan(pkvmla_plan_s* P, const std::vector<pkvmla::WorkItem>& items,
       rc = build_cascade_schedules(P, *l0, items, seq_indptr, seq_indices, &P->sched,
                                    &P->sched0, &P->slot_list);
     }
+  } else if (qo) {
+    // every unit in the level-0 table (row blocks of the 64-row kernel), no
+    // level-1 units; merges per query token over slot lists
+    P->cap_lanes0 = std::max(1, P->num_cu / P->cfg0.head_groups);
+    std::vector<int32_t> unit_seq;
+    if (!pkvmla::build_qo_row_schedule(qo->qo_indptr, qo->kv_lens, qo->num_requests,
+                                       P->num_heads, P->cap_lanes0, pkvmla::kTile,
+                                       P->cfg0.fixed_cost, &P->sched0, &unit_seq,
+                                       &P->sched.merges, &P->slot_list))
+      return fail(PKVMLA_EUNSUPPORTED, "row-block schedule construction failed (too many query rows)");
+    fill_page_fields(&P->sched0.units, seq_indptr, seq_indices, P->page_size, &unit_seq);
+    P->sched.grid = 0;
+    P->sched.wg_indptr.assign(1, 0);
+    P->sched.units.clear();
+    P->sched.n_slots = P->sched0.n_slots;
+    P->sched.total_rows = 0;
+    P->cap_units0 = (int32_t)(P->sched0.units.size() / pkvmla::kUnitRecordInts);
+    P->cap_slots = std::max(1, P->sched0.n_slots);
+    P->cap_list = (int32_t)P->slot_list.size();
+    rc = PKVMLA_OK;
   } else {
     rc = build_plan_schedule(P, items, seq_indptr, seq_indices, &P->sched);
   }
@@ -390,7 +422,8 @@ int finish_plan(pkvmla_plan_s* P, const std::vector<pkvmla::WorkItem>& items,
   P->off_units = P->off_wg + pad((size_t)P->cap_lanes + 1);
   P->off_merges = P->off_units + pad((size_t)P->cap_units * pkvmla::kUnitRecordInts);
   P->off_wg0 = P->off_merges + pad((size_t)P->cap_merges * pkvmla::kMergeRecordInts);
-  P->off_units0 = P->off_wg0 + pad(l0 ? (size_t)P->cap_lanes0 + 1 : 0);
+  const bool has_l0 = l0 || qo;
+  P->off_units0 = P->off_wg0 + pad(has_l0 ? (size_t)P->cap_lanes0 + 1 : 0);
   P->off_list = P->off_units0 + pad((size_t)P->cap_units0 * pkvmla::kUnitRecordInts);
   P->off_sip = P->off_list + pad((size_t)P->cap_list);
   P->off_sl = P->off_sip + pad(seq_indptr.size());
@@ -414,7 +447,7 @@ int finish_plan(pkvmla_plan_s* P, const std::vector<pkvmla::WorkItem>& items,
   const size_t rows = (size_t)P->cap_slots * P->num_heads;
   PKVMLA_HIP(hipMalloc(&P->d_part, rows * (pkvmla::kCkvDim * sizeof(uint16_t) + sizeof(float))));
   return upload_tables(P, P->sched, seq_indptr, seq_lens, seq_indices, stream,
-                       l0 ? &P->sched0 : nullptr, l0 ? &P->slot_list : nullptr);
+                       has_l0 ? &P->sched0 : nullptr, has_l0 ? &P->slot_list : nullptr);
 }
 
 void free_plan(pkvmla_plan_s* P) {
@@ -549,6 +582,50 @@ int pkvmla_schedule_chain_host(const int32_t* group_req_indptr, int32_t num_grou
   return ok();
 }
 
+int pkvmla_schedule_qo_rows_host(const int32_t* qo_indptr, const int32_t* kv_lens,
+                                 int32_t batch, int32_t num_heads, int32_t num_wg, int32_t tile,
+                                 int32_t fixed_cost, int32_t* wg_indptr, int64_t cap_wg,
+                                 int32_t* units, int64_t cap_units, int32_t* merges,
+                                 int64_t cap_merges, int32_t* slot_list, int64_t cap_list,
+                                 int32_t* counts) {
+  if (!qo_indptr || !kv_lens || !counts || batch < 1)
+    return fail(PKVMLA_EINVAL, "null argument or batch < 1");
+  if (num_wg < 1 || tile < 1 || fixed_cost < 0)
+    return fail(PKVMLA_EINVAL, "num_wg and tile must be >= 1, fixed_cost >= 0");
+  if (num_heads != 16 && num_heads != 32)
+    return fail(PKVMLA_EUNSUPPORTED, "row blocks of query tokens need 16 or 32 heads (got %d)",
+                num_heads);
+  if (qo_indptr[0] != 0) return fail(PKVMLA_EINVAL, "qo_indptr[0] must be 0");
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t n = (int64_t)qo_indptr[b + 1] - qo_indptr[b];
+    if (n < 1 || n > kv_lens[b])
+      return fail(PKVMLA_EINVAL, "request %d: %lld query tokens for kv_len %d", b, (long long)n,
+                  kv_lens[b]);
+  }
+  pkvmla::RowSchedule s;
+  std::vector<int32_t> seq, m, l;
+  if (!pkvmla::build_qo_row_schedule(qo_indptr, kv_lens, batch, num_heads, num_wg, tile,
+                                     fixed_cost, &s, &seq, &m, &l))
+    return fail(PKVMLA_EINVAL, "row-block schedule construction failed");
+  counts[0] = s.grid;
+  counts[1] = (int32_t)(s.units.size() / pkvmla::kUnitRecordInts);
+  counts[2] = (int32_t)(m.size() / pkvmla::kMergeRecordInts);
+  counts[3] = (int32_t)l.size();
+  counts[4] = s.n_slots;
+  counts[5] = pkvmla::qo_uses_row_blocks(qo_indptr, batch, num_heads) ? 1 : 0;
+  if ((int64_t)s.wg_indptr.size() > cap_wg || (int64_t)s.units.size() > cap_units ||
+      (int64_t)m.size() > cap_merges || (int64_t)l.size() > cap_list)
+    return fail(PKVMLA_EINVAL, "output capacity too small");
+  if (!wg_indptr || (!s.units.empty() && !units) || (!m.empty() && !merges) ||
+      (!l.empty() && !slot_list))
+    return fail(PKVMLA_EINVAL, "null output");
+  std::copy(s.wg_indptr.begin(), s.wg_indptr.end(), wg_indptr);
+  std::copy(s.units.begin(), s.units.end(), units);
+  std::copy(m.begin(), m.end(), merges);
+  std::copy(l.begin(), l.end(), slot_list);
+  return ok();
+}
+
 int pkvmla_plan_create_with_capacity(const int32_t* kv_indptr, const int32_t* kv_indices,
                                      const int32_t* kv_lens, int32_t batch, int32_t num_pages,
                                      int32_t num_heads, int32_t ckv_dim, int32_t kpe_dim,
@@ -600,6 +677,16 @@ int pkvmla_plan_create_qo(const int32_t* qo_indptr, const int32_t* kv_indptr,
                           const int32_t* kv_indices, const int32_t* kv_lens, int32_t batch,
                           int32_t num_pages, int32_t num_heads, int32_t ckv_dim, int32_t kpe_dim,
                           int32_t page_size, float sm_scale, void* stream, pkvmla_plan* out) {
+  return pkvmla_plan_create_qo_layout(qo_indptr, kv_indptr, kv_indices, kv_lens, batch,
+                                      num_pages, num_heads, ckv_dim, kpe_dim, page_size, sm_scale,
+                                      PKVMLA_QO_AUTO, stream, out);
+}
+
+int pkvmla_plan_create_qo_layout(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                                 const int32_t* kv_indices, const int32_t* kv_lens, int32_t batch,
+                                 int32_t num_pages, int32_t num_heads, int32_t ckv_dim,
+                                 int32_t kpe_dim, int32_t page_size, float sm_scale,
+                                 int32_t layout, void* stream, pkvmla_plan* out) {
   if (!out) return fail(PKVMLA_EINVAL, "null plan output pointer");
   *out = nullptr;
   int32_t log2_ps;
@@ -618,11 +705,19 @@ int pkvmla_plan_create_qo(const int32_t* qo_indptr, const int32_t* kv_indptr,
       return fail(PKVMLA_EINVAL, "request %d: %lld query tokens but kv_len %d (the new tokens are part "
                   "of the KV)", b, (long long)n, kv_lens[b]);
   }
+  if (layout != PKVMLA_QO_AUTO && layout != PKVMLA_QO_TOKENS && layout != PKVMLA_QO_ROW_BLOCKS)
+    return fail(PKVMLA_EINVAL, "unknown query-token layout %d", layout);
+  if (layout == PKVMLA_QO_ROW_BLOCKS && num_heads != 16 && num_heads != 32)
+    return fail(PKVMLA_EUNSUPPORTED, "row blocks of query tokens need 16 or 32 heads (got %d)",
+                num_heads);
+  const bool rows_layout = layout == PKVMLA_QO_ROW_BLOCKS ||
+                           (layout == PKVMLA_QO_AUTO &&
+                            pkvmla::qo_uses_row_blocks(qo_indptr, batch, num_heads));
   const int32_t rows = qo_indptr[batch];
   pkvmla_plan_s* P = new pkvmla_plan_s();
   P->batch = rows;  // one query row per (request, new token)
   P->num_requests = batch;
-  P->is_qo = 1;
+  P->is_qo = rows_layout ? 2 : 1;
   P->num_heads = num_heads;
   P->page_size = page_size;
   P->log2_ps = log2_ps;
@@ -633,18 +728,27 @@ int pkvmla_plan_create_qo(const int32_t* qo_indptr, const int32_t* kv_indptr,
   pkvmla::kernel_config_for(num_heads, &P->cfg);
   // Query row r = qo_indptr[b] + j sits at position kv_len - qo_len + j and
   // attends tokens 0 .. that position of request b's page list (causal among
-  // the request's new tokens, every earlier token visible): one work item of
-  // that length over sequence b.
-  std::vector<pkvmla::WorkItem> items((size_t)rows);
-  for (int32_t b = 0; b < batch; ++b) {
-    const int32_t n = qo_indptr[b + 1] - qo_indptr[b];
-    for (int32_t j = 0; j < n; ++j)
-      items[qo_indptr[b] + j] = pkvmla::WorkItem{qo_indptr[b] + j, b, kv_lens[b] - n + 1 + j};
-  }
+  // the request's new tokens, every earlier token visible).  Either one work
+  // item of that length over sequence b per query token, or row blocks of
+  // 64 query rows (several tokens' heads), each over the whole sequence with
+  // the causal bound per row, so one KV tile serves all of them.
+  std::vector<pkvmla::WorkItem> items;
   std::vector<int32_t> sip(kv_indptr, kv_indptr + batch + 1);
   std::vector<int32_t> sl(kv_lens, kv_lens + batch);
   std::vector<int32_t> si(kv_indices, kv_indices + kv_indptr[batch]);
-  rc = finish_plan(P, items, sip, sl, si, (hipStream_t)stream);
+  if (rows_layout) {
+    P->cfg0 = pkvmla::KernelConfig{8, 16, 4, 1, 4, 1};
+    const QoRows qr{qo_indptr, kv_lens, batch};
+    rc = finish_plan(P, items, sip, sl, si, (hipStream_t)stream, nullptr, &qr);
+  } else {
+    items.resize((size_t)rows);
+    for (int32_t b = 0; b < batch; ++b) {
+      const int32_t n = qo_indptr[b + 1] - qo_indptr[b];
+      for (int32_t j = 0; j < n; ++j)
+        items[qo_indptr[b] + j] = pkvmla::WorkItem{qo_indptr[b] + j, b, kv_lens[b] - n + 1 + j};
+    }
+    rc = finish_plan(P, items, sip, sl, si, (hipStream_t)stream);
+  }
   if (rc) {
     std::string msg = g_last_error;
     free_plan(P);
@@ -967,9 +1071,12 @@ int run_impl(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* ck
   const int slot_ev = (int)(P->timed_runs % pkvmla_plan_s::kTimingSlots);
   d.stamps = P->timing ? P->d_stamps + 2 * slot_ev : nullptr;
   if (P->timing) PKVMLA_HIP(hipEventRecord(P->ev[2 * slot_ev], s));
-  if (P->is_cascade && (P->sched0.grid > 0 || P->fixed_launch)) {
-    // level 0: the groups' query rows over their shared prefixes
+  d.qo_log2h = -1;
+  if ((P->is_cascade || P->is_qo == 2) && (P->sched0.grid > 0 || P->fixed_launch)) {
+    // level 0: the groups' query rows over their shared prefixes, or the row
+    // blocks of several query tokens per request (causal bound per row)
     pkvmla::DecodeParams d0 = d;
+    d0.qo_log2h = P->is_qo == 2 ? (P->num_heads == 16 ? 4 : 5) : -1;
     d0.wg_indptr = P->d_wg0;
     d0.units = P->d_units0;
     d0.head_groups = P->cfg0.head_groups;
@@ -1142,7 +1249,9 @@ int pkvmla_gather_rows(pkvmla_plan P, int64_t* n_rows) {
 int pkvmla_gather(pkvmla_plan P, const void* ckv_cache, const void* kpe_cache, void* rows,
                   void* stream) {
   if (!P) return fail(PKVMLA_EINVAL, "null plan");
-  if (!ckv_cache || !kpe_cache || (!rows && P->sched.total_rows > 0))
+  int64_t n_rows = 0;
+  (void)pkvmla_gather_rows(P, &n_rows);
+  if (!ckv_cache || !kpe_cache || (!rows && n_rows > 0))
     return fail(PKVMLA_EINVAL, "null tensor pointer");
   if (!aligned16(ckv_cache) || !aligned16(kpe_cache) || !aligned16(rows))
     return fail(PKVMLA_EINVAL, "device pointers must be 16-byte aligned");
@@ -1161,13 +1270,14 @@ int pkvmla_gather(pkvmla_plan P, const void* ckv_cache, const void* kpe_cache, v
   g.ckv_stride = pkvmla::kCkvDim * 2;
   g.kpe_stride = pkvmla::kKpeDim * 2;
   const int n_units = (int)(P->sched.units.size() / pkvmla::kUnitRecordInts);
-  if (!P->is_cascade) {
+  if (!P->is_cascade && P->is_qo != 2) {
     PKVMLA_HIP(pkvmla::launch_gather(g, n_units, (hipStream_t)stream));
     return ok();
   }
   // cascade: the level-0 pieces (prefix tokens, once per row-block piece)
-  // then the suffix units, as gather records (request field unused, row =
-  // tokens before); a temporary table, and a wait before it is freed
+  // then the suffix units; query-token row blocks: their pieces; as gather
+  // records (request and sequence fields unused, row = tokens before); a
+  // temporary table, and a wait before it is freed
   std::vector<int32_t> gu;
   int64_t row = 0;
   auto add = [&](const std::vector<int32_t>& us) {

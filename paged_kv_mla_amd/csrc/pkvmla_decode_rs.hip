@@ -47,11 +47,18 @@
 // its rows in the partial-state rows (rho + offset) and the end of the
 // group's rows in place of request, slot and gathered-row index; its rows
 // always write partial states, which the merge combines with the suffix's.
+// The same units serve several new query tokens per request (16 or 32 heads):
+// the 64 rows are t * H + head of 4 or 2 tokens of one request over its own
+// pages, each QK wave's 16 rows the heads of one token t, masked at that
+// token's causal bound (positions below t + the record's second field); a
+// block the schedule left whole writes out and lse itself (slot kRowsDirect).
 //
-// Masking.  Only the last tile of a unit can be partial.  Its ckv slots past
-// kv_end copy the last valid row (finite data), its kpe slots the page's own
-// rows; the QK waves set those slots' scores to -inf (a select) before the
-// softmax, so they add exactly zero to PV.
+// Masking.  Only the last tile of a unit can be partial, except in row blocks
+// of query tokens, where a wave's token may see a tile partly or not at all.
+// A partial tile's ckv slots past kv_end copy the last valid row (finite
+// data), its kpe slots the page's own rows; the QK waves set the scores of
+// slots they may not see to -inf (a select) before the softmax, so they add
+// exactly zero to PV.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -103,12 +110,14 @@ struct UnitCursor {
   int tile;     // tile index within the unit
   int ntiles;   // tiles in the unit
   int b, kv0, kv1, slot, rend;
+  int caus;     // row blocks of query tokens: token t sees positions below t + caus
   bool cont;    // this unit continues the previous one's state
 };
 
 __device__ __forceinline__ void cursor_load(UnitCursor& c, idx_ptr units) {
   idx_ptr rec = units + (size_t)c.u * kUnitInts;
   c.b = rec[0];
+  c.caus = rec[1];
   c.kv0 = rec[2];
   c.kv1 = rec[3];
   c.slot = rec[4];
@@ -143,7 +152,8 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
                      const int32_t* __restrict__ wg_indptr_g, const int32_t* __restrict__ units_g,
                      const int32_t* __restrict__ seq_indices_g, int H, int n_hg, int n_lanes,
                      int log2_ps, float sm_scale, float C, float thr, int cs_arg,
-                     int ks_arg, unsigned long long* stamps, float v_scale, float kpe_ratio) {
+                     int ks_arg, unsigned long long* stamps, float v_scale, float kpe_ratio,
+                     int qo_log2h) {
   const int cs = PACKED ? kCkvDim * 2 : cs_arg;
   const int ks = PACKED ? kKpeDim * 2 : ks_arg;
   const idx_ptr wg_indptr = (idx_ptr)wg_indptr_g;
@@ -276,7 +286,13 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
           load_q(q_row(nrec[0], ROWS ? nrec[5] : 0));
         }
         // ---- softmax of this tile: lane (g, li) holds tokens tb*16 + g*4 + k ----
-        const int valid = min(cq.kv1 - (cq.kv0 + cq.tile * kTile), kTile);
+        // tokens of the tile this wave's rows see: the unit's end, and in
+        // row blocks of query tokens the causal bound of the wave's token (its
+        // 16 rows are heads of one token); 0 or less: none (a whole tile
+        // masked, possible only in row blocks)
+        int kv_lim = cq.kv1;
+        if (ROWS && qo_log2h >= 0) kv_lim = min(kv_lim, ((cq.b + hg * HEADS + r * 16) >> qo_log2h) + cq.caus);
+        const int valid = min(kv_lim - (cq.kv0 + cq.tile * kTile), kTile);
         float sv[8];
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
@@ -296,9 +312,11 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
         // than thr (probabilities stay <= 2^thr*C); the first tile always sets it
         const bool grow = mx > m_run + thr;
         const float m_new = grow ? mx : m_run;
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * C);
+        // (row blocks: a row may see nothing yet, m stays -inf; the factor is
+        // then 0, as on any unit's first tile, and the probabilities 0)
+        const float alpha = ROWS && m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * C);
         m_run = m_new;
-        const float mc = m_run * C;
+        const float mc = ROWS && m_run == -INFINITY ? 0.f : m_run * C;
         float pv[8];
         bf16x8_t pT;
 #pragma unroll
@@ -321,7 +339,10 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
             *(LDS_AS float*)(smem + kXlOff + (par * 64 + li * 4 + r) * 4) = l;
             if (ROWS) {
               const int row = cq.b + hg * HEADS + r * 16 + li;
-              if (row < cq.rend) part_lse[cq.slot + row] = lse;
+              if (row < cq.rend) {
+                if (cq.slot == kRowsDirect) lse_out[row] = lse;
+                else part_lse[cq.slot + row] = lse;
+              }
             } else if (cq.slot < 0) {
               lse_out[(size_t)cq.b * H + head] = lse;
             } else {
@@ -438,7 +459,12 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
         const f32x4_t l4 = *(const LDS_AS f32x4_t*)(smem + kXlOff + (par * 64 + lie * 4) * 4);
         float linv[HB];
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb) linv[hb] = __builtin_amdgcn_rcpf(l4[hb]) * (FP8 ? v_scale : 1.f);
+        for (int hb = 0; hb < HB; ++hb) {
+          linv[hb] = __builtin_amdgcn_rcpf(l4[hb]) * (FP8 ? v_scale : 1.f);
+          // (row blocks: a row that saw no token of this piece has O = 0 and
+          // l = 0; its state is (0, -inf), weight 0 in the merge)
+          if (ROWS) linv[hb] = l4[hb] > 0.f ? linv[hb] : 0.f;
+        }
         // Lane (g, li) holds dims r*128 + db*16 + g*4 .. +3 of head hb*16 + li.
         // For a pair of dim blocks (2dp, 2dp+1) one row swap (rows 0<->1 and
         // 2<->3, v_permlane16_swap) gives every lane 8 consecutive dims: even
@@ -449,9 +475,11 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
         // a whole request's rows go to out, a split unit's to its partial slot
         // (both bf16)
         // (a row block's rows: partial-state rows from its first row plus
-        // the unit's offset; head blocks past its group's rows store nothing)
+        // the unit's offset, or out's own rows for a whole block of query
+        // tokens; head blocks past the block's rows store nothing)
         char* obase = reinterpret_cast<char*>(
-            ROWS ? part_o + (size_t)(cp.slot + cp.b + hg * HEADS) * kCkvDim
+            ROWS ? (cp.slot == kRowsDirect ? out + (size_t)(cp.b + hg * HEADS) * kCkvDim
+                                           : part_o + (size_t)(cp.slot + cp.b + hg * HEADS) * kCkvDim)
             : cp.slot < 0 ? out + ((size_t)cp.b * H + hg * HEADS) * kCkvDim
                           : part_o + ((size_t)cp.slot * H + hg * HEADS) * kCkvDim);
 #pragma unroll
@@ -618,7 +646,7 @@ bool launch_decode_rs(const DecodeParams& p, hipStream_t stream, hipError_t* err
   p.q_nope, p.q_pe, p.ckv, p.kpe, p.out, p.lse, p.part_o, p.part_lse, p.wg_indptr, p.units, \
       p.seq_indices, p.num_heads, p.head_groups, p.n_lanes, p.log2_ps, p.sm_scale,     \
       p.score_log2, p.rescale_thr, p.ckv_stride, p.kpe_stride, p.stamps, p.v_scale,    \
-      p.kpe_ratio
+      p.kpe_ratio, p.qo_log2h
 #define PKVMLA_RS_LAUNCH3(HBV, PK, RB, F8)                                                     \
   if (big) mla_decode_rs_kernel<true, HBV, PK, RB, F8><<<grid, block, 0, stream>>>(PKVMLA_RS_ARGS); \
   else mla_decode_rs_kernel<false, HBV, PK, RB, F8><<<grid, block, 0, stream>>>(PKVMLA_RS_ARGS);

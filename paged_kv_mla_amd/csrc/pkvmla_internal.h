@@ -18,6 +18,9 @@ constexpr int kMergeInts = 4;       // b, first_slot (or first list entry), coun
 // workgroup's list instead of writing it (a chained cascade request: its last
 // prefix piece, then its suffix).
 constexpr int32_t kChainNext = INT32_MIN;
+// Slot field of a row-block unit that writes its rows' out and lse itself
+// (a block of several query tokens left whole by the schedule).
+constexpr int32_t kRowsDirect = INT32_MIN + 1;
 constexpr int kStageBytes = kTile * kCkvDim * 2 + kTile * kKpeDim * 2;  // 36864
 constexpr int kIndexPad = 64;       // margin of valid page ids after the device index table
 
@@ -60,6 +63,9 @@ struct DecodeParams {
   int32_t fp8;               // caches hold OCP E4M3 codes (ckv, kpe as bytes)
   float v_scale;             // fp8: ckv scale (output rows); else unused
   float kpe_ratio;           // fp8: kpe scale / ckv scale; else unused
+  int32_t qo_log2h;          // row blocks of several query tokens: log2 H (query token
+                             // t = row >> qo_log2h sees positions below t + the unit's
+                             // second field); -1: no causal bound
 };
 
 struct MergeParams {

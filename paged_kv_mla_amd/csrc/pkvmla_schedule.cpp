@@ -276,3 +276,75 @@ void build_cascade_merges(const RowSchedule& l0, const std::vector<int32_t>& l1_
 }
 
 }  // namespace pkvmla
+
+namespace pkvmla {
+
+// A 64-row workgroup costs about what a 16- or 32-head one costs per tile, so
+// row blocks pay as soon as one request brings two tokens (its tiles then
+// serve both), and only a batch of single tokens keeps one item per token.
+bool qo_uses_row_blocks(const int32_t* qo_indptr, int32_t batch, int32_t num_heads) {
+  return (num_heads == 16 || num_heads == 32) && qo_indptr[batch] > batch;
+}
+
+// Row blocks of several new tokens per request.  The blocks are the work items
+// of the flat walk (item k over its request's sequence, whole KV length); its
+// units and merges are then rewritten for rows: slot field kRowsDirectSlot for
+// a whole block, else walk slot * 64 - row0 (so walk slot s holds the 64 / H
+// partial slots of H rows from s * 64 / H on, one per token of the block); a
+// split block's merge becomes one merge per token over a list of its slots.
+bool build_qo_row_schedule(const int32_t* qo_indptr, const int32_t* kv_lens, int32_t batch,
+                           int32_t num_heads, int32_t num_wg, int32_t tile, int32_t fixed,
+                           RowSchedule* s, std::vector<int32_t>* unit_seq,
+                           std::vector<int32_t>* merges, std::vector<int32_t>* slot_list) {
+  if ((num_heads != 16 && num_heads != 32) || batch < 1) return false;
+  struct Block {
+    int32_t b, row0, row_end;
+  };
+  std::vector<Block> blocks;
+  std::vector<WorkItem> items;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t lo = (int64_t)qo_indptr[b] * num_heads;
+    const int64_t hi = (int64_t)qo_indptr[b + 1] * num_heads;
+    if (hi > INT32_MAX) return false;
+    for (int64_t r = lo; r < hi; r += kQoBlockRows) {
+      items.push_back(WorkItem{(int32_t)blocks.size(), b, kv_lens[b]});
+      blocks.push_back(Block{b, (int32_t)r, (int32_t)std::min<int64_t>(r + kQoBlockRows, hi)});
+    }
+  }
+  Schedule flat;
+  if (!build_schedule(items, (int32_t)blocks.size(), num_wg, tile, fixed, &flat)) return false;
+  const int32_t per = kQoBlockRows / num_heads;
+  if ((int64_t)flat.n_slots * per > INT32_MAX / 2) return false;
+  s->grid = flat.grid;
+  s->wg_indptr = flat.wg_indptr;
+  s->units = flat.units;
+  s->n_slots = flat.n_slots * per;
+  unit_seq->clear();
+  for (size_t i = 0; i < s->units.size(); i += kUnitRecordInts) {
+    int32_t* u = &s->units[i];
+    const Block& k = blocks[(size_t)u[0]];
+    const int32_t n = qo_indptr[k.b + 1] - qo_indptr[k.b];
+    unit_seq->push_back(k.b);
+    const int32_t slot = u[4];
+    u[0] = k.row0;
+    u[1] = kv_lens[k.b] - n + 1 - qo_indptr[k.b];  // token t sees positions < t + u[1]
+    u[4] = slot < 0 ? kRowsDirectSlot : slot * kQoBlockRows - k.row0;
+    u[5] = k.row_end;
+    u[6] = 0;
+    u[7] = 0;
+  }
+  merges->clear();
+  slot_list->clear();
+  for (size_t i = 0; i < flat.merges.size(); i += kMergeRecordInts) {
+    const Block& k = blocks[(size_t)flat.merges[i]];
+    const int32_t first = flat.merges[i + 1], count = flat.merges[i + 2];
+    for (int32_t j = 0; j < (k.row_end - k.row0) / num_heads; ++j) {
+      merges->insert(merges->end(),
+                     {k.row0 / num_heads + j, (int32_t)slot_list->size(), count, 1});
+      for (int32_t p = 0; p < count; ++p) slot_list->push_back((first + p) * per + j);
+    }
+  }
+  return true;
+}
+
+}  // namespace pkvmla

@@ -75,6 +75,32 @@ void build_cascade_merges(const RowSchedule& l0, const std::vector<int32_t>& l1_
                           int32_t batch, int32_t num_heads, std::vector<int32_t>* merges,
                           std::vector<int32_t>* slot_list);
 
+// Several new query tokens per request as row blocks (16 or 32 heads): request
+// b's query rows t * H + h (its tokens t = qo_indptr[b] .. qo_indptr[b+1] - 1)
+// in blocks of 64, each block over the request's whole KV length with the
+// causal bound per row.  The layout is used when some request brings more
+// than one token (qo_indptr[batch] > batch); otherwise the plan has one work
+// item per query token.
+constexpr int32_t kQoBlockRows = 64;
+// slot field of a row-block unit that writes out and lse directly (the
+// kernels' kRowsDirect)
+constexpr int32_t kRowsDirectSlot = INT32_MIN + 1;
+bool qo_uses_row_blocks(const int32_t* qo_indptr, int32_t batch, int32_t num_heads);
+
+// The row-block schedule: the blocks are the items of build_schedule's walk
+// (`fixed`: the 64-row kernel's cost per segment), whose units become records
+// row0, c_b, kv_begin, kv_end, slot field, row_end, 0, 0 with
+// c_b = kv_lens[b] - n_b + 1 - qo_indptr[b] (token t sees the positions below
+// t + c_b) and slot field kRowsDirectSlot (a whole block) or
+// walk slot * 64 - row0 (partial row = field + row, slots of H rows).  A split
+// block gives one merge record (t, first list entry, count, 1) per token t,
+// its list the token's slot in each piece.  unit_seq: the request (sequence)
+// of each unit, for the page fields.  n_slots counts slots of H rows.
+bool build_qo_row_schedule(const int32_t* qo_indptr, const int32_t* kv_lens, int32_t batch,
+                           int32_t num_heads, int32_t num_wg, int32_t tile, int32_t fixed,
+                           RowSchedule* s, std::vector<int32_t>* unit_seq,
+                           std::vector<int32_t>* merges, std::vector<int32_t>* slot_list);
+
 }  // namespace pkvmla
 
 #endif  // PKVMLA_SCHEDULE_H_

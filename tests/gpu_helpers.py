@@ -100,10 +100,13 @@ def oracle_cascade(inp, requests=None, fp8: bool = False):
     return np.stack(outs), np.stack(lses)
 
 
-def oracle_qo(inp):
-    """fp64 oracle for inputs with several new query tokens per request."""
-    return oracle.attend_qo(inp.q_nope, inp.q_pe, inp.ckv, inp.kpe, inp.qo_indptr, inp.kv_indptr,
-                            inp.kv_indices, inp.kv_lens, inp.page_size, sm_scale=inp.sm_scale)
+def oracle_qo(inp, fp8: bool = False):
+    """fp64 oracle for inputs with several new query tokens per request (fp8:
+    of its E4M3 caches and scales)."""
+    ckv, kpe, sc = _kv(inp, fp8)
+    return oracle.attend_qo(inp.q_nope, inp.q_pe, ckv, kpe, inp.qo_indptr, inp.kv_indptr,
+                            inp.kv_indices, inp.kv_lens, inp.page_size, sm_scale=inp.sm_scale,
+                            kv_scales=sc)
 
 
 def compare(out_gpu: torch.Tensor, lse_gpu: torch.Tensor, out_ref, lse_ref, requests=None,

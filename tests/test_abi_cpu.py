@@ -346,3 +346,45 @@ def test_schedule_host_matches_reference_qo():
     lens = np.array([40, 300, 1, 2000])
     _compare(qo_items(qo, lens), int(qo[-1]), 128, 32, 4)
     _compare(qo_items(qo, lens), int(qo[-1]), 7, 32, 2)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_qo_row_schedule_host_matches_reference(seed):
+    """The library's row-block schedule of several query tokens per request
+    equals the independent re-derivation bit for bit (units, merges, slot
+    list, slot count), and so does its layout rule."""
+    from oracle.schedule_ref import qo_rows_ref, qo_uses_rows
+    rng = np.random.default_rng(1000 + seed)
+    H = int(rng.choice([16, 32]))
+    B = int(rng.integers(1, 9))
+    qo = rng.integers(1, 24 if seed % 3 else 3, size=B)
+    kv = np.maximum(qo, rng.integers(1, 5000, size=B))
+    qi = np.concatenate([[0], np.cumsum(qo)]).astype(np.int32)
+    W = int(rng.choice([1, 3, 17, 64, 256]))
+    fixed = int(rng.choice([1, 4]))
+    got = pk.schedule_qo_rows_host(qi, kv, H, W, 32, fixed)
+    ref = qo_rows_ref(qi, kv, H, W, 32, fixed)
+    for g, r in zip(got[:4], ref[:4]):
+        np.testing.assert_array_equal(g, r)
+    assert got[4] == ref[4]
+    assert got[5] == qo_uses_rows(qi, H)
+
+
+@pytest.mark.parametrize("layout,H,code", [
+    (7, 16, pk.EINVAL),                      # unknown layout
+    (pk.QO_ROW_BLOCKS, 64, pk.EUNSUPPORTED),  # row blocks need 16 or 32 heads
+    (pk.QO_ROW_BLOCKS, 128, pk.EUNSUPPORTED),
+])
+def test_plan_qo_layout_rejects(layout, H, code):
+    with pytest.raises(pk.PkvmlaError) as e:
+        pk.plan_qo([0, 2, 3], [0, 2, 3], [0, 1, 2], [20, 5], H, 16, 4, layout=layout)
+    assert e.value.code == code
+
+
+def test_qo_row_schedule_host_rejects():
+    with pytest.raises(pk.PkvmlaError) as e:
+        pk.schedule_qo_rows_host([0, 2], [10], 64, 8)
+    assert e.value.code == pk.EUNSUPPORTED
+    with pytest.raises(pk.PkvmlaError) as e:
+        pk.schedule_qo_rows_host([0, 11], [10], 16, 8)      # more tokens than kv_len
+    assert e.value.code == pk.EINVAL

@@ -418,7 +418,7 @@ def test_qo_decode(name):
 def test_qo_stress_and_export(H, ps):
     inp = stress_variant(make_qo("qs", 137 + H, 4, H, ps, [4, 70, 300, 1500], [4, 2, 3, 4]), "qx8")
     note(f"qo stress H{H} ps{ps}")
-    plan = pk.plan_for(inp)
+    plan = pk.plan_for(inp, qo_layout=pk.QO_TOKENS)
     out, lse = run_gpu(plan, Dev(inp))
     compare(out, lse, *oracle_qo(inp), name=f"qo qx8 H{H}")
     # the uploaded schedule is the rule's, one item per query row
@@ -432,3 +432,99 @@ def test_qo_stress_and_export(H, ps):
     np.testing.assert_array_equal(ex.wg_indptr, wg)
     np.testing.assert_array_equal(ex.units, units)
     np.testing.assert_array_equal(ex.merges, merges)
+
+
+# Row blocks of query tokens (16 and 32 heads): each case runs in both
+# layouts, each checked against the oracle; the row-block plan's tables are
+# checked against the oracle's schedule re-derivation bit for bit.
+QO_ROW_CASES = {
+    "h16_qo4_ps1": lambda: make_qo("r1", 141, 4, 16, 1, [4, 31, 33, 300], [4] * 4),
+    "h16_qo3_ps16": lambda: make_qo("r2", 142, 5, 16, 16, [3, 17, 64, 200, 777], [3] * 5),
+    "h32_mixed_ps8": QO_CASES["h32_mixed_ps8"],
+    "h32_qo2_ps64": lambda: make_qo("r3", 143, 3, 32, 64, [2, 700, 2049], [2, 2, 2]),
+    # one request's 40 tokens (10 blocks) over 640 tokens split in 32-token
+    # pieces: the first tokens see no token of the last piece at all
+    "h16_masked_pieces_ps16": lambda: make_qo("r4", 144, 3, 16, 16, [640, 100, 90], [40, 1, 6]),
+    "h32_masked_pieces_ps1": lambda: make_qo("r5", 145, 2, 32, 1, [400, 33], [36, 2]),
+    # partial blocks: 5 tokens at 16 heads (80 rows), 3 at 32 (96 rows)
+    "h16_h32_tails": lambda: make_qo("r6", 146, 4, 16, 32, [5, 900, 63, 64], [5, 5, 2, 7]),
+}
+
+
+def qo_row_tables_ref(inp, num_cu):
+    from oracle.schedule_ref import qo_rows_ref
+    return qo_rows_ref(inp.qo_indptr, inp.kv_lens, inp.num_heads, num_cu,
+                       pages=(inp.kv_indptr, inp.kv_indices, inp.page_size))
+
+
+def fully_masked_waves(units, H):
+    """Waves (16 rows of one token) of row-block units that see no token of
+    their piece."""
+    n = 0
+    for r0, c, k0, k1, _, r1, _, _ in units.tolist():
+        for w in range(4):
+            row = r0 + 16 * w
+            if row < r1 and (row // H) + c <= k0:
+                n += 1
+    return n
+
+
+@pytest.mark.parametrize("name", sorted(QO_ROW_CASES))
+def test_qo_row_blocks(name):
+    from oracle.schedule_ref import QO_ROWS_DIRECT
+    inp = QO_ROW_CASES[name]()
+    H = inp.num_heads
+    note(f"qo rows {name}: {int(inp.qo_indptr[-1])} query tokens, H{H}")
+    d = Dev(inp)
+    ref_o, ref_l = oracle_qo(inp)
+    plan = pk.plan_for(inp, qo_layout=pk.QO_ROW_BLOCKS)
+    ex = plan.export()
+    assert int(ex.header[26]) == 2 and int(ex.header[27]) == inp.batch
+    wg, units, merges, slot_list, n_slots = qo_row_tables_ref(inp, ex.num_cu)
+    np.testing.assert_array_equal(ex.wg_indptr0, wg)
+    np.testing.assert_array_equal(ex.units0, units)
+    np.testing.assert_array_equal(ex.merges, merges)
+    np.testing.assert_array_equal(ex.slot_list, slot_list)
+    assert ex.units.shape[0] == 0 and int(ex.header[15]) == n_slots
+    if "masked" in name:
+        assert fully_masked_waves(units, H) > 0
+        assert (units[:, 4] != QO_ROWS_DIRECT).any()
+    out, lse = run_gpu(plan, d)
+    compare(out, lse, ref_o, ref_l, name=f"qo rows {name}")
+    # the same inputs one item per token
+    out2, lse2 = run_gpu(pk.plan_for(inp, qo_layout=pk.QO_TOKENS), d)
+    compare(out2, lse2, ref_o, ref_l, name=f"qo tokens {name}")
+
+
+@pytest.mark.parametrize("kind", STRESS_KINDS)
+def test_qo_row_blocks_stress(kind):
+    inp = stress_variant(make_qo("rs", 147, 4, 16, 16, [4, 70, 300, 1500], [4, 9, 3, 16]), kind)
+    note(f"qo rows stress {kind}")
+    plan = pk.plan_for(inp, qo_layout=pk.QO_ROW_BLOCKS)
+    out, lse = run_gpu(plan, Dev(inp))
+    compare(out, lse, *oracle_qo(inp), name=f"qo rows {kind}")
+
+
+def test_qo_row_blocks_poison_permutation_bit_identity():
+    """Pages no table names hold NaN and the pool is permuted: the outputs
+    are bit-identical to the plain layout's."""
+    base = make_qo("rp", 148, 3, 32, 16, [64, 500, 333], [3, 8, 2])
+    note("qo rows poison + permutation")
+    o1, l1 = run_gpu(pk.plan_for(base, qo_layout=pk.QO_ROW_BLOCKS), Dev(base))
+    alt = poison_unreferenced(permute_pages(base, 5))
+    o2, l2 = run_gpu(pk.plan_for(alt, qo_layout=pk.QO_ROW_BLOCKS), Dev(alt))
+    assert np.array_equal(bits_of(o1), bits_of(o2))
+    assert torch.equal(l1, l2)
+
+
+def test_qo_row_blocks_full_size():
+    """64 requests of 4 new tokens at 16 heads, kv_len uniform in
+    [1024, 4096], page size 64: every query row against the oracle."""
+    rng = np.random.default_rng(149)
+    lens = rng.integers(1024, 4096, size=64, endpoint=True)
+    inp = make_qo("rf", 149, 64, 16, 64, lens.tolist(), [4] * 64)
+    note("qo rows full size B64 H16 qo4")
+    plan = pk.plan_for(inp)
+    assert int(plan.export().header[26]) == 2        # the rule picks row blocks
+    out, lse = run_gpu(plan, Dev(inp))
+    compare(out, lse, *oracle_qo(inp), name="qo rows full size")

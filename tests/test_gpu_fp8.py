@@ -11,9 +11,9 @@ import numpy as np
 import pytest
 import torch
 
-from mla_workloads import (make_flat, make_cascade, make_config, stress_variant, quantize_kv_fp8,
-                           poison_unreferenced, permute_pages)
-from gpu_helpers import Dev, run_gpu, oracle_flat, oracle_cascade, compare, bits_of
+from mla_workloads import (make_flat, make_cascade, make_config, make_qo, stress_variant,
+                           quantize_kv_fp8, poison_unreferenced, permute_pages)
+from gpu_helpers import Dev, run_gpu, oracle_flat, oracle_cascade, oracle_qo, compare, bits_of
 
 pytestmark = pytest.mark.gpu
 
@@ -132,3 +132,14 @@ def test_fp8_rejects():
         plan.run(b.q_nope, b.q_pe, b.ckv, b.kpe, kv_scales=(1.0, 1.0))
     with pytest.raises(ValueError):                  # fp8 caches without scales
         plan.run(d.q_nope, d.q_pe, d.ckv, d.kpe)
+
+
+@pytest.mark.parametrize("layout", ["tokens", "rows"])
+def test_fp8_several_query_tokens(layout):
+    """fp8 caches under a plan with several query tokens per request, in both
+    layouts (row blocks include pieces some tokens see nothing of)."""
+    inp = q8(make_qo("e8", 611, 3, 16, 16, [640, 100, 90], [40, 1, 6]))
+    note(f"fp8 qo {layout}")
+    lay = pk.QO_ROW_BLOCKS if layout == "rows" else pk.QO_TOKENS
+    out, lse = run_gpu(pk.plan_for(inp, qo_layout=lay), Dev(inp, fp8=True))
+    compare(out, lse, *oracle_qo(inp, fp8=True), name=f"fp8 qo {layout}")

@@ -117,3 +117,29 @@ def test_page_permutation_invariance():
     out, lse = _qo(inp)
     o2, l2 = _qo(permute_pages(inp, seed=5))
     assert np.array_equal(out, o2) and np.array_equal(lse, l2)
+
+
+def test_fp8_caches_reduce_to_flat_fp8_at_each_causal_length():
+    """With E4M3 caches, query token j of request b equals the flat oracle's
+    fp8 decode of that token's query over the first kv_len - n + 1 + j tokens
+    of b's pages (the flat fp8 path has its own pins)."""
+    from mla_workloads import quantize_kv_fp8
+    inp = quantize_kv_fp8(make_qo("q8", 35, 3, 16, 8, [7, 40, 65], [3, 4, 2]), 0.02, 0.03)
+    sc = (inp.ckv_scale, inp.kpe_scale)
+    out, lse = oracle.attend_qo(inp.q_nope, inp.q_pe, inp.ckv8, inp.kpe8, inp.qo_indptr,
+                                inp.kv_indptr, inp.kv_indices, inp.kv_lens, inp.page_size,
+                                kv_scales=sc)
+    ref_b, _ = oracle.attend_qo(inp.q_nope, inp.q_pe, inp.ckv, inp.kpe, inp.qo_indptr,
+                                inp.kv_indptr, inp.kv_indices, inp.kv_lens, inp.page_size)
+    assert not np.allclose(out, ref_b, atol=1e-9)       # the codes, not the bf16 values
+    for b in range(inp.batch):
+        n = int(inp.qo_indptr[b + 1] - inp.qo_indptr[b])
+        for j in range(n):
+            row = int(inp.qo_indptr[b]) + j
+            L = int(inp.kv_lens[b]) - n + 1 + j
+            o, l = oracle.attend_flat(inp.q_nope[row:row + 1], inp.q_pe[row:row + 1], inp.ckv8,
+                                      inp.kpe8, np.array([0, inp.kv_indptr[b + 1] - inp.kv_indptr[b]]),
+                                      inp.kv_indices[inp.kv_indptr[b]:inp.kv_indptr[b + 1]],
+                                      np.array([L]), inp.page_size, kv_scales=sc)
+            np.testing.assert_allclose(out[row], o[0], atol=1e-12, rtol=0)
+            np.testing.assert_allclose(lse[row], l[0], atol=1e-12, rtol=0)

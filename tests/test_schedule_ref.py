@@ -177,15 +177,15 @@ def test_unit_page_fields_hand_case():
 
 
 def test_qo_rows_layout_rule_hand_cases():
-    """Row blocks when H <= 32 and the 64-row blocks average more than half full."""
+    """Row blocks at 16 or 32 heads when some request has two or more tokens."""
     from oracle.schedule_ref import qo_uses_rows
-    assert not qo_uses_rows([0, 2], 16)          # 32 rows in one block: exactly half
-    assert qo_uses_rows([0, 3], 16)              # 48 rows in one block
-    assert not qo_uses_rows([0, 1], 32)          # 32 rows in one block
-    assert qo_uses_rows([0, 2], 32)              # one full block
+    assert qo_uses_rows([0, 2], 16)
+    assert not qo_uses_rows([0, 1], 32)          # one token: a plain decode
+    assert not qo_uses_rows([0, 1, 2, 3], 16)    # one token each
+    assert qo_uses_rows([0, 2], 32)
     assert not qo_uses_rows([0, 4], 64)          # 64 heads or more: one item per token
-    assert not qo_uses_rows([0, 1, 2, 3, 8], 16)  # 128 rows in 5 blocks (< 160)
-    assert qo_uses_rows([0, 1, 2, 10], 16)       # 160 rows in 4 blocks (> 128)
+    assert not qo_uses_rows([0, 4], 128)
+    assert qo_uses_rows([0, 1, 2, 3, 5], 16)     # one request with two tokens
 
 
 def test_qo_rows_schedule_hand_case():
