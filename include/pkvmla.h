@@ -153,7 +153,7 @@ enum {
  *   PKVMLA_QO_ROW_BLOCKS (num_heads 16 or 32, else PKVMLA_EUNSUPPORTED): the
  *   query rows t * H + h of request b's tokens are cut into blocks of 64 rows
  *   (64 / H tokens each, the last block possibly short); a block is one work
- *   item over the request's whole sequence, split over lanes like a flat
+ *   item over the positions its last token sees, split over lanes like a flat
  *   request, and every 64-row workgroup scores each KV tile once for all of
  *   its tokens, each row masked at its own causal bound.  A block left whole
  *   writes out and lse itself; a split one writes a partial state per token
@@ -378,8 +378,9 @@ int pkvmla_schedule_chain_host(const int32_t* group_req_indptr, int32_t num_grou
  * (PKVMLA_QO_ROW_BLOCKS), computed on the host exactly as the plan does (no
  * GPU needed; a plan uses num_wg = CUs, fixed_cost = 4, tile = 32).  Request
  * b's rows [qo_indptr[b] * H, qo_indptr[b+1] * H) are cut into blocks of 64
- * rows in request order; block k is the work item (k, b, kv_lens[b]) of
- * pkvmla_schedule_host's walk.  Each walk unit becomes the record
+ * rows in request order; block k is the work item (k, b, t_last + c_b) of
+ * pkvmla_schedule_host's walk, t_last being the block's last token (the
+ * positions it sees; no row of the block sees more).  Each walk unit becomes the record
  * (row0, c_b, kv_begin, kv_end, slot field, row_end, 0, 0) with
  * c_b = kv_lens[b] - qo_len(b) + 1 - qo_indptr[b] (query token t, rows
  * t * H .. t * H + H - 1, attends the positions below t + c_b) and slot field

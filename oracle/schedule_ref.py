@@ -94,9 +94,10 @@ def qo_rows_ref(qo_indptr, kv_lens, num_heads: int, num_wg: int, tile: int = PLA
 
     * request b's rows [qo_indptr[b] * H, qo_indptr[b+1] * H) are cut into
       blocks of 64 (the last may be short), in request order; block k of
-      request b is a work item (k, b, kv_lens[b]) of the flat walk
-      (schedule_ref, batch = number of blocks, the 64-row kernel's fixed cost):
-      every block attends its whole sequence, the causal bound is per row;
+      request b is a work item (k, b, t_last + c_b) of the flat walk
+      (schedule_ref, batch = number of blocks, the 64-row kernel's fixed cost),
+      t_last being the block's last token: the positions its last token sees,
+      the most any of its rows sees (the causal bound itself is per row);
     * each walk unit (k, b, kv_begin, kv_end, slot) becomes the record
       (row0, c_b, kv_begin, kv_end, slot field, row_end, page fields) with
       c_b = kv_lens[b] - n_b + 1 - qo_indptr[b], so that token t
@@ -120,7 +121,10 @@ def qo_rows_ref(qo_indptr, kv_lens, num_heads: int, num_wg: int, tile: int = PLA
         lo, hi = int(qo_indptr[b]) * H, int(qo_indptr[b + 1]) * H
         for r in range(lo, hi, QO_BLOCK_ROWS):
             blocks.append((b, r, min(r + QO_BLOCK_ROWS, hi)))
-    items = [(k, b, int(kv_lens[b])) for k, (b, _, _) in enumerate(blocks)]
+    def reach(b, r1):     # positions seen by the block's last token (rows .. r1 - 1)
+        n = int(qo_indptr[b + 1]) - int(qo_indptr[b])
+        return (r1 // H - 1) + int(kv_lens[b]) - n + 1 - int(qo_indptr[b])
+    items = [(k, b, reach(b, r1)) for k, (b, _, r1) in enumerate(blocks)]
     wg, fu, fm = schedule_ref(items, len(blocks), num_wg, tile, fixed)
     units = np.zeros_like(fu)
     walk_slots = 0

@@ -287,7 +287,8 @@ bool qo_uses_row_blocks(const int32_t* qo_indptr, int32_t batch, int32_t num_hea
 }
 
 // Row blocks of several new tokens per request.  The blocks are the work items
-// of the flat walk (item k over its request's sequence, whole KV length); its
+// of the flat walk (item k over its request's sequence, up to the positions its
+// last token sees: no tile past them has a visible position for any row); its
 // units and merges are then rewritten for rows: slot field kRowsDirectSlot for
 // a whole block, else walk slot * 64 - row0 (so walk slot s holds the 64 / H
 // partial slots of H rows from s * 64 / H on, one per token of the block); a
@@ -306,9 +307,12 @@ bool build_qo_row_schedule(const int32_t* qo_indptr, const int32_t* kv_lens, int
     const int64_t lo = (int64_t)qo_indptr[b] * num_heads;
     const int64_t hi = (int64_t)qo_indptr[b + 1] * num_heads;
     if (hi > INT32_MAX) return false;
+    const int32_t c = kv_lens[b] - (qo_indptr[b + 1] - qo_indptr[b]) + 1 - qo_indptr[b];
     for (int64_t r = lo; r < hi; r += kQoBlockRows) {
-      items.push_back(WorkItem{(int32_t)blocks.size(), b, kv_lens[b]});
-      blocks.push_back(Block{b, (int32_t)r, (int32_t)std::min<int64_t>(r + kQoBlockRows, hi)});
+      const int32_t r1 = (int32_t)std::min<int64_t>(r + kQoBlockRows, hi);
+      // the block's work ends where its last token's causal range ends
+      items.push_back(WorkItem{(int32_t)blocks.size(), b, r1 / num_heads - 1 + c});
+      blocks.push_back(Block{b, (int32_t)r, r1});
     }
   }
   Schedule flat;

@@ -77,8 +77,8 @@ void build_cascade_merges(const RowSchedule& l0, const std::vector<int32_t>& l1_
 
 // Several new query tokens per request as row blocks (16 or 32 heads): request
 // b's query rows t * H + h (its tokens t = qo_indptr[b] .. qo_indptr[b+1] - 1)
-// in blocks of 64, each block over the request's whole KV length with the
-// causal bound per row.  The layout is used when some request brings more
+// in blocks of 64, each block over the positions its last token sees, with
+// the causal bound per row.  The layout is used when some request brings more
 // than one token (qo_indptr[batch] > batch); otherwise the plan has one work
 // item per query token.
 constexpr int32_t kQoBlockRows = 64;
@@ -88,7 +88,8 @@ constexpr int32_t kRowsDirectSlot = INT32_MIN + 1;
 bool qo_uses_row_blocks(const int32_t* qo_indptr, int32_t batch, int32_t num_heads);
 
 // The row-block schedule: the blocks are the items of build_schedule's walk
-// (`fixed`: the 64-row kernel's cost per segment), whose units become records
+// (`fixed`: the 64-row kernel's cost per segment; length t_last + c_b, t_last
+// the block's last token), whose units become records
 // row0, c_b, kv_begin, kv_end, slot field, row_end, 0, 0 with
 // c_b = kv_lens[b] - n_b + 1 - qo_indptr[b] (token t sees the positions below
 // t + c_b) and slot field kRowsDirectSlot (a whole block) or

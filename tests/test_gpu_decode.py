@@ -442,9 +442,13 @@ QO_ROW_CASES = {
     "h16_qo3_ps16": lambda: make_qo("r2", 142, 5, 16, 16, [3, 17, 64, 200, 777], [3] * 5),
     "h32_mixed_ps8": QO_CASES["h32_mixed_ps8"],
     "h32_qo2_ps64": lambda: make_qo("r3", 143, 3, 32, 64, [2, 700, 2049], [2, 2, 2]),
-    # one request's 40 tokens (10 blocks) over 640 tokens split in 32-token
-    # pieces: the first tokens see no token of the last piece at all
-    "h16_masked_pieces_ps16": lambda: make_qo("r4", 144, 3, 16, 16, [640, 100, 90], [40, 1, 6]),
+    # one request's 40 tokens (10 blocks) over 101 positions, split in
+    # 32-token pieces: a block's last piece can start past its first tokens'
+    # reach, so they see no token of it at all
+    "h16_masked_pieces_ps16": lambda: make_qo("r4", 144, 3, 16, 16, [101, 100, 90], [40, 1, 6]),
+    # a prefill (every token new) beside decodes: early blocks stop early
+    "h16_prefill_mix_ps16": lambda: make_qo("r7", 150, 4, 16, 16, [512, 300, 90, 700],
+                                            [512, 1, 6, 1]),
     "h32_masked_pieces_ps1": lambda: make_qo("r5", 145, 2, 32, 1, [400, 33], [36, 2]),
     # partial blocks: 5 tokens at 16 heads (80 rows), 3 at 32 (96 rows)
     "h16_h32_tails": lambda: make_qo("r6", 146, 4, 16, 32, [5, 900, 63, 64], [5, 5, 2, 7]),

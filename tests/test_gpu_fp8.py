@@ -138,7 +138,7 @@ def test_fp8_rejects():
 def test_fp8_several_query_tokens(layout):
     """fp8 caches under a plan with several query tokens per request, in both
     layouts (row blocks include pieces some tokens see nothing of)."""
-    inp = q8(make_qo("e8", 611, 3, 16, 16, [640, 100, 90], [40, 1, 6]))
+    inp = q8(make_qo("e8", 611, 3, 16, 16, [101, 100, 90], [40, 1, 6]))
     note(f"fp8 qo {layout}")
     lay = pk.QO_ROW_BLOCKS if layout == "rows" else pk.QO_TOKENS
     out, lse = run_gpu(pk.plan_for(inp, qo_layout=lay), Dev(inp, fp8=True))

@@ -190,16 +190,17 @@ def test_qo_rows_layout_rule_hand_cases():
 
 def test_qo_rows_schedule_hand_case():
     """H = 16, requests with 5 and 2 new tokens, kv_lens 100 and 40, 8 lanes.
-    Blocks: rows [0, 64) and [64, 80) of request 0, [80, 112) of request 1;
-    items of 4, 4 and 2 tiles at fixed cost 4, C = 22.  cap 5 (one tile per
-    unit) needs 10 lanes, cap 6 (two tiles) needs 5: request 0's blocks are cut
-    at token 64 into walk slots 0, 1 and 2, 3; the last block stays whole.
-    Causal offsets: 100 - 5 + 1 - 0 = 96 and 40 - 2 + 1 - 5 = 34."""
+    Blocks: rows [0, 64) and [64, 80) of request 0, [80, 112) of request 1.
+    Causal offsets: 100 - 5 + 1 - 0 = 96 and 40 - 2 + 1 - 5 = 34, so the
+    blocks' last tokens 3, 4 and 6 reach 99, 100 and 40 positions: items of
+    4, 4 and 2 tiles at fixed cost 4, C = 22.  cap 5 (one tile per unit)
+    needs 10 lanes, cap 6 (two tiles) needs 5: request 0's blocks are cut at
+    position 64 into walk slots 0, 1 and 2, 3; the last block stays whole."""
     from oracle.schedule_ref import qo_rows_ref, QO_ROWS_DIRECT
     wg, units, merges, slot_list, n_slots = qo_rows_ref([0, 5, 7], [100, 40], 16, 8)
     assert wg.tolist() == [0, 1, 2, 3, 4, 5]
     assert [u[:6] for u in units.tolist()] == [
-        [0, 96, 0, 64, 0, 64], [0, 96, 64, 100, 64, 64],
+        [0, 96, 0, 64, 0, 64], [0, 96, 64, 99, 64, 64],
         [64, 96, 0, 64, 64, 80], [64, 96, 64, 100, 128, 80],
         [80, 34, 0, 40, QO_ROWS_DIRECT, 112]]
     # four 16-row slots per walk slot: token t of block 0 sits in slots t and
@@ -212,10 +213,11 @@ def test_qo_rows_schedule_hand_case():
 
 @pytest.mark.parametrize("seed", range(40))
 def test_qo_rows_schedule_invariants(seed):
-    """Any qo row-block schedule: each token's causal range [0, t + c) lies
-    inside its block's token cover, which the block's pieces tile exactly
-    once; every partial row is written by exactly one (piece, token) and read
-    by that token's merge alone; whole blocks have no merge."""
+    """Any qo row-block schedule: the block's pieces tile [0, t_last + c)
+    exactly once, t_last being its last token (so every row's causal range
+    [0, t + c) is covered and no tile lies wholly past all of them); every
+    partial row is written by exactly one (piece, token) and read by that
+    token's merge alone; whole blocks have no merge."""
     from oracle.schedule_ref import qo_rows_ref, QO_ROWS_DIRECT
     rng = np.random.default_rng(seed)
     H = int(rng.choice([16, 32]))
@@ -240,10 +242,11 @@ def test_qo_rows_schedule_invariants(seed):
                 assert (sl + t * H) % H == 0 and 0 <= s < n_slots
                 assert s not in writers
                 writers[s] = t
+    ends = {u[0]: (u[5], u[1]) for u in units.tolist()}
     for r0, pieces in cover.items():
         pieces.sort()
-        b = int(np.searchsorted(qo_indptr * H, r0, side="right")) - 1
-        assert pieces[0][0] == 0 and pieces[-1][1] == int(kv[b])
+        r1, c = ends[r0]
+        assert pieces[0][0] == 0 and pieces[-1][1] == (r1 // H - 1) + c
         assert all(pieces[i][1] == pieces[i + 1][0] for i in range(len(pieces) - 1))
         assert (len(pieces) == 1) == (pieces[0][2] == QO_ROWS_DIRECT)
     merged = {}
