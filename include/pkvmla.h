@@ -131,8 +131,8 @@ int pkvmla_plan_update(pkvmla_plan plan, const int32_t* kv_indptr, const int32_t
  * q_nope [qo_indptr[batch], num_heads, 512], q_pe [.., 64], out [.., 512],
  * lse [qo_indptr[batch], num_heads], row qo_indptr[b] + j for token j of b.
  * The layout is chosen as pkvmla_plan_create_qo_layout does with
- * PKVMLA_QO_AUTO.  Plans of this kind take no page-table update
- * (PKVMLA_EUNSUPPORTED). */
+ * PKVMLA_QO_AUTO.  Plans of this kind are updated in place with
+ * pkvmla_plan_update_qo (pkvmla_plan_update refuses them). */
 int pkvmla_plan_create_qo(const int32_t* qo_indptr, const int32_t* kv_indptr,
                           const int32_t* kv_indices, const int32_t* kv_lens, int32_t batch,
                           int32_t num_pages, int32_t num_heads, int32_t ckv_dim, int32_t kpe_dim,
@@ -170,6 +170,31 @@ int pkvmla_plan_create_qo_layout(const int32_t* qo_indptr, const int32_t* kv_ind
                                  int32_t num_pages, int32_t num_heads, int32_t ckv_dim,
                                  int32_t kpe_dim, int32_t page_size, float sm_scale,
                                  int32_t layout, void* stream, pkvmla_plan* out);
+
+/* pkvmla_plan_create_qo_layout sized for later pkvmla_plan_update_qo calls
+ * (index_capacity > 0: page ids the device table holds, at least the first
+ * table's; 0 is pkvmla_plan_create_qo_layout).  The "[WIP][Kernel] Flashinfer
+ * MLA support" page reports graph capture of the MLA decode path as broken;
+ * a plan with a capacity keeps its device tables, split workspace and
+ * launch shapes, sized for any split of the same qo_indptr[batch] query
+ * tokens over the same batch, so a HIP graph captured around its run stays
+ * valid across updates (as for pkvmla_plan_create_with_capacity). */
+int pkvmla_plan_create_qo_with_capacity(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                                        const int32_t* kv_indices, const int32_t* kv_lens,
+                                        int32_t batch, int32_t num_pages, int32_t num_heads,
+                                        int32_t ckv_dim, int32_t kpe_dim, int32_t page_size,
+                                        float sm_scale, int32_t layout, int64_t index_capacity,
+                                        void* stream, pkvmla_plan* out);
+
+/* Rewrite a plan of several query tokens per request in place for new page
+ * tables and a new split of its query tokens: the same batch, the same total
+ * qo_indptr[batch] (the run's tensors keep their shapes), each request 1 ..
+ * kv_lens[b] tokens.  The plan keeps its layout (as pkvmla_plan_export header
+ * word 26 reports it).  Ordering and capacity rules as pkvmla_plan_update;
+ * PKVMLA_EINVAL for a different token count, malformed arrays or a table
+ * beyond the plan's capacities (the plan is then unchanged). */
+int pkvmla_plan_update_qo(pkvmla_plan plan, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                          const int32_t* kv_indices, const int32_t* kv_lens, void* stream);
 
 /* Build a two-level (cascade) plan.  Requests are partitioned into
  * num_groups contiguous groups by group_req_indptr (host int32[G+1], from 0

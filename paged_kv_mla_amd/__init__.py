@@ -61,6 +61,11 @@ _lib.pkvmla_plan_create_qo_layout.argtypes = [_i32p, _i32p, _i32p, _i32p, ctypes
                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
                                               ctypes.c_int32, _vp, ctypes.POINTER(_vp)]
+_lib.pkvmla_plan_create_qo_with_capacity.argtypes = [
+    _i32p, _i32p, _i32p, _i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+    ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_int64, _vp,
+    ctypes.POINTER(_vp)]
+_lib.pkvmla_plan_update_qo.argtypes = [_vp, _i32p, _i32p, _i32p, _i32p, _vp]
 _lib.pkvmla_schedule_qo_rows_host.argtypes = [_i32p, _i32p, ctypes.c_int32, ctypes.c_int32,
                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                               _i32p, ctypes.c_int64, _i32p, ctypes.c_int64,
@@ -101,6 +106,7 @@ EXPORTED_SYMBOLS = (
     "pkvmla_run_noalloc", "pkvmla_plan_create_qo", "pkvmla_schedule_rows_host",
     "pkvmla_plan_create_cascade_with_capacity", "pkvmla_plan_update_cascade", "pkvmla_run_fp8",
     "pkvmla_schedule_chain_host", "pkvmla_plan_create_qo_layout", "pkvmla_schedule_qo_rows_host",
+    "pkvmla_plan_create_qo_with_capacity", "pkvmla_plan_update_qo",
 )
 
 # work layouts of a plan with several query tokens per request
@@ -386,6 +392,25 @@ class Plan:
                                                _ptr(ip), _ptr(ix), _ptr(ln),
                                                _stream_handle(stream)))
 
+    def update_qo(self, qo_indptr, kv_indptr, kv_indices, kv_lens, stream=None) -> None:
+        """Replace the page tables and token split of a plan with several query
+        tokens per request in place (same number of requests and of query
+        tokens), as :meth:`update` does for flat plans."""
+        qi = _i32(qo_indptr)
+        ip, ix, ln = _i32(kv_indptr), _i32(kv_indices), _i32(kv_lens)
+        _check_csr("kv", ip, ix, ln)
+        nreq = getattr(self, "num_requests", None)
+        if nreq is None:
+            raise ValueError("update_qo needs a plan built by plan_qo")
+        if len(ln) != nreq or qi.ndim != 1 or len(qi) != nreq + 1:
+            raise ValueError(f"update_qo needs {nreq} requests and {nreq + 1} qo_indptr entries")
+        if int(qi[-1]) != self.batch:
+            raise ValueError(f"update_qo needs {self.batch} query tokens (got {int(qi[-1])})")
+        if ix.size == 0:
+            ix = np.zeros(1, np.int32)
+        _check(_lib.pkvmla_plan_update_qo(self._h, _ptr(qi), _ptr(ip), _ptr(ix), _ptr(ln),
+                                          _stream_handle(stream)))
+
     def run_ptrs(self, q_nope: int, q_pe: int, ckv: int, kpe: int, out: int, lse: int,
                  stream: int) -> None:
         """Raw-pointer form of :meth:`run` (no checks beyond the library's)."""
@@ -477,13 +502,16 @@ def plan(kv_indptr, kv_indices, kv_lens, num_heads: int, page_size: int, num_pag
 
 def plan_qo(qo_indptr, kv_indptr, kv_indices, kv_lens, num_heads: int, page_size: int,
             num_pages: int, ckv_dim: int = 512, kpe_dim: int = 64,
-            sm_scale: Optional[float] = None, stream=None, layout: int = QO_AUTO) -> Plan:
+            sm_scale: Optional[float] = None, stream=None, layout: int = QO_AUTO,
+            index_capacity: int = 0) -> Plan:
     """Plan with qo_indptr[b+1] - qo_indptr[b] new query tokens for request b,
     causal among them (they are the request's last tokens).  The run takes and
     returns one row per query token ([qo_indptr[-1], H, ...]); the Plan's
     ``batch`` is that row count.  ``layout``: QO_AUTO, QO_TOKENS (a work item
     per token) or QO_ROW_BLOCKS (16 or 32 heads: blocks of 64 query rows that
-    score each KV tile once for several tokens)."""
+    score each KV tile once for several tokens).  index_capacity > 0 sizes the
+    plan for :meth:`Plan.update_qo` (same batch and token count) and fixes its
+    launch shapes."""
     qi = _i32(qo_indptr)
     ip, ix, ln = _i32(kv_indptr), _i32(kv_indices), _i32(kv_lens)
     _check_csr("kv", ip, ix, ln)
@@ -492,12 +520,14 @@ def plan_qo(qo_indptr, kv_indptr, kv_indices, kv_lens, num_heads: int, page_size
     if ix.size == 0:
         ix = np.zeros(1, np.int32)
     h = ctypes.c_void_p()
-    _check(_lib.pkvmla_plan_create_qo_layout(
+    _check(_lib.pkvmla_plan_create_qo_with_capacity(
         _ptr(qi), _ptr(ip), _ptr(ix), _ptr(ln), int(len(ln)), int(num_pages), int(num_heads),
         int(ckv_dim), int(kpe_dim), int(page_size), float(sm_scale or 0.0), int(layout),
-        _stream_handle(stream) if stream else None, ctypes.byref(h)))
-    return Plan(h.value, int(qi[-1]), int(num_heads), int(page_size), int(num_pages),
-                _current_device())
+        int(index_capacity), _stream_handle(stream) if stream else None, ctypes.byref(h)))
+    p = Plan(h.value, int(qi[-1]), int(num_heads), int(page_size), int(num_pages),
+             _current_device())
+    p.num_requests = int(len(ln))
+    return p
 
 
 def _cascade_arrays(group_req_indptr, prefix_indptr, prefix_indices, prefix_lens, kv_indptr,

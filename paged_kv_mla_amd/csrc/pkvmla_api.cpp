@@ -335,6 +335,54 @@ struct QoRows {
 
 static_assert(pkvmla::kRowsDirect == pkvmla::kRowsDirectSlot, "direct row-block slot marker");
 
+// Query-token index of a plan with several new tokens per request: every
+// request brings 1 .. kv_len of them.
+int check_qo(const int32_t* qo_indptr, const int32_t* kv_lens, int32_t batch) {
+  if (!qo_indptr) return fail(PKVMLA_EINVAL, "null qo_indptr");
+  if (qo_indptr[0] != 0) return fail(PKVMLA_EINVAL, "qo_indptr[0] must be 0");
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t n = (int64_t)qo_indptr[b + 1] - qo_indptr[b];
+    if (n < 1) return fail(PKVMLA_EINVAL, "request %d has %lld query tokens (>= 1 needed)", b, (long long)n);
+    if (n > kv_lens[b])
+      return fail(PKVMLA_EINVAL, "request %d: %lld query tokens but kv_len %d (the new tokens are part "
+                  "of the KV)", b, (long long)n, kv_lens[b]);
+  }
+  return PKVMLA_OK;
+}
+
+// One work item per query token: row qo_indptr[b] + j over sequence b, of its
+// causal length (position + 1).
+std::vector<pkvmla::WorkItem> qo_token_items(const int32_t* qo_indptr, const int32_t* kv_lens,
+                                             int32_t batch) {
+  std::vector<pkvmla::WorkItem> items((size_t)qo_indptr[batch]);
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t n = qo_indptr[b + 1] - qo_indptr[b];
+    for (int32_t j = 0; j < n; ++j)
+      items[qo_indptr[b] + j] = pkvmla::WorkItem{qo_indptr[b] + j, b, kv_lens[b] - n + 1 + j};
+  }
+  return items;
+}
+
+// The tables of a row-block plan: its units in the level-0 table, merges per
+// query token over a slot list, no level-1 units.
+int build_qo_row_tables(const pkvmla_plan_s* P, const int32_t* qo_indptr, const int32_t* kv_lens,
+                        int32_t batch, const std::vector<int32_t>& seq_indptr,
+                        const std::vector<int32_t>& seq_indices, pkvmla::Schedule* sched,
+                        pkvmla::RowSchedule* sched0, std::vector<int32_t>* slot_list) {
+  std::vector<int32_t> unit_seq;
+  if (!pkvmla::build_qo_row_schedule(qo_indptr, kv_lens, batch, P->num_heads, P->cap_lanes0,
+                                     pkvmla::kTile, P->cfg0.fixed_cost, sched0, &unit_seq,
+                                     &sched->merges, slot_list))
+    return fail(PKVMLA_EUNSUPPORTED, "row-block schedule construction failed (too many query rows)");
+  fill_page_fields(&sched0->units, seq_indptr, seq_indices, P->page_size, &unit_seq);
+  sched->grid = 0;
+  sched->wg_indptr.assign(1, 0);
+  sched->units.clear();
+  sched->n_slots = sched0->n_slots;
+  sched->total_rows = 0;
+  return PKVMLA_OK;
+}
+
 bool chain_eligible(const pkvmla_plan_s* P, const Level0Groups& l0) {
   if (P->fixed_launch || P->num_heads < 64) return false;
   for (int32_t g = 0; g < l0.num_groups; ++g)
@@ -395,22 +443,27 @@ int finish_plan(pkvmla_plan_s* P, const std::vector<pkvmla::WorkItem>& items,
     // every unit in the level-0 table (row blocks of the 64-row kernel), no
     // level-1 units; merges per query token over slot lists
     P->cap_lanes0 = std::max(1, P->num_cu / P->cfg0.head_groups);
-    std::vector<int32_t> unit_seq;
-    if (!pkvmla::build_qo_row_schedule(qo->qo_indptr, qo->kv_lens, qo->num_requests,
-                                       P->num_heads, P->cap_lanes0, pkvmla::kTile,
-                                       P->cfg0.fixed_cost, &P->sched0, &unit_seq,
-                                       &P->sched.merges, &P->slot_list))
-      return fail(PKVMLA_EUNSUPPORTED, "row-block schedule construction failed (too many query rows)");
-    fill_page_fields(&P->sched0.units, seq_indptr, seq_indices, P->page_size, &unit_seq);
-    P->sched.grid = 0;
-    P->sched.wg_indptr.assign(1, 0);
-    P->sched.units.clear();
-    P->sched.n_slots = P->sched0.n_slots;
-    P->sched.total_rows = 0;
-    P->cap_units0 = (int32_t)(P->sched0.units.size() / pkvmla::kUnitRecordInts);
-    P->cap_slots = std::max(1, P->sched0.n_slots);
-    P->cap_list = (int32_t)P->slot_list.size();
-    rc = PKVMLA_OK;
+    rc = build_qo_row_tables(P, qo->qo_indptr, qo->kv_lens, qo->num_requests, seq_indptr,
+                             seq_indices, &P->sched, &P->sched0, &P->slot_list);
+    if (rc) return rc;
+    if (P->fixed_launch) {
+      // any query-token split of the same T tokens over the same B requests:
+      // blocks <= T * H / 64 + B, a unit per block plus one per lane cut, a
+      // walk slot per unit holding 64 / H partial slots, as many list entries
+      const int64_t per = pkvmla::kQoBlockRows / P->num_heads;
+      const int64_t blocks = ((int64_t)P->batch * P->num_heads + pkvmla::kQoBlockRows - 1) /
+                                 pkvmla::kQoBlockRows + qo->num_requests;
+      const int64_t units = blocks + P->cap_lanes0;
+      if (units * per > INT32_MAX / 2 || units > INT32_MAX / pkvmla::kUnitRecordInts)
+        return fail(PKVMLA_EUNSUPPORTED, "too many query rows for a plan with a capacity");
+      P->cap_units0 = (int32_t)units;
+      P->cap_slots = (int32_t)(units * per);
+      P->cap_list = (int32_t)(units * per);
+    } else {
+      P->cap_units0 = (int32_t)(P->sched0.units.size() / pkvmla::kUnitRecordInts);
+      P->cap_slots = std::max(1, P->sched0.n_slots);
+      P->cap_list = (int32_t)P->slot_list.size();
+    }
   } else {
     rc = build_plan_schedule(P, items, seq_indptr, seq_indices, &P->sched);
   }
@@ -677,9 +730,9 @@ int pkvmla_plan_create_qo(const int32_t* qo_indptr, const int32_t* kv_indptr,
                           const int32_t* kv_indices, const int32_t* kv_lens, int32_t batch,
                           int32_t num_pages, int32_t num_heads, int32_t ckv_dim, int32_t kpe_dim,
                           int32_t page_size, float sm_scale, void* stream, pkvmla_plan* out) {
-  return pkvmla_plan_create_qo_layout(qo_indptr, kv_indptr, kv_indices, kv_lens, batch,
-                                      num_pages, num_heads, ckv_dim, kpe_dim, page_size, sm_scale,
-                                      PKVMLA_QO_AUTO, stream, out);
+  return pkvmla_plan_create_qo_with_capacity(qo_indptr, kv_indptr, kv_indices, kv_lens, batch,
+                                             num_pages, num_heads, ckv_dim, kpe_dim, page_size,
+                                             sm_scale, PKVMLA_QO_AUTO, 0, stream, out);
 }
 
 int pkvmla_plan_create_qo_layout(const int32_t* qo_indptr, const int32_t* kv_indptr,
@@ -687,6 +740,17 @@ int pkvmla_plan_create_qo_layout(const int32_t* qo_indptr, const int32_t* kv_ind
                                  int32_t num_pages, int32_t num_heads, int32_t ckv_dim,
                                  int32_t kpe_dim, int32_t page_size, float sm_scale,
                                  int32_t layout, void* stream, pkvmla_plan* out) {
+  return pkvmla_plan_create_qo_with_capacity(qo_indptr, kv_indptr, kv_indices, kv_lens, batch,
+                                             num_pages, num_heads, ckv_dim, kpe_dim, page_size,
+                                             sm_scale, layout, 0, stream, out);
+}
+
+int pkvmla_plan_create_qo_with_capacity(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                                        const int32_t* kv_indices, const int32_t* kv_lens,
+                                        int32_t batch, int32_t num_pages, int32_t num_heads,
+                                        int32_t ckv_dim, int32_t kpe_dim, int32_t page_size,
+                                        float sm_scale, int32_t layout, int64_t index_capacity,
+                                        void* stream, pkvmla_plan* out) {
   if (!out) return fail(PKVMLA_EINVAL, "null plan output pointer");
   *out = nullptr;
   int32_t log2_ps;
@@ -696,15 +760,12 @@ int pkvmla_plan_create_qo_layout(const int32_t* qo_indptr, const int32_t* kv_ind
   if (rc) return rc;
   rc = check_pages("kv", kv_indptr, kv_indices, kv_lens, batch, num_pages, page_size, 1);
   if (rc) return rc;
-  if (!qo_indptr) return fail(PKVMLA_EINVAL, "null qo_indptr");
-  if (qo_indptr[0] != 0) return fail(PKVMLA_EINVAL, "qo_indptr[0] must be 0");
-  for (int32_t b = 0; b < batch; ++b) {
-    const int64_t n = (int64_t)qo_indptr[b + 1] - qo_indptr[b];
-    if (n < 1) return fail(PKVMLA_EINVAL, "request %d has %lld query tokens (>= 1 needed)", b, (long long)n);
-    if (n > kv_lens[b])
-      return fail(PKVMLA_EINVAL, "request %d: %lld query tokens but kv_len %d (the new tokens are part "
-                  "of the KV)", b, (long long)n, kv_lens[b]);
-  }
+  rc = check_qo(qo_indptr, kv_lens, batch);
+  if (rc) return rc;
+  if (index_capacity < 0) return fail(PKVMLA_EINVAL, "index_capacity must be >= 0");
+  if (index_capacity > 0 && index_capacity < kv_indptr[batch])
+    return fail(PKVMLA_EINVAL, "index_capacity %lld is below the table's %d page ids",
+                (long long)index_capacity, kv_indptr[batch]);
   if (layout != PKVMLA_QO_AUTO && layout != PKVMLA_QO_TOKENS && layout != PKVMLA_QO_ROW_BLOCKS)
     return fail(PKVMLA_EINVAL, "unknown query-token layout %d", layout);
   if (layout == PKVMLA_QO_ROW_BLOCKS && num_heads != 16 && num_heads != 32)
@@ -725,6 +786,8 @@ int pkvmla_plan_create_qo_layout(const int32_t* qo_indptr, const int32_t* kv_ind
   P->kpe_dim = kpe_dim;
   P->num_pages = num_pages;
   P->sm_scale = scale;
+  P->index_capacity_request = index_capacity;
+  P->fixed_launch = index_capacity > 0 ? 1 : 0;
   pkvmla::kernel_config_for(num_heads, &P->cfg);
   // Query row r = qo_indptr[b] + j sits at position kv_len - qo_len + j and
   // attends tokens 0 .. that position of request b's page list (causal among
@@ -741,12 +804,7 @@ int pkvmla_plan_create_qo_layout(const int32_t* qo_indptr, const int32_t* kv_ind
     const QoRows qr{qo_indptr, kv_lens, batch};
     rc = finish_plan(P, items, sip, sl, si, (hipStream_t)stream, nullptr, &qr);
   } else {
-    items.resize((size_t)rows);
-    for (int32_t b = 0; b < batch; ++b) {
-      const int32_t n = qo_indptr[b + 1] - qo_indptr[b];
-      for (int32_t j = 0; j < n; ++j)
-        items[qo_indptr[b] + j] = pkvmla::WorkItem{qo_indptr[b] + j, b, kv_lens[b] - n + 1 + j};
-    }
+    items = qo_token_items(qo_indptr, kv_lens, batch);
     rc = finish_plan(P, items, sip, sl, si, (hipStream_t)stream);
   }
   if (rc) {
@@ -772,7 +830,7 @@ int pkvmla_plan_update(pkvmla_plan P, const int32_t* kv_indptr, const int32_t* k
                        const int32_t* kv_lens, void* stream) {
   if (!P) return fail(PKVMLA_EINVAL, "null plan");
   if (P->is_cascade) return fail(PKVMLA_EINVAL, "a cascade plan is updated with pkvmla_plan_update_cascade");
-  if (P->is_qo) return fail(PKVMLA_EUNSUPPORTED, "update of a plan with several query tokens per request");
+  if (P->is_qo) return fail(PKVMLA_EINVAL, "a plan with several query tokens per request is updated with pkvmla_plan_update_qo");
   int rc = check_pages("kv", kv_indptr, kv_indices, kv_lens, P->batch, P->num_pages,
                        P->page_size, 1);
   if (rc) return rc;
@@ -796,6 +854,58 @@ int pkvmla_plan_update(pkvmla_plan P, const int32_t* kv_indptr, const int32_t* k
       sched.grid > P->cap_lanes || sched.n_slots > P->cap_units)
     return fail(PKVMLA_EINVAL, "schedule exceeds the plan's capacities");
   // the plan takes the new schedule only once its tables are on the device
+  rc = upload_tables(P, sched, sip, sl, si, (hipStream_t)stream);
+  if (rc) return rc;
+  P->sched = std::move(sched);
+  return ok();
+}
+
+int pkvmla_plan_update_qo(pkvmla_plan P, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                          const int32_t* kv_indices, const int32_t* kv_lens, void* stream) {
+  if (!P) return fail(PKVMLA_EINVAL, "null plan");
+  if (!P->is_qo) return fail(PKVMLA_EINVAL, "not a plan with several query tokens per request");
+  const int32_t B = P->num_requests;
+  int rc = check_pages("kv", kv_indptr, kv_indices, kv_lens, B, P->num_pages, P->page_size, 1);
+  if (rc) return rc;
+  rc = check_qo(qo_indptr, kv_lens, B);
+  if (rc) return rc;
+  if (qo_indptr[B] != P->batch)
+    return fail(PKVMLA_EINVAL, "%d query tokens, the plan's tensors have %d", qo_indptr[B], P->batch);
+  if ((int64_t)kv_indptr[B] > P->cap_indices)
+    return fail(PKVMLA_EINVAL, "%d page ids exceed the plan's capacity of %lld", kv_indptr[B],
+                (long long)P->cap_indices);
+  int dev = -1;
+  PKVMLA_HIP(hipGetDevice(&dev));
+  if (dev != P->device)
+    return fail(PKVMLA_EINVAL, "plan was built on device %d, current device is %d", P->device,
+                dev);
+  std::vector<int32_t> sip(kv_indptr, kv_indptr + B + 1);
+  std::vector<int32_t> sl(kv_lens, kv_lens + B);
+  std::vector<int32_t> si(kv_indices, kv_indices + kv_indptr[B]);
+  pkvmla::Schedule sched;
+  pkvmla::RowSchedule sched0;
+  std::vector<int32_t> list;
+  if (P->is_qo == 2) {
+    // the plan keeps its layout (row blocks) whatever the new split
+    rc = build_qo_row_tables(P, qo_indptr, kv_lens, B, sip, si, &sched, &sched0, &list);
+    if (rc) return rc;
+    if (sched0.grid > P->cap_lanes0 ||
+        (int64_t)sched0.units.size() > (int64_t)P->cap_units0 * pkvmla::kUnitRecordInts ||
+        sched.n_slots > P->cap_slots || (int64_t)list.size() > P->cap_list ||
+        (int64_t)sched.merges.size() > (int64_t)P->cap_merges * pkvmla::kMergeRecordInts)
+      return fail(PKVMLA_EINVAL, "schedule exceeds the plan's capacities");
+    rc = upload_tables(P, sched, sip, sl, si, (hipStream_t)stream, &sched0, &list);
+    if (rc) return rc;
+    P->sched = std::move(sched);
+    P->sched0 = std::move(sched0);
+    P->slot_list = std::move(list);
+    return ok();
+  }
+  rc = build_plan_schedule(P, qo_token_items(qo_indptr, kv_lens, B), sip, si, &sched);
+  if (rc) return rc;
+  if ((int64_t)sched.units.size() > (int64_t)P->cap_units * pkvmla::kUnitRecordInts ||
+      sched.grid > P->cap_lanes || sched.n_slots > P->cap_slots)
+    return fail(PKVMLA_EINVAL, "schedule exceeds the plan's capacities");
   rc = upload_tables(P, sched, sip, sl, si, (hipStream_t)stream);
   if (rc) return rc;
   P->sched = std::move(sched);
@@ -1054,7 +1164,8 @@ int run_impl(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* ck
   d.num_heads = P->num_heads;
   d.head_groups = P->cfg.head_groups;
   // lanes past the schedule's have no units (their workgroups return at once)
-  d.n_lanes = P->fixed_launch ? P->cap_lanes : P->sched.grid;
+  // (row-block plans of query tokens have every unit in the level-0 table)
+  d.n_lanes = P->is_qo == 2 ? 0 : P->fixed_launch ? P->cap_lanes : P->sched.grid;
   d.waves = P->cfg.waves;
   d.heads_per_wave = P->cfg.heads_per_wave;
   d.stages = P->cfg.stages;

@@ -210,3 +210,80 @@ def test_graph_replay_and_update_cascade(H, ps):
             assert torch.equal(out, ref_o), (step, rep)
             assert torch.equal(lse, ref_l), (step, rep)
         note(f"graph cascade step {step}: 3 replays bit-identical")
+
+
+@pytest.mark.parametrize("H,ps,layout", [(16, 16, "rows"), (32, 1, "rows"), (128, 64, "tokens"),
+                                         (16, 64, "tokens")])
+def test_graph_replay_and_update_qo(H, ps, layout):
+    """Several query tokens per request: one captured run serves new page
+    tables and new splits of the same 12 tokens over the same 4 requests."""
+    from mla_workloads import make_qo
+    from gpu_helpers import oracle_qo
+    lay = pk.QO_ROW_BLOCKS if layout == "rows" else pk.QO_TOKENS
+    specs = [([40, 333, 1000, 64], [3, 3, 3, 3]), ([700, 5, 129, 64], [1, 5, 2, 4]),
+             ([9, 64, 6, 1200], [6, 1, 1, 4])]
+    if ps == 1:
+        specs = [([40, 33, 100, 64], [3, 3, 3, 3]), ([70, 5, 29, 64], [1, 5, 2, 4]),
+                 ([9, 64, 6, 120], [6, 1, 1, 4])]
+    pool = 400                  # pages of every bundle's pool (same tensor shapes)
+    bundles = [make_qo(f"gq{i}", 220 + i, 4, H, ps, lens, qo, pool_pages=pool)
+               for i, (lens, qo) in enumerate(specs)]
+    cap = max(len(b.kv_indices) for b in bundles) + 7
+    A = bundles[0]
+    note(f"graph qo H={H} ps={ps} {layout} cap={cap}")
+    plan = pk.plan_qo(A.qo_indptr, A.kv_indptr, A.kv_indices, A.kv_lens, H, ps, pool,
+                      layout=lay, index_capacity=cap)
+    hdr = plan.export().header
+    assert hdr[24] == 1 and hdr[26] == (2 if layout == "rows" else 1)
+    dev = Dev(A)
+    T = int(A.qo_indptr[-1])
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    ref_o, ref_l = eager(plan, dev, out, lse, side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        plan.run(dev.q_nope, dev.q_pe, dev.ckv, dev.kpe, out=out, lse=lse, stream=side)
+    torch.cuda.synchronize()
+    for step, inp in enumerate(bundles + [A]):
+        if step > 0:
+            plan.update_qo(inp.qo_indptr, inp.kv_indptr, inp.kv_indices, inp.kv_lens, stream=side)
+            load_into(dev, inp)
+            torch.cuda.synchronize()
+            ref_o, ref_l = eager(plan, dev, out, lse, side)
+            fresh = pk.plan_qo(inp.qo_indptr, inp.kv_indptr, inp.kv_indices, inp.kv_lens, H, ps,
+                               pool, layout=lay)
+            fo, fl = eager(fresh, dev, torch.empty_like(out), torch.empty_like(lse), side)
+            assert torch.equal(fo, ref_o) and torch.equal(fl, ref_l)
+        compare(ref_o, ref_l, *oracle_qo(inp), name=f"qo update {step}")
+        for rep in range(3):
+            out.fill_(7.0)
+            lse.fill_(-1.0)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref_o), (step, rep)
+            assert torch.equal(lse, ref_l), (step, rep)
+        note(f"graph qo step {step}: 3 replays bit-identical")
+
+
+def test_update_qo_rejects():
+    from mla_workloads import make_qo
+    A = make_qo("gr", 230, 3, 16, 16, [50, 60, 70], [2, 3, 4], pool_pages=POOL)
+    plan = pk.plan_qo(A.qo_indptr, A.kv_indptr, A.kv_indices, A.kv_lens, 16, 16, POOL,
+                      index_capacity=len(A.kv_indices) + 4)
+    before = plan.export()
+    with pytest.raises(ValueError, match="query tokens"):
+        plan.update_qo([0, 2, 3, 5], A.kv_indptr, A.kv_indices, A.kv_lens)   # 5 tokens, not 9
+    lens = A.kv_lens.copy()
+    lens[2] = 3                                        # 4 tokens but kv_len 3
+    with pytest.raises(pk.PkvmlaError) as e:
+        plan.update_qo(A.qo_indptr, A.kv_indptr, A.kv_indices, lens)
+    assert e.value.code == pk.EINVAL
+    # the flat update refuses the plan
+    ip, ix, ln = (np.ascontiguousarray(x, dtype=np.int32)
+                  for x in (A.kv_indptr, A.kv_indices, A.kv_lens))
+    assert pk._lib.pkvmla_plan_update(plan._h, pk._ptr(ip), pk._ptr(ix), pk._ptr(ln), None) == pk.EINVAL
+    after = plan.export()
+    for f in ("wg_indptr0", "units0", "merges", "slot_list", "seq_lens", "seq_indices"):
+        assert np.array_equal(getattr(before, f), getattr(after, f)), f
