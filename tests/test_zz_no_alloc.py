@@ -70,3 +70,29 @@ def test_noalloc_refuses_a_workspace_beyond_the_scratch():
         plan.run_noalloc_ptrs(z.data_ptr(), z.data_ptr(), z.data_ptr(), z.data_ptr(),
                               z.data_ptr(), z.data_ptr(), 0)
     assert e.value.code == pk.EUNSUPPORTED and "scratch" in str(e.value)
+
+
+def test_noalloc_row_blocks_of_query_tokens():
+    """A row-block plan of several query tokens per request (partial rows at
+    an offset from each block's first row, per-token merges over slot lists)
+    through the static scratch: bitwise equal to the ordinary run."""
+    from mla_workloads import make_qo
+    from gpu_helpers import oracle_qo
+    inp = make_qo("na3", 303, 4, 16, 16, [101, 900, 64, 2000], [40, 3, 1, 6])
+    plan = pk.plan_for(inp, qo_layout=pk.QO_ROW_BLOCKS)
+    ex = plan.export()
+    assert int(ex.header[26]) == 2 and ex.merges.shape[0] > 0
+    d = Dev(inp)
+    T, H = int(inp.qo_indptr[-1]), inp.num_heads
+    o1, l1 = plan.run(d.q_nope, d.q_pe, d.ckv, d.kpe)
+    for rep in range(2):
+        o2 = torch.full((T, H, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+        l2 = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
+        plan.run_noalloc_ptrs(d.q_nope.data_ptr(), d.q_pe.data_ptr(), d.ckv.data_ptr(),
+                              d.kpe.data_ptr(), o2.data_ptr(), l2.data_ptr(),
+                              int(torch.cuda.current_stream().cuda_stream))
+        torch.cuda.synchronize()
+        note(f"noalloc qo rows, call {rep}")
+        assert np.array_equal(bits_of(o1), bits_of(o2))
+        assert torch.equal(l1, l2)
+    compare(o2, l2, *oracle_qo(inp), name="noalloc qo rows")
