@@ -11,15 +11,22 @@ as they would across the layers of a real model.  Inputs are seeded synthetic
 bf16 (N(0,1)*0.5) with the workload's shapes; they are resident in HBM before
 the timed region starts.  Prints one JSON line.
 
-Timing.  The timed region is K steps back to back with a HIP event recorded
-after every step (events created without the system-scope fence, so a record
-adds no cache write-back); ms_per_step is the mean, and the median and p10/p90
-of the per-step intervals are reported beside it.  A second pass of K steps
-runs with the library's kernel timing on: a HIP event pair around every decode
-launch on its own stream, and the kernel's own span (earliest wave start to
-latest wave end on the GPU's 100 MHz real-time counter).  The event interval
-also holds the dispatch gap before the kernel; the span does not, and is what
-a rocprofv3 kernel trace reports as the kernel's duration.
+Timing.  The timed region is K steps back to back between two HIP events
+(created without the system-scope fence); ms_per_step is their interval over
+K.  During those same K steps the library's timing records are on: every
+workgroup of every decode and merge launch stores its start and end on the
+GPU's 100 MHz real-time counter (plain stores to its own words: no events or
+atomics between or inside the steps, which would change how the launches run;
+measured cost under 1% of a step).  The decode launches' duration of a step is
+its merge's first block start minus its decode's first workgroup start (the
+kernels run back to back, so this is the dispatch-to-next-dispatch duration a
+rocprofv3 kernel trace reports; the next step's start when a step has no
+merge), averaged over exactly the timed steps; the in-kernel span (first
+workgroup start to last workgroup end) is reported beside it.  A second pass of 64
+steps, recorded the same way, gives the per-step median and p10/p90 from the
+intervals between consecutive launch starts.  The default warm-up (1000
+steps, under 0.1 s) runs the GPU into its steady clock state: after an idle
+period the first few hundred steps run at another speed before they settle.
 
 Roofline of the dominant kernel (the fused decode kernel): algorithmic bytes
 per launch = 1152 B per unique KV token + query (1152 B per head) + output
@@ -205,7 +212,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default="deepseek", choices=sorted(WORKLOAD_DESC))
     ap.add_argument("--layers", type=int, default=0,
                     help="KV copies cycled over (0: enough to exceed the last-level cache)")
@@ -318,20 +325,6 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    def timed_pass(first, n):
-        evs = [hip.create() for _ in range(n + 1)]
-        torch.cuda.synchronize()
-        hip.record(evs[0], sh)
-        for i in range(n):
-            step(first + i)
-            hip.record(evs[i + 1], sh)
-        torch.cuda.synchronize()
-        per = np.array([hip.elapsed(evs[i], evs[i + 1]) for i in range(n)])
-        total = hip.elapsed(evs[0], evs[-1])
-        for e in evs:
-            hip.destroy(e)
-        return total, per
-
     def timed_total(first, n):
         # the K timed steps, with one event before and one after them: an
         # event recorded between two steps delays the next step's dispatch
@@ -347,24 +340,31 @@ def main():
         hip.destroy(e1)
         return t
 
-    total_ms = timed_total(args.warmup, args.steps)
-    # per-step distribution: a separate pass of at least 50 steps with an event
-    # after every step (those events add their own delay to each step)
-    stats_steps = max(args.steps, 50)
-    _, per_step = timed_pass(args.warmup + args.steps, stats_steps)
-    # second pass: the decode kernel's event intervals and in-kernel spans (the
-    # library keeps the last 256 runs' records)
+    if args.steps > 256:
+        print("--steps is at most 256 (the library keeps 256 timing records)", file=sys.stderr)
+        sys.exit(2)
     plan.set_timing(True)
-    timing_steps = min(args.steps, 256)
-    total2_ms, per_step2 = timed_pass(args.warmup + 2 * stats_steps, timing_steps)
-    kern_ev_ms, kern_span_ms, kern_n = plan.kernel_timing()
-    plan.set_timing(False)
+    total_ms = timed_total(args.warmup, args.steps)
+    spans_us, t_start, t_merge = plan.timing_runs()
     ms_per_step = total_ms / args.steps
-    kern_ev_avg = kern_ev_ms / max(kern_n, 1)
-    kern_avg_ms = kern_span_ms / max(kern_n, 1)
-    if kern_avg_ms > float(np.median(per_step2)) or kern_avg_ms <= 0.0:
-        print(f"inconsistent timing: decode kernel span {kern_avg_ms:.5f} ms against a step "
-              f"of {np.median(per_step2):.5f} ms", file=sys.stderr)
+    durs = [t_merge[i] - t_start[i] if t_merge[i] >= 0 else t_start[i + 1] - t_start[i]
+            for i in range(len(t_start)) if t_merge[i] >= 0 or i + 1 < len(t_start)]
+    # per-step statistics: a second pass of 64 steps, back to back (no event
+    # between the steps), from the intervals between launch starts
+    stats_steps = 64
+    plan.set_timing(True)
+    total2_ms = timed_total(args.warmup + args.steps, stats_steps)
+    _, starts_us, _ = plan.timing_runs()
+    plan.set_timing(False)
+    if len(spans_us) != args.steps or len(starts_us) != stats_steps:
+        print(f"timing records: {len(spans_us)} and {len(starts_us)} runs", file=sys.stderr)
+        sys.exit(3)
+    per_step = np.diff(starts_us) * 1e-3           # ms, launch start to launch start
+    kern_avg_ms = float(np.mean(durs)) * 1e-3
+    span_avg_ms = float(np.mean(spans_us)) * 1e-3
+    if kern_avg_ms > ms_per_step or span_avg_ms > kern_avg_ms * 1.02 or kern_avg_ms <= 0.0:
+        print(f"inconsistent timing: decode {kern_avg_ms:.5f} ms (span {span_avg_ms:.5f} ms) "
+              f"against a step of {ms_per_step:.5f} ms", file=sys.stderr)
         sys.exit(3)
 
     value = attended / (ms_per_step * 1e-3)
@@ -411,13 +411,14 @@ def main():
         "ms_per_step_median": round(float(np.median(per_step)), 5),
         "ms_per_step_p10": round(float(np.percentile(per_step, 10)), 5),
         "ms_per_step_p90": round(float(np.percentile(per_step, 90)), 5),
-        "per_step_stats_steps": int(stats_steps),
-        "per_step_stats_source": "separate pass, HIP event after every step",
+        "per_step_stats_steps": int(len(per_step)),
+        "per_step_stats_source": "second pass of 64 steps, back to back: intervals between "
+                                 "consecutive decode launch starts (in-kernel real-time stamps)",
         "decode_kernel_ms": round(kern_avg_ms, 5),
-        "decode_kernel_source": "in-kernel real-time stamps (earliest wave start to latest "
-                                "wave end), second pass of the same steps",
-        "decode_event_ms": round(kern_ev_avg, 5),
-        "ms_per_step_timing_pass": round(total2_ms / timing_steps, 5),
+        "decode_kernel_source": "the K timed steps: first merge block start minus first decode "
+                                "workgroup start (in-kernel real-time stamps), mean",
+        "decode_span_ms": round(span_avg_ms, 5),
+        "ms_per_step_timing_pass": round(total2_ms / stats_steps, 5),
         "alg_bytes_per_step": int(alg_bytes),
         "alg_flops_per_step": alg_flops,
         "plan_host_ms": round(plan_ms, 2),

@@ -312,18 +312,32 @@ int pkvmla_run_noalloc(pkvmla_plan plan, const void* q_nope, const void* q_pe,
                        const void* ckv_cache, const void* kpe_cache, void* out, float* lse,
                        void* stream);
 
-/* Kernel timing for benchmarks.  With enable != 0, every later pkvmla_run
- * records a HIP event pair on its stream around the fused decode kernel, and
- * the kernel itself records the earliest start and the latest end of its
- * waves on the GPU's 100 MHz real-time counter (the kernel's own span, without
- * the dispatch gap the events also contain).  The event and stamp buffers are
- * created here, so run still allocates nothing; the run counter is reset.
- * pkvmla_plan_timing synchronises the device and returns, over the last
- * min(n, 256) timed runs, the summed event intervals (ms), the summed kernel
- * spans (ms) and that count.  Timing must be off while a run is being
- * captured into a HIP graph. */
+/* Kernel timing for benchmarks.  enable 1: in every later pkvmla_run each
+ * workgroup of the decode launch(es) stores its start and its end (wave 0,
+ * after the workgroup's final barrier) on the GPU's 100 MHz real-time counter
+ * into its own words of a per-run record (plain stores, no atomics and no
+ * stream events, so the timed launches run as they do untimed); a run's span
+ * is its earliest workgroup start to its latest workgroup end.  enable 2: the
+ * same plus a HIP event pair on the stream around the decode launch(es)
+ * (events between kernels change how the launches that follow run).  0: off.
+ * The record and event buffers are created here, so run still allocates
+ * nothing; the run counter is reset.  pkvmla_plan_timing synchronises the
+ * device and returns, over the last min(n, 256) timed runs, the summed event
+ * intervals (ms; 0 without events), the summed spans (ms) and that count.
+ * Timing must be off while a run is being captured into a HIP graph. */
 int pkvmla_plan_set_timing(pkvmla_plan plan, int32_t enable);
 int pkvmla_plan_timing(pkvmla_plan plan, double* event_ms, double* span_ms, int64_t* n_runs);
+
+/* Per timed run (the last min(n, 256), oldest first): span_us[i] the run's
+ * decode span, start_us[i] its earliest decode workgroup start and
+ * merge_start_us[i] its earliest merge block start (-1: no merge launch), the
+ * last two relative to the first returned run's start (microseconds).  With
+ * back-to-back runs, consecutive starts give each step's period and
+ * merge_start_us[i] - start_us[i] the decode launches' duration as a trace
+ * counts it (dispatch to the next kernel's start), without events between
+ * them.  *n_runs = the count; PKVMLA_EINVAL when it exceeds cap. */
+int pkvmla_plan_timing_runs(pkvmla_plan plan, double* span_us, double* start_us,
+                            double* merge_start_us, int64_t cap, int64_t* n_runs);
 
 /* Free the plan's device buffers (synchronises the device first).  NULL is a
  * no-op.  The plan is built once per batch of page tables and reused across

@@ -95,6 +95,10 @@ _lib.pkvmla_plan_export.argtypes = [_vp, _i32p, ctypes.c_int64, _i64p]
 _lib.pkvmla_gather.argtypes = [_vp, _vp, _vp, _vp, _vp]
 _lib.pkvmla_gather_rows.argtypes = [_vp, _i64p]
 _lib.pkvmla_plan_set_timing.argtypes = [_vp, ctypes.c_int32]
+_lib.pkvmla_plan_timing_runs.argtypes = [_vp, ctypes.POINTER(ctypes.c_double),
+                                         ctypes.POINTER(ctypes.c_double),
+                                         ctypes.POINTER(ctypes.c_double), ctypes.c_int64,
+                                         ctypes.POINTER(ctypes.c_int64)]
 _lib.pkvmla_plan_timing.argtypes = [_vp, ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(ctypes.c_double), _i64p]
 
@@ -106,7 +110,7 @@ EXPORTED_SYMBOLS = (
     "pkvmla_run_noalloc", "pkvmla_plan_create_qo", "pkvmla_schedule_rows_host",
     "pkvmla_plan_create_cascade_with_capacity", "pkvmla_plan_update_cascade", "pkvmla_run_fp8",
     "pkvmla_schedule_chain_host", "pkvmla_plan_create_qo_layout", "pkvmla_schedule_qo_rows_host",
-    "pkvmla_plan_create_qo_with_capacity", "pkvmla_plan_update_qo",
+    "pkvmla_plan_create_qo_with_capacity", "pkvmla_plan_update_qo", "pkvmla_plan_timing_runs",
 )
 
 # work layouts of a plan with several query tokens per request
@@ -430,9 +434,23 @@ class Plan:
         the library's static per-device scratch; packed caches)."""
         _check(_lib.pkvmla_run_noalloc(self._h, q_nope, q_pe, ckv, kpe, out, lse, stream))
 
-    def set_timing(self, enable: bool = True) -> None:
-        """Record HIP events around the decode kernel of every later run."""
-        _check(_lib.pkvmla_plan_set_timing(self._h, 1 if enable else 0))
+    def set_timing(self, enable=True, events: bool = False) -> None:
+        """Record every later run's decode span (per-workgroup in-kernel
+        stamps); with events=True also a HIP event pair around the launch."""
+        _check(_lib.pkvmla_plan_set_timing(self._h, (2 if events else 1) if enable else 0))
+
+    def timing_runs(self):
+        """(span_us, start_us, merge_start_us) arrays of the last timed runs,
+        oldest first; starts relative to the first run's start (merge start
+        -1 for a run without a merge launch)."""
+        n = ctypes.c_int64(0)
+        cap = 256
+        span = (ctypes.c_double * cap)()
+        start = (ctypes.c_double * cap)()
+        mstart = (ctypes.c_double * cap)()
+        _check(_lib.pkvmla_plan_timing_runs(self._h, span, start, mstart, cap, ctypes.byref(n)))
+        k = int(n.value)
+        return np.array(span[:k]), np.array(start[:k]), np.array(mstart[:k])
 
     def kernel_timing(self):
         """(summed decode-kernel event ms, summed in-kernel span ms, number of

@@ -96,10 +96,16 @@ struct pkvmla_plan_s {
   int32_t* d_slot_list = nullptr;
   void* d_part = nullptr;  // part_o bf16 [slots][H][512] then part_lse fp32 [slots][H]
   size_t table_ints = 0;
-  // optional per-run timing of the decode kernel (events created up front)
+  // optional per-run timing: every workgroup's start and end stamps, per run
+  // slot [kTimingSlots][timing_wgs0 + timing_wgs + timing_wgsm][2] (the
+  // level-0 decode launch's workgroups, the decode launch's, then the merge
+  // launch's blocks), the grids each run launched, and in mode 2 a HIP event
+  // pair around the decode launches (events created up front)
   static constexpr int kTimingSlots = 256;
   hipEvent_t ev[2 * kTimingSlots] = {};
-  unsigned long long* d_stamps = nullptr;  // [kTimingSlots][2] kernel span stamps
+  unsigned long long* d_stamps = nullptr;
+  int32_t timing_wgs0 = 0, timing_wgs = 0, timing_wgsm = 0;
+  int32_t timing_grid[kTimingSlots][3] = {};
   int timing = 0;
   int64_t timed_runs = 0;
 };
@@ -1180,8 +1186,13 @@ int run_impl(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* ck
   d.v_scale = kv.ckv_scale;
   d.kpe_ratio = kv.fp8 ? (float)((double)kv.kpe_scale / (double)kv.ckv_scale) : 1.f;
   const int slot_ev = (int)(P->timed_runs % pkvmla_plan_s::kTimingSlots);
-  d.stamps = P->timing ? P->d_stamps + 2 * slot_ev : nullptr;
-  if (P->timing) PKVMLA_HIP(hipEventRecord(P->ev[2 * slot_ev], s));
+  unsigned long long* rec =
+      P->timing ? P->d_stamps + (size_t)slot_ev * 2 *
+                                    (P->timing_wgs0 + P->timing_wgs + P->timing_wgsm)
+                : nullptr;
+  d.stamps = rec ? rec + 2 * (size_t)P->timing_wgs0 : nullptr;
+  if (P->timing == 2) PKVMLA_HIP(hipEventRecord(P->ev[2 * slot_ev], s));
+  int32_t grid0 = 0;
   d.qo_log2h = -1;
   if ((P->is_cascade || P->is_qo == 2) && (P->sched0.grid > 0 || P->fixed_launch)) {
     // level 0: the groups' query rows over their shared prefixes, or the row
@@ -1196,12 +1207,16 @@ int run_impl(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* ck
     d0.heads_per_wave = P->cfg0.heads_per_wave;
     d0.stages = P->cfg0.stages;
     d0.row_blocks = P->cascade_chain ? 0 : 1;
+    d0.stamps = rec;
+    grid0 = d0.n_lanes > 0 ? pkvmla::decode_grid(d0.n_lanes, d0.head_groups) : 0;
     PKVMLA_HIP(pkvmla::launch_decode(d0, s));
   }
   PKVMLA_HIP(pkvmla::launch_decode(d, s));
   if (P->timing) {
-    PKVMLA_HIP(hipEventRecord(P->ev[2 * slot_ev + 1], s));
-    ++P->timed_runs;
+    if (P->timing == 2) PKVMLA_HIP(hipEventRecord(P->ev[2 * slot_ev + 1], s));
+    P->timing_grid[slot_ev][0] = grid0;
+    P->timing_grid[slot_ev][1] = d.n_lanes > 0 ? pkvmla::decode_grid(d.n_lanes, d.head_groups) : 0;
+    P->timing_grid[slot_ev][2] = 0;
   }
   // fixed launches cover every merge record slot (records past the live ones
   // have count 0 and are skipped by the kernel)
@@ -1217,8 +1232,11 @@ int run_impl(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* ck
     m.out = d.out;
     m.lse = lse;
     m.num_heads = P->num_heads;
+    m.stamps = rec ? rec + 2 * (size_t)(P->timing_wgs0 + P->timing_wgs) : nullptr;
+    if (rec) P->timing_grid[slot_ev][2] = n_merges * (P->num_heads / 4);
     PKVMLA_HIP(pkvmla::launch_merge(m, n_merges, s));
   }
+  if (P->timing) ++P->timed_runs;
   return ok();
 }
 
@@ -1236,50 +1254,120 @@ void pkvmla_plan_destroy(pkvmla_plan P) { free_plan(P); }
 
 int pkvmla_plan_set_timing(pkvmla_plan P, int32_t enable) {
   if (!P) return fail(PKVMLA_EINVAL, "null plan");
-  if (enable && !P->ev[0]) {
+  if (enable < 0 || enable > 2) return fail(PKVMLA_EINVAL, "timing mode must be 0, 1 or 2");
+  if (enable == 2 && !P->ev[0]) {
     // timing-only events: no system-scope fence (cache write-back and
     // invalidation) at each record, which would add its own cost to the
     // interval and to the kernels that follow
     for (hipEvent_t& e : P->ev) PKVMLA_HIP(hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
   }
   if (enable) {
-    // one {earliest start, latest end} pair per timed run, reset here (not per
-    // run: a reset launch would sit between the timed kernels)
-    const size_t n = 2 * (size_t)pkvmla_plan_s::kTimingSlots;
-    if (!P->d_stamps) PKVMLA_HIP(hipMalloc(&P->d_stamps, n * sizeof(unsigned long long)));
-    std::vector<unsigned long long> init(n);
-    for (size_t i = 0; i < n; i += 2) {
-      init[i] = ~0ull;
-      init[i + 1] = 0ull;
+    // records for the largest launches the plan can make (its capacities)
+    const bool has_l0 = P->is_cascade || P->is_qo == 2;
+    const int32_t w0 = has_l0 ? pkvmla::decode_grid(std::max(P->cap_lanes0, 1), P->cfg0.head_groups) : 0;
+    const int32_t w1 = pkvmla::decode_grid(std::max(P->cap_lanes, 1), P->cfg.head_groups);
+    const int32_t wm = std::max(P->cap_merges, 1) * (P->num_heads / 4);
+    if (!P->d_stamps || w0 != P->timing_wgs0 || w1 != P->timing_wgs || wm != P->timing_wgsm) {
+      if (P->d_stamps) {
+        PKVMLA_HIP(hipDeviceSynchronize());
+        PKVMLA_HIP(hipFree(P->d_stamps));
+        P->d_stamps = nullptr;
+      }
+      const size_t n = (size_t)pkvmla_plan_s::kTimingSlots * 2 * (size_t)(w0 + w1 + wm);
+      PKVMLA_HIP(hipMalloc(&P->d_stamps, n * sizeof(unsigned long long)));
+      P->timing_wgs0 = w0;
+      P->timing_wgs = w1;
+      P->timing_wgsm = wm;
     }
-    PKVMLA_HIP(hipDeviceSynchronize());
-    PKVMLA_HIP(hipMemcpy(P->d_stamps, init.data(), n * sizeof(unsigned long long),
-                         hipMemcpyHostToDevice));
   }
-  P->timing = enable ? 1 : 0;
+  P->timing = enable;
   P->timed_runs = 0;
   return ok();
 }
 
+namespace {
+
+// Per recorded run (oldest first): the span of its decode launches (earliest
+// workgroup start to latest workgroup end) and its start, in real-time
+// counter ticks (100 MHz).
+int timing_records(pkvmla_plan P, std::vector<unsigned long long>* start,
+                   std::vector<unsigned long long>* span,
+                   std::vector<unsigned long long>* merge_start = nullptr) {
+  PKVMLA_HIP(hipDeviceSynchronize());
+  const int64_t K = pkvmla_plan_s::kTimingSlots;
+  const int64_t n = std::min<int64_t>(P->timed_runs, K);
+  const size_t per = 2 * (size_t)(P->timing_wgs0 + P->timing_wgs + P->timing_wgsm);
+  std::vector<unsigned long long> all(std::max<size_t>(1, (size_t)K * per));
+  if (n > 0)
+    PKVMLA_HIP(hipMemcpy(all.data(), P->d_stamps, (size_t)K * per * sizeof(unsigned long long),
+                         hipMemcpyDeviceToHost));
+  start->clear();
+  span->clear();
+  if (merge_start) merge_start->clear();
+  for (int64_t r = P->timed_runs - n; r < P->timed_runs; ++r) {
+    const int64_t slot = r % K;
+    const unsigned long long* rec = all.data() + (size_t)slot * per;
+    unsigned long long lo = ~0ull, hi = 0;
+    auto scan = [&](const unsigned long long* x, int32_t wgs) {
+      for (int32_t b = 0; b < wgs; ++b) {
+        lo = std::min(lo, x[2 * b]);
+        hi = std::max(hi, x[2 * b + 1]);
+      }
+    };
+    scan(rec, P->timing_grid[slot][0]);
+    scan(rec + 2 * (size_t)P->timing_wgs0, P->timing_grid[slot][1]);
+    start->push_back(lo);
+    span->push_back(hi >= lo ? hi - lo : 0);
+    if (merge_start) {
+      // earliest merge block start (0: the run launched no merge)
+      const unsigned long long* mrec = rec + 2 * (size_t)(P->timing_wgs0 + P->timing_wgs);
+      unsigned long long ms = ~0ull;
+      for (int32_t b = 0; b < P->timing_grid[slot][2]; ++b) ms = std::min(ms, mrec[2 * b]);
+      merge_start->push_back(P->timing_grid[slot][2] > 0 ? ms : 0);
+    }
+  }
+  return PKVMLA_OK;
+}
+
+}  // namespace
+
 int pkvmla_plan_timing(pkvmla_plan P, double* event_ms, double* span_ms, int64_t* n_runs) {
   if (!P || !event_ms || !span_ms || !n_runs) return fail(PKVMLA_EINVAL, "null argument");
-  PKVMLA_HIP(hipDeviceSynchronize());
-  const int64_t n = std::min<int64_t>(P->timed_runs, pkvmla_plan_s::kTimingSlots);
-  double tot = 0.0, span = 0.0;
-  std::vector<unsigned long long> st(2 * (size_t)std::max<int64_t>(n, 1));
-  if (n > 0)
-    PKVMLA_HIP(hipMemcpy(st.data(), P->d_stamps, 2 * n * sizeof(unsigned long long),
-                         hipMemcpyDeviceToHost));
+  std::vector<unsigned long long> start, span;
+  int rc = timing_records(P, &start, &span);
+  if (rc) return rc;
+  const int64_t n = (int64_t)span.size();
+  double tot = 0.0, sp = 0.0;
   for (int64_t i = 0; i < n; ++i) {
-    float ms = 0.f;
-    PKVMLA_HIP(hipEventElapsedTime(&ms, P->ev[2 * i], P->ev[2 * i + 1]));
-    tot += ms;
-    // the real-time counter runs at 100 MHz: 1e-5 ms per tick
-    if (st[2 * i + 1] >= st[2 * i]) span += (double)(st[2 * i + 1] - st[2 * i]) * 1e-5;
+    if (P->timing == 2 && P->ev[0]) {
+      const int64_t slot = (P->timed_runs - n + i) % pkvmla_plan_s::kTimingSlots;
+      float ms = 0.f;
+      PKVMLA_HIP(hipEventElapsedTime(&ms, P->ev[2 * slot], P->ev[2 * slot + 1]));
+      tot += ms;
+    }
+    sp += (double)span[i] * 1e-5;  // 100 MHz ticks -> ms
   }
   *event_ms = tot;
-  *span_ms = span;
+  *span_ms = sp;
   *n_runs = n;
+  return ok();
+}
+
+int pkvmla_plan_timing_runs(pkvmla_plan P, double* span_us, double* start_us,
+                            double* merge_start_us, int64_t cap, int64_t* n_runs) {
+  if (!P || !n_runs) return fail(PKVMLA_EINVAL, "null argument");
+  std::vector<unsigned long long> start, span, mstart;
+  int rc = timing_records(P, &start, &span, &mstart);
+  if (rc) return rc;
+  const int64_t n = (int64_t)span.size();
+  *n_runs = n;
+  if (n > cap || (n > 0 && (!span_us || !start_us || !merge_start_us)))
+    return fail(PKVMLA_EINVAL, "output capacity too small (%lld runs)", (long long)n);
+  for (int64_t i = 0; i < n; ++i) {
+    span_us[i] = (double)span[i] * 1e-2;
+    start_us[i] = (double)(start[i] - start[0]) * 1e-2;
+    merge_start_us[i] = mstart[i] ? (double)(mstart[i] - start[0]) * 1e-2 : -1.0;
+  }
   return ok();
 }
 

@@ -172,8 +172,10 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
   // apart, which the dispatcher places on the same XCD.
   const int hg = (int)(blockIdx.x >> 3) % n_hg;
   const int sl = (int)(blockIdx.x / (8 * n_hg)) * 8 + (int)(blockIdx.x & 7);
-  const bool stamp_lane = stamps && (threadIdx.x & 63) == 0;
-  if (stamp_lane && wave == 0) stamp_start(stamps);
+  // timing runs: workgroup start and end (wave 0 ends after the final
+  // barrier, which every wave of the workgroup passes)
+  const bool stamp_lane = stamps && threadIdx.x == 0;
+  if (stamp_lane) stamp_start(stamps);
   if (sl >= n_lanes || wg_indptr[sl] >= wg_indptr[sl + 1]) {
     if (stamp_lane) stamp_end(stamps);
     return;
@@ -508,7 +510,6 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
     }
-    if (stamp_lane) stamp_end(stamps);
   } else if constexpr (FP8) {
     // ================= copy role, fp8 caches =================
     // copy wave cw loads copy slot cw of every tile into registers (five
@@ -566,7 +567,6 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
       publish();
       if (i + 1 >= G) break;
     }
-    if (stamp_lane) stamp_end(stamps);
   } else {
     // ======================= copy role =======================
     // copy wave cw issues copy slots 2cw and 2cw+1 of every tile (18 copies;
@@ -622,7 +622,6 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
       lds_barrier();
     }
     wait_vmcnt<0>();
-    if (stamp_lane) stamp_end(stamps);
   }
 }
 

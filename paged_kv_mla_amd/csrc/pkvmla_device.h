@@ -143,14 +143,15 @@ __device__ __forceinline__ int lane_id_fresh() {
   return x;
 }
 
-// Kernel span stamps for timing runs (stamps != null): the earliest start and
-// the latest end over the launch's waves on the 100 MHz real-time counter.
-// One lane per caller; the atomics need no return value.
+// Timing runs: each workgroup stores its start and end on the 100 MHz
+// real-time counter into its own pair of a launch's record (plain stores to
+// distinct words, no atomics: a single word updated by every workgroup would
+// itself delay the launch it measures).  One lane per workgroup.
 __device__ __forceinline__ void stamp_start(unsigned long long* stamps) {
-  if (stamps) atomicMin(stamps, (unsigned long long)__builtin_amdgcn_s_memrealtime());
+  if (stamps) stamps[2 * blockIdx.x] = __builtin_amdgcn_s_memrealtime();
 }
 __device__ __forceinline__ void stamp_end(unsigned long long* stamps) {
-  if (stamps) atomicMax(stamps + 1, (unsigned long long)__builtin_amdgcn_s_memrealtime());
+  if (stamps) stamps[2 * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
 }
 
 // Workgroup barrier that orders LDS traffic (every LDS access of this wave has

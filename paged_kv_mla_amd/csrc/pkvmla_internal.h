@@ -77,6 +77,7 @@ struct MergeParams {
   uint16_t* out;
   float* lse;
   int32_t num_heads;
+  unsigned long long* stamps;  // null, or per-block {start, end} records (timing runs)
 };
 
 struct GatherParams {

@@ -25,9 +25,15 @@ namespace pkvmla {
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) mla_merge_kernel(MergeParams p) {
   constexpr int kChunk = 4;  // partial states whose loads are in flight together
+  // timing runs: the block's start and end on the real-time counter
+  const uint32_t sb = blockIdx.y * gridDim.x + blockIdx.x;
+  if (p.stamps && threadIdx.x == 0) p.stamps[2 * sb] = __builtin_amdgcn_s_memrealtime();
   const int32_t* mr = p.merges + (size_t)blockIdx.x * kMergeInts;
   const int b = mr[0], s0 = mr[1], n = mr[2];
-  if (n <= 0) return;  // an unused record slot of a plan with fixed launches
+  if (n <= 0) {  // an unused record slot of a plan with fixed launches
+    if (p.stamps && threadIdx.x == 0) p.stamps[2 * sb + 1] = __builtin_amdgcn_s_memrealtime();
+    return;
+  }
   // kind 1: the request's slots are listed (a cascade plan's prefix states
   // sit in its level-0 row blocks' slots)
   const int32_t* list = mr[3] == 1 ? p.slot_list + s0 : nullptr;
@@ -81,6 +87,7 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(MergeParams p) {
       make_uint4(packed[0], packed[1], packed[2], packed[3]);
   if ((threadIdx.x & 63) == 0)
     p.lse[(size_t)b * H + h] = M + __builtin_amdgcn_logf(wsum) * 0.69314718055994531f;
+  if (p.stamps && threadIdx.x == 0) p.stamps[2 * sb + 1] = __builtin_amdgcn_s_memrealtime();
 }
 
 // ---------------------------------------------------------------------------
