@@ -39,6 +39,18 @@
 // shares (36 operations) in flight: the vmcnt counter holds at most 63, and a
 // wave with more outstanding cannot wait for them exactly.
 //
+// At 16 and 32 heads (bf16 caches) progress counters in LDS replace the
+// per-tile barrier, and each role waits only for what its next step needs:
+// a copy wave publishes the tiles whose share has landed (after its exact
+// vmcnt wait) and refills a stage once the PV waves have finished the tile
+// four back; a QK wave scores tile i once it has landed and writes P^T into
+// an exchange buffer once the PV waves have finished tile i-2 (the same
+// parity), then publishes i+1; a PV wave takes tile t once every QK wave has
+// published it and the next tile has landed, and publishes t+1 once its
+// reads have returned.  Every dependency points at strictly earlier work,
+// and every wait is bounded.  At 64 heads the PV waves' registers leave no
+// room for the waits (the variant spilled), and the barrier stays.
+//
 // Row-block units (the level-0 launch of a cascade plan).  The 64 rows of a
 // workgroup are then not the heads of one request but 64 consecutive query
 // rows rho = b * H + head of a prefix group (four requests at 16 heads, two at
@@ -96,8 +108,37 @@ static_assert((kRsRing - 2) * 2 * kCopiesPerWave < 64, "copies in flight exceed 
 constexpr int kXpOff = kRsRing * kStageBytes;         // P^T exchange: [parity][hb] 1 KB blocks
 constexpr int kXaOff = kXpOff + 2 * kRsMaxHB * 1024;  // rescale factors: [parity][li][hb] floats
 constexpr int kXlOff = kXaOff + 2 * 64 * 4;        // unit row sums:   [parity][li][hb] floats
-constexpr int kRsLds = kXlOff + 2 * 64 * 4;
+// progress counters (bf16 caches): tiles landed per copy wave, tiles whose
+// P^T is published per QK wave, tiles finished per PV wave
+constexpr int kLandedOff = kXlOff + 2 * 64 * 4;
+constexpr int kReadyOff = kLandedOff + 4 * kRsCopyWaves;
+constexpr int kDoneOff = kReadyOff + 4 * kRsMaxHB;
+constexpr int kRsLds = kDoneOff + 4 * kRsPvWaves;
 static_assert(kRsLds <= 160 * 1024, "LDS budget");
+
+// Bounded wait until each of the n LDS counters c[0..n-1] holds at least
+// target.  A wave gives up after kSpinLimit polls (about 0.1 s), so a
+// protocol error shows as wrong results, never as a workgroup that does not
+// end.
+constexpr int kSpinLimit = 1 << 20;
+template <int N>
+__device__ __forceinline__ void wait_counters(const volatile LDS_AS int* c, int target) {
+  for (int it = 0; it < kSpinLimit; ++it) {
+    int m = c[0];
+#pragma unroll
+    for (int j = 1; j < N; ++j) m = min(m, c[j]);
+    if (__builtin_amdgcn_readfirstlane(m) >= target) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");  // no LDS access moves above the wait
+}
+// Publishes v in the wave's counter once all of the wave's LDS accesses
+// issued so far have completed (their data written, or read out).
+__device__ __forceinline__ void publish_counter(volatile LDS_AS int* c, int v) {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt open
+  asm volatile("" ::: "memory");
+  *c = v;
+}
 
 // Unit cursor: the unit and tile a role is at, with the unit's fields.  For
 // a row-block unit, b is its first query row, slot the offset of its rows in
@@ -185,7 +226,15 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
   const char* ckv = reinterpret_cast<const char*>(ckv_cache);
   const char* kpe = reinterpret_cast<const char*>(kpe_cache);
 
-  // Tiles of the workgroup (both roles run the same number of barriers).
+  // 16 and 32 heads with bf16 caches: the roles synchronise through the
+  // progress counters (each waits only for what its next step reads or
+  // overwrites); 64 heads, and fp8 caches: one workgroup barrier per tile
+  // (at 64 heads the PV waves' registers leave no room for the waits)
+  constexpr bool FLAGS = !FP8 && HB < 4;
+  volatile LDS_AS int* landed = (volatile LDS_AS int*)(smem + kLandedOff);
+  volatile LDS_AS int* ready = (volatile LDS_AS int*)(smem + kReadyOff);
+  volatile LDS_AS int* done = (volatile LDS_AS int*)(smem + kDoneOff);
+  // Tiles of the workgroup (with barriers every role runs the same number).
   int G = 0;
   for (int u = u_begin; u < u_end; ++u) {
     idx_ptr rec = units + (size_t)u * kUnitInts;
@@ -225,15 +274,20 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
       for (int k2 = 0; k2 < 2; ++k2)
         q[16 + k2] = *reinterpret_cast<const bf16x8_t*>(qp + (k2 * 32 + g * 8) * 2);
     };
+    if (FLAGS) ready[r] = 0;
     // the query loads go out after the copy waves have issued tile 0, so that
     // tile's copies do not queue behind them in the memory pipeline
     lds_barrier();
     load_q(q_row(cq.b, cq.rend));
     float m_run = -INFINITY, l_run = 0.f;
 
-    lds_barrier();  // tile 0 has landed
+    if (!FLAGS) lds_barrier();  // tile 0 has landed
+    int land_seen = 0;  // landed tiles, as last read
     for (int i = 0; i <= G; ++i) {
       if (i < G) {
+        // tile i has landed (usually known from the read during the last
+        // tile's softmax)
+        if (FLAGS && land_seen < i + 1) wait_counters<kRsCopyWaves>(landed, i + 1);
         const int stage = i % kRsRing;
         const int par = i & 1;
         if (cq.tile == 0 && !cq.cont) {
@@ -287,6 +341,7 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
           idx_ptr nrec = units + (size_t)(cq.u + 1) * kUnitInts;
           load_q(q_row(nrec[0], ROWS ? nrec[5] : 0));
         }
+        if (FLAGS) land_seen = min(landed[0], landed[1]);
         // ---- softmax of this tile: lane (g, li) holds tokens tb*16 + g*4 + k ----
         // tokens of the tile this wave's rows see: the unit's end, and in
         // row blocks of query tokens the causal bound of the wave's token (its
@@ -329,6 +384,9 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
         // the lane's share of the row sum as a tree (depth 3, not 8)
         const float ps = ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
         l_run = l_run * alpha + ps;
+        // the exchange buffers of this parity held tile i-2's: the PV waves
+        // have read them once they have finished tile i-2
+        if (FLAGS && i >= 2) wait_counters<kRsPvWaves>(done, i - 1);
         *(LDS_AS bf16x8_t*)(smem + kXpOff + (par * kRsMaxHB + r) * 1024 + lane * 16) = pT;
         if (g == 0) *(LDS_AS float*)(smem + kXaOff + (par * 64 + li * 4 + r) * 4) = alpha;
         if (cq.tile == cq.ntiles - 1 && cq.slot != kChainNext) {
@@ -352,11 +410,15 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
             }
           }
         }
+        if (FLAGS) {
+          publish_counter(ready + r, i + 1);
+          land_seen = __builtin_amdgcn_readfirstlane(land_seen);
+        }
         cursor_next(cq, units, u_end);
       }
-      lds_barrier();
+      if (!FLAGS) lds_barrier();
     }
-    if (stamp_lane) stamp_end(stamps);
+    if (!FLAGS && stamp_lane) stamp_end(stamps);
   } else if (wave < HB + kRsPvWaves) {
     // ======================= PV and epilogue role =======================
     const int lane0 = threadIdx.x & 63;
@@ -369,8 +431,9 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
       const int qq = li0 & 3;
       offV[tb] = lds_ckv_off(tV, qq >> 1) + (qq & 1) * 8;
     }
+    if (FLAGS) done[r] = 0;
     lds_barrier();  // tile 0's copies are out
-    lds_barrier();  // tile 0 has landed
+    if (!FLAGS) lds_barrier();  // tile 0 has landed
 
     UnitCursor cp;
     cp.u = u_begin;
@@ -388,7 +451,7 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
       for (int hb = 0; hb < HB; ++hb) o[db][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     // ---- iteration 0: the QK waves take tile 0 ----
-    lds_barrier();
+    if (!FLAGS) lds_barrier();
     constexpr int VP = kRsVAhead;
     int oV0 = offV[0], oV1 = offV[1];
     asm volatile("" : "+v"(oV0), "+v"(oV1));
@@ -399,12 +462,19 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
     };
     // the first dim block's V fragments of the next tile, read before the
     // barrier that starts its iteration (one block: the register budget)
+    if (FLAGS) wait_counters<kRsCopyWaves>(landed, 1);
     bf16x4_t vn0 = ldV(0, 0, 0), vn1 = ldV(0, 0, 1);
 
     // ---- iteration t+1: PV of tile t, copies of tile t+3 ----
     for (int t = 0; t < G; ++t) {
       const int stage = t % kRsRing;
       const int par = t & 1;
+      if (FLAGS) {
+        // P^T of tile t is published, and tile t+1 has landed (its first V
+        // block is read after this tile's MFMAs; the QK waves need it now)
+        wait_counters<HB>(ready, t + 1);
+        if (t + 1 < G) wait_counters<kRsCopyWaves>(landed, t + 2);
+      }
       const int lane = lane_id_fresh();
       bf16x8_t pB[HB];
 #pragma unroll
@@ -504,12 +574,21 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
         }
       }
       cursor_next(cp, units, u_end);
-      // this role writes no LDS, and its reads still in flight are of a tile
-      // that stays resident for two more iterations: no wait before the barrier
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
+      if (FLAGS) {
+        // tile t's stage and exchange buffers are free once this wave's reads
+        // of them have returned
+        publish_counter(done + r, t + 1);
+      } else {
+        // this role writes no LDS, and its reads still in flight are of a tile
+        // that stays resident for two more iterations: no wait before the barrier
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      }
     }
+    // (with counters no barrier ends the workgroup: its end is the first PV
+    // wave's)
+    if (FLAGS && stamps && threadIdx.x == HB * 64) stamp_end(stamps);
   } else if constexpr (FP8) {
     // ================= copy role, fp8 caches =================
     // copy wave cw loads copy slot cw of every tile into registers (five
@@ -610,18 +689,35 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
       }
       book_tile();
     };
+    if (FLAGS) landed[cw] = 0;
     if (ts.u < ts.u_end) issue_tile();
     lds_barrier();  // the QK waves load their queries from here on
-    if (ts.u < ts.u_end) issue_tile();
-    wait_vm_le(vmc - vmc_of(0));
-    lds_barrier();
-    for (int i = 0; i <= G; ++i) {
-      // tile i+2 into the stage PV(i-2) released at the last barrier
+    if constexpr (FLAGS) {
+      // Tile t goes into stage t mod 4 once the PV waves have finished tile
+      // t-4 (the QK waves finished it before), and the wave then waits, with
+      // an exact vmcnt, for its share of tile t-1: at most two tiles in flight.
+      for (int t = 1; t < G; ++t) {
+        if (t >= kRsRing) wait_counters<kRsPvWaves>(done, t - kRsRing + 1);
+        issue_tile();
+        wait_vm_le(vmc - vmc_of(t - 1));
+        asm volatile("" ::: "memory");
+        landed[cw] = t;  // tiles 0 .. t-1 have landed
+      }
+      wait_vmcnt<0>();
+      asm volatile("" ::: "memory");
+      landed[cw] = G;
+    } else {
       if (ts.u < ts.u_end) issue_tile();
-      if (i + 1 < G) wait_vm_le(vmc - vmc_of(i + 1));
+      wait_vm_le(vmc - vmc_of(0));
       lds_barrier();
+      for (int i = 0; i <= G; ++i) {
+        // tile i+2 into the stage PV(i-2) released at the last barrier
+        if (ts.u < ts.u_end) issue_tile();
+        if (i + 1 < G) wait_vm_le(vmc - vmc_of(i + 1));
+        lds_barrier();
+      }
+      wait_vmcnt<0>();
     }
-    wait_vmcnt<0>();
   }
 }
 
