@@ -394,6 +394,38 @@ def test_many_tiny_requests():
     compare(out, lse, ref_o, ref_l, name="tiny requests")
 
 
+def lane_tiles(ex):
+    """Tiles each workgroup of a plan walks (its units' 32-token tiles)."""
+    wg, u = ex.wg_indptr, ex.units
+    return [int(sum((u[k, 3] - u[k, 2] + 31) // 32 for k in range(wg[l], wg[l + 1])))
+            for l in range(len(wg) - 1) if wg[l + 1] > wg[l]]
+
+
+# (requests, lengths drawn from [1, hi), page size): together their
+# workgroups walk every tile count from 1 to 8, around the 4-stage ring
+PROGRESS_CASES = [(100, 300, 1), (300, 100, 16), (120, 600, 64), (100, 900, 16), (64, 2000, 1)]
+
+
+@pytest.mark.parametrize("H", [16, 32])
+def test_progress_counters_short_workgroups(H):
+    """At 16 and 32 heads the roles of a workgroup synchronise through LDS
+    progress counters; workgroups with 1..8 tiles exercise the copy waves'
+    first refills of the 4-stage ring and the end of every wait."""
+    seen = set()
+    for i, (n, hi, ps) in enumerate(PROGRESS_CASES):
+        rng = np.random.default_rng(4000 + 10 * H + i)
+        lens = rng.integers(1, hi, size=n).tolist()
+        inp = small(4000 + 10 * H + i, lens, H=H, ps=ps)
+        plan = pk.plan_for(inp)
+        g = lane_tiles(plan.export())
+        seen.update(g)
+        note(f"counters H{H} case {i}: {n} requests ps{ps}, tiles per workgroup {min(g)}..{max(g)}")
+        out, lse = run_gpu(plan, Dev(inp))
+        ref_o, ref_l = oracle_flat(inp)
+        compare(out, lse, ref_o, ref_l, name=f"counters H{H} case {i}")
+    assert set(range(1, 9)) <= seen, sorted(seen)
+
+
 # ------------------------------------- several new query tokens per request
 QO_CASES = {
     "h16_qo2_ps16": lambda: make_qo("q1", 131, 5, 16, 16, [2, 17, 64, 200, 777], [2] * 5),
