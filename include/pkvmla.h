@@ -312,14 +312,28 @@ int pkvmla_run_noalloc(pkvmla_plan plan, const void* q_nope, const void* q_pe,
                        const void* ckv_cache, const void* kpe_cache, void* out, float* lse,
                        void* stream);
 
+/* Bounded waits of the 16- and 32-head decode kernels (bf16 caches), whose
+ * roles synchronise through progress counters in LDS instead of a per-tile
+ * barrier: a wave polls a counter at most `polls` times (default 2^20, about
+ * 0.1 s) and then gives up; a wave that gave up writes NaN to out and lse for
+ * every unit it finishes afterwards (a stall anywhere in a workgroup reaches
+ * the waits of the waves that write), so a broken protocol shows as
+ * non-finite results and never as a launch that does not end.  0 makes every
+ * such wait give up at once (the failure path, for tests); other kernels are
+ * unaffected.  PKVMLA_EINVAL for polls < 0.  Applies to later runs of the
+ * plan; not for use while a run is being captured. */
+int pkvmla_plan_set_wait_limit(pkvmla_plan plan, int32_t polls);
+
 /* Kernel timing for benchmarks.  enable 1: in every later pkvmla_run each
- * workgroup of the decode launch(es) stores its start and its end (wave 0,
- * after the workgroup's final barrier) on the GPU's 100 MHz real-time counter
- * into its own words of a per-run record (plain stores, no atomics and no
- * stream events, so the timed launches run as they do untimed); a run's span
- * is its earliest workgroup start to its latest workgroup end.  enable 2: the
- * same plus a HIP event pair on the stream around the decode launch(es)
- * (events between kernels change how the launches that follow run).  0: off.
+ * workgroup of the decode launch(es) stores its start and its end (wave 0
+ * after the workgroup's final barrier; at 16 and 32 heads, where no barrier
+ * ends the workgroup, the first PV wave after its last tile) on the GPU's
+ * 100 MHz real-time counter into its own words of a per-run record (plain
+ * stores, no atomics and no stream events, so the timed launches run as they
+ * do untimed); a run's span is its earliest workgroup start to its latest
+ * workgroup end.  enable 2: the same plus a HIP event pair on the stream
+ * around the decode launch(es) (events between kernels change how the
+ * launches that follow run).  0: off.
  * The record and event buffers are created here, so run still allocates
  * nothing; the run counter is reset.  pkvmla_plan_timing synchronises the
  * device and returns, over the last min(n, 256) timed runs, the summed event

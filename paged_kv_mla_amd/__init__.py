@@ -95,6 +95,7 @@ _lib.pkvmla_plan_export.argtypes = [_vp, _i32p, ctypes.c_int64, _i64p]
 _lib.pkvmla_gather.argtypes = [_vp, _vp, _vp, _vp, _vp]
 _lib.pkvmla_gather_rows.argtypes = [_vp, _i64p]
 _lib.pkvmla_plan_set_timing.argtypes = [_vp, ctypes.c_int32]
+_lib.pkvmla_plan_set_wait_limit.argtypes = [_vp, ctypes.c_int32]
 _lib.pkvmla_plan_timing_runs.argtypes = [_vp, ctypes.POINTER(ctypes.c_double),
                                          ctypes.POINTER(ctypes.c_double),
                                          ctypes.POINTER(ctypes.c_double), ctypes.c_int64,
@@ -111,6 +112,7 @@ EXPORTED_SYMBOLS = (
     "pkvmla_plan_create_cascade_with_capacity", "pkvmla_plan_update_cascade", "pkvmla_run_fp8",
     "pkvmla_schedule_chain_host", "pkvmla_plan_create_qo_layout", "pkvmla_schedule_qo_rows_host",
     "pkvmla_plan_create_qo_with_capacity", "pkvmla_plan_update_qo", "pkvmla_plan_timing_runs",
+    "pkvmla_plan_set_wait_limit",
 )
 
 # work layouts of a plan with several query tokens per request
@@ -433,6 +435,13 @@ class Plan:
         """Raw-pointer form of the allocation-free run (the split workspace is
         the library's static per-device scratch; packed caches)."""
         _check(_lib.pkvmla_run_noalloc(self._h, q_nope, q_pe, ckv, kpe, out, lse, stream))
+
+    def set_wait_limit(self, polls: int = 1 << 20) -> None:
+        """Polls before a progress-counter wait of the 16- and 32-head decode
+        kernels gives up (outputs of later units then read NaN); 2^20 by
+        default.  0 makes every such wait give up at once: the failure path,
+        for tests."""
+        _check(_lib.pkvmla_plan_set_wait_limit(self._h, int(polls)))
 
     def set_timing(self, enable=True, events: bool = False) -> None:
         """Record every later run's decode span (per-workgroup in-kernel

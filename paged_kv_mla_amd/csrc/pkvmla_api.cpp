@@ -108,6 +108,7 @@ struct pkvmla_plan_s {
   int32_t timing_grid[kTimingSlots][3] = {};
   int timing = 0;
   int64_t timed_runs = 0;
+  int32_t wait_limit = 1 << 20;  // polls before a progress-counter wait gives up
 };
 
 namespace {
@@ -1194,6 +1195,7 @@ int run_impl(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* ck
   if (P->timing == 2) PKVMLA_HIP(hipEventRecord(P->ev[2 * slot_ev], s));
   int32_t grid0 = 0;
   d.qo_log2h = -1;
+  d.wait_limit = P->wait_limit;
   if ((P->is_cascade || P->is_qo == 2) && (P->sched0.grid > 0 || P->fixed_launch)) {
     // level 0: the groups' query rows over their shared prefixes, or the row
     // blocks of several query tokens per request (causal bound per row)
@@ -1251,6 +1253,13 @@ int pkvmla_run(pkvmla_plan P, const void* q_nope, const void* q_pe, const void* 
 }
 
 void pkvmla_plan_destroy(pkvmla_plan P) { free_plan(P); }
+
+int pkvmla_plan_set_wait_limit(pkvmla_plan P, int32_t polls) {
+  if (!P) return fail(PKVMLA_EINVAL, "null plan");
+  if (polls < 0) return fail(PKVMLA_EINVAL, "wait limit must be >= 0");
+  P->wait_limit = polls;
+  return ok();
+}
 
 int pkvmla_plan_set_timing(pkvmla_plan P, int32_t enable) {
   if (!P) return fail(PKVMLA_EINVAL, "null plan");

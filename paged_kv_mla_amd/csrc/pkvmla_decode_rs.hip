@@ -117,20 +117,34 @@ constexpr int kRsLds = kDoneOff + 4 * kRsPvWaves;
 static_assert(kRsLds <= 160 * 1024, "LDS budget");
 
 // Bounded wait until each of the n LDS counters c[0..n-1] holds at least
-// target.  A wave gives up after kSpinLimit polls (about 0.1 s), so a
-// protocol error shows as wrong results, never as a workgroup that does not
-// end.
-constexpr int kSpinLimit = 1 << 20;
+// target; false when the wave gave up after `limit` polls (the plan's wait
+// limit, 2^20 by default: about 0.1 s).  A QK or PV wave whose wait gave up
+// writes NaN for every unit it finishes afterwards, so a protocol error ends
+// the workgroup and shows as non-finite results, never as a workgroup that
+// does not end or as plausible wrong values (a stalled copy wave stalls the
+// QK and PV waves' waits in turn).
 template <int N>
-__device__ __forceinline__ void wait_counters(const volatile LDS_AS int* c, int target) {
-  for (int it = 0; it < kSpinLimit; ++it) {
-    int m = c[0];
+__device__ __forceinline__ bool counters_reach(const volatile LDS_AS int* c, int target) {
+  int m = c[0];
 #pragma unroll
-    for (int j = 1; j < N; ++j) m = min(m, c[j]);
-    if (__builtin_amdgcn_readfirstlane(m) >= target) break;
-    __builtin_amdgcn_s_sleep(1);
+  for (int j = 1; j < N; ++j) m = min(m, c[j]);
+  return __builtin_amdgcn_readfirstlane(m) >= target;
+}
+template <int N>
+__device__ __forceinline__ bool wait_counters(const volatile LDS_AS int* c, int target, int limit) {
+  // the first poll straight-line (it usually succeeds), the loop only after it
+  bool ok = limit > 0 && counters_reach<N>(c, target);
+  if (!ok) {
+    for (int it = 1; it < limit; ++it) {
+      __builtin_amdgcn_s_sleep(1);
+      if (counters_reach<N>(c, target)) {
+        ok = true;
+        break;
+      }
+    }
   }
   asm volatile("" ::: "memory");  // no LDS access moves above the wait
+  return ok;
 }
 // Publishes v in the wave's counter once all of the wave's LDS accesses
 // issued so far have completed (their data written, or read out).
@@ -194,7 +208,7 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
                      const int32_t* __restrict__ seq_indices_g, int H, int n_hg, int n_lanes,
                      int log2_ps, float sm_scale, float C, float thr, int cs_arg,
                      int ks_arg, unsigned long long* stamps, float v_scale, float kpe_ratio,
-                     int qo_log2h) {
+                     int qo_log2h, int wait_limit) {
   const int cs = PACKED ? kCkvDim * 2 : cs_arg;
   const int ks = PACKED ? kKpeDim * 2 : ks_arg;
   const idx_ptr wg_indptr = (idx_ptr)wg_indptr_g;
@@ -234,6 +248,7 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
   volatile LDS_AS int* landed = (volatile LDS_AS int*)(smem + kLandedOff);
   volatile LDS_AS int* ready = (volatile LDS_AS int*)(smem + kReadyOff);
   volatile LDS_AS int* done = (volatile LDS_AS int*)(smem + kDoneOff);
+  bool waits_ok = true;  // (counters) every wait of this wave so far succeeded
   // Tiles of the workgroup (with barriers every role runs the same number).
   int G = 0;
   for (int u = u_begin; u < u_end; ++u) {
@@ -287,7 +302,8 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
       if (i < G) {
         // tile i has landed (usually known from the read during the last
         // tile's softmax)
-        if (FLAGS && land_seen < i + 1) wait_counters<kRsCopyWaves>(landed, i + 1);
+        if (FLAGS && land_seen < i + 1)
+          waits_ok &= wait_counters<kRsCopyWaves>(landed, i + 1, wait_limit);
         const int stage = i % kRsRing;
         const int par = i & 1;
         if (cq.tile == 0 && !cq.cont) {
@@ -386,7 +402,7 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
         l_run = l_run * alpha + ps;
         // the exchange buffers of this parity held tile i-2's: the PV waves
         // have read them once they have finished tile i-2
-        if (FLAGS && i >= 2) wait_counters<kRsPvWaves>(done, i - 1);
+        if (FLAGS && i >= 2) waits_ok &= wait_counters<kRsPvWaves>(done, i - 1, wait_limit);
         *(LDS_AS bf16x8_t*)(smem + kXpOff + (par * kRsMaxHB + r) * 1024 + lane * 16) = pT;
         if (g == 0) *(LDS_AS float*)(smem + kXaOff + (par * 64 + li * 4 + r) * 4) = alpha;
         if (cq.tile == cq.ntiles - 1 && cq.slot != kChainNext) {
@@ -394,7 +410,8 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
           float l = l_run;
           l += __shfl_xor(l, 16);
           l += __shfl_xor(l, 32);
-          const float lse = m_run * sm_scale + __builtin_amdgcn_logf(l) * 0.69314718055994531f;
+          float lse = m_run * sm_scale + __builtin_amdgcn_logf(l) * 0.69314718055994531f;
+          if (FLAGS && !waits_ok) lse = __builtin_nanf("");
           if (g == 0) {
             *(LDS_AS float*)(smem + kXlOff + (par * 64 + li * 4 + r) * 4) = l;
             if (ROWS) {
@@ -462,7 +479,7 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
     };
     // the first dim block's V fragments of the next tile, read before the
     // barrier that starts its iteration (one block: the register budget)
-    if (FLAGS) wait_counters<kRsCopyWaves>(landed, 1);
+    if (FLAGS) waits_ok &= wait_counters<kRsCopyWaves>(landed, 1, wait_limit);
     bf16x4_t vn0 = ldV(0, 0, 0), vn1 = ldV(0, 0, 1);
 
     // ---- iteration t+1: PV of tile t, copies of tile t+3 ----
@@ -472,8 +489,8 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
       if (FLAGS) {
         // P^T of tile t is published, and tile t+1 has landed (its first V
         // block is read after this tile's MFMAs; the QK waves need it now)
-        wait_counters<HB>(ready, t + 1);
-        if (t + 1 < G) wait_counters<kRsCopyWaves>(landed, t + 2);
+        waits_ok &= wait_counters<HB>(ready, t + 1, wait_limit);
+        if (t + 1 < G) waits_ok &= wait_counters<kRsCopyWaves>(landed, t + 2, wait_limit);
       }
       const int lane = lane_id_fresh();
       bf16x8_t pB[HB];
@@ -536,6 +553,10 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
           // (row blocks: a row that saw no token of this piece has O = 0 and
           // l = 0; its state is (0, -inf), weight 0 in the merge)
           if (ROWS) linv[hb] = l4[hb] > 0.f ? linv[hb] : 0.f;
+        }
+        if (FLAGS && !waits_ok) {
+#pragma unroll
+          for (int hb = 0; hb < HB; ++hb) linv[hb] = __builtin_nanf("");
         }
         // Lane (g, li) holds dims r*128 + db*16 + g*4 .. +3 of head hb*16 + li.
         // For a pair of dim blocks (2dp, 2dp+1) one row swap (rows 0<->1 and
@@ -697,7 +718,7 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
       // t-4 (the QK waves finished it before), and the wave then waits, with
       // an exact vmcnt, for its share of tile t-1: at most two tiles in flight.
       for (int t = 1; t < G; ++t) {
-        if (t >= kRsRing) wait_counters<kRsPvWaves>(done, t - kRsRing + 1);
+        if (t >= kRsRing) wait_counters<kRsPvWaves>(done, t - kRsRing + 1, wait_limit);
         issue_tile();
         wait_vm_le(vmc - vmc_of(t - 1));
         asm volatile("" ::: "memory");
@@ -741,7 +762,7 @@ bool launch_decode_rs(const DecodeParams& p, hipStream_t stream, hipError_t* err
   p.q_nope, p.q_pe, p.ckv, p.kpe, p.out, p.lse, p.part_o, p.part_lse, p.wg_indptr, p.units, \
       p.seq_indices, p.num_heads, p.head_groups, p.n_lanes, p.log2_ps, p.sm_scale,     \
       p.score_log2, p.rescale_thr, p.ckv_stride, p.kpe_stride, p.stamps, p.v_scale,    \
-      p.kpe_ratio, p.qo_log2h
+      p.kpe_ratio, p.qo_log2h, p.wait_limit
 #define PKVMLA_RS_LAUNCH3(HBV, PK, RB, F8)                                                     \
   if (big) mla_decode_rs_kernel<true, HBV, PK, RB, F8><<<grid, block, 0, stream>>>(PKVMLA_RS_ARGS); \
   else mla_decode_rs_kernel<false, HBV, PK, RB, F8><<<grid, block, 0, stream>>>(PKVMLA_RS_ARGS);

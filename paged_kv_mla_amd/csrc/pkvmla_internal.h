@@ -66,6 +66,7 @@ struct DecodeParams {
   int32_t qo_log2h;          // row blocks of several query tokens: log2 H (query token
                              // t = row >> qo_log2h sees positions below t + the unit's
                              // second field); -1: no causal bound
+  int32_t wait_limit;        // polls before a progress-counter wait gives up
 };
 
 struct MergeParams {

@@ -426,6 +426,32 @@ def test_progress_counters_short_workgroups(H):
     assert set(range(1, 9)) <= seen, sorted(seen)
 
 
+@pytest.mark.parametrize("H", [16, 32, 128])
+def test_wait_limit_failure_path(H):
+    """The failure path of the progress counters, forced from the host: with a
+    wait limit of 0 polls every counter wait gives up at once and marks its
+    workgroup, so every output of the 16- and 32-head kernels reads NaN (all
+    accesses stay in bounds and the launch ends normally); the 128-head kernel
+    keeps its barrier and ignores the limit; at the default limit the results
+    match the oracle again."""
+    inp = small(4100 + H, [1, 40, 300, 900, 2000, 77], H=H, ps=16)
+    plan = pk.plan_for(inp)
+    dev = Dev(inp)
+    with pytest.raises(pk.PkvmlaError):
+        plan.set_wait_limit(-1)
+    plan.set_wait_limit(0)
+    note(f"wait limit 0, H{H}")
+    out, lse = run_gpu(plan, dev)
+    ref_o, ref_l = oracle_flat(inp)
+    if H < 64:
+        assert bool(torch.isnan(out.float()).all()) and bool(torch.isnan(lse).all())
+    else:
+        compare(out, lse, ref_o, ref_l, name=f"wait limit 0, H{H}")
+    plan.set_wait_limit()
+    out, lse = run_gpu(plan, dev)
+    compare(out, lse, ref_o, ref_l, name=f"default wait limit, H{H}")
+
+
 # ------------------------------------- several new query tokens per request
 QO_CASES = {
     "h16_qo2_ps16": lambda: make_qo("q1", 131, 5, 16, 16, [2, 17, 64, 200, 777], [2] * 5),
