@@ -61,6 +61,7 @@ typedef enum {
 typedef struct pkvmla_plan_s* pkvmla_plan;
 
 /* Build a flat decode plan.
+ *   batch >= 1 (an empty batch is PKVMLA_EINVAL: a caller skips the run).
  *   kv_indptr  host int32[batch+1]: kv_indptr[0] == 0, non-decreasing.
  *   kv_indices host int32[kv_indptr[batch]]: page ids in [0, num_pages).
  *   kv_lens    host int32[batch]: 1 <= kv_lens[b] <= pages(b) * page_size.

@@ -150,6 +150,7 @@ def _flat_args(**kw):
     (dict(kv_indptr=[1, 2, 3]), pk.EINVAL),                 # indptr[0] != 0
     (dict(kv_indptr=[0, 3, 2]), pk.EINVAL),                 # non-monotone
     (dict(kv_lens=[0, 5]), pk.EINVAL),                      # empty request
+    (dict(kv_indptr=[0], kv_indices=[], kv_lens=[]), pk.EINVAL),  # empty batch
     (dict(kv_lens=[33, 5]), pk.EINVAL),                     # more tokens than 2 pages hold
     (dict(kv_indices=[0, 9, 2]), pk.EINVAL),                # page id outside the pool
     (dict(kv_indices=[0, -1, 2]), pk.EINVAL),
