@@ -206,8 +206,22 @@ int upload_tables(pkvmla_plan_s* P, const pkvmla::Schedule& sched,
                   const std::vector<int32_t>& seq_indices, hipStream_t stream,
                   const pkvmla::RowSchedule* sched0 = nullptr,
                   const std::vector<int32_t>* slot_list = nullptr) {
-  std::vector<int32_t> host(P->table_ints, 0);
+  // every table must fit its region of the allocation: a schedule beyond the
+  // plan's capacities is an error, never an overflow into the next table
   const std::vector<int32_t>& wg = sched.wg_indptr;
+  if ((int64_t)wg.size() > (int64_t)P->cap_lanes + 1 ||
+      (int64_t)sched.units.size() > (int64_t)P->cap_units * pkvmla::kUnitRecordInts ||
+      (int64_t)sched.merges.size() > (int64_t)P->cap_merges * pkvmla::kMergeRecordInts ||
+      sched.n_slots > P->cap_slots ||
+      (int64_t)seq_indptr.size() > (int64_t)(P->off_sl - P->off_sip) ||
+      (int64_t)seq_lens.size() > (int64_t)(P->off_si - P->off_sl) ||
+      (int64_t)seq_indices.size() > (int64_t)(P->table_ints - P->off_si) ||
+      (sched0 && ((int64_t)sched0->wg_indptr.size() > (int64_t)P->cap_lanes0 + 1 ||
+                  (int64_t)sched0->units.size() > (int64_t)P->cap_units0 * pkvmla::kUnitRecordInts ||
+                  sched0->n_slots > P->cap_slots ||
+                  (int64_t)slot_list->size() > (int64_t)P->cap_list)))
+    return fail(PKVMLA_EUNSUPPORTED, "schedule exceeds the plan's tables");
+  std::vector<int32_t> host(P->table_ints, 0);
   for (int32_t l = 0; l <= P->cap_lanes; ++l)
     host[P->off_wg + l] = l < (int32_t)wg.size() ? wg[l] : wg.back();
   std::copy(sched.units.begin(), sched.units.end(), host.begin() + P->off_units);

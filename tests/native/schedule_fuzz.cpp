@@ -124,7 +124,14 @@ static void cascade_case(std::mt19937& rng) {
   RowSchedule c;
   std::vector<int32_t> cm, cl;
   CHECK(build_chain_schedule(gi.data(), G, pl.data(), kl.data(), B, W, tile, &c, &cm, &cl));
-  std::vector<int> pre(B, 0), suf(B, 0), outs(B, 0);
+  // the plan's table bounds: a unit per prefix piece (at most max(W, B)) and
+  // per suffix (B); as many slots at most
+  const int64_t cap = std::max<int64_t>(W, B) + B;
+  CHECK((int64_t)(c.units.size() / kUnitRecordInts) <= cap && c.n_slots <= cap &&
+        (int64_t)cl.size() <= cap);
+  std::vector<int> pre(B, 0), outs(B, 0);
+  std::vector<std::vector<char>> sufcov(B);
+  for (int b = 0; b < B; ++b) sufcov[b].assign((size_t)std::max(kl[b], 0), 0);
   std::vector<int> seen(c.n_slots, 0);
   for (size_t i = 0; i < c.units.size(); i += kUnitRecordInts) {
     const int32_t* u = &c.units[i];
@@ -135,11 +142,15 @@ static void cascade_case(std::mt19937& rng) {
       if (u[4] == kChainNextSlot) {
         CHECK(i + kUnitRecordInts < c.units.size());
         const int32_t* n = u + kUnitRecordInts;
-        CHECK(n[0] == b && n[1] == G + b && n[2] == 0 && n[3] == kl[b]);
+        CHECK(n[0] == b && n[1] == G + b && n[2] == 0 && n[3] > 0 && n[3] <= kl[b]);
       }
     } else {
-      CHECK(u[1] == G + b && u[2] == 0 && u[3] == kl[b]);
-      suf[b] += u[3];
+      // a request's suffix, each token once
+      CHECK(u[1] == G + b && u[2] % tile == 0 && u[2] < u[3] && u[3] <= kl[b]);
+      for (int t = u[2]; t < u[3]; ++t) {
+        CHECK(!sufcov[b][t]);
+        sufcov[b][t] = 1;
+      }
     }
     if (u[4] == -1) ++outs[b];
     if (u[4] >= 0) {
@@ -150,7 +161,8 @@ static void cascade_case(std::mt19937& rng) {
   for (int b = 0; b < B; ++b) {
     int g = 0;
     while (gi[g + 1] <= b) ++g;
-    CHECK(pre[b] == pl[g] && suf[b] == kl[b]);
+    CHECK(pre[b] == pl[g]);
+    for (char x : sufcov[b]) CHECK(x);
   }
   std::vector<int> merged(B, 0);
   for (size_t i = 0; i < cm.size(); i += 4) merged[cm[i]] = 1;
