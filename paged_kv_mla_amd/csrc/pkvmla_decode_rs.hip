@@ -211,8 +211,13 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
                      int qo_log2h, int wait_limit) {
   const int cs = PACKED ? kCkvDim * 2 : cs_arg;
   const int ks = PACKED ? kKpeDim * 2 : ks_arg;
-  const idx_ptr wg_indptr = (idx_ptr)wg_indptr_g;
-  const idx_ptr units = (idx_ptr)units_g;
+  // the two table pointers are read from the kernel arguments up front, with
+  // the others, not in a dependent round trip just before their first use
+  const int32_t* wgp = wg_indptr_g;
+  const int32_t* unp = units_g;
+  asm volatile("" : "+s"(wgp), "+s"(unp));
+  const idx_ptr wg_indptr = (idx_ptr)wgp;
+  const idx_ptr units = (idx_ptr)unp;
   const idx_ptr seq_indices = (idx_ptr)seq_indices_g;
   __shared__ __attribute__((aligned(1024))) char smem_raw[kRsLds];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
@@ -250,8 +255,25 @@ mla_decode_rs_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __rest
   volatile LDS_AS int* done = (volatile LDS_AS int*)(smem + kDoneOff);
   bool waits_ok = true;  // (counters) every wait of this wave so far succeeded
   // Tiles of the workgroup (with barriers every role runs the same number).
+  // The first four units' bounds are loaded together (indices clamped to the
+  // last unit, so every load is in the table; the empty asm keeps the compiler
+  // from sinking each load into its own conditional), one round trip where a
+  // loop would take one per unit.
   int G = 0;
-  for (int u = u_begin; u < u_end; ++u) {
+  {
+    int kb[4], ke[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      idx_ptr rec = units + (size_t)min(u_begin + k, u_end - 1) * kUnitInts;
+      kb[k] = rec[2];
+      ke[k] = rec[3];
+    }
+    asm volatile("" : "+s"(kb[0]), "+s"(ke[0]), "+s"(kb[1]), "+s"(ke[1]), "+s"(kb[2]), "+s"(ke[2]),
+                 "+s"(kb[3]), "+s"(ke[3]));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) G += u_begin + k < u_end ? (ke[k] - kb[k] + kTile - 1) / kTile : 0;
+  }
+  for (int u = u_begin + 4; u < u_end; ++u) {
     idx_ptr rec = units + (size_t)u * kUnitInts;
     G += (rec[3] - rec[2] + kTile - 1) / kTile;
   }

@@ -28,15 +28,20 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(MergeParams p) {
   // timing runs: the block's start and end on the real-time counter
   const uint32_t sb = blockIdx.y * gridDim.x + blockIdx.x;
   if (p.stamps && threadIdx.x == 0) p.stamps[2 * sb] = __builtin_amdgcn_s_memrealtime();
-  const int32_t* mr = p.merges + (size_t)blockIdx.x * kMergeInts;
-  const int b = mr[0], s0 = mr[1], n = mr[2];
+  // The record and the slot list are read-only tables, read with scalar
+  // loads: the slot numbers then sit in scalar registers, and no wait for a
+  // vector load of the list stands between a chunk's partial-state loads
+  // (which would take a round trip per state).  The record is one load.
+  const idx_ptr mr = (idx_ptr)p.merges + (size_t)blockIdx.x * kMergeInts;
+  int b = mr[0], s0 = mr[1], n = mr[2], kind = mr[3];
+  asm volatile("" : "+s"(b), "+s"(s0), "+s"(n), "+s"(kind));
   if (n <= 0) {  // an unused record slot of a plan with fixed launches
     if (p.stamps && threadIdx.x == 0) p.stamps[2 * sb + 1] = __builtin_amdgcn_s_memrealtime();
     return;
   }
   // kind 1: the request's slots are listed (a cascade plan's prefix states
   // sit in its level-0 row blocks' slots)
-  const int32_t* list = mr[3] == 1 ? p.slot_list + s0 : nullptr;
+  const idx_ptr list = kind == 1 ? (idx_ptr)p.slot_list + s0 : nullptr;
   const int H = p.num_heads;
   const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
   const int d0 = (threadIdx.x & 63) * 8;
@@ -48,10 +53,17 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(MergeParams p) {
     // and carry weight 0 (a select, so they add exactly nothing)
     uint4 x[kChunk];
     float lv[kChunk];
+    int slot[kChunk];
+    if (list) {  // one uniform branch, so the chunk's list loads go out together
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) slot[j] = list[min(i0 + j, n - 1)];
+    } else {
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) slot[j] = s0 + min(i0 + j, n - 1);
+    }
 #pragma unroll
     for (int j = 0; j < kChunk; ++j) {
-      const int e = min(i0 + j, n - 1);
-      const size_t base = (size_t)(list ? list[e] : s0 + e) * H + h;
+      const size_t base = (size_t)slot[j] * H + h;
       lv[j] = p.part_lse[base];
       x[j] = *reinterpret_cast<const uint4*>(p.part_o + base * kCkvDim + d0);
     }
