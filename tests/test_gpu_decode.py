@@ -380,18 +380,24 @@ def test_one_request_over_every_lane():
     compare(out, lse, ref_o, ref_l, name="one request")
 
 
-def test_many_tiny_requests():
-    """2048 requests of 1..8 tokens at page size 1: many units per lane, no
-    splits, every request written by the decode kernel directly."""
+@pytest.mark.parametrize("H", [16, 128])
+def test_many_tiny_requests(H):
+    """2048 requests of 1..8 tokens at page size 1: many units per lane (more
+    than the four whose bounds the kernel's prologue loads together, so the
+    tile count also takes its per-unit loop), no splits, every request
+    written by the decode kernel directly."""
     rng = np.random.default_rng(98)
     lens = rng.integers(1, 9, size=2048).tolist()
-    inp = small(98, lens, H=16, ps=1)
+    inp = small(98, lens, H=H, ps=1)
     ex = pk.plan_for(inp).export()
-    note(f"2048 tiny requests: {ex.units.shape[0]} units on {ex.grid} lanes")
+    per_lane = np.diff(ex.wg_indptr)
+    note(f"2048 tiny requests H{H}: {ex.units.shape[0]} units on {ex.grid} lanes, "
+         f"up to {per_lane.max()} per lane")
     assert ex.merges.shape[0] == 0
+    assert per_lane.max() > 4
     out, lse = run_gpu(pk.plan_for(inp), Dev(inp))
     ref_o, ref_l = oracle_flat(inp)
-    compare(out, lse, ref_o, ref_l, name="tiny requests")
+    compare(out, lse, ref_o, ref_l, name=f"tiny requests H{H}")
 
 
 def lane_tiles(ex):
